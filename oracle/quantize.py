@@ -1,0 +1,297 @@
+"""CPU oracle for the quantize-on-append step: group statistics, outlier isolation, quantizer
+fit, encoding and packing of one KV row at a time.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
+
+Pages cited (titles abridged):
+  [P1] "Hierarchical Token Routing and Sub-2-Bit Non-Linear KV Compression ..."
+       section "Paradigm 2: Sub-2-Bit Non-Linear KV-Cache Quantization": subsection
+       "1. Dynamic Outlier Isolation", subsection "2. Centroid Vector Quantization for
+       Residuals" and the ``Sub2BitQuantizedKVCache.compress_kv_head`` listing that follows.
+  [P3] "Sub-5ms MoE Inference: Sub-Byte KV Quantization and Expert Pipelining at Scale",
+       section "Sub-Byte KV-Cache Quantization" (fp16 outlier tensor, 2-bit packing).
+  [P4] "The Sub-10ms Barrier: Fusing Sparse MoE Routing with FP4 KV-Cache Quantization",
+       section "2. FP4/INT4 KV-Cache Quantization" (the equations Q = Round(Clamp(X/Scale +
+       ZeroPoint, Min, Max)) and S = (max - min)/(2^b - 1), groups of 32 or 64 along the head
+       dimension, E2M1).
+
+Readings taken where the pages are silent (each is listed in the design doc):
+  * every quantity that decides a code is computed in float32 with IEEE round-to-nearest-even,
+    no fused multiply-add, correctly rounded division, subnormals kept;
+  * every sum over a group uses one fixed pairwise tree (``tree_sum``);
+  * statistics are per (row, group of ``g`` channels); the spread is the unbiased standard
+    deviation (the listing's ``std``), the comparison is strict, one pass, and the statistics
+    include the outliers themselves (the listing computes mean/std before masking);
+  * the quantizer is fitted on the non-outliers only ([P1] "remaining non-outlier" values);
+    an outlier position is encoded as the code of 0.0 (the listing zero-fills those slots
+    before quantizing them);
+  * outlier records keep the ORIGINAL value rounded to the outlier dtype (the listing casts
+    ``kv_tensor[outlier_mask]``);
+  * 2-bit centroids: 4 per group, seeded at the midpoints of the four quartile bins of the
+    sorted non-outliers, then a fixed number of Lloyd (k-means) iterations; nearest centroid by
+    absolute difference with the first index on ties (the listing's ``argmin``); an empty
+    cluster keeps its centroid; centroids stored as fp16;
+  * INT4: offset form of the equation: zero = fp16(min), code = Round(Clamp((x - zero)/S, 0,
+    15)), which is the page's ZeroPoint = -zero/S written without a quantized-unit zero;
+  * FP4: E4M3 block scale = absmax/6 (6 is the largest E2M1 magnitude);
+  * FP8 tier: per-row scale absmax/448 in fp32, no outliers.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+from . import formats as F
+
+F32 = np.float32
+
+FORMATS = ("int4", "fp4", "c2", "fp8row")
+OUTLIER_DTYPES = ("none", "fp16", "e4m3")
+CODE_BITS = {"int4": 4, "fp4": 4, "c2": 2, "fp8row": 8}
+
+
+@dataclass(frozen=True)
+class QuantSpec:
+    fmt: str            # one of FORMATS
+    group: int          # channels per group (ignored by fp8row)
+    outlier: str        # one of OUTLIER_DTYPES
+    sigma: float = 3.0  # outlier threshold tau, in standard deviations
+    lloyd_iters: int = 8
+
+    def __post_init__(self):
+        assert self.fmt in FORMATS and self.outlier in OUTLIER_DTYPES
+        if self.fmt == "fp8row":
+            assert self.outlier == "none", "the FP8 tier keeps no outliers"
+
+
+def meta_bytes_per_row(spec: QuantSpec, D: int) -> int:
+    if spec.fmt == "fp8row":
+        return 4
+    ng = D // spec.group
+    return ng * {"int4": 4, "fp4": 1, "c2": 8}[spec.fmt]
+
+
+def code_bytes_per_row(spec: QuantSpec, D: int) -> int:
+    return D * CODE_BITS[spec.fmt] // 8
+
+
+# ----------------------------------------------------------------------------- reductions
+def tree_sum(a: np.ndarray) -> np.ndarray:
+    """Fixed pairwise tree over the last axis (length a power of two): for w = n/2, n/4, ..., 1
+    set a[i] <- fl32(a[i] + a[i + w]) for i < w; the result is a[0]."""
+    a = np.asarray(a, dtype=F32)
+    n = a.shape[-1]
+    assert n & (n - 1) == 0
+    w = n // 2
+    while w >= 1:
+        a = (a[..., :w] + a[..., w:2 * w]).astype(F32)
+        w //= 2
+    return a[..., 0]
+
+
+# ----------------------------------------------------------------------------- outliers
+def outlier_mask(xg: np.ndarray, sigma: float) -> np.ndarray:
+    """[P1] "1. Dynamic Outlier Isolation" and the listing's mask: |x - mean| > tau * std, with
+    mean and unbiased std over the g channels of the group.  Evaluated without sqrt or division:
+    x_i is an outlier iff fl32(e_i * (g-1)) > fl32(fl32(tau*tau) * Q2), where d_i = x_i - mean,
+    e_i = d_i^2 and Q2 = sum of e over the group."""
+    g = xg.shape[-1]
+    mean = (tree_sum(xg) * F32(1.0 / g)).astype(F32)  # 1/g is a power of two: exact
+    d = (xg - mean[..., None]).astype(F32)
+    e = (d * d).astype(F32)
+    q2 = tree_sum(e)
+    tau2 = (F32(sigma) * F32(sigma)).astype(F32)
+    lhs = (e * F32(g - 1)).astype(F32)
+    rhs = (tau2 * q2).astype(F32)
+    return lhs > rhs[..., None]
+
+
+# ----------------------------------------------------------------------------- fits
+def _fit_int4(xg, keep):
+    """[P4] S = (max - min)/(2^b - 1) with b = 4 over the non-outliers; fp16 scale and zero."""
+    mn = np.min(np.where(keep, xg, np.inf), axis=-1).astype(F32)
+    mx = np.max(np.where(keep, xg, -np.inf), axis=-1).astype(F32)
+    s = ((mx - mn).astype(F32) / F32(15.0)).astype(F32)
+    s_h = F.fp16_round(s)
+    z_h = F.fp16_round(mn)
+    xx = np.where(keep, xg, F32(0.0)).astype(F32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        y = ((xx - z_h[..., None]).astype(F32) / s_h[..., None]).astype(F32)
+    q = np.rint(np.clip(y, F32(0.0), F32(15.0)))
+    q = np.where(s_h[..., None] > 0, q, 0).astype(np.uint8)
+    meta = np.stack([F.fp16_bits(s_h), F.fp16_bits(z_h)], axis=-1)  # [..., ng, 2] uint16
+    return q, meta.view(np.uint8).reshape(*xg.shape[:-2], -1)
+
+
+def _fit_fp4(xg, keep):
+    """E2M1 codes with an E4M3 block scale absmax/6 over the non-outliers."""
+    a = np.max(np.where(keep, np.abs(xg), F32(0.0)), axis=-1).astype(F32)
+    s8 = F.e4m3_encode((a / F32(6.0)).astype(F32))
+    s8v = F.e4m3_decode(s8).astype(F32)  # exact
+    xx = np.where(keep, xg, F32(0.0)).astype(F32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        y = (xx / s8v[..., None]).astype(F32)
+    y = np.where(s8v[..., None] > 0, y, F32(0.0))
+    codes = F.e2m1_encode(y)
+    codes = np.where(s8v[..., None] > 0, codes, 0).astype(np.uint8)
+    return codes, s8.reshape(*xg.shape[:-2], -1)
+
+
+def _nearest(x, c):
+    """argmin_j fl32(|x - c_j|), first index on ties ([P1] listing: distances.argmin)."""
+    dist = np.abs((x[..., None] - c[..., None, :]).astype(F32))
+    return np.argmin(dist, axis=-1)
+
+
+def _fit_c2(xg, keep, iters):
+    """[P1] "2. Centroid Vector Quantization for Residuals": a 4-centroid codebook per group
+    fitted by k-means (Lloyd) on the non-outliers."""
+    g = xg.shape[-1]
+    lead = xg.shape[:-1]
+    flat_x = xg.reshape(-1, g)
+    flat_k = keep.reshape(-1, g)
+    n = flat_k.sum(axis=-1)
+    v = np.sort(np.where(flat_k, flat_x, np.inf), axis=-1)
+    j = np.arange(4)
+    seed_idx = ((2 * j[None, :] + 1) * n[:, None]) // 8
+    c = np.take_along_axis(v, seed_idx, axis=-1).astype(F32)  # [G, 4]
+    for _ in range(iters):
+        a = _nearest(flat_x, c)
+        new_c = c.copy()
+        for k in range(4):
+            member = flat_k & (a == k)
+            cnt = member.sum(axis=-1)
+            ssum = tree_sum(np.where(member, flat_x, F32(0.0)).astype(F32))
+            upd = cnt > 0
+            new_c[upd, k] = (ssum[upd] / cnt[upd].astype(F32)).astype(F32)
+        c = new_c
+    c_h = F.fp16_round(c)
+    xx = np.where(flat_k, flat_x, F32(0.0)).astype(F32)
+    codes = _nearest(xx, c_h).astype(np.uint8).reshape(*lead, g)
+    meta = F.fp16_bits(c_h).reshape(*lead[:-1], -1, 4)  # [..., ng, 4] uint16
+    return codes, meta.view(np.uint8).reshape(*lead[:-1], -1)
+
+
+def _fit_fp8row(x):
+    """FP8 tier ([P2] "Tier 1: High-Precision FP8"): per-row scale absmax/448 (1 if the row is
+    all zero), codes = E4M3(x / scale)."""
+    a = np.max(np.abs(x), axis=-1).astype(F32)
+    s = np.where(a > 0, (a / F32(F.E4M3_MAX)).astype(F32), F32(1.0)).astype(F32)
+    codes = F.e4m3_encode((x / s[..., None]).astype(F32))
+    return codes, s.view(np.uint8).reshape(*x.shape[:-1], 4)
+
+
+# ----------------------------------------------------------------------------- packing
+def pack_codes(codes: np.ndarray, bits: int) -> np.ndarray:
+    """LSB-first packing along the channel axis: a 2-bit byte k holds channels 4k..4k+3 with
+    channel 4k+r in bits 2r..2r+1; a 4-bit byte k holds channel 2k in bits 0-3 and 2k+1 in
+    bits 4-7; 8-bit codes are stored as they are."""
+    c = np.asarray(codes, dtype=np.uint8)
+    if bits == 8:
+        return c.copy()
+    per = 8 // bits
+    c = c.reshape(*c.shape[:-1], -1, per).astype(np.uint16)
+    out = np.zeros(c.shape[:-1], dtype=np.uint16)
+    for r in range(per):
+        out |= c[..., r] << (bits * r)
+    return out.astype(np.uint8)
+
+
+def unpack_codes(packed: np.ndarray, bits: int, D: int) -> np.ndarray:
+    p = np.asarray(packed, dtype=np.uint8)
+    if bits == 8:
+        return p.copy()
+    per = 8 // bits
+    mask = (1 << bits) - 1
+    parts = [(p >> (bits * r)) & mask for r in range(per)]
+    return np.stack(parts, axis=-1).reshape(*p.shape[:-1], D).astype(np.uint8)
+
+
+# ----------------------------------------------------------------------------- rows
+@dataclass
+class QuantRows:
+    codes: np.ndarray      # [R, D] uint8, one logical code per element
+    packed: np.ndarray     # [R, code_bytes] uint8
+    meta: np.ndarray       # [R, meta_bytes] uint8
+    mask: np.ndarray       # [R, D] bool, outlier positions
+    outlier_bits: np.ndarray  # [R, D] uint16: fp16 bits or E4M3 code of the original value
+
+
+def quantize_rows(x: np.ndarray, spec: QuantSpec) -> QuantRows:
+    """Quantize rows x [R, D] (float32) independently (O1-O7)."""
+    x = np.asarray(x, dtype=F32)
+    if not np.all(np.isfinite(x)):
+        raise ValueError("quantize_rows: non-finite input is rejected")
+    R, D = x.shape
+    if spec.fmt == "fp8row":
+        codes, meta = _fit_fp8row(x)
+        mask = np.zeros((R, D), dtype=bool)
+        obits = np.zeros((R, D), dtype=np.uint16)
+        return QuantRows(codes, pack_codes(codes, 8), meta, mask, obits)
+    g = spec.group
+    assert D % g == 0 and g & (g - 1) == 0
+    xg = x.reshape(R, D // g, g)
+    if spec.outlier == "none":
+        mask_g = np.zeros(xg.shape, dtype=bool)
+    else:
+        mask_g = outlier_mask(xg, spec.sigma)
+    keep = ~mask_g
+    if spec.fmt == "int4":
+        codes, meta = _fit_int4(xg, keep)
+    elif spec.fmt == "fp4":
+        codes, meta = _fit_fp4(xg, keep)
+    else:
+        codes, meta = _fit_c2(xg, keep, spec.lloyd_iters)
+    codes = codes.reshape(R, D)
+    mask = mask_g.reshape(R, D)
+    if spec.outlier == "fp16":
+        obits = F.fp16_bits(x)
+    elif spec.outlier == "e4m3":
+        obits = F.e4m3_encode(x).astype(np.uint16)
+    else:
+        obits = np.zeros((R, D), dtype=np.uint16)
+    obits = np.where(mask, obits, 0).astype(np.uint16)
+    return QuantRows(codes, pack_codes(codes, CODE_BITS[spec.fmt]), meta.reshape(R, -1), mask,
+                     obits)
+
+
+# ----------------------------------------------------------------------------- dequant
+def decode_outlier(bits: np.ndarray, outlier: str) -> np.ndarray:
+    if outlier == "fp16":
+        return F.fp16_from_bits(bits)
+    if outlier == "e4m3":
+        return F.e4m3_decode(np.asarray(bits).astype(np.uint8))
+    raise ValueError(outlier)
+
+
+def dequantize_codes(codes: np.ndarray, meta: np.ndarray, spec: QuantSpec) -> np.ndarray:
+    """Code + per-group metadata -> float64 values, before outlier patching (O8)."""
+    codes = np.asarray(codes, dtype=np.int64)
+    R, D = codes.shape
+    meta = np.ascontiguousarray(meta, dtype=np.uint8)
+    if spec.fmt == "fp8row":
+        s = meta.view(np.float32).reshape(R).astype(np.float64)
+        return F.e4m3_decode(codes.astype(np.uint8)) * s[:, None]
+    g = spec.group
+    ng = D // g
+    cg = codes.reshape(R, ng, g)
+    if spec.fmt == "int4":
+        sz = F.fp16_from_bits(meta.view(np.uint16).reshape(R, ng, 2))
+        out = cg * sz[..., 0:1] + sz[..., 1:2]
+    elif spec.fmt == "fp4":
+        s8 = F.e4m3_decode(meta.reshape(R, ng))
+        out = F.e2m1_decode(cg) * s8[..., None]
+    else:
+        cent = F.fp16_from_bits(meta.view(np.uint16).reshape(R, ng, 4))
+        out = np.take_along_axis(cent, cg, axis=-1)
+    return out.reshape(R, D)
+
+
+def dequantize_rows(q: QuantRows, spec: QuantSpec) -> np.ndarray:
+    """Dequantized rows with outlier positions overwritten by the stored outlier value."""
+    base = dequantize_codes(q.codes, q.meta, spec)
+    if spec.outlier == "none":
+        return base
+    return np.where(q.mask, decode_outlier(q.outlier_bits, spec.outlier), base)

@@ -1,0 +1,344 @@
+"""Pins for the oracle's quantizer: reduction tree structure, outlier predicate (closed-form rate,
+hard per-group cap, Samuelson bound, fp64 re-expression of the listing's rule, a constructed
+equality case), INT4 / FP4 / FP8 round-trip bounds and exact grids, 2-bit seeds, Lloyd against
+an independent float64 implementation, and brute-force optimal partitions."""
+
+import itertools
+
+import numpy as np
+import pytest
+from scipy import stats
+
+from oracle import formats as F
+from oracle import quantize as Q
+
+F32 = np.float32
+
+
+# ----------------------------------------------------------------------------- tree
+def test_tree_sum_pairs_across_halves():
+    # for w = 2 then 1: (a0 + a2) + (a1 + a3).  Adjacent pairing or a sequential sum gives 0 or 1.
+    a = np.array([1e8, 1.0, -1e8, 1.0], dtype=F32)
+    assert Q.tree_sum(a) == 2.0
+    assert ((F32(1e8) + F32(1.0)) + F32(-1e8)) + F32(1.0) == 1.0  # a sequential sum differs
+
+
+def test_tree_sum_exact_on_integers():
+    rng = np.random.default_rng(0)
+    for g in (32, 64, 128):
+        a = rng.integers(-1000, 1000, size=(50, g)).astype(F32)
+        assert np.array_equal(Q.tree_sum(a), a.astype(np.int64).sum(axis=1).astype(F32))
+
+
+# ----------------------------------------------------------------------------- outliers
+def _tail_prob(g, tau):
+    # studentized residual r = d / s (s unbiased): r^2 g / (g-1)^2 ~ Beta(1/2, (g-2)/2)
+    x = tau * tau * g / (g - 1) ** 2
+    return stats.beta.sf(x, 0.5, (g - 2) / 2)
+
+
+@pytest.mark.parametrize("g,tau", [(32, 3.0), (64, 3.0), (64, 2.5)])
+def test_outlier_rate_closed_form(g, tau):
+    rng = np.random.default_rng(10 + g)
+    x = rng.standard_normal((200000, g)).astype(F32)
+    rate = Q.outlier_mask(x, tau).mean()
+    p = _tail_prob(g, tau)
+    n = x.size
+    sd = np.sqrt(p * (1 - p) / n)
+    assert abs(rate - p) < 5 * sd, (rate, p)
+
+
+def test_outlier_closed_form_values_quoted():
+    # the survey's numbers for tau = 3 (sanity of the closed form itself)
+    assert abs(_tail_prob(32, 3.0) - 1.1837e-3) < 1e-6
+    assert abs(_tail_prob(64, 3.0) - 1.8992e-3) < 1e-6
+
+
+@pytest.mark.parametrize("g,tau,cap", [(32, 3.0, 3), (64, 3.0, 6), (32, 3.5, 2), (64, 3.5, 5)])
+def test_outlier_hard_cap(g, tau, cap):
+    # m outliers need m * tau^2 * Q2 / (g-1) < Q2, so m <= ceil((g-1)/tau^2) - 1
+    rng = np.random.default_rng(g)
+    x = rng.standard_normal((20000, g)).astype(F32)
+    # heavy tails and planted spikes push towards the cap
+    k = rng.integers(0, cap + 3, size=20000)
+    for i in range(20000):
+        pos = rng.choice(g, size=k[i], replace=False)
+        x[i, pos] += (rng.choice([-1, 1], size=k[i]) * rng.uniform(20, 200, size=k[i])).astype(F32)
+    cnt = Q.outlier_mask(x, tau).sum(axis=1)
+    assert cnt.max() <= cap
+    # a balanced pattern of m = 2*floor(cap/2) spikes +-A (mean 0) reaches m: (g-1) > tau^2 m
+    m = 2 * (cap // 2)
+    y = np.zeros((1, g), dtype=F32)
+    y[0, :m] = np.tile([50.0, -50.0], m // 2)
+    assert Q.outlier_mask(y, tau).sum() == m
+
+
+def test_samuelson_bound_and_constant_group():
+    rng = np.random.default_rng(5)
+    x = (rng.standard_t(1.5, size=(20000, 32)) * 10).astype(F32)
+    # max |x - mean| / s <= (g-1)/sqrt(g) = 5.48 for g = 32: tau = 5.6 can never flag
+    assert not Q.outlier_mask(x, 5.6).any()
+    assert Q.outlier_mask(x, 3.0).any()
+    assert not Q.outlier_mask(np.full((3, 64), 7.25, dtype=F32), 3.0).any()
+
+
+def test_outlier_rule_matches_fp64_listing_rule():
+    # the listing: mean over the head-group, unbiased std, strict |x - mean| > tau * std
+    rng = np.random.default_rng(6)
+    x = (rng.standard_normal((30000, 64)) * rng.lognormal(0, 1, (30000, 1))).astype(F32)
+    x[rng.random(x.shape) < 0.01] *= 9
+    got = Q.outlier_mask(x, 3.0)
+    xd = x.astype(np.float64)
+    mu = xd.mean(axis=1, keepdims=True)
+    sd = xd.std(axis=1, ddof=1, keepdims=True)
+    z = np.abs(xd - mu) / sd
+    ref = z > 3.0
+    clear = np.abs(z - 3.0) > 1e-5
+    assert np.array_equal(got[clear], ref[clear])
+    assert (~clear).mean() < 1e-3
+
+
+def test_outlier_strict_inequality_constructed_equality():
+    # g = 64, tau = 2: six +4, six -4, seven +2, seven -2, two +1, two -1, 34 zeros.
+    # mean 0, Q2 = 12*16 + 14*4 + 4 = 252, and for the +-4 entries 63 * 16 = 1008 = 4 * 252:
+    # exact equality, so the strict test flags nothing; tau = 1.99 flags the twelve +-4.
+    x = np.zeros((1, 64), dtype=F32)
+    vals = [4] * 6 + [-4] * 6 + [2] * 7 + [-2] * 7 + [1, 1, -1, -1]
+    x[0, :len(vals)] = vals
+    assert not Q.outlier_mask(x, 2.0).any()
+    assert Q.outlier_mask(x, 1.99).sum() == 12
+
+
+def test_outlier_mask_scale_invariance():
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((5000, 64)).astype(F32)
+    m = Q.outlier_mask(x, 3.0)
+    for k in (-3, 5):
+        assert np.array_equal(Q.outlier_mask((x * F32(2.0 ** k)).astype(F32), 3.0), m)
+
+
+# ----------------------------------------------------------------------------- INT4
+def test_int4_exact_on_grid():
+    rng = np.random.default_rng(8)
+    R = 500
+    z = F.fp16_round(rng.uniform(-5, 5, R).astype(F32))
+    s = F.fp16_round(rng.uniform(0.01, 0.5, R).astype(F32))
+    k = rng.integers(0, 16, size=(R, 128))
+    k[:, 0], k[:, 1] = 0, 15
+    for gi in range(4):
+        k[:, 32 * gi], k[:, 32 * gi + 1] = 0, 15
+    x = (z[:, None].astype(np.float64) + k * s[:, None].astype(np.float64)).astype(F32)
+    exact = x.astype(np.float64) == z[:, None] + k * s[:, None].astype(np.float64)
+    rows = exact.all(axis=1)
+    spec = Q.QuantSpec("int4", 32, "none")
+    q = Q.quantize_rows(x[rows], spec)
+    d = Q.dequantize_rows(q, spec)
+    # S = (max-min)/15 must come back exactly as s for grid data
+    assert np.array_equal(q.codes, k[rows].astype(np.uint8))
+    assert np.array_equal(d, x[rows].astype(np.float64))
+
+
+def test_int4_roundtrip_bound_and_monotone():
+    rng = np.random.default_rng(9)
+    spec = Q.QuantSpec("int4", 32, "fp16")
+    for off, sc in [(0, 1), (100, 0.3), (-1000, 30), (0, 1e-3)]:
+        x = (off + sc * rng.standard_normal((2000, 128))).astype(F32)
+        q = Q.quantize_rows(x, spec)
+        d = Q.dequantize_rows(q, spec)
+        xg = x.reshape(-1, 32).astype(np.float64)
+        keep = ~q.mask.reshape(-1, 32)
+        mn = np.where(keep, xg, np.inf).min(1)
+        mx = np.where(keep, xg, -np.inf).max(1)
+        sz = F.fp16_from_bits(q.meta.view(np.uint16).reshape(-1, 2))
+        s_exact = (mx - mn) / 15
+        bound = 0.5 * sz[:, 0] + 15 * np.abs(s_exact - sz[:, 0]) + np.abs(mn - sz[:, 1])
+        err = np.abs(d.reshape(-1, 32) - xg)
+        lim = bound[:, None] + 2.0 ** -20 * np.maximum(np.abs(xg), np.abs(sz[:, 1:2]))
+        assert np.all((err <= lim)[keep])
+        codes = q.codes.reshape(-1, 32).astype(int)
+        # codes are monotone in x within a group (non-outliers)
+        for i in range(0, len(xg), 97):
+            o = np.argsort(xg[i][keep[i]], kind="stable")
+            assert np.all(np.diff(codes[i][keep[i]][o]) >= 0)
+        # min -> 0 and max -> 15 wherever the fp16 rounding of zero and scale moves the ends by
+        # less than half a step
+        safe = (np.abs(mn - sz[:, 1]) + 15 * np.abs(s_exact - sz[:, 0])) < 0.45 * sz[:, 0]
+        assert safe.mean() > 0.5
+        cmax = np.where(keep, codes, -1).max(1)
+        cmin = np.where(keep, codes, 99).min(1)
+        assert np.all(cmax[safe] == 15) and np.all(cmin[safe] == 0)
+        # outlier values are the original values rounded to fp16
+        assert np.array_equal(d[q.mask], F.fp16_round(x[q.mask]).astype(np.float64))
+
+
+def test_int4_matches_pages_zero_point_form_fp64():
+    # Q = Round(Clamp(X/Scale + ZeroPoint, 0, 15)) with ZeroPoint = -zero/Scale, in fp64
+    rng = np.random.default_rng(10)
+    x = (rng.standard_normal((3000, 128)) * 2 + 1).astype(F32)
+    spec = Q.QuantSpec("int4", 32, "fp16")
+    q = Q.quantize_rows(x, spec)
+    sz = F.fp16_from_bits(q.meta.view(np.uint16).reshape(-1, 2))
+    xg = np.where(q.mask, 0, x).reshape(-1, 32).astype(np.float64)
+    y = xg / sz[:, :1] - sz[:, 1:] / sz[:, :1]
+    ref = np.rint(np.clip(y, 0, 15))
+    frac = np.abs(np.abs(y - np.floor(y)) - 0.5)
+    clear = frac > 1e-4
+    assert np.array_equal(q.codes.reshape(-1, 32)[clear], ref[clear])
+
+
+# ----------------------------------------------------------------------------- FP4
+def test_fp4_roundtrip_bound():
+    rng = np.random.default_rng(11)
+    spec = Q.QuantSpec("fp4", 32, "fp16")
+    x = (rng.standard_normal((4000, 128)) * rng.lognormal(0, 1, (4000, 1))).astype(F32)
+    q = Q.quantize_rows(x, spec)
+    d = Q.dequantize_rows(q, spec)
+    s8 = F.e4m3_decode(q.meta.reshape(-1))  # [R*4]
+    xg = x.reshape(-1, 32).astype(np.float64)
+    dg = d.reshape(-1, 32)
+    keep = ~q.mask.reshape(-1, 32)
+    y = np.abs(xg) / s8[:, None]
+    step = np.where(y <= 2, 0.25, np.where(y <= 4, 0.5, 1.0))
+    lim = s8[:, None] * step + 2.0 ** -23 * np.abs(xg)
+    assert np.all((np.abs(dg - xg) <= lim)[keep])
+    # scale: E4M3 of absmax/6 over non-outliers; the max maps next to 6
+    a = np.where(keep, np.abs(xg), 0).max(1)
+    assert np.array_equal(q.meta.reshape(-1), F.e4m3_encode((a / 6).astype(F32)))
+
+
+def test_fp4_tiny_group_all_zero():
+    x = np.full((1, 32), 6 * 2.0 ** -11, dtype=F32)  # absmax/6 = 2^-11 < half of 2^-9
+    q = Q.quantize_rows(x, Q.QuantSpec("fp4", 32, "none"))
+    assert q.meta[0, 0] == 0 and not q.codes.any()
+
+
+# ----------------------------------------------------------------------------- FP8 row
+def test_fp8row_roundtrip():
+    rng = np.random.default_rng(12)
+    spec = Q.QuantSpec("fp8row", 0, "none")
+    x = (rng.standard_normal((3000, 128)) * rng.lognormal(0, 2, (3000, 1))).astype(F32)
+    q = Q.quantize_rows(x, spec)
+    d = Q.dequantize_rows(q, spec)
+    s = q.meta.view(np.float32).reshape(-1).astype(np.float64)
+    a = np.abs(x).max(1)
+    assert np.allclose(s, a / 448, rtol=2 ** -23)
+    err = np.abs(d - x)
+    lim = np.maximum(np.abs(x) * 2.0 ** -4, s[:, None] * 2.0 ** -10) * (1 + 2 ** -20)
+    assert np.all(err <= lim)
+    z = Q.quantize_rows(np.zeros((1, 128), F32), spec)
+    assert z.meta.view(np.float32)[0] == 1.0 and not z.codes.any()
+
+
+# ----------------------------------------------------------------------------- 2-bit
+def test_c2_seeds_are_quartile_bin_midpoints():
+    x = np.arange(64, dtype=F32)[None, :]
+    q = Q.quantize_rows(x, Q.QuantSpec("c2", 64, "none", lloyd_iters=0))
+    cent = F.fp16_from_bits(q.meta.view(np.uint16).reshape(4))
+    assert cent.tolist() == [8.0, 24.0, 40.0, 56.0]
+    # with 4 outliers removed n = 60: ranks floor(7.5), floor(22.5), floor(37.5), floor(52.5)
+    x = np.arange(64, dtype=F32)
+    x[[3, 20, 40, 60]] = [5000, -5000, 4000, -4000]
+    q = Q.quantize_rows(x[None, :], Q.QuantSpec("c2", 64, "e4m3", sigma=1.0, lloyd_iters=0))
+    keep = np.sort(x[~q.mask[0]])
+    assert len(keep) == 60
+    cent = F.fp16_from_bits(q.meta.view(np.uint16).reshape(4))
+    assert cent.tolist() == [float(keep[7]), float(keep[22]), float(keep[37]), float(keep[52])]
+
+
+def test_c2_four_equal_population_values_exact():
+    rng = np.random.default_rng(13)
+    for _ in range(200):
+        vals = np.sort(F.fp16_round(rng.uniform(-3, 3, 4).astype(F32)))
+        if len(np.unique(vals)) < 4:
+            continue
+        x = rng.permutation(np.repeat(vals, 16)).astype(F32)[None, :]
+        q = Q.quantize_rows(x, Q.QuantSpec("c2", 64, "none"))
+        assert np.array_equal(Q.dequantize_rows(q, Q.QuantSpec("c2", 64, "none"))[0],
+                              x[0].astype(np.float64))
+
+
+def _lloyd_fp64(x, iters):
+    """Independent float64 Lloyd (plain loops) with the same seeding and tie rules."""
+    v = sorted(x)
+    n = len(v)
+    c = [v[((2 * j + 1) * n) // 8] for j in range(4)]
+    for _ in range(iters):
+        sums, cnts = [0.0] * 4, [0] * 4
+        for xi in x:
+            d = [abs(xi - cj) for cj in c]
+            a = d.index(min(d))
+            sums[a] += xi
+            cnts[a] += 1
+        c = [sums[j] / cnts[j] if cnts[j] else c[j] for j in range(4)]
+    return np.array(c)
+
+
+def test_c2_lloyd_matches_independent_fp64():
+    rng = np.random.default_rng(14)
+    x = (rng.standard_normal((300, 64)) * rng.lognormal(0, 1, (300, 1))).astype(F32)
+    spec = Q.QuantSpec("c2", 64, "none")
+    q = Q.quantize_rows(x, spec)
+    cent = F.fp16_from_bits(q.meta.view(np.uint16).reshape(300, 4))
+    ref = np.array([_lloyd_fp64([float(t) for t in row], 8) for row in x])
+    close = np.all(np.abs(cent - ref) <= 2.0 ** -10 * np.maximum(np.abs(ref), 1e-3) * 2, axis=1)
+    assert close.mean() > 0.98
+
+
+def test_c2_sse_vs_bruteforce_optimum_and_monotone():
+    rng = np.random.default_rng(15)
+    spec_it = [Q.QuantSpec("c2", 64, "none", lloyd_iters=i) for i in range(9)]
+    for trial in range(20):
+        x = rng.standard_normal(64).astype(F32)
+        xs = np.sort(x.astype(np.float64))
+        # brute force: best split of the sorted data into 4 contiguous non-empty intervals
+        pre = np.concatenate([[0], np.cumsum(xs)])
+        pre2 = np.concatenate([[0], np.cumsum(xs * xs)])
+
+        def sse(i, j):
+            n = j - i
+            s = pre[j] - pre[i]
+            return pre2[j] - pre2[i] - s * s / n
+
+        best = min(sse(0, a) + sse(a, b) + sse(b, c) + sse(c, 64)
+                   for a, b, c in itertools.combinations(range(1, 64), 3))
+        prev = np.inf
+        for it in range(9):
+            q = Q.quantize_rows(x[None, :], spec_it[it])
+            d = Q.dequantize_rows(q, spec_it[it])[0]
+            e = np.sum((d - x) ** 2)
+            assert e >= best * (1 - 1e-3)   # fp16 centroids can sit a hair off the optimum
+            assert e <= prev * (1 + 1e-3) + 1e-6
+            prev = e
+        cent = F.fp16_from_bits(q.meta.view(np.uint16).reshape(4))
+        assert np.all(np.diff(cent) >= 0)
+
+
+def test_c2_fit_excludes_outliers_and_codes_zero_at_outliers():
+    rng = np.random.default_rng(16)
+    x = rng.standard_normal((500, 128)).astype(F32)
+    x[:, 5] = 300.0
+    x[:, 100] = -250.0
+    spec = Q.QuantSpec("c2", 64, "e4m3")
+    q = Q.quantize_rows(x, spec)
+    assert q.mask[:, 5].all() and q.mask[:, 100].all()
+    cent = F.fp16_from_bits(q.meta.view(np.uint16).reshape(500, 2, 4))
+    assert np.abs(cent).max() < 10
+    # outlier slots hold the code of 0.0 under the group's codebook
+    for r in range(0, 500, 50):
+        for c in (5, 100):
+            gcent = cent[r, c // 64]
+            assert q.codes[r, c] == int(np.argmin(np.abs(gcent)))
+    d = Q.dequantize_rows(q, spec)
+    assert np.all(d[:, 5] == 288.0) and np.all(d[:, 100] == -256.0)  # E4M3 of 300 / -250
+
+
+def test_c2_scale_invariance():
+    rng = np.random.default_rng(17)
+    x = rng.standard_normal((200, 128)).astype(F32)
+    spec = Q.QuantSpec("c2", 64, "e4m3")
+    q0 = Q.quantize_rows(x, spec)
+    q1 = Q.quantize_rows((x * F32(4.0)).astype(F32), spec)
+    assert np.array_equal(q0.codes, q1.codes) and np.array_equal(q0.mask, q1.mask)
+    c0 = F.fp16_from_bits(q0.meta.view(np.uint16))
+    c1 = F.fp16_from_bits(q1.meta.view(np.uint16))
+    assert np.array_equal(c0 * 4, c1)
