@@ -1,0 +1,261 @@
+// Fused dequantize + flash-decoding attention, VALU (fp32) variant for every format and
+// layout, plus the log-sum-exp merge of split-K partials.
+//
+// "Hierarchical Token Routing and Sub-2-Bit Non-Linear KV Compression ...", section
+// "Hardware-Kernel Fusion: Eliminating DRAM Round-Trips": compressed codes are streamed from
+// HBM and expanded on chip, never written back dequantized; "The Sub-10ms Barrier ...",
+// figure in "The Twin Bottlenecks": the attention phase is a flash-decoding engine fed by the
+// quantized cache.  Chunks of tokens produce partial (max, sum, unnormalized output) states
+// that a second kernel merges by log-sum-exp.
+//
+// Work unit: one workgroup per (chunk, KV head, sequence) holding the GQA group's query rows.
+// Each 64-token step dequantizes K and V rows into LDS as fp32 (outlier positions overwritten
+// from the side lists), computes scores in fp32, updates the online softmax and accumulates
+// P.V in fp32.  Exact fp32 dequantization makes this the path for formats whose values are
+// not fp16-representable (INT4 scale * code + zero).
+#include "kvq_device.h"
+#include "kvq_launch.h"
+
+namespace kvq {
+namespace {
+
+constexpr int kT = 64;      // tokens per step
+constexpr int kStride = kHeadDim + 1;
+constexpr int kMaxRows = 16;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t v) { return as_f32((uint32_t)v << 16); }
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int w = 32; w >= 1; w >>= 1) v = fmaxf(v, __shfl_xor(v, w, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int w = 32; w >= 1; w >>= 1) v += __shfl_xor(v, w, 64);
+  return v;
+}
+
+// dequantize channels [32*part, 32*part + 32) of one row into dst (fp32)
+template <int FMT, int GS>
+__device__ __forceinline__ void dequant32(const RowRef& r, int part, float* dst) {
+  if (r.tier1) {
+    const uint32_t* cw = (const uint32_t*)(r.codes + 32 * part);
+    const float s = *(const float*)r.meta;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const uint32_t u = cw[w];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) dst[4 * w + k] = e4m3_to_f32((u >> (8 * k)) & 0xFFu) * s;
+    }
+    return;
+  }
+  if constexpr (FMT == FMT_C2) {
+    const uint2 cw = *(const uint2*)(r.codes + 8 * part);
+    const uint2 mw = *(const uint2*)(r.meta + 8 * (part >> 1));
+    const float c[4] = {half_bits_to_f32(mw.x & 0xFFFFu), half_bits_to_f32(mw.x >> 16),
+                        half_bits_to_f32(mw.y & 0xFFFFu), half_bits_to_f32(mw.y >> 16)};
+#pragma unroll
+    for (int k = 0; k < 16; ++k) dst[k] = c[(cw.x >> (2 * k)) & 3u];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) dst[16 + k] = c[(cw.y >> (2 * k)) & 3u];
+  } else {
+    const uint4 cw = *(const uint4*)(r.codes + 16 * part);
+    const uint32_t wv[4] = {cw.x, cw.y, cw.z, cw.w};
+    const int gi = (32 * part) / GS;
+    if constexpr (FMT == FMT_INT4) {
+      const uint32_t m = *(const uint32_t*)(r.meta + 4 * gi);
+      const float S = half_bits_to_f32(m & 0xFFFFu), Z = half_bits_to_f32(m >> 16);
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) dst[8 * w + k] = fmaf((float)((wv[w] >> (4 * k)) & 15u), S, Z);
+    } else {  // FP4
+      const float s = e4m3_to_f32(r.meta[gi]);
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) dst[8 * w + k] = e2m1_to_f32((wv[w] >> (4 * k)) & 15u) * s;
+    }
+  }
+}
+
+__device__ __forceinline__ float outlier_value(const void* vals, int64_t i, int outl) {
+  if (outl == KVQ_OUTL_FP16) return half_bits_to_f32(((const uint16_t*)vals)[i]);
+  return e4m3_to_f32(((const uint8_t*)vals)[i]);
+}
+
+template <int FMT, int GS>
+__global__ void __launch_bounds__(256) decode_generic_kernel(DecodeLaunch d) {
+  __shared__ float s_q[kMaxRows][kHeadDim];
+  __shared__ float s_k[kT][kStride];
+  __shared__ float s_v[kT][kStride];
+  __shared__ float s_s[kMaxRows][kT];
+  __shared__ float s_alpha[kMaxRows];
+  __shared__ float s_m[kMaxRows];
+  __shared__ float s_l[kMaxRows];
+
+  const Layout& L = d.L;
+  const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int S = d.seq_lens[b];
+  if (S < 1 || S > L.S_cap) {
+    if (threadIdx.x == 0 && chunk == 0 && h == 0) report(d.cache.status, KVQ_ERR_INVALID_ARG);
+    return;
+  }
+  const int t0 = chunk * d.chunk;
+  if (t0 >= S) return;
+  const int t1 = min(t0 + d.chunk, S);
+  const int G = d.Hq / L.H;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+
+  for (int i = tid; i < G * kHeadDim; i += 256) {
+    const int r = i / kHeadDim, ch = i % kHeadDim;
+    s_q[r][ch] = bf16_to_f32(d.q[((size_t)b * d.Hq + (size_t)h * G + r) * kHeadDim + ch]);
+  }
+  if (tid < kMaxRows) { s_m[tid] = -INFINITY; s_l[tid] = 0.0f; }
+  float o[kMaxRows / 2];
+#pragma unroll
+  for (int k = 0; k < kMaxRows / 2; ++k) o[k] = 0.0f;
+
+  const size_t lidK = list_id(L, b, h, 0), lidV = lidK + 1;
+  const int32_t* bsK = d.cache.outl_block_start + lidK * (size_t)L.nblk;
+  const int32_t* bsV = d.cache.outl_block_start + lidV * (size_t)L.nblk;
+  const size_t lbase = ((size_t)b * L.H + h) * (size_t)L.outl_cap;
+  const size_t vbytes = d.outl == KVQ_OUTL_FP16 ? 2 : 1;
+  __syncthreads();
+
+  for (int ts = t0; ts < t1; ts += kT) {
+    const int te = min(ts + kT, t1);
+    {  // dequantize 64 rows of K and V: thread -> (token tid/4, 32 channels)
+      const int tt = tid >> 2, part = tid & 3;
+      float buf[32];
+      const int t = ts + tt;
+      const RowRef rk = row_ref(L, d.cache, 0, b, h, t < te ? t : ts, d.block_table);
+      if (t < te && rk.ok) {
+        dequant32<FMT, GS>(rk, part, buf);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 32; ++k) buf[k] = 0.0f;
+      }
+#pragma unroll
+      for (int k = 0; k < 32; ++k) s_k[tt][32 * part + k] = buf[k];
+      const RowRef rv = row_ref(L, d.cache, 1, b, h, t < te ? t : ts, d.block_table);
+      if (t < te && rv.ok) dequant32<FMT, GS>(rv, part, buf);
+      if (t < te && (!rk.ok || !rv.ok) && part == 0) report(d.cache.status, KVQ_ERR_INVALID_ARG);
+#pragma unroll
+      for (int k = 0; k < 32; ++k) s_v[tt][32 * part + k] = buf[k];
+    }
+    __syncthreads();
+    if (d.outl != KVQ_OUTL_NONE) {  // overwrite outlier positions of this step
+      for (int kv = 0; kv < 2; ++kv) {
+        const int32_t* bs = kv ? bsV : bsK;
+        const int64_t cnt = d.cache.outl_count[kv ? lidV : lidK];
+        const int64_t r0 = max((int64_t)0, min((int64_t)bs[ts >> 4], L.outl_cap));
+        const int64_t r1 = max(r0, min((te < S) ? (int64_t)bs[te >> 4] : cnt, L.outl_cap));
+        const uint32_t* idx = d.cache.outl_idx[kv] + lbase;
+        const void* vals = (const uint8_t*)d.cache.outl_val[kv] + lbase * vbytes;
+        float (*tile)[kStride] = kv ? s_v : s_k;
+        for (int64_t r = r0 + tid; r < r1; r += 256) {
+          const uint32_t ix = idx[r];
+          const int t = (int)(ix / kHeadDim), ch = (int)(ix % kHeadDim);
+          if (t >= ts && t < te) tile[t - ts][ch] = outlier_value(vals, r, d.outl);
+        }
+      }
+    }
+    __syncthreads();
+    {  // scores (log2 domain): thread -> (token lane, rows wave, wave+4, ...)
+      const int t = ts + lane;
+      for (int r = wave; r < G; r += 4) {
+        float acc = 0.0f;
+#pragma unroll 8
+        for (int ch = 0; ch < kHeadDim; ++ch) acc = fmaf(s_q[r][ch], s_k[lane][ch], acc);
+        s_s[r][lane] = t < te ? acc * d.scale_log2 : -INFINITY;
+      }
+    }
+    __syncthreads();
+    for (int r = wave; r < G; r += 4) {  // online softmax, one row per wave
+      const float v = s_s[r][lane];
+      const float mold = s_m[r];
+      const float mnew = fmaxf(mold, wave_max(v));
+      const float p = exp2f(v - mnew);
+      const float sum = wave_sum(p);
+      const float alpha = exp2f(mold - mnew);
+      s_s[r][lane] = p;
+      if (lane == 0) { s_l[r] = s_l[r] * alpha + sum; s_m[r] = mnew; s_alpha[r] = alpha; }
+    }
+    __syncthreads();
+    {  // P.V: thread -> (channel tid % 128, rows tid/128, +2, ...)
+      const int ch = tid & 127, rh = tid >> 7;
+#pragma unroll
+      for (int k = 0; k < kMaxRows / 2; ++k) {
+        const int r = rh + 2 * k;
+        if (r < G) {
+          float acc = o[k] * s_alpha[r];
+#pragma unroll 8
+          for (int tt = 0; tt < kT; ++tt) acc = fmaf(s_s[r][tt], s_v[tt][ch], acc);
+          o[k] = acc;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  const int ch = tid & 127, rh = tid >> 7;
+#pragma unroll
+  for (int k = 0; k < kMaxRows / 2; ++k) {
+    const int r = rh + 2 * k;
+    if (r >= G) continue;
+    const size_t hq = (size_t)h * G + r;
+    if (d.n_chunks == 1) {
+      d.out[((size_t)b * d.Hq + hq) * kHeadDim + ch] = o[k] / s_l[r];
+    } else {
+      float* pp = d.partials + (((size_t)b * d.Hq + hq) * d.n_chunks + chunk) * (kHeadDim + 2);
+      if (ch == 0) { pp[0] = s_m[r]; pp[1] = s_l[r]; }
+      pp[2 + ch] = o[k];
+    }
+  }
+}
+
+// out[b][hq] = sum_c 2^(m_c - M) o_c / sum_c 2^(m_c - M) l_c over the chunks holding tokens
+__global__ void __launch_bounds__(128) lse_merge_kernel(DecodeLaunch d) {
+  const int hq = blockIdx.x, b = blockIdx.y, ch = threadIdx.x;
+  const int S = d.seq_lens[b];
+  const int nc = min((S + d.chunk - 1) / d.chunk, d.n_chunks);
+  const float* pp = d.partials + ((size_t)b * d.Hq + hq) * d.n_chunks * (kHeadDim + 2);
+  float M = -INFINITY;
+  for (int c = 0; c < nc; ++c) M = fmaxf(M, pp[(size_t)c * (kHeadDim + 2)]);
+  float num = 0.0f, den = 0.0f;
+  for (int c = 0; c < nc; ++c) {
+    const float* q = pp + (size_t)c * (kHeadDim + 2);
+    const float w = exp2f(q[0] - M);
+    den = fmaf(w, q[1], den);
+    num = fmaf(w, q[2 + ch], num);
+  }
+  d.out[((size_t)b * d.Hq + hq) * kHeadDim + ch] = num / den;
+}
+
+}  // namespace
+
+hipError_t launch_decode_generic(const DecodeLaunch& d, hipStream_t st) {
+  dim3 grid(d.n_chunks, d.L.H, d.L.B);
+  switch (d.fmt) {
+    case FMT_INT4:
+      if (d.group == 32) decode_generic_kernel<FMT_INT4, 32><<<grid, 256, 0, st>>>(d);
+      else decode_generic_kernel<FMT_INT4, 64><<<grid, 256, 0, st>>>(d);
+      break;
+    case FMT_FP4:
+      if (d.group == 32) decode_generic_kernel<FMT_FP4, 32><<<grid, 256, 0, st>>>(d);
+      else decode_generic_kernel<FMT_FP4, 64><<<grid, 256, 0, st>>>(d);
+      break;
+    case FMT_C2: decode_generic_kernel<FMT_C2, 64><<<grid, 256, 0, st>>>(d); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_lse_merge(const DecodeLaunch& d, hipStream_t st) {
+  lse_merge_kernel<<<dim3(d.Hq, d.L.B), 128, 0, st>>>(d);
+  return hipGetLastError();
+}
+
+}  // namespace kvq

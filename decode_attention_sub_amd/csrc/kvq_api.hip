@@ -1,0 +1,242 @@
+// C ABI of libkvq.so: argument validation, buffer sizing and kernel launches.
+// The contract of every entry point is documented in include/kvq.h.
+#include <math.h>
+#include <string.h>
+
+#include "kvq_device.h"
+#include "kvq_launch.h"
+
+using namespace kvq;
+
+namespace {
+
+constexpr int kDefaultPagedChunk = 2048;
+
+bool is_quant_fmt(int f) { return f == FMT_INT4 || f == FMT_FP4 || f == FMT_C2; }
+
+int32_t check_params(const kvq_params* p) {
+  if (!p) return KVQ_ERR_INVALID_ARG;
+  if (p->batch < 1 || p->num_kv_heads < 1 || p->num_q_heads < 1 || p->max_seq_len < 1)
+    return KVQ_ERR_INVALID_ARG;
+  if (p->head_dim != kHeadDim) return KVQ_ERR_UNSUPPORTED;
+  if (p->num_q_heads % p->num_kv_heads != 0) return KVQ_ERR_INVALID_ARG;
+  const int G = p->num_q_heads / p->num_kv_heads;
+  if (G > 16) return KVQ_ERR_UNSUPPORTED;
+  if (!is_quant_fmt(p->format)) return KVQ_ERR_UNSUPPORTED;
+  if (p->group_size != 32 && p->group_size != 64) return KVQ_ERR_UNSUPPORTED;
+  if (p->format == FMT_C2 && p->group_size != 64) return KVQ_ERR_UNSUPPORTED;
+  if (p->outlier_dtype < KVQ_OUTL_NONE || p->outlier_dtype > KVQ_OUTL_FP8_E4M3)
+    return KVQ_ERR_INVALID_ARG;
+  if (p->outlier_dtype != KVQ_OUTL_NONE && !(p->outlier_sigma > 0.0f && isfinite(p->outlier_sigma)))
+    return KVQ_ERR_INVALID_ARG;
+  if (p->format == FMT_C2 && (p->lloyd_iters < 0 || p->lloyd_iters > 64)) return KVQ_ERR_INVALID_ARG;
+  if (p->page_size != 0 && p->page_size != kBlock) return KVQ_ERR_UNSUPPORTED;
+  if (p->page_size) {
+    if (p->format != FMT_C2) return KVQ_ERR_UNSUPPORTED;
+    if (p->num_pages < 0 || p->num_pages_fp8 < 0 || p->max_pages_per_seq < 1) return KVQ_ERR_INVALID_ARG;
+    if ((int64_t)p->max_pages_per_seq * kBlock < p->max_seq_len) return KVQ_ERR_INVALID_ARG;
+  }
+  if ((int64_t)p->max_seq_len * kHeadDim > 0xFFFFFFFFll) return KVQ_ERR_INVALID_ARG;  // uint32 index
+  return KVQ_OK;
+}
+
+uint32_t code_bytes(const kvq_params* p) { return kHeadDim * code_bits(p->format) / 8; }
+uint32_t meta_bytes(const kvq_params* p) {
+  return (kHeadDim / p->group_size) * meta_bytes_per_group(p->format);
+}
+
+Layout make_layout(const kvq_params* p, int64_t outl_cap) {
+  Layout L;
+  L.B = p->batch;
+  L.H = p->num_kv_heads;
+  L.S_cap = p->max_seq_len;
+  L.paged = p->page_size ? 1 : 0;
+  L.max_pages = p->max_pages_per_seq;
+  L.code_bytes = (int)code_bytes(p);
+  L.meta_bytes = (int)meta_bytes(p);
+  L.nblk = (p->max_seq_len + kBlock - 1) / kBlock;
+  L.outl_cap = outl_cap;
+  L.num_pages = p->page_size ? p->num_pages : 0;
+  L.num_pages_fp8 = p->page_size ? p->num_pages_fp8 : 0;
+  return L;
+}
+
+int32_t check_cache(const kvq_params* p, const kvq_cache* c) {
+  if (!c) return KVQ_ERR_INVALID_ARG;
+  for (int kv = 0; kv < 2; ++kv) {
+    if (!c->codes[kv] || !c->meta[kv]) return KVQ_ERR_INVALID_ARG;
+    if (p->page_size && p->num_pages_fp8 > 0 && (!c->codes8[kv] || !c->scale8[kv]))
+      return KVQ_ERR_INVALID_ARG;
+    if (p->outlier_dtype != KVQ_OUTL_NONE && (!c->outl_idx[kv] || !c->outl_val[kv]))
+      return KVQ_ERR_INVALID_ARG;
+  }
+  if (!c->outl_count || !c->outl_block_start) return KVQ_ERR_INVALID_ARG;
+  if (p->outlier_dtype != KVQ_OUTL_NONE && c->outl_capacity < 1) return KVQ_ERR_INVALID_ARG;
+  return KVQ_OK;
+}
+
+int resolve_chunk(const kvq_params* p, int32_t split_chunk) {
+  if (split_chunk < 0) return -1;
+  if (split_chunk == 0) {
+    if (p->page_size) return kDefaultPagedChunk;
+    return ((p->max_seq_len + 63) / 64) * 64;
+  }
+  if (split_chunk % 64) return -1;
+  return split_chunk;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t kvq_kv_bytes(const kvq_params* p, int32_t num_layers, int64_t num_tokens,
+                     int64_t num_outliers, uint64_t* out_bytes) {
+  if (!p || !out_bytes || num_layers < 0 || num_tokens < 0 || num_outliers < 0 ||
+      p->num_kv_heads < 1 || p->head_dim < 1)
+    return KVQ_ERR_INVALID_ARG;
+  const uint64_t LH = 2ull * (uint64_t)num_layers * (uint64_t)p->num_kv_heads * (uint64_t)num_tokens;
+  if (p->format == KVQ_FMT_FP16 || p->format == KVQ_FMT_BF16) {
+    *out_bytes = LH * (uint64_t)p->head_dim * 2ull;
+    return KVQ_OK;
+  }
+  uint64_t row;
+  if (p->format == FMT_FP8ROW) {
+    row = (uint64_t)p->head_dim + 4ull;
+  } else {
+    if (!is_quant_fmt(p->format) || p->group_size < 1 || p->head_dim % p->group_size)
+      return KVQ_ERR_INVALID_ARG;
+    row = (uint64_t)p->head_dim * code_bits(p->format) / 8 +
+          (uint64_t)(p->head_dim / p->group_size) * meta_bytes_per_group(p->format);
+  }
+  uint64_t vb = p->outlier_dtype == KVQ_OUTL_FP16 ? 2 : (p->outlier_dtype == KVQ_OUTL_FP8_E4M3 ? 1 : 0);
+  *out_bytes = LH * row + (uint64_t)num_outliers * (vb ? vb + 4ull : 0ull);
+  return KVQ_OK;
+}
+
+int32_t kvq_cache_sizes(const kvq_params* p, int64_t outl_capacity, kvq_cache_sizes_t* out) {
+  int32_t st = check_params(p);
+  if (st) return st;
+  if (!out || outl_capacity < 0) return KVQ_ERR_INVALID_ARG;
+  memset(out, 0, sizeof(*out));
+  out->code_bytes_per_row = code_bytes(p);
+  out->meta_bytes_per_row = meta_bytes(p);
+  const uint64_t BH = (uint64_t)p->batch * p->num_kv_heads;
+  if (p->page_size) {
+    const uint64_t rows = (uint64_t)p->num_pages * p->num_kv_heads * kBlock;
+    const uint64_t rows8 = (uint64_t)p->num_pages_fp8 * p->num_kv_heads * kBlock;
+    out->codes = rows * out->code_bytes_per_row;
+    out->meta = rows * out->meta_bytes_per_row;
+    out->codes8 = rows8 * kHeadDim;
+    out->scale8 = rows8 * 4;
+  } else {
+    const uint64_t rows = BH * (uint64_t)p->max_seq_len;
+    out->codes = rows * out->code_bytes_per_row;
+    out->meta = rows * out->meta_bytes_per_row;
+  }
+  const uint64_t vb = p->outlier_dtype == KVQ_OUTL_FP16 ? 2 : 1;
+  out->outl_idx = BH * (uint64_t)outl_capacity * 4;
+  out->outl_val = BH * (uint64_t)outl_capacity * vb;
+  out->outl_count = BH * 2 * 4;
+  out->outl_block_start = BH * 2 * (uint64_t)((p->max_seq_len + kBlock - 1) / kBlock) * 4;
+  return KVQ_OK;
+}
+
+int32_t kvq_quantize_append(const kvq_params* p, const kvq_cache* cache, const float* k_new,
+                            const float* v_new, int32_t max_new, const int32_t* positions,
+                            const int32_t* counts, const int32_t* block_table, void* stream) {
+  int32_t st = check_params(p);
+  if (st) return st;
+  st = check_cache(p, cache);
+  if (st) return st;
+  if (!k_new || !v_new || !positions || !counts || max_new < 1) return KVQ_ERR_INVALID_ARG;
+  if (p->page_size && !block_table) return KVQ_ERR_INVALID_ARG;
+  QuantizeLaunch q;
+  q.L = make_layout(p, cache->outl_capacity);
+  q.cache = *cache;
+  q.k_new = k_new;
+  q.v_new = v_new;
+  q.positions = positions;
+  q.counts = counts;
+  q.block_table = p->page_size ? block_table : nullptr;
+  q.max_new = max_new;
+  q.outl = p->outlier_dtype;
+  q.tau2 = p->outlier_sigma * p->outlier_sigma;
+  q.lloyd = p->lloyd_iters;
+  q.fmt = p->format;
+  q.group = p->group_size;
+  if (launch_quantize_append(q, (hipStream_t)stream) != hipSuccess) return KVQ_ERR_HIP;
+  return KVQ_OK;
+}
+
+int32_t kvq_workspace_bytes(const kvq_params* p, int32_t split_chunk, uint64_t* out_bytes) {
+  int32_t st = check_params(p);
+  if (st) return st;
+  if (!out_bytes) return KVQ_ERR_INVALID_ARG;
+  const int chunk = resolve_chunk(p, split_chunk);
+  if (chunk < 0) return KVQ_ERR_INVALID_ARG;
+  const uint64_t nc = (uint64_t)((p->max_seq_len + chunk - 1) / chunk);
+  *out_bytes = nc <= 1 ? 0 : (uint64_t)p->batch * p->num_q_heads * nc * (kHeadDim + 2) * 4ull;
+  return KVQ_OK;
+}
+
+int32_t kvq_decode_attention(const kvq_params* p, const kvq_cache* cache, const void* q_bf16,
+                             const int32_t* seq_lens, const int32_t* block_table,
+                             float sm_scale, int32_t split_chunk, float* out, void* workspace,
+                             uint64_t ws_bytes, void* stream) {
+  int32_t st = check_params(p);
+  if (st) return st;
+  st = check_cache(p, cache);
+  if (st) return st;
+  if (!q_bf16 || !seq_lens || !out || !isfinite(sm_scale)) return KVQ_ERR_INVALID_ARG;
+  if (p->page_size && !block_table) return KVQ_ERR_INVALID_ARG;
+  const int chunk = resolve_chunk(p, split_chunk);
+  if (chunk < 0) return KVQ_ERR_INVALID_ARG;
+  uint64_t need = 0;
+  kvq_workspace_bytes(p, chunk, &need);
+  if (need && (!workspace || ws_bytes < need)) return KVQ_ERR_WORKSPACE;
+  DecodeLaunch d;
+  d.L = make_layout(p, cache->outl_capacity);
+  d.cache = *cache;
+  d.q = (const uint16_t*)q_bf16;
+  d.seq_lens = seq_lens;
+  d.block_table = p->page_size ? block_table : nullptr;
+  d.out = out;
+  d.Hq = p->num_q_heads;
+  d.fmt = p->format;
+  d.group = p->group_size;
+  d.outl = p->outlier_dtype;
+  d.chunk = chunk;
+  d.n_chunks = (p->max_seq_len + chunk - 1) / chunk;
+  d.partials = d.n_chunks > 1 ? (float*)workspace : nullptr;
+  d.scale_log2 = sm_scale * 1.4426950408889634f;
+  hipStream_t s = (hipStream_t)stream;
+  bool handled = false;
+  if (launch_decode_mfma(d, s, &handled) != hipSuccess) return KVQ_ERR_HIP;
+  if (!handled && launch_decode_generic(d, s) != hipSuccess) return KVQ_ERR_HIP;
+  if (d.n_chunks > 1 && launch_lse_merge(d, s) != hipSuccess) return KVQ_ERR_HIP;
+  return KVQ_OK;
+}
+
+int32_t kvq_probe_read(const void* src, uint64_t bytes, void* sink, void* stream) {
+  if (!src || !sink || bytes == 0 || bytes % 16) return KVQ_ERR_INVALID_ARG;
+  return launch_probe_read(src, bytes, sink, (hipStream_t)stream) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+int32_t kvq_probe_copy(const void* src, void* dst, uint64_t bytes, void* stream) {
+  if (!src || !dst || bytes == 0 || bytes % 16) return KVQ_ERR_INVALID_ARG;
+  return launch_probe_copy(src, dst, bytes, (hipStream_t)stream) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+const char* kvq_status_string(int32_t s) {
+  switch (s) {
+    case KVQ_OK: return "ok";
+    case KVQ_ERR_INVALID_ARG: return "invalid argument";
+    case KVQ_ERR_UNSUPPORTED: return "unsupported format / shape";
+    case KVQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case KVQ_ERR_HIP: return "HIP launch error";
+    case KVQ_ERR_CAPACITY: return "outlier list capacity exceeded";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

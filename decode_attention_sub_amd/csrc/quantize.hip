@@ -1,0 +1,474 @@
+// Quantize-on-append: group statistics, outlier isolation, quantizer fit, encoding, packing
+// and ordered compaction of outlier records into the per-list COO side lists.
+//
+// "Hierarchical Token Routing and Sub-2-Bit Non-Linear KV Compression ...", section
+// "Paradigm 2": outliers beyond tau standard deviations kept apart at higher precision, the
+// rest coded against a 4-centroid codebook fitted by k-means; "The Sub-10ms Barrier ...",
+// section "2. FP4/INT4 KV-Cache Quantization": per-group scale (max - min)/(2^b - 1) computed
+// at token insertion; "Hierarchical Token Gating and Tiered KV-Cache Paging ...", section
+// "2. Entropy-Guided Tiered KV-Cache Quantization": FP8 tier rows.
+//
+// Bit-exactness contract: every decision is taken in float32 with round-to-nearest-even, no
+// fused multiply-add (contraction is off in this file), correctly rounded division, and every
+// sum over a group follows one fixed pairwise tree: for w = g/2, g/4, ..., 1:
+// a[i] += a[i + w] for i < w.  With L = g/4 lanes per group and lane j holding group elements
+// j, j+L, j+2L, j+3L, the steps w = 2L and w = L are in-lane and the steps w < L are xor
+// exchanges between lanes (every lane then holds the root by commutativity of addition).
+#pragma clang fp contract(off)
+
+#include "kvq_device.h"
+#include "kvq_launch.h"
+
+namespace kvq {
+namespace {
+
+constexpr int kRowLanes = 32;  // lanes per row: 128 channels, 4 per lane
+
+struct QArgs {
+  Layout L;
+  kvq_cache cache;
+  const float* k_new;
+  const float* v_new;
+  const int32_t* positions;
+  const int32_t* counts;
+  const int32_t* block_table;
+  int max_new;
+  int outl;          // kvq_outlier_dtype
+  float tau2;        // fl32(tau * tau)
+  int lloyd;
+};
+
+// ---------------------------------------------------------------- group reductions
+template <int L>
+__device__ __forceinline__ float group_sum_tree(float a0, float a1, float a2, float a3) {
+  float t = (a0 + a2) + (a1 + a3);   // tree steps w = 2L, w = L
+  if constexpr (L >= 32) t = t + xor_f32<16>(t);
+  if constexpr (L >= 16) t = t + xor_f32<8>(t);
+  if constexpr (L >= 8) t = t + xor_f32<4>(t);
+  if constexpr (L >= 4) t = t + xor_f32<2>(t);
+  if constexpr (L >= 2) t = t + xor_f32<1>(t);
+  return t;
+}
+template <int L>
+__device__ __forceinline__ int group_isum(int v) {
+  if constexpr (L >= 32) v += xor_i32<16>(v);
+  if constexpr (L >= 16) v += xor_i32<8>(v);
+  if constexpr (L >= 8) v += xor_i32<4>(v);
+  if constexpr (L >= 4) v += xor_i32<2>(v);
+  if constexpr (L >= 2) v += xor_i32<1>(v);
+  return v;
+}
+template <int L>
+__device__ __forceinline__ int group_ior(int v) {
+  if constexpr (L >= 32) v |= xor_i32<16>(v);
+  if constexpr (L >= 16) v |= xor_i32<8>(v);
+  if constexpr (L >= 8) v |= xor_i32<4>(v);
+  if constexpr (L >= 4) v |= xor_i32<2>(v);
+  if constexpr (L >= 2) v |= xor_i32<1>(v);
+  return v;
+}
+template <int L>
+__device__ __forceinline__ float group_min(float v) {
+  if constexpr (L >= 32) v = fminf(v, xor_f32<16>(v));
+  if constexpr (L >= 16) v = fminf(v, xor_f32<8>(v));
+  if constexpr (L >= 8) v = fminf(v, xor_f32<4>(v));
+  if constexpr (L >= 4) v = fminf(v, xor_f32<2>(v));
+  if constexpr (L >= 2) v = fminf(v, xor_f32<1>(v));
+  return v;
+}
+template <int L>
+__device__ __forceinline__ float group_max(float v) {
+  if constexpr (L >= 32) v = fmaxf(v, xor_f32<16>(v));
+  if constexpr (L >= 16) v = fmaxf(v, xor_f32<8>(v));
+  if constexpr (L >= 8) v = fmaxf(v, xor_f32<4>(v));
+  if constexpr (L >= 4) v = fmaxf(v, xor_f32<2>(v));
+  if constexpr (L >= 2) v = fmaxf(v, xor_f32<1>(v));
+  return v;
+}
+
+// ---------------------------------------------------------------- per-row state
+struct RowOut {
+  uint32_t code[4];   // per element
+  uint32_t flag[4];   // outlier flags
+  uint32_t meta[2];   // group metadata held by the group's lane 0 (up to 8 bytes)
+};
+
+// nearest of 4 centroids by |x - c| (fl32), first index on ties
+__device__ __forceinline__ uint32_t nearest4(float x, const float c[4]) {
+  float best = __builtin_fabsf(x - c[0]);
+  uint32_t k = 0;
+#pragma unroll
+  for (int j = 1; j < 4; ++j) {
+    const float d = __builtin_fabsf(x - c[j]);
+    if (d < best) { best = d; k = (uint32_t)j; }
+  }
+  return k;
+}
+
+// Outlier predicate: e * (g-1) > fl32(tau^2) * Q2 with e = (x - mean)^2, Q2 = sum of e.
+template <int G>
+__device__ __forceinline__ void outlier_flags(const float x[4], float tau2, bool keep[4]) {
+  constexpr int L = G / 4;
+  const float mean = group_sum_tree<L>(x[0], x[1], x[2], x[3]) * (1.0f / (float)G);
+  float e[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { const float d = x[i] - mean; e[i] = d * d; }
+  const float q2 = group_sum_tree<L>(e[0], e[1], e[2], e[3]);
+  const float rhs = tau2 * q2;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) keep[i] = !(e[i] * (float)(G - 1) > rhs);
+}
+
+template <int G>
+__device__ void fit_int4(const float x[4], const bool keep[4], RowOut& o) {
+  constexpr int L = G / 4;
+  float mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (keep[i]) { mn = fminf(mn, x[i]); mx = fmaxf(mx, x[i]); }
+  mn = group_min<L>(mn) + 0.0f;  // a zero minimum is taken as +0
+  mx = group_max<L>(mx) + 0.0f;
+  const float s = (mx - mn) / 15.0f;
+  const uint32_t sh = f32_to_half_bits(s), zh = f32_to_half_bits(mn);
+  const float S = half_bits_to_f32(sh), Z = half_bits_to_f32(zh);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float xx = keep[i] ? x[i] : 0.0f;
+    uint32_t q = 0;
+    if (S > 0.0f) {
+      const float y = (xx - Z) / S;
+      q = (uint32_t)__builtin_rintf(fminf(fmaxf(y, 0.0f), 15.0f));
+    }
+    o.code[i] = q;
+  }
+  o.meta[0] = sh | (zh << 16);
+  o.meta[1] = 0;
+}
+
+template <int G>
+__device__ void fit_fp4(const float x[4], const bool keep[4], RowOut& o) {
+  constexpr int L = G / 4;
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (keep[i]) a = fmaxf(a, __builtin_fabsf(x[i]));
+  a = group_max<L>(a);
+  const uint32_t s8 = f32_to_e4m3(a / 6.0f);
+  const float sv = e4m3_to_f32(s8);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float xx = keep[i] ? x[i] : 0.0f;
+    o.code[i] = sv > 0.0f ? f32_to_e2m1(xx / sv) : 0u;
+  }
+  o.meta[0] = s8;
+  o.meta[1] = 0;
+}
+
+// 2-bit centroids: seeds at ranks floor((2j+1) n / 8) of the sorted non-outliers, then
+// `iters` Lloyd iterations (empty clusters keep their centroid), fp16 centroids.
+template <int G>
+__device__ void fit_c2(const float x[4], const bool keep[4], int jg, int iters, RowOut& o) {
+  constexpr int L = G / 4;
+  int nloc = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) nloc += keep[i] ? 1 : 0;
+  const int n = group_isum<L>(nloc);
+  // stable rank of each kept element among the kept elements of the group
+  int rank[4] = {0, 0, 0, 0};
+  const uint32_t xb[4] = {as_u32(x[0]), as_u32(x[1]), as_u32(x[2]), as_u32(x[3])};
+  const uint32_t kb = (keep[0] ? 1u : 0u) | (keep[1] ? 2u : 0u) | (keep[2] ? 4u : 0u) |
+                      (keep[3] ? 8u : 0u);
+  const int lane32 = (int)(threadIdx.x & 31);
+  const int gbase = lane32 - jg;  // first lane of this group within the 32-lane half
+#pragma unroll
+  for (int src = 0; src < L; ++src) {
+    // broadcast lane gbase + src of this group (bpermute within the wave)
+    const int srcl = ((int)threadIdx.x & 32) + gbase + src;  // lane within the wave
+    const uint32_t kbs = (uint32_t)__shfl((int)kb, srcl, 64);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float v = as_f32((uint32_t)__shfl((int)xb[e], srcl, 64));
+      const bool vk = (kbs >> e) & 1u;
+      const int vidx = src + L * e;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int myidx = jg + L * i;
+        const bool less = v < x[i] || (v == x[i] && vidx < myidx);
+        rank[i] += (vk && less) ? 1 : 0;
+      }
+    }
+  }
+  float c[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = ((2 * j + 1) * n) >> 3;
+    uint32_t bits = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) bits |= (keep[i] && rank[i] == r) ? xb[i] : 0u;
+    c[j] = as_f32((uint32_t)group_ior<L>((int)bits));
+  }
+  for (int it = 0; it < iters; ++it) {
+    uint32_t a[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = nearest4(x[i], c);
+    float nc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float s[4];
+      int cl = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool m = keep[i] && a[i] == (uint32_t)j;
+        s[i] = m ? x[i] : 0.0f;
+        cl += m ? 1 : 0;
+      }
+      const float sum = group_sum_tree<L>(s[0], s[1], s[2], s[3]);
+      const int cnt = group_isum<L>(cl);
+      nc[j] = cnt > 0 ? sum / (float)cnt : c[j];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) c[j] = nc[j];
+  }
+  uint32_t hb[4];
+  float ch[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) { hb[j] = f32_to_half_bits(c[j]); ch[j] = half_bits_to_f32(hb[j]); }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o.code[i] = nearest4(keep[i] ? x[i] : 0.0f, ch);
+  o.meta[0] = hb[0] | (hb[1] << 16);
+  o.meta[1] = hb[2] | (hb[3] << 16);
+}
+
+// FP8 tier row: scale = absmax/448 over the 128 channels (1 if zero), codes E4M3(x/scale)
+__device__ void fit_fp8row(const float x[4], RowOut& o) {
+  float a = fmaxf(fmaxf(__builtin_fabsf(x[0]), __builtin_fabsf(x[1])),
+                  fmaxf(__builtin_fabsf(x[2]), __builtin_fabsf(x[3])));
+  a = group_max<32>(a);
+  const float s = a > 0.0f ? a / 448.0f : 1.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { o.code[i] = f32_to_e4m3(x[i] / s); o.flag[i] = 0; }
+  o.meta[0] = as_u32(s);
+  o.meta[1] = 0;
+}
+
+// ---------------------------------------------------------------- kernel
+template <int FMT, int G, int NW>
+__global__ void __launch_bounds__(64 * NW) quantize_append_kernel(QArgs a) {
+  constexpr int L = G / 4;          // lanes per group
+  constexpr int RPI = 2 * NW;       // rows per iteration
+  constexpr int CB = kHeadDim * code_bits(FMT) / 8;
+  __shared__ uint8_t s_code[RPI][kHeadDim];
+  __shared__ uint8_t s_flag[RPI][kHeadDim];
+  __shared__ float s_x[RPI][kHeadDim];
+  __shared__ uint32_t s_meta[RPI][8];
+  __shared__ int s_tier[RPI];
+  __shared__ int s_rowtot[RPI];
+  __shared__ int s_trunc;
+
+  const Layout& Lo = a.L;
+  const int list = blockIdx.x;
+  const int kv = list & 1;
+  const int h = (list >> 1) % Lo.H;
+  const int b = (list >> 1) / Lo.H;
+  const int tid = threadIdx.x;
+  const int slot = tid / kRowLanes;
+  const int lane = tid % kRowLanes;
+  const int gi = lane / L;          // group within the row
+  const int jg = lane % L;          // lane within the group
+
+  const int p = a.positions[b];
+  const int n = a.counts[b];
+  if (n <= 0) return;
+  if (p < 0 || n > a.max_new || (int64_t)p + n > Lo.S_cap) {
+    if (tid == 0) report(a.cache.status, KVQ_ERR_INVALID_ARG);
+    return;
+  }
+  const size_t lid = list_id(Lo, b, h, kv);
+  int32_t* bstart = a.cache.outl_block_start + lid * (size_t)Lo.nblk;
+  uint32_t* oidx = a.cache.outl_idx[kv] + ((size_t)b * Lo.H + h) * (size_t)Lo.outl_cap;
+  uint8_t* oval = (uint8_t*)a.cache.outl_val[kv] +
+                  ((size_t)b * Lo.H + h) * (size_t)Lo.outl_cap * (a.outl == KVQ_OUTL_FP16 ? 2 : 1);
+
+  // truncate the list to the records of tokens < p
+  if (tid == 0) s_trunc = 0;
+  __syncthreads();
+  int64_t running = 0;
+  if (p > 0) {
+    const int64_t start = max((int64_t)0, min((int64_t)bstart[(p - 1) >> 4], Lo.outl_cap));
+    const int64_t old = max((int64_t)0, min((int64_t)a.cache.outl_count[lid], Lo.outl_cap));
+    int cnt = 0;
+    for (int64_t r = start + tid; r < old && r < start + 256; r += blockDim.x)
+      cnt += (oidx[r] < (uint32_t)p * kHeadDim) ? 1 : 0;
+    if (cnt) atomicAdd(&s_trunc, cnt);
+    __syncthreads();
+    running = start + s_trunc;
+  }
+
+  const float* src = (kv == 0 ? a.k_new : a.v_new) + ((size_t)b * Lo.H + h) * (size_t)a.max_new * kHeadDim;
+
+  for (int i0 = 0; i0 < n; i0 += RPI) {
+    const int r = i0 + slot;
+    const bool valid = r < n;
+    const int t = p + r;
+    float x[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      x[e] = valid ? src[(size_t)r * kHeadDim + gi * G + jg + L * e] : 0.0f;
+    int tier1 = 0;
+    size_t pslot = 0;
+    bool row_ok = valid;
+    if (Lo.paged && valid) {
+      row_ok = page_slot(Lo, a.block_table, b, t, &tier1, &pslot);
+      if (!row_ok && lane == 0) report(a.cache.status, KVQ_ERR_INVALID_ARG);
+    }
+    RowOut o;
+    if (tier1) {
+      fit_fp8row(x, o);
+    } else {
+      bool keep[4] = {true, true, true, true};
+      if (a.outl != KVQ_OUTL_NONE) outlier_flags<G>(x, a.tau2, keep);
+      if constexpr (FMT == FMT_INT4) fit_int4<G>(x, keep, o);
+      else if constexpr (FMT == FMT_FP4) fit_fp4<G>(x, keep, o);
+      else fit_c2<G>(x, keep, jg, a.lloyd, o);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o.flag[e] = keep[e] ? 0u : 1u;
+    }
+    // stage the row in LDS
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int c = gi * G + jg + L * e;
+      s_code[slot][c] = (uint8_t)o.code[e];
+      s_flag[slot][c] = valid ? (uint8_t)o.flag[e] : 0;
+      s_x[slot][c] = x[e];
+    }
+    if (tier1) {
+      if (lane == 0) s_meta[slot][0] = o.meta[0];
+    } else if (jg == 0) {
+      constexpr int MB = meta_bytes_per_group(FMT);
+      if constexpr (MB == 8) { s_meta[slot][2 * gi] = o.meta[0]; s_meta[slot][2 * gi + 1] = o.meta[1]; }
+      else if constexpr (MB == 4) { s_meta[slot][gi] = o.meta[0]; }
+      else { ((uint8_t*)s_meta[slot])[gi] = (uint8_t)o.meta[0]; }
+    }
+    if (lane == 0) s_tier[slot] = tier1;
+    __syncthreads();
+
+    // pack codes and write the row
+    if (row_ok) {
+      const int tr = s_tier[slot];
+      uint8_t* codes_dst;
+      uint8_t* meta_dst;
+      int cb, mb;
+      if (!Lo.paged) {
+        const size_t row = ((size_t)b * Lo.H + h) * (size_t)Lo.S_cap + (size_t)t;
+        codes_dst = (uint8_t*)a.cache.codes[kv] + row * CB;
+        meta_dst = (uint8_t*)a.cache.meta[kv] + row * Lo.meta_bytes;
+        cb = CB; mb = Lo.meta_bytes;
+      } else {
+        const size_t prow = (pslot * Lo.H + h) * kBlock + (t & 15);
+        if (tr) {
+          codes_dst = (uint8_t*)a.cache.codes8[kv] + prow * kHeadDim;
+          meta_dst = (uint8_t*)(a.cache.scale8[kv] + prow);
+          cb = kHeadDim; mb = 4;
+        } else {
+          codes_dst = (uint8_t*)a.cache.codes[kv] + prow * CB;
+          meta_dst = (uint8_t*)a.cache.meta[kv] + prow * Lo.meta_bytes;
+          cb = CB; mb = Lo.meta_bytes;
+        }
+      }
+      const int bits = tr ? 8 : code_bits(FMT);
+      const int per_word = 32 / bits;
+      if (lane < cb / 4) {
+        uint32_t w = 0;
+        for (int k = 0; k < per_word; ++k)
+          w |= (uint32_t)s_code[slot][lane * per_word + k] << (bits * k);
+        ((uint32_t*)codes_dst)[lane] = w;
+      }
+      if (lane < mb / 4) ((uint32_t*)meta_dst)[lane] = s_meta[slot][lane];
+      else if (mb < 4 && lane == 0) {
+        for (int k = 0; k < mb; ++k) meta_dst[k] = ((uint8_t*)s_meta[slot])[k];
+      }
+    }
+
+    // ordered compaction of outlier records: channels 4*lane .. 4*lane+3 of this row
+    uint32_t fl = 0;
+    int cnt = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t f = s_flag[slot][4 * lane + k];
+      fl |= f << k;
+      cnt += (int)f;
+    }
+    int incl = cnt;  // inclusive scan over the 32 lanes of the row
+#pragma unroll
+    for (int d = 1; d < 32; d <<= 1) {
+      const int y = __shfl_up(incl, d, 32);
+      if (lane >= d) incl += y;
+    }
+    if (lane == 31) s_rowtot[slot] = incl;
+    __syncthreads();
+    int64_t base = running;
+    for (int s = 0; s < slot; ++s) base += s_rowtot[s];
+    int64_t total = 0;
+    for (int s = 0; s < RPI; ++s) total += s_rowtot[s];
+    if (valid) {
+      if ((t & 15) == 0 && lane == 0) bstart[t >> 4] = (int32_t)min(base, (int64_t)INT32_MAX);
+      int64_t k = base + (incl - cnt);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if ((fl >> q) & 1u) {
+          const int c = 4 * lane + q;
+          if (k < Lo.outl_cap) {
+            oidx[k] = (uint32_t)t * kHeadDim + (uint32_t)c;
+            const float xv = s_x[slot][c];
+            if (a.outl == KVQ_OUTL_FP16) ((uint16_t*)oval)[k] = (uint16_t)f32_to_half_bits(xv);
+            else oval[k] = (uint8_t)f32_to_e4m3(xv);
+          } else {
+            report(a.cache.status, KVQ_ERR_CAPACITY);
+          }
+          ++k;
+        }
+      }
+    }
+    running += total;
+    __syncthreads();
+  }
+  if (tid == 0) a.cache.outl_count[lid] = (int32_t)min(running, Lo.outl_cap);
+}
+
+template <int FMT, int G>
+hipError_t launch_quantize_t(const QArgs& qa, int nlists, int max_new, hipStream_t st) {
+  if (max_new <= 2) {
+    quantize_append_kernel<FMT, G, 1><<<nlists, 64, 0, st>>>(qa);
+  } else {
+    quantize_append_kernel<FMT, G, 4><<<nlists, 256, 0, st>>>(qa);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quantize_append(const QuantizeLaunch& q, hipStream_t st) {
+  QArgs qa;
+  qa.L = q.L;
+  qa.cache = q.cache;
+  qa.k_new = q.k_new;
+  qa.v_new = q.v_new;
+  qa.positions = q.positions;
+  qa.counts = q.counts;
+  qa.block_table = q.block_table;
+  qa.max_new = q.max_new;
+  qa.outl = q.outl;
+  qa.tau2 = q.tau2;
+  qa.lloyd = q.lloyd;
+  const int nlists = q.L.B * q.L.H * 2;
+  switch (q.fmt) {
+    case FMT_INT4: return q.group == 32 ? launch_quantize_t<FMT_INT4, 32>(qa, nlists, q.max_new, st)
+                                        : launch_quantize_t<FMT_INT4, 64>(qa, nlists, q.max_new, st);
+    case FMT_FP4: return q.group == 32 ? launch_quantize_t<FMT_FP4, 32>(qa, nlists, q.max_new, st)
+                                       : launch_quantize_t<FMT_FP4, 64>(qa, nlists, q.max_new, st);
+    case FMT_C2: return launch_quantize_t<FMT_C2, 64>(qa, nlists, q.max_new, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace kvq

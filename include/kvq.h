@@ -1,0 +1,196 @@
+/*
+ * kvq — quantized-KV decode attention for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libkvq.so.  Every pointer argument named "device" is a HIP device pointer; every
+ * other pointer is host memory.  The caller owns and frees every buffer; the library keeps no
+ * global state and allocates no device memory.  Work is enqueued on the caller's stream
+ * (``stream`` is a hipStream_t, passed as void*; NULL is the default stream) and the call
+ * returns before the work completes.  Functions return KVQ_OK (0) or a negative kvq_status.
+ *
+ * What is computed (pages cited by title and section):
+ *  - "Hierarchical Token Routing and Sub-2-Bit Non-Linear KV Compression ...", section
+ *    "Paradigm 2: Sub-2-Bit Non-Linear KV-Cache Quantization": outliers beyond tau standard
+ *    deviations are isolated and kept in FP8 (E4M3); the remaining values are coded against a
+ *    4-centroid (2-bit) codebook fitted by k-means per group; section "Hardware-Kernel Fusion:
+ *    Eliminating DRAM Round-Trips": dequantization is fused into the attention kernel.
+ *  - "The Sub-10ms Barrier: Fusing Sparse MoE Routing with FP4 KV-Cache Quantization",
+ *    section "2. FP4/INT4 KV-Cache Quantization": block-wise asymmetric INT4 with
+ *    S = (max - min)/(2^b - 1) per group of 32 or 64 along the head dimension, or FP4 E2M1,
+ *    computed at token insertion and dequantized inside flash-decoding.
+ *  - "Hierarchical Token Gating and Tiered KV-Cache Paging ...", section "2. Entropy-Guided
+ *    Tiered KV-Cache Quantization": 16-token pages held either in an FP8 tier or in the 2-bit
+ *    tier, read through a paged-attention block table.
+ *  - "Sub-5ms MoE Inference ...", section "Sub-Byte KV-Cache Quantization": fp16 outlier
+ *    tensor beside packed 2-bit codes.
+ *
+ * Logical row encoding (one row = D values of one token, one KV head, K or V; a group = g
+ * consecutive channels):
+ *  - statistics per group in float32 with a fixed pairwise reduction tree; value x is an
+ *    outlier iff (x - mean)^2 * (g - 1) > tau^2 * sum((x - mean)^2)  (i.e. |x - mean| > tau *
+ *    unbiased std), one pass, strict;
+ *  - the quantizer is fitted on the non-outliers; an outlier slot holds the code of 0.0;
+ *  - INT4_ASYM: codes 0..15, per group fp16 scale S and fp16 zero z (= fp16(min)),
+ *    value = code * S + z.  Metadata per group: [S, z] (4 bytes).
+ *  - FP4_E2M1: codes sign<<3 | magnitude index into {0,.5,1,1.5,2,3,4,6}, per group an E4M3
+ *    scale = E4M3(absmax / 6) (1 byte).  value = e2m1(code) * scale.
+ *  - CENTROID2: codes 0..3, per group 4 fp16 centroids (8 bytes) from quartile-bin seeds and
+ *    ``lloyd_iters`` Lloyd iterations.  value = centroid[code].
+ *  - FP8_E4M3_ROW: codes E4M3(x / s), one fp32 scale s = absmax / 448 per row (4 bytes), no
+ *    outliers.  value = e4m3(code) * s.
+ *  Codes are packed LSB-first along the channel axis (2-bit: channel 4k+r in bits 2r..2r+1 of
+ *  byte k; 4-bit: channel 2k in bits 0-3, 2k+1 in bits 4-7 of byte k).
+ *
+ * Outlier side lists: one per (sequence b, KV head h, K=0 / V=1), records in ascending
+ * (token, channel) order: uint32 index = token * D + channel and the ORIGINAL value rounded to
+ * the outlier dtype (fp16 bits or an E4M3 byte).  outl_count[b][h][kv] holds the record
+ * count; outl_block_start[b][h][kv][blk] holds the number of records with token < 16 * blk
+ * (written when token 16 * blk is appended).  Dequantization overwrites the code value at an
+ * outlier position with the record's value.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVQ_OK = 0,
+  KVQ_ERR_INVALID_ARG = -1,  /* shape, pointer or range check failed on the host or device */
+  KVQ_ERR_UNSUPPORTED = -2,  /* format / group / head-dim combination not implemented */
+  KVQ_ERR_WORKSPACE = -3,    /* workspace pointer NULL or smaller than kvq_workspace_bytes */
+  KVQ_ERR_HIP = -4,          /* a HIP launch returned an error */
+  KVQ_ERR_CAPACITY = -5      /* device status only: an outlier list overflowed its capacity */
+} kvq_status;
+
+typedef enum {
+  KVQ_FMT_FP16 = 0,          /* unquantized, for kvq_kv_bytes only */
+  KVQ_FMT_FP8_E4M3_ROW = 1,  /* FP8 tier of a paged cache */
+  KVQ_FMT_INT4_ASYM = 2,
+  KVQ_FMT_FP4_E2M1 = 3,
+  KVQ_FMT_CENTROID2 = 4,
+  KVQ_FMT_BF16 = 5           /* unquantized, for kvq_kv_bytes only */
+} kvq_format;
+
+typedef enum { KVQ_OUTL_NONE = 0, KVQ_OUTL_FP16 = 1, KVQ_OUTL_FP8_E4M3 = 2 } kvq_outlier_dtype;
+
+/* Problem description (the pages' GQA heads H, head dim D, context S, batch B, group size,
+ * bit width via the format, and outlier threshold tau).  Constraints checked on the host:
+ * head_dim == 128; num_q_heads % num_kv_heads == 0 with 1 <= num_q_heads/num_kv_heads <= 16;
+ * group_size in {32, 64} dividing head_dim (INT4 / FP4: 32 or 64; CENTROID2: 64);
+ * max_seq_len >= 1; outlier_sigma > 0; lloyd_iters in [0, 64]; page_size 0 (contiguous) or 16
+ * (paged, tiered: tier 2 = ``format``, tier 1 = FP8_E4M3_ROW; only CENTROID2 tier 2). */
+typedef struct {
+  int32_t batch;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t max_seq_len;       /* token capacity per sequence */
+  int32_t format;            /* kvq_format of the (tier-2) codes */
+  int32_t group_size;
+  int32_t outlier_dtype;     /* kvq_outlier_dtype */
+  float outlier_sigma;       /* tau */
+  int32_t lloyd_iters;       /* CENTROID2 only */
+  int32_t page_size;         /* 0 = contiguous, 16 = paged */
+  int32_t num_pages;         /* paged: slots in the tier-2 page pool */
+  int32_t num_pages_fp8;     /* paged: slots in the FP8 tier-1 page pool */
+  int32_t max_pages_per_seq; /* paged: row length of the block table */
+} kvq_params;
+
+/* Device buffers of one cache layer; index [0] = keys, [1] = values.
+ * Contiguous:  codes[kv]  [B][H][max_seq_len][code_bytes]      code_bytes = D*bits/8
+ *              meta[kv]   [B][H][max_seq_len][meta_bytes]      per-row group metadata
+ * Paged:       codes[kv]  [num_pages][H][16][code_bytes]       tier-2 pool (128-byte aligned)
+ *              meta[kv]   [num_pages][H][16][meta_bytes]
+ *              codes8[kv] [num_pages_fp8][H][16][D]            FP8 tier-1 pool
+ *              scale8[kv] [num_pages_fp8][H][16] float         per-row FP8 scales
+ * Outliers:    outl_idx[kv] [B][H][outl_capacity] uint32, outl_val[kv] [B][H][outl_capacity]
+ *              (uint16 fp16 bits or uint8 E4M3), outl_count [B][H][2] int32,
+ *              outl_block_start [B][H][2][ceil(max_seq_len/16)] int32.
+ * status: one int32 the kernels set (first error wins) to KVQ_ERR_CAPACITY or
+ *         KVQ_ERR_INVALID_ARG when a device-side check fails; the library never clears it.
+ * Buffers may be uninitialised except outl_count / status (zero before first use). */
+typedef struct {
+  void* codes[2];
+  void* meta[2];
+  void* codes8[2];
+  float* scale8[2];
+  uint32_t* outl_idx[2];
+  void* outl_val[2];
+  int32_t* outl_count;
+  int32_t* outl_block_start;
+  int64_t outl_capacity;
+  int32_t* status;
+} kvq_cache;
+
+/* Byte sizes of every buffer of kvq_cache for these params (host only). */
+typedef struct {
+  uint64_t codes;        /* per kv */
+  uint64_t meta;         /* per kv */
+  uint64_t codes8;       /* per kv, paged */
+  uint64_t scale8;       /* per kv, paged */
+  uint64_t outl_idx;     /* per kv, for outl_capacity records per list */
+  uint64_t outl_val;     /* per kv */
+  uint64_t outl_count;
+  uint64_t outl_block_start;
+  uint32_t code_bytes_per_row;
+  uint32_t meta_bytes_per_row;
+} kvq_cache_sizes_t;
+
+/* KV bytes for num_tokens tokens over num_layers layers: for FP16/BF16 exactly
+ * 2 * L * H * D * 2 * tokens ("Hierarchical Token Routing ...", section "The Bottleneck",
+ * KV size per token = 2 x L x H x D x precision); for quantized formats
+ * 2 * L * H * tokens * (code_bytes + meta_bytes per row) + num_outliers * (value bytes + 4).
+ * Uses num_kv_heads, head_dim, format, group_size, outlier_dtype of *p.  Host only. */
+int32_t kvq_kv_bytes(const kvq_params* p, int32_t num_layers, int64_t num_tokens,
+                     int64_t num_outliers, uint64_t* out_bytes);
+
+int32_t kvq_cache_sizes(const kvq_params* p, int64_t outl_capacity, kvq_cache_sizes_t* out);
+
+/* Quantize-on-append ("computed dynamically ... during token insertion", "The Sub-10ms
+ * Barrier", section "2. FP4/INT4 KV-Cache Quantization", item 2).
+ * k_new, v_new: device float32 [B][H][max_new][D].  positions, counts: device int32 [B];
+ * sequence b receives rows i < counts[b] at tokens positions[b] + i.  Appending at position p
+ * first truncates every outlier list of b to the records of tokens < p (so re-appending a
+ * token replaces it); tokens < p must already be in the cache.  block_table: device int32
+ * [B][max_pages_per_seq] (paged) or NULL; entry bit 31 = FP8 tier, bits 0..30 = slot in that
+ * tier's pool.  Device-side errors (position + count > max_seq_len, list overflow) set
+ * *status; overflowing records are dropped. */
+int32_t kvq_quantize_append(const kvq_params* p, const kvq_cache* cache, const float* k_new,
+                            const float* v_new, int32_t max_new, const int32_t* positions,
+                            const int32_t* counts, const int32_t* block_table, void* stream);
+
+/* Workspace for kvq_decode_attention: split-K partials B * Hq * ceil(max_seq_len/chunk) *
+ * (D + 2) floats (0 when a single chunk covers max_seq_len).  split_chunk 0 selects the
+ * default (whole sequence in one chunk for contiguous caches, 2048 for paged). */
+int32_t kvq_workspace_bytes(const kvq_params* p, int32_t split_chunk, uint64_t* out_bytes);
+
+/* Fused dequantize + flash-decoding attention ("Fused Dequantization & FlashAttention
+ * Kernel" of the figure in "The Bottleneck"; "Attention Phase / Flash-Decoding Engine" of
+ * the figure in "The Twin Bottlenecks").  For each b and query head hq (KV head
+ * hq * H / Hq): out[b][hq] = softmax_t(sm_scale * q . k_t) . v_t over tokens t < seq_lens[b],
+ * with k_t, v_t dequantized on the fly; chunks of split_chunk tokens (a multiple of 64) are
+ * merged by log-sum-exp.  q_bf16: device bfloat16 [B][Hq][D] (values must be finite and
+ * within fp16 range); seq_lens: device int32 [B], 1 <= seq_lens[b] <= max_seq_len and no more
+ * than the tokens appended; block_table as above (paged) or NULL; out: device float32
+ * [B][Hq][D]; workspace: device, ws_bytes >= kvq_workspace_bytes. */
+int32_t kvq_decode_attention(const kvq_params* p, const kvq_cache* cache, const void* q_bf16,
+                             const int32_t* seq_lens, const int32_t* block_table,
+                             float sm_scale, int32_t split_chunk, float* out, void* workspace,
+                             uint64_t ws_bytes, void* stream);
+
+/* Streaming read of `bytes` (multiple of 16) from device buffer src, XOR-reduced into sink
+ * (device, >= 4 * 1024 * 256 bytes): measures the practical HBM read ceiling. */
+int32_t kvq_probe_read(const void* src, uint64_t bytes, void* sink, void* stream);
+/* Device-to-device copy of `bytes` (multiple of 16), used to calibrate byte counters. */
+int32_t kvq_probe_copy(const void* src, void* dst, uint64_t bytes, void* stream);
+
+const char* kvq_status_string(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

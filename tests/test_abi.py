@@ -1,0 +1,111 @@
+"""CPU tests of the C ABI: the library loads, exports every function include/kvq.h declares,
+and its host-side arithmetic and argument validation behave as documented (no GPU calls)."""
+
+import os
+import re
+
+import pytest
+
+import decode_attention_sub_amd as K
+from oracle import kvbytes as KB
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "kvq.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:int32_t|const char\*)\s+(kvq_\w+)\(", src, re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 8
+    for n in names:
+        assert hasattr(K._lib, n), n
+    assert set(names) == set(K.EXPORTED)
+
+
+def test_kv_bytes_matches_formula_and_oracle():
+    p = K.make_params(64, 64, 8, 32768, "fp16", 64, "none")
+    assert K.kvq_kv_bytes(p, 80, 1) == 327680
+    assert K.kvq_kv_bytes(p, 1, 64 * 32768) == 8589934592
+    for fmt, g, out in [("int4", 32, "fp16"), ("fp4", 32, "fp16"), ("c2", 64, "e4m3")]:
+        p = K.make_params(4, 32, 8, 1000, fmt, g, out)
+        for L, T, n in [(1, 1, 0), (80, 12345, 678), (3, 7, 1)]:
+            assert K.kvq_kv_bytes(p, L, T, n) == KB.kv_bytes(fmt, L, 8, 128, T, g, n, out)
+
+
+def test_cache_sizes_and_workspace():
+    p = K.make_params(64, 64, 8, 32768, "c2", 64, "e4m3")
+    s = K.kvq_cache_sizes(p, 100)
+    assert (s.code_bytes_per_row, s.meta_bytes_per_row) == (32, 16)
+    assert s.codes == 64 * 8 * 32768 * 32 and s.meta == 64 * 8 * 32768 * 16
+    assert s.outl_idx == 64 * 8 * 100 * 4 and s.outl_val == 64 * 8 * 100
+    assert s.outl_block_start == 64 * 8 * 2 * 2048 * 4
+    assert K.kvq_workspace_bytes(p) == 0                       # one chunk covers the sequence
+    assert K.kvq_workspace_bytes(p, 2048) == 64 * 64 * 16 * 130 * 4
+    p4 = K.make_params(4, 64, 8, 131072, "fp4", 32, "fp16")
+    s4 = K.kvq_cache_sizes(p4, 10)
+    assert (s4.code_bytes_per_row, s4.meta_bytes_per_row) == (64, 4)
+    pp = K.make_params(2, 8, 2, 100, "c2", 64, "e4m3", page_size=16, num_pages=9,
+                       num_pages_fp8=4, max_pages_per_seq=7)
+    sp = K.kvq_cache_sizes(pp, 10)
+    assert sp.codes == 9 * 2 * 16 * 32 and sp.codes8 == 4 * 2 * 16 * 128 and sp.scale8 == 4 * 2 * 16 * 4
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=64), K.KVQ_ERR_UNSUPPORTED),
+    (dict(Hq=12, H=8), K.KVQ_ERR_INVALID_ARG),
+    (dict(Hq=64, H=2), K.KVQ_ERR_UNSUPPORTED),            # GQA group of 32
+    (dict(group=48), K.KVQ_ERR_UNSUPPORTED),
+    (dict(fmt="c2", group=32), K.KVQ_ERR_UNSUPPORTED),
+    (dict(S_cap=0), K.KVQ_ERR_INVALID_ARG),
+    (dict(sigma=0.0), K.KVQ_ERR_INVALID_ARG),
+    (dict(sigma=float("nan")), K.KVQ_ERR_INVALID_ARG),
+    (dict(fmt="fp16"), K.KVQ_ERR_UNSUPPORTED),
+])
+def test_invalid_params_rejected(kw, status):
+    base = dict(B=2, Hq=8, H=2, S_cap=100, fmt="c2", group=64, outlier="e4m3", sigma=3.0, D=128)
+    base.update(kw)
+    p = K.make_params(base["B"], base["Hq"], base["H"], base["S_cap"], base["fmt"],
+                      base["group"], base["outlier"], base["sigma"], D=base["D"])
+    with pytest.raises(K.KvqError) as e:
+        K.kvq_workspace_bytes(p)
+    assert e.value.status == status
+
+
+def test_paged_params_validation():
+    bad = K.make_params(2, 8, 2, 100, "c2", 64, "e4m3", page_size=16, num_pages=9,
+                        num_pages_fp8=4, max_pages_per_seq=6)          # 6 * 16 < 100
+    with pytest.raises(K.KvqError):
+        K.kvq_workspace_bytes(bad)
+    bad = K.make_params(2, 8, 2, 100, "int4", 32, "fp16", page_size=16, num_pages=9,
+                        max_pages_per_seq=7)                             # paged tier 2 is 2-bit only
+    with pytest.raises(K.KvqError):
+        K.kvq_workspace_bytes(bad)
+    bad = K.make_params(2, 8, 2, 100, "c2", 64, "e4m3", page_size=32, max_pages_per_seq=7)
+    with pytest.raises(K.KvqError):
+        K.kvq_workspace_bytes(bad)
+
+
+def test_split_chunk_must_be_multiple_of_64():
+    p = K.make_params(2, 8, 2, 1000, "c2", 64, "e4m3")
+    assert K.kvq_workspace_bytes(p, 128) == 2 * 8 * 8 * 130 * 4
+    with pytest.raises(K.KvqError):
+        K.kvq_workspace_bytes(p, 100)
+
+
+def test_null_pointers_rejected_before_launch():
+    p = K.make_params(2, 8, 2, 100, "c2", 64, "e4m3")
+    c = K.kvq_cache()
+    st = K._lib.kvq_decode_attention(K.C.byref(p), K.C.byref(c), None, None, None, 0.1, 0,
+                                     None, None, 0, None)
+    assert st == K.KVQ_ERR_INVALID_ARG
+    st = K._lib.kvq_quantize_append(K.C.byref(p), K.C.byref(c), None, None, 1, None, None, None,
+                                    None)
+    assert st == K.KVQ_ERR_INVALID_ARG
+
+
+def test_status_strings():
+    for s in (0, -1, -2, -3, -4, -5):
+        assert K.kvq_status_string(s) != "unknown status"

@@ -1,0 +1,159 @@
+"""GPU parity: the HIP quantize-append kernel against the oracle bit for bit (codes, metadata,
+outlier lists, block starts), and the HIP decode attention against the oracle's float64
+attention on the same dequantized values (max-abs <= 2e-3), at sizes the oracle finishes in
+seconds that still span several 64-token steps, several split-K chunks and a ragged tail."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+from workloads import CONFIGS  # noqa: E402
+from workloads import device as WD  # noqa: E402
+
+from gpu_util import (ATOL, assert_list_equal, log, oracle_attention, oracle_list,  # noqa: E402
+                      page_tiers_of, read_list, run_decode)
+
+SMALL = {
+    # INT4 g32 + fp16 outliers with the x20 channels, GQA 4, ragged S
+    "int4_small": WD.variant(CONFIGS["int4_b1_s1k"], B=2, S=777),
+    # 2-bit g64 + E4M3 outliers with Laplace spikes, GQA 4
+    "c2_small": WD.variant(CONFIGS["c2_b16_s8k"], B=2, H=2, Hq=8, S=1000),
+    # 2-bit, LogNormal key channels, GQA 8
+    "c2_g8_small": WD.variant(CONFIGS["c2_b64_s32k"], B=2, H=2, Hq=16, S=1100),
+    # FP4 g32 + fp16 outliers, GQA 8
+    "fp4_small": WD.variant(CONFIGS["fp4_b4_s128k"], B=2, H=2, Hq=16, S=3000),
+    # tiered paged cache, variable lengths
+    "tiered_small": WD.variant(CONFIGS["tiered_b32_paged"], B=3, H=2, Hq=8, S=3000,
+                               S_range=(90, 3000), fp8_page_frac=0.3),
+}
+
+
+@pytest.fixture(scope="module", params=sorted(SMALL))
+def small(request):
+    w = SMALL[request.param]
+    log(f"[gpu] building {request.param} {w}")
+    dc = WD.build(w)
+    assert dc.cache.status() == 0
+    return request.param, dc
+
+
+def test_quantize_bit_exact(small):
+    name, dc = small
+    w = dc.w
+    for b in range(w.B):
+        for h in range(w.H):
+            for kv in (0, 1):
+                S = int(dc.seq_lens_host[b])
+                got = read_list(dc, b, h, kv)
+                ref = oracle_list(w, b, h, kv, S, page_tiers_of(dc, b))
+                assert_list_equal(got, ref, f"{name} b={b} h={h} kv={kv}")
+
+
+@pytest.mark.parametrize("split", [0, 128, 512])
+def test_decode_matches_oracle(small, split):
+    name, dc = small
+    w = dc.w
+    if dc.w.paged and split == 0:
+        split = 256
+    log(f"[gpu] decode {name} split={split}")
+    sm = 1.0 / math.sqrt(w.D)
+    got = run_decode(dc, split_chunk=split, sm_scale=sm)
+    for b in range(w.B):
+        ref = oracle_attention(dc, b, range(w.Hq), sm)
+        for hq, o in ref.items():
+            err = np.abs(got[b, hq] - o).max()
+            assert err <= ATOL, f"{name} b={b} hq={hq} split={split}: max-abs {err}"
+
+
+def test_decode_deterministic(small):
+    name, dc = small
+    a = run_decode(dc, split_chunk=256)
+    b = run_decode(dc, split_chunk=256)
+    assert np.array_equal(a, b)
+
+
+def test_bulk_equals_incremental():
+    """Appending S tokens in one call equals S one-token appends, bit for bit."""
+    import decode_attention_sub_amd as K
+    from workloads import generate as G
+    w = WD.variant(CONFIGS["c2_b16_s8k"], B=2, H=2, Hq=8, S=70)
+    bulk = WD.build(w)
+    p = bulk.params
+    inc = K.KVCache.allocate(p, bulk.cache.outl_capacity)
+    for t in range(w.S):
+        k = np.stack([[G.kv_rows(w, b, h, 0, t, t + 1) for h in range(w.H)] for b in range(w.B)])
+        v = np.stack([[G.kv_rows(w, b, h, 1, t, t + 1) for h in range(w.H)] for b in range(w.B)])
+        pos = torch.full((w.B,), t, dtype=torch.int32, device="cuda")
+        cnt = torch.ones(w.B, dtype=torch.int32, device="cuda")
+        K.kvq_quantize_append(p, inc, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(),
+                              pos, cnt)
+    torch.cuda.synchronize()
+    for key in ("codes0", "codes1", "meta0", "meta1", "count", "bstart"):
+        assert torch.equal(bulk.cache.tensors[key], inc.tensors[key]), key
+    dci = WD.DeviceCache(w, p, inc, bulk.seq_lens_host, bulk.seq_lens, None, None, bulk.q_host,
+                         bulk.q)
+    for b in range(w.B):
+        for h in range(w.H):
+            for kv in (0, 1):
+                g1, g2 = read_list(bulk, b, h, kv), read_list(dci, b, h, kv)
+                assert np.array_equal(g1["idx"], g2["idx"]) and np.array_equal(g1["vals"], g2["vals"])
+
+
+def test_reappend_truncates_lists():
+    """Re-appending from position p replaces tokens >= p: lists end up as if built directly."""
+    import decode_attention_sub_amd as K
+    from workloads import generate as G
+    w = WD.variant(CONFIGS["c2_b16_s8k"], B=2, H=2, Hq=8, S=200)
+    dc = WD.build(w)
+    p = dc.params
+    # overwrite tokens 150..199 with the values of tokens 37..86 of another sequence
+    t0, n = 150, 50
+    k = np.stack([[G.kv_rows(w, 1 - b, h, 0, 37, 37 + n) for h in range(w.H)] for b in range(w.B)])
+    v = np.stack([[G.kv_rows(w, 1 - b, h, 1, 37, 37 + n) for h in range(w.H)] for b in range(w.B)])
+    pos = torch.full((w.B,), t0, dtype=torch.int32, device="cuda")
+    cnt = torch.full((w.B,), n, dtype=torch.int32, device="cuda")
+    K.kvq_quantize_append(p, dc.cache, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(), pos, cnt)
+    torch.cuda.synchronize()
+    from oracle import cache as OC
+    from gpu_util import specs
+    spec, _ = specs(w)
+    for b in range(w.B):
+        for h in range(w.H):
+            for kv in (0, 1):
+                x = np.concatenate([G.kv_rows(w, b, h, kv, 0, t0), G.kv_rows(w, 1 - b, h, kv, 37, 37 + n)])
+                ref = OC.build_list(x, spec)
+                assert_list_equal(read_list(dc, b, h, kv), ref, f"b={b} h={h} kv={kv}")
+
+
+def test_capacity_overflow_reports_status():
+    """A tiny outlier capacity makes the kernel drop records and report KVQ_ERR_CAPACITY."""
+    import decode_attention_sub_amd as K
+    from workloads import generate as G
+    w = WD.variant(CONFIGS["c2_b16_s8k"], B=1, H=1, Hq=4, S=300)
+    p = WD.make_params(w, w.S)
+    cache = K.KVCache.allocate(p, 3)
+    k = torch.from_numpy(G.kv_rows(w, 0, 0, 0, 0, w.S)[None, None]).cuda()
+    v = torch.from_numpy(G.kv_rows(w, 0, 0, 1, 0, w.S)[None, None]).cuda()
+    zero = torch.zeros(1, dtype=torch.int32, device="cuda")
+    cnt = torch.full((1,), w.S, dtype=torch.int32, device="cuda")
+    K.kvq_quantize_append(p, cache, k, v, zero, cnt)
+    torch.cuda.synchronize()
+    assert cache.status() == K.KVQ_ERR_CAPACITY
+    assert int(cache.tensors["count"][0].item()) == 3
+
+
+def test_out_of_range_position_reports_status():
+    import decode_attention_sub_amd as K
+    w = WD.variant(CONFIGS["c2_b16_s8k"], B=1, H=1, Hq=4, S=64)
+    p = WD.make_params(w, 64)
+    cache = K.KVCache.allocate(p, 100)
+    k = torch.zeros((1, 1, 8, 128), dtype=torch.float32, device="cuda")
+    pos = torch.full((1,), 60, dtype=torch.int32, device="cuda")
+    cnt = torch.full((1,), 8, dtype=torch.int32, device="cuda")
+    K.kvq_quantize_append(p, cache, k, k, pos, cnt)
+    torch.cuda.synchronize()
+    assert cache.status() == K.KVQ_ERR_INVALID_ARG

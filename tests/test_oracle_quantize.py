@@ -342,3 +342,12 @@ def test_c2_scale_invariance():
     c0 = F.fp16_from_bits(q0.meta.view(np.uint16))
     c1 = F.fp16_from_bits(q1.meta.view(np.uint16))
     assert np.array_equal(c0 * 4, c1)
+
+
+def test_int4_zero_minimum_is_positive_zero():
+    x = np.zeros((1, 32), dtype=F32)
+    x[0, 3] = -0.0
+    x[0, 5] = 1.5
+    q = Q.quantize_rows(x, Q.QuantSpec("int4", 32, "none"))
+    z_bits = q.meta.view(np.uint16)[0, 1]
+    assert z_bits == 0x0000
