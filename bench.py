@@ -1,0 +1,236 @@
+"""Benchmark of the quantized-KV decode step on one MI355X.
+
+One step = quantize-append of one new token per sequence (re-appending the last position, so the
+context stays at S) followed by fused dequantize + decode attention over S tokens.  Inputs are
+seeded synthetic data resident in HBM before timing starts.
+
+Prints one JSON line.  ``value`` is algorithmic KV bytes moved per second by the whole step;
+``roofline`` reports the decode kernel alone (its bytes / its average launch time measured with
+HIP events on the stream it runs on) against the 8 TB/s HBM peak; ``cpu_baseline`` is the oracle
+timed on a bounded sample of the same step on the host cores.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--workload c2_b64_s32k]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "decode-attn KV bytes/s and % of HBM peak; us/step at B=64,S=32k 2-bit"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(dc, n_outliers: int, seq_lens: np.ndarray) -> int:
+    """Bytes the decode must move: codes + per-group metadata of every row, outlier records
+    (value + 4-byte index) actually present, the bf16 query read and the fp32 output written,
+    plus the block table of a paged cache."""
+    import decode_attention_sub_amd as K
+    w, p = dc.w, dc.params
+    sz = K.kvq_cache_sizes(p, 1)
+    tokens = int(seq_lens.sum())
+    vb = 2 if w.outlier == "fp16" else 1
+    if w.paged:
+        tiers = (dc.block_table_host.view(np.uint32) >> 31) == 1
+        pages_fp8 = sum(int(tiers[b, :(int(s) + 15) // 16].sum()) for b, s in enumerate(seq_lens))
+        tok8 = pages_fp8 * 16  # whole pages (the last page of a sequence may be partial)
+        tok8 = min(tok8, tokens)
+        kv = 2 * w.H * ((tokens - tok8) * (sz.code_bytes_per_row + sz.meta_bytes_per_row)
+                        + tok8 * (w.D + 4))
+        table = sum((int(s) + 15) // 16 for s in seq_lens) * 4
+    else:
+        kv = 2 * w.H * tokens * (sz.code_bytes_per_row + sz.meta_bytes_per_row)
+        table = 0
+    return kv + n_outliers * (vb + 4) + w.B * w.Hq * w.D * (2 + 4) + table
+
+
+def read_ceiling_gbs(device="cuda") -> float:
+    import torch
+    import decode_attention_sub_amd as K
+    buf = torch.empty(4 << 30, dtype=torch.uint8, device=device)
+    buf.fill_(1)
+    sink = torch.empty(1024 * 256, dtype=torch.int32, device=device)
+    K.kvq_probe_read(buf, sink)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        K.kvq_probe_read(buf, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = 5 * buf.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del buf
+    return gbs
+
+
+def cpu_baseline(dc, budget_s: float = 12.0):
+    """The oracle (float64 dequantization + attention, float32 quantization of the new token),
+    as it stands, on a sample of (sequence, KV head) groups of the same step; extrapolated to
+    the full step and expressed in the metric's unit (GB/s of algorithmic bytes)."""
+    from threadpoolctl import threadpool_info
+    from oracle import attention as OA
+    from oracle import cache as OC
+    from oracle import quantize as OQ
+    from workloads import generate as G
+    from workloads.device import read_list
+
+    w = dc.w
+    spec = OQ.QuantSpec(w.fmt, w.group, w.outlier, w.sigma, w.lloyd_iters)
+    spec8 = OQ.QuantSpec("fp8row", 0, "none") if w.paged else None
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    pairs = [(b, h) for b in range(w.B) for h in range(w.H)]
+    rng = np.random.default_rng(0)
+    rng.shuffle(pairs)
+    done, t_total, bytes_done = 0, 0.0, 0
+    sm = 1.0 / math.sqrt(w.D)
+    for b, h in pairs:
+        lists = [read_list(dc, b, h, kv) for kv in (0, 1)]   # device bytes, read outside timing
+        S = int(dc.seq_lens_host[b])
+        x_new = [G.new_rows(w, b, h, G.NEW_K + kv, 0) for kv in (0, 1)]
+        t0 = time.perf_counter()
+        for kv in (0, 1):
+            OQ.quantize_rows(x_new[kv], spec)                # append of the new token
+        KV = []
+        for g in lists:
+            codes = OQ.unpack_codes(g["packed"], OQ.CODE_BITS[w.fmt], w.D)
+            KV.append(OC.dequantize_list(codes, g["meta"], g["idx"], g["vals"], spec, w.D,
+                                         g["tier1"], g.get("packed8"), g.get("meta8"), spec8))
+        qf = OA.bf16_to_f64(dc.q_host[b])
+        G_ = w.Hq // w.H
+        for hq in range(h * G_, (h + 1) * G_):
+            OA.attention_one(qf[hq], KV[0], KV[1], sm)
+        t_total += time.perf_counter() - t0
+        n_out = len(lists[0]["idx"]) + len(lists[1]["idx"])
+        sz_row = lists[0]["packed"].shape[1] + lists[0]["meta"].shape[1]
+        bytes_done += 2 * S * sz_row + n_out * ((2 if w.outlier == "fp16" else 1) + 4) \
+            + G_ * w.D * 6
+        done += 1
+        if t_total >= budget_s:
+            break
+    gbs = bytes_done / t_total / 1e9
+    return {"value": round(gbs, 6), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {len(pairs)} (sequence, KV head) groups of one step "
+                      f"({done * (w.Hq // w.H)} query heads over their full context), "
+                      f"{t_total:.1f} s of oracle time, extrapolated by bytes"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c2_b64_s32k")
+    ap.add_argument("--split", type=int, default=-1, help="split-K chunk (default: workload's)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the decode path is "
+              "sharded by (sequence, KV head) with no exchange, see DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import decode_attention_sub_amd as K
+    from workloads import CONFIGS
+    from workloads import device as WD
+    from workloads import generate as G
+
+    w = CONFIGS[args.workload]
+    torch.cuda.set_device(0)
+    ceiling = read_ceiling_gbs()
+    log(f"measured read ceiling {ceiling:.0f} GB/s")
+    t0 = time.time()
+    dc = WD.build(w, log=log if w.S >= 32768 else None)
+    log(f"cache built in {time.time() - t0:.1f} s")
+    p, cache = dc.params, dc.cache
+    split = w.split_chunk if args.split < 0 else args.split
+    ws = K.kvq_workspace_bytes(p, split)
+    work = torch.empty(max(ws // 4, 1), dtype=torch.float32, device="cuda") if ws else None
+    out = torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device="cuda")
+    lens = dc.seq_lens
+    pos = (lens - 1).to(torch.int32)
+    ones = torch.ones(w.B, dtype=torch.int32, device="cuda")
+    n_total = args.warmup + args.steps
+    new_k, new_v = [], []
+    for s in range(n_total):
+        k = np.stack([[G.new_rows(w, b, h, G.NEW_K, s)[0] for h in range(w.H)] for b in range(w.B)])
+        v = np.stack([[G.new_rows(w, b, h, G.NEW_V, s)[0] for h in range(w.H)] for b in range(w.B)])
+        new_k.append(torch.from_numpy(k[:, :, None, :]).cuda())
+        new_v.append(torch.from_numpy(v[:, :, None, :]).cuda())
+    stream = torch.cuda.current_stream()
+
+    def step(s, ev=None):
+        K.kvq_quantize_append(p, cache, new_k[s], new_v[s], pos, ones, dc.block_table)
+        if ev is not None:
+            ev[0].record(stream)
+        K.kvq_decode_attention(p, cache, dc.q, lens, out, work, dc.block_table, split_chunk=split)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    g0.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    g1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = g0.elapsed_time(g1) / args.steps
+    dec_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    status = cache.status()
+    if status != 0:
+        raise RuntimeError(f"device status {status}: {K.kvq_status_string(status)}")
+
+    n_out = int(cache.tensors["count"].sum().item())
+    lens_h = dc.seq_lens_host
+    dec_bytes = algorithmic_bytes(dc, n_out, lens_h)
+    app_bytes = w.B * w.H * 2 * (w.D * 4 + K.kvq_cache_sizes(p, 1).code_bytes_per_row
+                                 + K.kvq_cache_sizes(p, 1).meta_bytes_per_row)
+    step_bytes = dec_bytes + app_bytes
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    achieved = dec_bytes / (dec_ms * 1e-3) / 1e9
+    elems = 2 * w.H * int(lens_h.sum()) * w.D
+    res = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16" if w.fmt in ("c2", "fp4") else "f32", "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "H": w.H, "D": w.D,
+                   "S": int(lens_h.max()), "format": w.fmt, "group": w.group,
+                   "outliers": w.outlier, "tau": w.sigma, "split_chunk": split or "whole",
+                   "layers": 1},
+        "us_per_step_decode": round(dec_ms * 1e3, 2),
+        "us_per_step": round(ms_step * 1e3, 2),
+        "pct_hbm_peak": round(100 * achieved / HBM_PEAK_GBS, 2),
+        "pct_read_ceiling": round(100 * achieved / ceiling, 2),
+        "read_ceiling_GBs": round(ceiling, 1),
+        "tokens_heads_per_s": round(int(lens_h.sum()) * w.H / (dec_ms * 1e-3), 1),
+        "outliers": n_out, "outlier_fraction": round(n_out / elems, 6),
+        "decode_bytes": dec_bytes,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the oracle on a sample of the step")
+        res["cpu_baseline"] = cpu_baseline(dc)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -26,6 +26,12 @@ SMALL = {
     "c2_g8_small": WD.variant(CONFIGS["c2_b64_s32k"], B=2, H=2, Hq=16, S=1100),
     # FP4 g32 + fp16 outliers, GQA 8
     "fp4_small": WD.variant(CONFIGS["fp4_b4_s128k"], B=2, H=2, Hq=16, S=3000),
+    # FP4 with groups of 64 and INT4 with groups of 64 (generic kernel)
+    "fp4_g64_small": WD.variant(CONFIGS["fp4_b4_s128k"], B=1, H=2, Hq=8, S=900, group=64),
+    "int4_g64_small": WD.variant(CONFIGS["int4_b1_s1k"], B=1, S=500, group=64),
+    # 2-bit with GQA 16 (every MFMA row used) and with MHA (one row)
+    "c2_g16_small": WD.variant(CONFIGS["c2_b64_s32k"], B=1, H=1, Hq=16, S=1500),
+    "c2_mha_small": WD.variant(CONFIGS["c2_b16_s8k"], B=2, H=3, Hq=3, S=333),
     # tiered paged cache, variable lengths
     "tiered_small": WD.variant(CONFIGS["tiered_b32_paged"], B=3, H=2, Hq=8, S=3000,
                                S_range=(90, 3000), fp8_page_frac=0.3),

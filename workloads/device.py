@@ -98,3 +98,48 @@ def build(w: Workload, S_cap: Optional[int] = None, device: str = "cuda",
 
 def variant(w: Workload, **kw) -> Workload:
     return dataclasses.replace(w, **kw)
+
+
+def read_list(dc, b: int, h: int, kv: int):
+    """Device cache -> host arrays of one (b, h, kv) list in logical token order: packed codes,
+    metadata (FP8-tier rows separately for paged caches), outlier records and block starts."""
+    import decode_attention_sub_amd as K
+    w, p, t = dc.w, dc.params, dc.cache.tensors
+    S = int(dc.seq_lens_host[b])
+    sz = K.kvq_cache_sizes(p, dc.cache.outl_capacity)
+    CB, MB = sz.code_bytes_per_row, sz.meta_bytes_per_row
+    out = {}
+    if not w.paged:
+        codes = t[f"codes{kv}"].view(w.B, w.H, p.max_seq_len, CB)[b, h, :S].cpu().numpy()
+        meta = t[f"meta{kv}"].view(w.B, w.H, p.max_seq_len, MB)[b, h, :S].cpu().numpy()
+        out.update(packed=codes, meta=meta, tier1=None)
+    else:
+        ent = dc.block_table_host[b].view(np.uint32).astype(np.int64)[(np.arange(S) // 16)]
+        tier1 = (ent >> 31) == 1
+        slot = ent & 0x7FFFFFFF
+        j = np.arange(S) % 16
+        c2 = t[f"codes{kv}"].view(-1, w.H, 16, CB).cpu().numpy()
+        m2 = t[f"meta{kv}"].view(-1, w.H, 16, MB).cpu().numpy()
+        packed = np.zeros((S, CB), np.uint8)
+        meta = np.zeros((S, MB), np.uint8)
+        packed[~tier1] = c2[slot[~tier1], h, j[~tier1]]
+        meta[~tier1] = m2[slot[~tier1], h, j[~tier1]]
+        packed8 = np.zeros((S, w.D), np.uint8)
+        meta8 = np.zeros((S, 4), np.uint8)
+        if p.num_pages_fp8 > 0:
+            c8 = t[f"codes8_{kv}"].view(-1, w.H, 16, w.D).cpu().numpy()
+            s8 = t[f"scale8_{kv}"].view(-1, w.H, 16).cpu().numpy().view(np.uint8).reshape(-1, w.H, 16, 4)
+            packed8[tier1] = c8[slot[tier1], h, j[tier1]]
+            meta8[tier1] = s8[slot[tier1], h, j[tier1]]
+        out.update(packed=packed, meta=meta, tier1=tier1, packed8=packed8, meta8=meta8)
+    lid = (b * w.H + h) * 2 + kv
+    cnt = int(t["count"][lid].item())
+    cap = dc.cache.outl_capacity
+    idx = t[f"idx{kv}"].view(w.B, w.H, cap)[b, h, :cnt].cpu().numpy().view(np.uint32)
+    vb = 2 if w.outlier == "fp16" else 1
+    raw = t[f"val{kv}"].view(w.B, w.H, cap * vb)[b, h, :cnt * vb].cpu().numpy()
+    vals = raw.view(np.uint16) if vb == 2 else raw
+    nblk_all = (p.max_seq_len + 15) // 16
+    bstart = t["bstart"].view(w.B, w.H, 2, nblk_all)[b, h, kv, :(S + 15) // 16].cpu().numpy()
+    out.update(idx=idx, vals=vals, count=cnt, block_start=bstart)
+    return out
