@@ -135,6 +135,8 @@ def main():
     ap.add_argument("--workload", default="c2_b64_s32k")
     ap.add_argument("--split", type=int, default=-1, help="split-K chunk (default: workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one 1 GiB device copy (reference for byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the decode path is "
@@ -151,6 +153,12 @@ def main():
     torch.cuda.set_device(0)
     ceiling = read_ceiling_gbs()
     log(f"measured read ceiling {ceiling:.0f} GB/s")
+    if args.calibrate_copy:
+        src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        K.kvq_probe_copy(src, dst)
+        torch.cuda.synchronize()
+        del src, dst
     t0 = time.time()
     dc = WD.build(w, log=log if w.S >= 32768 else None)
     log(f"cache built in {time.time() - t0:.1f} s")
@@ -213,7 +221,7 @@ def main():
         "dtype": "f16" if w.fmt in ("c2", "fp4") else "f32", "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "H": w.H, "D": w.D,
                    "S": int(lens_h.max()), "format": w.fmt, "group": w.group,
-                   "outliers": w.outlier, "tau": w.sigma, "split_chunk": split or "whole",
+                   "outliers": w.outlier, "tau": w.sigma, "split_chunk": split if split else "default",
                    "layers": 1},
         "us_per_step_decode": round(dec_ms * 1e3, 2),
         "us_per_step": round(ms_step * 1e3, 2),

@@ -12,6 +12,8 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-fno-gpu-rdc", "-Wall", "-Wno-unused-function",
+    # keep MFMA accumulators in VGPRs: the online-softmax rescale touches them with VALU ops
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
 
 

@@ -66,25 +66,27 @@ template <> struct Buf<FMT_FP4> { uint4 kc0, kc1, vc0, vc1; uint32_t km, vm; };
 struct Recs {       // up to 128 outlier records per list per step, two per lane
   uint32_t kidx0, kidx1, vidx0, vidx1;
   uint32_t kval0, kval1, vval0, vval1;
-  int kr0, kr1, vr0, vr1;   // record range of the step (uniform)
+  int kr0, nk, vr0, nv;     // first record and record count of the step (uniform)
 };
 
-template <int FMT>
-__device__ __forceinline__ void load_codes(Buf<FMT>& bf, const uint8_t* ck, const uint8_t* cv,
-                                           const uint8_t* mk, const uint8_t* mv) {
-  if constexpr (FMT == FMT_C2) {
-    bf.kc = *(const uint4*)ck;
-    bf.vc = *(const uint4*)cv;
-    bf.km = *(const uint2*)mk;
-    bf.vm = *(const uint2*)mv;
-  } else {
-    bf.kc0 = *(const uint4*)ck;
-    bf.kc1 = *(const uint4*)(ck + 16);
-    bf.vc0 = *(const uint4*)cv;
-    bf.vc1 = *(const uint4*)(cv + 16);
-    bf.km = *(const uint16_t*)mk;
-    bf.vm = *(const uint16_t*)mv;
-  }
+// raw buffer resource (gfx9 family): loads at byte offsets >= num_records return zero
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 ld128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ uint2 ld64(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ uint32_t ld32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ uint32_t ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ uint32_t ld8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, (int)off, 0, 0);
 }
 
 // 64 channels of one 2-bit row -> 64 fp16 in transposed-block order at dst
@@ -130,21 +132,33 @@ __device__ __forceinline__ void expand_fp4(uint4 c0, uint4 c1, uint32_t m, _Floa
   }
 }
 
-__device__ __forceinline__ uint32_t outl_half_bits(uint32_t v, int outl) {
-  return outl == KVQ_OUTL_FP16 ? v : f32_to_half_bits(e4m3_to_f32(v));
+// stored outlier value -> fp16 bits (E4M3 values are exact in fp16)
+// E4M3 bits placed as fp16 bits ((code & 0x7F) << 7 | sign << 15) encode value * 2^-8 for every
+// code, subnormals included (both formats' subnormal steps line up); one exact fp16 multiply by
+// 256 restores the value.
+template <int OUTL>
+__device__ __forceinline__ _Float16 outl_half(uint32_t v) {
+  if constexpr (OUTL == KVQ_OUTL_FP16) {
+    return __builtin_bit_cast(_Float16, (uint16_t)v);
+  } else {
+    const uint32_t h = ((v & 0x7Fu) << 7) | ((v & 0x80u) << 8);
+    return __builtin_bit_cast(_Float16, (uint16_t)h) * (_Float16)256.0f;
+  }
 }
 
-template <int FMT>
-__device__ __forceinline__ void patch(_Float16* tile, uint32_t idx, uint32_t val, int ts, int nval,
-                                      int outl) {
-  if (idx == 0xFFFFFFFFu) return;
-  const int t = (int)(idx >> 7) - ts;
-  if (t < 0 || t >= nval) return;
-  const int c = (int)(idx & 127u);
-  tile[t * kRow + chan_pos<FMT>(c)] = __builtin_bit_cast(_Float16, (uint16_t)outl_half_bits(val, outl));
+// Overwrite one outlier position in a tile.  Records outside the step (or past the step's
+// record count) are written to a pad slot (row 0, column 128) that no operand read touches.
+template <int FMT, int OUTL>
+__device__ __forceinline__ void patch(_Float16* tile, bool have, uint32_t idx, uint32_t val,
+                                      int ts, int nval) {
+  const uint32_t t = (idx >> 7) - (uint32_t)ts;
+  const uint32_t c = idx & 127u;
+  const bool ok = have && t < (uint32_t)nval;
+  const uint32_t at = ok ? t * (uint32_t)kRow + (uint32_t)chan_pos<FMT>((int)c) : (uint32_t)kHeadDim;
+  tile[at] = outl_half<OUTL>(val);
 }
 
-template <int FMT>
+template <int FMT, int OUTL>
 __global__ void __launch_bounds__(256) decode_mfma_kernel(DecodeLaunch d) {
   __shared__ __attribute__((aligned(16))) _Float16 s_lds[kWaves * kWaveLds];
   __shared__ float s_ml[kWaves][16][2];
@@ -160,11 +174,14 @@ __global__ void __launch_bounds__(256) decode_mfma_kernel(DecodeLaunch d) {
   if (t0 >= S) return;
   const int t1 = min(t0 + d.chunk, S);
   const int G = d.Hq / L.H;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   const int r = lane & 15, kg = lane >> 4;           // MFMA lane coordinates
   const int trow = lane & 31, half = lane >> 5;      // dequant lane coordinates
   constexpr int CB = FMT == FMT_C2 ? 32 : 64;
   constexpr int MB = FMT == FMT_C2 ? 16 : 4;
+  constexpr int VB = OUTL == KVQ_OUTL_FP16 ? 2 : 1;
+  constexpr bool HAS_OUTL = OUTL != KVQ_OUTL_NONE;
 
   _Float16* ktile = s_lds + wave * kWaveLds;
   _Float16* vtile = ktile + kTile;
@@ -172,85 +189,105 @@ __global__ void __launch_bounds__(256) decode_mfma_kernel(DecodeLaunch d) {
   // query operand (B of S^T = K^ Q^T): lane (row r, k-group kg), positions 32*ks + 8*kg + e
   half8 qop[4];
   {
+    // every lane reads a valid row (padding rows read row 0 and are zeroed after the load)
     const uint16_t* qrow = d.q + ((size_t)b * d.Hq + (size_t)h * G + (r < G ? r : 0)) * kHeadDim;
+    uint16_t raw[4][8];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int c = chan_pos<FMT>(32 * ks + 8 * kg + e);  // the order is an involution
-        const float v = r < G ? as_f32((uint32_t)qrow[c] << 16) : 0.0f;
-        qop[ks][e] = (_Float16)v;
-      }
+      for (int e = 0; e < 8; ++e) raw[ks][e] = qrow[chan_pos<FMT>(32 * ks + 8 * kg + e)];
+    const float keep = r < G ? 1.0f : 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qop[ks][e] = (_Float16)(as_f32((uint32_t)raw[ks][e] << 16) * keep);
   }
 
+  // buffer resources: rows [0, t1) of this (sequence, KV head); rows past t1 read as zero
   const size_t rowbase = ((size_t)b * L.H + h) * (size_t)L.S_cap;
-  const uint8_t* codesK = (const uint8_t*)d.cache.codes[0] + rowbase * CB + half * (CB / 2);
-  const uint8_t* codesV = (const uint8_t*)d.cache.codes[1] + rowbase * CB + half * (CB / 2);
-  const uint8_t* metaK = (const uint8_t*)d.cache.meta[0] + rowbase * MB + half * (MB / 2);
-  const uint8_t* metaV = (const uint8_t*)d.cache.meta[1] + rowbase * MB + half * (MB / 2);
-  const size_t lidK = list_id(L, b, h, 0), lidV = lidK + 1;
-  const int32_t* bsK = d.cache.outl_block_start + lidK * (size_t)L.nblk;
-  const int32_t* bsV = d.cache.outl_block_start + lidV * (size_t)L.nblk;
-  const size_t lbase = ((size_t)b * L.H + h) * (size_t)L.outl_cap;
-  const uint32_t* oidxK = d.cache.outl_idx[0] + lbase;
-  const uint32_t* oidxV = d.cache.outl_idx[1] + lbase;
-  const int outl = d.outl;
-  const int vbytes = outl == KVQ_OUTL_FP16 ? 2 : 1;
-  const uint8_t* ovalK = (const uint8_t*)d.cache.outl_val[0] + lbase * vbytes;
-  const uint8_t* ovalV = (const uint8_t*)d.cache.outl_val[1] + lbase * vbytes;
-  const int cntK = d.cache.outl_count[lidK], cntV = d.cache.outl_count[lidV];
+  const __amdgpu_buffer_rsrc_t rcK = make_rsrc((const uint8_t*)d.cache.codes[0] + rowbase * CB, (uint32_t)t1 * CB);
+  const __amdgpu_buffer_rsrc_t rcV = make_rsrc((const uint8_t*)d.cache.codes[1] + rowbase * CB, (uint32_t)t1 * CB);
+  const __amdgpu_buffer_rsrc_t rmK = make_rsrc((const uint8_t*)d.cache.meta[0] + rowbase * MB, (uint32_t)t1 * MB);
+  const __amdgpu_buffer_rsrc_t rmV = make_rsrc((const uint8_t*)d.cache.meta[1] + rowbase * MB, (uint32_t)t1 * MB);
+  const uint32_t coff = (uint32_t)(trow * CB + half * (CB / 2));
+  const uint32_t moff = (uint32_t)(trow * MB + half * (MB / 2));
+
+  const size_t lidK = list_id(L, b, h, 0);
   const int cap = (int)min(L.outl_cap, (int64_t)INT32_MAX);
+  __amdgpu_buffer_rsrc_t riK, riV, rvK, rvV, rbs;
+  int cntK = 0, cntV = 0;
+  const uint32_t* oidxK = nullptr;
+  const uint32_t* oidxV = nullptr;
+  const uint8_t* ovalK = nullptr;
+  const uint8_t* ovalV = nullptr;
+  if constexpr (HAS_OUTL) {
+    const size_t lbase = ((size_t)b * L.H + h) * (size_t)L.outl_cap;
+    oidxK = d.cache.outl_idx[0] + lbase;
+    oidxV = d.cache.outl_idx[1] + lbase;
+    ovalK = (const uint8_t*)d.cache.outl_val[0] + lbase * VB;
+    ovalV = (const uint8_t*)d.cache.outl_val[1] + lbase * VB;
+    riK = make_rsrc(oidxK, (uint32_t)cap * 4);
+    riV = make_rsrc(oidxV, (uint32_t)cap * 4);
+    rvK = make_rsrc(ovalK, (uint32_t)cap * VB);
+    rvV = make_rsrc(ovalV, (uint32_t)cap * VB);
+    rbs = make_rsrc(d.cache.outl_block_start + lidK * (size_t)L.nblk, (uint32_t)L.nblk * 8);
+    cntK = max(0, min(d.cache.outl_count[lidK], cap));
+    cntV = max(0, min(d.cache.outl_count[lidK + 1], cap));
+  }
 
   const int nsteps = (t1 - t0 + kStep - 1) / kStep;
   const int nmine = wave < nsteps ? (nsteps - wave + kWaves - 1) / kWaves : 0;
   auto step_ts = [&](int j) { return t0 + kStep * (wave + kWaves * j); };
 
-  // ---- per-step loaders
   auto issue_codes = [&](Buf<FMT>& bf, int j) {
-    const int ts = step_ts(j);
-    const int t = min(ts + trow, t1 - 1);
-    load_codes<FMT>(bf, codesK + (size_t)t * CB, codesV + (size_t)t * CB,
-                    metaK + (size_t)t * MB, metaV + (size_t)t * MB);
-  };
-  // lane 0..3 loads {K start, K end, V start, V end} of step j's records
-  auto issue_bounds = [&](int j) -> int {
-    if (outl == KVQ_OUTL_NONE) return 0;
-    const int ts = step_ts(j);
-    const int blk = ts >> 4;
-    const bool last = ts + kStep >= S;
-    int v = 0;
-    if (lane == 0) v = bsK[blk];
-    else if (lane == 1) v = last ? cntK : bsK[blk + 2];
-    else if (lane == 2) v = bsV[blk];
-    else if (lane == 3) v = last ? cntV : bsV[blk + 2];
-    return v;
-  };
-  auto issue_recs = [&](Recs& rc, int bnd) {
-    if (outl == KVQ_OUTL_NONE) { rc.kr0 = rc.kr1 = rc.vr0 = rc.vr1 = 0; return; }
-    rc.kr0 = max(0, min(__builtin_amdgcn_readlane(bnd, 0), cap));
-    rc.kr1 = max(rc.kr0, min(__builtin_amdgcn_readlane(bnd, 1), cap));
-    rc.vr0 = max(0, min(__builtin_amdgcn_readlane(bnd, 2), cap));
-    rc.vr1 = max(rc.vr0, min(__builtin_amdgcn_readlane(bnd, 3), cap));
-    const int a0 = rc.kr0 + lane, a1 = rc.kr0 + 64 + lane;
-    const int c0 = rc.vr0 + lane, c1 = rc.vr0 + 64 + lane;
-    rc.kidx0 = a0 < rc.kr1 ? oidxK[a0] : 0xFFFFFFFFu;
-    rc.kidx1 = a1 < rc.kr1 ? oidxK[a1] : 0xFFFFFFFFu;
-    rc.vidx0 = c0 < rc.vr1 ? oidxV[c0] : 0xFFFFFFFFu;
-    rc.vidx1 = c1 < rc.vr1 ? oidxV[c1] : 0xFFFFFFFFu;
-    if (vbytes == 2) {
-      rc.kval0 = a0 < rc.kr1 ? ((const uint16_t*)ovalK)[a0] : 0u;
-      rc.kval1 = a1 < rc.kr1 ? ((const uint16_t*)ovalK)[a1] : 0u;
-      rc.vval0 = c0 < rc.vr1 ? ((const uint16_t*)ovalV)[c0] : 0u;
-      rc.vval1 = c1 < rc.vr1 ? ((const uint16_t*)ovalV)[c1] : 0u;
+    const uint32_t ts = (uint32_t)step_ts(j);
+    if constexpr (FMT == FMT_C2) {
+      bf.kc = ld128(rcK, ts * CB + coff);
+      bf.vc = ld128(rcV, ts * CB + coff);
+      bf.km = ld64(rmK, ts * MB + moff);
+      bf.vm = ld64(rmV, ts * MB + moff);
     } else {
-      rc.kval0 = a0 < rc.kr1 ? ovalK[a0] : 0u;
-      rc.kval1 = a1 < rc.kr1 ? ovalK[a1] : 0u;
-      rc.vval0 = c0 < rc.vr1 ? ovalV[c0] : 0u;
-      rc.vval1 = c1 < rc.vr1 ? ovalV[c1] : 0u;
+      bf.kc0 = ld128(rcK, ts * CB + coff);
+      bf.kc1 = ld128(rcK, ts * CB + coff + 16);
+      bf.vc0 = ld128(rcV, ts * CB + coff);
+      bf.vc1 = ld128(rcV, ts * CB + coff + 16);
+      bf.km = ld16(rmK, ts * MB + moff);
+      bf.vm = ld16(rmV, ts * MB + moff);
+    }
+  };
+  // lanes 0..3 load {K start, K end, V start, V end} of step j's records (block starts)
+  auto issue_bounds = [&](int j) -> uint32_t {
+    if constexpr (!HAS_OUTL) return 0u;
+    const int blk = step_ts(j) >> 4;
+    const int which = lane & 3;  // 0: K blk, 1: K blk+2, 2: V blk, 3: V blk+2
+    const uint32_t off = (uint32_t)(((which >> 1) * L.nblk + blk + 2 * (which & 1)) * 4);
+    return ld32(rbs, off);
+  };
+  auto issue_recs = [&](Recs& rc, uint32_t bnd, int j) {
+    if constexpr (HAS_OUTL) {
+      const bool last = step_ts(j) + kStep >= S;
+      const int k0 = max(0, min(__builtin_amdgcn_readlane((int)bnd, 0), cap));
+      const int k1 = last ? cntK : max(0, min(__builtin_amdgcn_readlane((int)bnd, 1), cap));
+      const int v0 = max(0, min(__builtin_amdgcn_readlane((int)bnd, 2), cap));
+      const int v1 = last ? cntV : max(0, min(__builtin_amdgcn_readlane((int)bnd, 3), cap));
+      rc.kr0 = k0; rc.nk = max(k1 - k0, 0);
+      rc.vr0 = v0; rc.nv = max(v1 - v0, 0);
+      const uint32_t a0 = (uint32_t)(k0 + lane), a1 = a0 + 64u;
+      const uint32_t c0 = (uint32_t)(v0 + lane), c1 = c0 + 64u;
+      rc.kidx0 = ld32(riK, a0 * 4);
+      rc.kidx1 = ld32(riK, a1 * 4);
+      rc.vidx0 = ld32(riV, c0 * 4);
+      rc.vidx1 = ld32(riV, c1 * 4);
+      if constexpr (VB == 2) {
+        rc.kval0 = ld16(rvK, a0 * 2); rc.kval1 = ld16(rvK, a1 * 2);
+        rc.vval0 = ld16(rvV, c0 * 2); rc.vval1 = ld16(rvV, c1 * 2);
+      } else {
+        rc.kval0 = ld8(rvK, a0); rc.kval1 = ld8(rvK, a1);
+        rc.vval0 = ld8(rvV, c0); rc.vval1 = ld8(rvV, c1);
+      }
     }
   };
 
-  // ---- state
   floatx4 oacc[8];
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt) oacc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -260,7 +297,6 @@ __global__ void __launch_bounds__(256) decode_mfma_kernel(DecodeLaunch d) {
   auto consume = [&](const Buf<FMT>& bf, const Recs& rc, int j) {
     const int ts = step_ts(j);
     const int nval = min(kStep, t1 - ts);
-    // expand rows into the tiles
     _Float16* krow = ktile + trow * kRow + 64 * half;
     _Float16* vrow = vtile + trow * kRow + 64 * half;
     if constexpr (FMT == FMT_C2) {
@@ -270,19 +306,22 @@ __global__ void __launch_bounds__(256) decode_mfma_kernel(DecodeLaunch d) {
       expand_fp4(bf.kc0, bf.kc1, bf.km, krow);
       expand_fp4(bf.vc0, bf.vc1, bf.vm, vrow);
     }
-    if (outl != KVQ_OUTL_NONE) {
-      patch<FMT>(ktile, rc.kidx0, rc.kval0, ts, nval, outl);
-      patch<FMT>(ktile, rc.kidx1, rc.kval1, ts, nval, outl);
-      patch<FMT>(vtile, rc.vidx0, rc.vval0, ts, nval, outl);
-      patch<FMT>(vtile, rc.vidx1, rc.vval1, ts, nval, outl);
-      // more than 128 records in this step: the rest, read directly
-      for (int a = rc.kr0 + 128 + lane; a < rc.kr1; a += 64) {
-        const uint32_t v = vbytes == 2 ? ((const uint16_t*)ovalK)[a] : ovalK[a];
-        patch<FMT>(ktile, oidxK[a], v, ts, nval, outl);
-      }
-      for (int a = rc.vr0 + 128 + lane; a < rc.vr1; a += 64) {
-        const uint32_t v = vbytes == 2 ? ((const uint16_t*)ovalV)[a] : ovalV[a];
-        patch<FMT>(vtile, oidxV[a], v, ts, nval, outl);
+    if constexpr (HAS_OUTL) {
+      patch<FMT, OUTL>(ktile, lane < rc.nk, rc.kidx0, rc.kval0, ts, nval);
+      patch<FMT, OUTL>(ktile, lane + 64 < rc.nk, rc.kidx1, rc.kval1, ts, nval);
+      patch<FMT, OUTL>(vtile, lane < rc.nv, rc.vidx0, rc.vval0, ts, nval);
+      patch<FMT, OUTL>(vtile, lane + 64 < rc.nv, rc.vidx1, rc.vval1, ts, nval);
+      if (rc.nk > 128 || rc.nv > 128) {  // rare: the rest of a crowded step, read directly
+        for (int a = 128 + lane; a < rc.nk; a += 64) {
+          const int at = rc.kr0 + a;
+          const uint32_t v = VB == 2 ? ((const uint16_t*)ovalK)[at] : ovalK[at];
+          patch<FMT, OUTL>(ktile, true, oidxK[at], v, ts, nval);
+        }
+        for (int a = 128 + lane; a < rc.nv; a += 64) {
+          const int at = rc.vr0 + a;
+          const uint32_t v = VB == 2 ? ((const uint16_t*)ovalV)[at] : ovalV[at];
+          patch<FMT, OUTL>(vtile, true, oidxV[at], v, ts, nval);
+        }
       }
     }
     // S^T for tokens 0..15 and 16..31 of the step
@@ -297,13 +336,16 @@ __global__ void __launch_bounds__(256) decode_mfma_kernel(DecodeLaunch d) {
     // online softmax: lane holds query row r, tokens 4kg+v (tile 0) and 16+4kg+v (tile 1)
     float sc[8];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      sc[v] = (4 * kg + v) < nval ? s0[v] * sl2 : -INFINITY;
-      sc[4 + v] = (16 + 4 * kg + v) < nval ? s1[v] * sl2 : -INFINITY;
-    }
-    float mx = sc[0];
+    for (int v = 0; v < 4; ++v) { sc[v] = s0[v] * sl2; sc[4 + v] = s1[v] * sl2; }
+    if (nval < kStep) {
 #pragma unroll
-    for (int v = 1; v < 8; ++v) mx = fmaxf(mx, sc[v]);
+      for (int v = 0; v < 4; ++v) {
+        if (4 * kg + v >= nval) sc[v] = -INFINITY;
+        if (16 + 4 * kg + v >= nval) sc[4 + v] = -INFINITY;
+      }
+    }
+    float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
+                     fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float m_new = fmaxf(m_run, mx);
@@ -311,12 +353,14 @@ __global__ void __launch_bounds__(256) decode_mfma_kernel(DecodeLaunch d) {
     half8 phi, plo;
     float psum = 0.0f;
 #pragma unroll
-    for (int v = 0; v < 8; ++v) {
-      const float p = __builtin_amdgcn_exp2f(sc[v] - m_new);
-      psum += p;
-      const _Float16 hi = (_Float16)p;
-      phi[v] = hi;
-      plo[v] = (_Float16)(p - (float)hi);
+    for (int v = 0; v < 8; v += 2) {
+      const float p0 = __builtin_amdgcn_exp2f(sc[v] - m_new);
+      const float p1 = __builtin_amdgcn_exp2f(sc[v + 1] - m_new);
+      psum += p0 + p1;
+      const half2v hi = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(p0, p1));
+      const half2v lo = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(p0 - (float)hi[0], p1 - (float)hi[1]));
+      phi[v] = hi[0]; phi[v + 1] = hi[1];
+      plo[v] = lo[0]; plo[v + 1] = lo[1];
     }
     l_run = l_run * alpha + psum;
     m_run = m_new;
@@ -326,12 +370,12 @@ __global__ void __launch_bounds__(256) decode_mfma_kernel(DecodeLaunch d) {
     }
     // O^T += V^T P^T: A = V^T (16 channels x 32 tokens) through transposing LDS reads
     const lds_half* vbase = (const lds_half*)vtile;
+    const int col0 = 4 * (r & 3);
+    const int rowo = 4 * kg + (r >> 2);
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) {
-      const int col = 16 * mt + 4 * (r & 3);
-      const int rowo = 4 * kg + (r >> 2);
-      const half4v t0v = read_tr16(vbase + rowo * kRow + col);
-      const half4v t1v = read_tr16(vbase + (16 + rowo) * kRow + col);
+      const half4v t0v = read_tr16(vbase + rowo * kRow + 16 * mt + col0);
+      const half4v t1v = read_tr16(vbase + (16 + rowo) * kRow + 16 * mt + col0);
       const half8 av = {t0v[0], t0v[1], t0v[2], t0v[3], t1v[0], t1v[1], t1v[2], t1v[3]};
       oacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, phi, oacc[mt], 0, 0, 0);
       oacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, plo, oacc[mt], 0, 0, 0);
@@ -341,25 +385,27 @@ __global__ void __launch_bounds__(256) decode_mfma_kernel(DecodeLaunch d) {
   // ---- software pipeline: codes and records two steps ahead, record bounds three ahead
   Buf<FMT> buf[3];
   Recs rec[3];
-  int bnd[3];
+  uint32_t bnd[3] = {0u, 0u, 0u};
+  // Loads for steps past the wave's last step are issued anyway: their offsets lie past the
+  // buffer ranges (codes) or are clamped (records), so they return zeros or unused data without
+  // touching memory, and keeping every load unconditional lets the wait counters stay exact.
   if (nmine > 0) {
     bnd[0] = issue_bounds(0);
-    if (nmine > 1) bnd[1] = issue_bounds(1);
-    if (nmine > 2) bnd[2] = issue_bounds(2);
+    bnd[1] = issue_bounds(1);
+    bnd[2] = issue_bounds(2);
+    issue_recs(rec[0], bnd[0], 0);
     issue_codes(buf[0], 0);
-    issue_recs(rec[0], bnd[0]);
-    if (nmine > 1) { issue_codes(buf[1], 1); issue_recs(rec[1], bnd[1]); }
+    issue_recs(rec[1], bnd[1], 1);
+    issue_codes(buf[1], 1);
   }
   for (int j = 0; j < nmine; j += 3) {
 #pragma unroll
     for (int u = 0; u < 3; ++u) {
       const int jj = j + u;
       if (jj < nmine) {
-        if (jj + 3 < nmine) bnd[u] = issue_bounds(jj + 3);
-        if (jj + 2 < nmine) {
-          issue_recs(rec[(u + 2) % 3], bnd[(u + 2) % 3]);
-          issue_codes(buf[(u + 2) % 3], jj + 2);
-        }
+        bnd[u] = issue_bounds(jj + 3);
+        issue_recs(rec[(u + 2) % 3], bnd[(u + 2) % 3], jj + 2);
+        issue_codes(buf[(u + 2) % 3], jj + 2);
         consume(buf[u], rec[u], jj);
       }
     }
@@ -399,6 +445,15 @@ __global__ void __launch_bounds__(256) decode_mfma_kernel(DecodeLaunch d) {
   }
 }
 
+template <int FMT>
+void launch_fmt(const DecodeLaunch& d, dim3 grid, hipStream_t st) {
+  switch (d.outl) {
+    case KVQ_OUTL_NONE: decode_mfma_kernel<FMT, KVQ_OUTL_NONE><<<grid, 256, 0, st>>>(d); break;
+    case KVQ_OUTL_FP16: decode_mfma_kernel<FMT, KVQ_OUTL_FP16><<<grid, 256, 0, st>>>(d); break;
+    default: decode_mfma_kernel<FMT, KVQ_OUTL_FP8_E4M3><<<grid, 256, 0, st>>>(d); break;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_decode_mfma(const DecodeLaunch& d, hipStream_t st, bool* handled) {
@@ -407,8 +462,8 @@ hipError_t launch_decode_mfma(const DecodeLaunch& d, hipStream_t st, bool* handl
   if (d.fmt != FMT_C2 && !(d.fmt == FMT_FP4 && d.group == 32)) return hipSuccess;
   if (d.chunk % kStep) return hipSuccess;
   dim3 grid(d.n_chunks, d.L.H, d.L.B);
-  if (d.fmt == FMT_C2) decode_mfma_kernel<FMT_C2><<<grid, 256, 0, st>>>(d);
-  else decode_mfma_kernel<FMT_FP4><<<grid, 256, 0, st>>>(d);
+  if (d.fmt == FMT_C2) launch_fmt<FMT_C2>(d, grid, st);
+  else launch_fmt<FMT_FP4>(d, grid, st);
   *handled = true;
   return hipGetLastError();
 }

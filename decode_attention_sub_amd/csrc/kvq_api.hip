@@ -75,11 +75,18 @@ int32_t check_cache(const kvq_params* p, const kvq_cache* c) {
   return KVQ_OK;
 }
 
+// Default split: enough (sequence, KV head, chunk) units to give every CU of an MI355X (256)
+// two workgroups, the number that fit at once; never chunks shorter than 512 tokens.
 int resolve_chunk(const kvq_params* p, int32_t split_chunk) {
   if (split_chunk < 0) return -1;
   if (split_chunk == 0) {
     if (p->page_size) return kDefaultPagedChunk;
-    return ((p->max_seq_len + 63) / 64) * 64;
+    const int64_t units = (int64_t)p->batch * p->num_kv_heads;
+    const int64_t want = 512;
+    int64_t nchunks = units >= want ? 1 : (want + units - 1) / units;
+    int64_t chunk = (p->max_seq_len + nchunks - 1) / nchunks;
+    chunk = chunk < 512 ? 512 : chunk;
+    return (int)(((chunk + 63) / 64) * 64);
   }
   if (split_chunk % 64) return -1;
   return split_chunk;

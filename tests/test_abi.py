@@ -42,7 +42,7 @@ def test_cache_sizes_and_workspace():
     assert s.codes == 64 * 8 * 32768 * 32 and s.meta == 64 * 8 * 32768 * 16
     assert s.outl_idx == 64 * 8 * 100 * 4 and s.outl_val == 64 * 8 * 100
     assert s.outl_block_start == 64 * 8 * 2 * 2048 * 4
-    assert K.kvq_workspace_bytes(p) == 0                       # one chunk covers the sequence
+    assert K.kvq_workspace_bytes(p) == 0                       # 512 (b, h) units: one chunk
     assert K.kvq_workspace_bytes(p, 2048) == 64 * 64 * 16 * 130 * 4
     p4 = K.make_params(4, 64, 8, 131072, "fp4", 32, "fp16")
     s4 = K.kvq_cache_sizes(p4, 10)
