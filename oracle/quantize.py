@@ -32,7 +32,8 @@ Readings taken where the pages are silent (each is listed in the design doc):
     absolute difference with the first index on ties (the listing's ``argmin``); an empty
     cluster keeps its centroid; centroids stored as fp16;
   * INT4: offset form of the equation: zero = fp16(min), code = Round(Clamp((x - zero)/S, 0,
-    15)), which is the page's ZeroPoint = -zero/S written without a quantized-unit zero;
+    15)), which is the page's ZeroPoint = -zero/S written without a quantized-unit zero; a zero
+    min or max is taken as +0;
   * FP4: E4M3 block scale = absmax/6 (6 is the largest E2M1 magnitude);
   * FP8 tier: per-row scale absmax/448 in fp32, no outliers.
 """
@@ -111,8 +112,10 @@ def outlier_mask(xg: np.ndarray, sigma: float) -> np.ndarray:
 # ----------------------------------------------------------------------------- fits
 def _fit_int4(xg, keep):
     """[P4] S = (max - min)/(2^b - 1) with b = 4 over the non-outliers; fp16 scale and zero."""
-    mn = np.min(np.where(keep, xg, np.inf), axis=-1).astype(F32)
-    mx = np.max(np.where(keep, xg, -np.inf), axis=-1).astype(F32)
+    # min / max are order-free; a zero result is taken as +0 so the stored fp16 bits are
+    # defined (x + 0.0 maps -0.0 to +0.0 and leaves every other value unchanged)
+    mn = (np.min(np.where(keep, xg, np.inf), axis=-1).astype(F32) + F32(0.0)).astype(F32)
+    mx = (np.max(np.where(keep, xg, -np.inf), axis=-1).astype(F32) + F32(0.0)).astype(F32)
     s = ((mx - mn).astype(F32) / F32(15.0)).astype(F32)
     s_h = F.fp16_round(s)
     z_h = F.fp16_round(mn)
