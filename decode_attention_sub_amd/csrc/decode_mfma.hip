@@ -48,7 +48,10 @@ __device__ __forceinline__ half4v read_tr16(const lds_half* p) {
 
 constexpr int kWaves = 4;
 constexpr int kStep = 32;                  // tokens per wave step
-constexpr int kRow = 136;                  // LDS row stride in halfs (272 bytes)
+#ifndef KVQ_TILE_ROW
+#define KVQ_TILE_ROW 136
+#endif
+constexpr int kRow = KVQ_TILE_ROW;         // LDS row stride in halfs (272 bytes by default)
 constexpr int kTile = kStep * kRow;        // halfs per tile
 constexpr int kWaveLds = 2 * kTile;        // K tile + V tile
 

@@ -32,6 +32,9 @@ SMALL = {
     # 2-bit with GQA 16 (every MFMA row used) and with MHA (one row)
     "c2_g16_small": WD.variant(CONFIGS["c2_b64_s32k"], B=1, H=1, Hq=16, S=1500),
     "c2_mha_small": WD.variant(CONFIGS["c2_b16_s8k"], B=2, H=3, Hq=3, S=333),
+    # tau = 1.5: crowded steps with more than 128 records per list (the kernel's slow path)
+    "c2_dense_outliers": WD.variant(CONFIGS["c2_b16_s8k"], B=1, H=2, Hq=8, S=700, sigma=1.5),
+    "fp4_dense_outliers": WD.variant(CONFIGS["fp4_b4_s128k"], B=1, H=1, Hq=8, S=650, sigma=1.5),
     # tiered paged cache, variable lengths
     "tiered_small": WD.variant(CONFIGS["tiered_b32_paged"], B=3, H=2, Hq=8, S=3000,
                                S_range=(90, 3000), fp8_page_frac=0.3),
