@@ -55,10 +55,11 @@ __device__ __forceinline__ void dequant32(const RowRef& r, int part, float* dst)
     const uint2 mw = *(const uint2*)(r.meta + 8 * (part >> 1));
     const float c[4] = {half_bits_to_f32(mw.x & 0xFFFFu), half_bits_to_f32(mw.x >> 16),
                         half_bits_to_f32(mw.y & 0xFFFFu), half_bits_to_f32(mw.y >> 16)};
+    // channel 4s + j of a 16-channel word sits in byte j, bit pair s
 #pragma unroll
-    for (int k = 0; k < 16; ++k) dst[k] = c[(cw.x >> (2 * k)) & 3u];
+    for (int k = 0; k < 16; ++k) dst[k] = c[(cw.x >> (8 * (k & 3) + 2 * (k >> 2))) & 3u];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) dst[16 + k] = c[(cw.y >> (2 * k)) & 3u];
+    for (int k = 0; k < 16; ++k) dst[16 + k] = c[(cw.y >> (8 * (k & 3) + 2 * (k >> 2))) & 3u];
   } else {
     const uint4 cw = *(const uint4*)(r.codes + 16 * part);
     const uint32_t wv[4] = {cw.x, cw.y, cw.z, cw.w};

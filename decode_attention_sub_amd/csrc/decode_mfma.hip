@@ -22,10 +22,12 @@
 // merged in LDS; a chunk writes either the final output or a (max, sum, output) partial.
 //
 // 2-bit expansion: per 64-bit centroid word, two byte tables (low bytes and high bytes of the 4
-// fp16 centroids) are built once; four codes spread into the four bytes of a selector give the
-// low and high bytes of their centroids with one v_perm each, and two more v_perm interleave
-// them into two fp16 pairs.  This writes each 16-channel block in 4x4-transposed order
-// (position 4*(c%4) + c/4); queries, outlier positions and the output use the same order.
+// fp16 centroids) are built once; the four codes of one bit pair of a 32-bit code word (one per
+// byte) form a selector that gives the low and high bytes of their centroids with one v_perm
+// each, and two more v_perm interleave them into two fp16 pairs.  The packing puts channel 4s + j
+// of a 16-channel word in byte j, bit pair s, so bit pair s yields channels 4s .. 4s+3 in order.
+#include <type_traits>
+
 #include "kvq_device.h"
 #include "kvq_launch.h"
 
@@ -47,29 +49,40 @@ __device__ __forceinline__ half4v read_tr16(const lds_half* p) {
 }
 
 constexpr int kWaves = 4;
+#ifndef KVQ_PREFETCH_STEPS
+#define KVQ_PREFETCH_STEPS 2
+#endif
+constexpr int kPF = KVQ_PREFETCH_STEPS;    // steps of codes / records in flight per wave
 constexpr int kStep = 32;                  // tokens per wave step
 #ifndef KVQ_TILE_ROW
 #define KVQ_TILE_ROW 136
 #endif
 constexpr int kRow = KVQ_TILE_ROW;         // LDS row stride in halfs (272 bytes by default)
+#ifdef KVQ_WAVES_PER_EU
+#define KVQ_OCC __attribute__((amdgpu_waves_per_eu(KVQ_WAVES_PER_EU)))
+#else
+#define KVQ_OCC
+#endif
+#ifndef KVQ_ROTATE
+#define KVQ_ROTATE 1
+#endif
+#ifndef KVQ_TILES
+#define KVQ_TILES 2
+#endif
 constexpr int kTile = kStep * kRow;        // halfs per tile
-constexpr int kWaveLds = 2 * kTile;        // K tile + V tile
+constexpr int kWaveLds = KVQ_TILES * kTile; // K tile + V tile (or one tile for both)
 
-// position of channel c in the LDS row
-template <int FMT>
-__device__ __forceinline__ int chan_pos(int c) {
-  if constexpr (FMT == FMT_C2) return (c & ~15) | ((c & 3) << 2) | ((c >> 2) & 3);
-  else return c;
-}
 
 template <int FMT> struct Buf;
 template <> struct Buf<FMT_C2> { uint4 kc, vc; uint2 km, vm; };
 template <> struct Buf<FMT_FP4> { uint4 kc0, kc1, vc0, vc1; uint32_t km, vm; };
 
-struct Recs {       // up to 128 outlier records per list per step, two per lane
-  uint32_t kidx0, kidx1, vidx0, vidx1;
-  uint32_t kval0, kval1, vval0, vval1;
-  int kr0, nk, vr0, nv;     // first record and record count of the step (uniform)
+// Outlier records of one step: lane slots K0, K1 hold K records kr0 + lane and kr0 + 64 + lane,
+// slot V holds V record vr0 + lane.  Values are kept as the aligned 32-bit words that hold them.
+struct Recs {
+  uint32_t ik[2], vk[2];   // K: index words, value words
+  uint32_t iv, vv;         // V: index word, value word
+  int kr0, nk, vr0, nv;    // first record and record count of each list (uniform)
 };
 
 // raw buffer resource (gfx9 family): loads at byte offsets >= num_records return zero
@@ -135,34 +148,58 @@ __device__ __forceinline__ void expand_fp4(uint4 c0, uint4 c1, uint32_t m, _Floa
   }
 }
 
-// stored outlier value -> fp16 bits (E4M3 values are exact in fp16)
-// E4M3 bits placed as fp16 bits ((code & 0x7F) << 7 | sign << 15) encode value * 2^-8 for every
-// code, subnormals included (both formats' subnormal steps line up); one exact fp16 multiply by
-// 256 restores the value.
+// stored outlier value -> fp16 (E4M3 values are exact in fp16)
+// E4M3 bits placed as fp16 bits (exponent and mantissa shifted left by 7, sign on bit 15) encode
+// value * 2^-8 for every code, subnormals included (both formats' subnormal steps line up); one
+// exact fp16 multiply by 256 restores the value.  v + (v & 0x80) moves the sign bit up by one.
 template <int OUTL>
 __device__ __forceinline__ _Float16 outl_half(uint32_t v) {
   if constexpr (OUTL == KVQ_OUTL_FP16) {
     return __builtin_bit_cast(_Float16, (uint16_t)v);
   } else {
-    const uint32_t h = ((v & 0x7Fu) << 7) | ((v & 0x80u) << 8);
+    const uint32_t h = (v + (v & 0x80u)) << 7;
     return __builtin_bit_cast(_Float16, (uint16_t)h) * (_Float16)256.0f;
   }
 }
 
-// Overwrite one outlier position in a tile.  Records outside the step (or past the step's
-// record count) are written to a pad slot (row 0, column 128) that no operand read touches.
+// LDS tile position of record offset dd = 128 * t + c (token t of the step, channel c < 128);
+// the caller guarantees t < 32.
+__device__ __forceinline__ uint32_t tile_pos(uint32_t dd) {
+  static_assert(kRow == kHeadDim + 8, "row pad of 8 halfs assumed");
+  return dd + ((dd >> 7) << 3);   // t * kRow + c = dd + 8 t
+}
+
+// Overwrite one outlier position of a tile straight from the record (crowded or ragged steps).
+// A record outside the step goes to a pad slot (row 0, column 128) that no operand read touches.
 template <int FMT, int OUTL>
-__device__ __forceinline__ void patch(_Float16* tile, bool have, uint32_t idx, uint32_t val,
-                                      int ts, int nval) {
-  const uint32_t t = (idx >> 7) - (uint32_t)ts;
-  const uint32_t c = idx & 127u;
-  const bool ok = have && t < (uint32_t)nval;
-  const uint32_t at = ok ? t * (uint32_t)kRow + (uint32_t)chan_pos<FMT>((int)c) : (uint32_t)kHeadDim;
+__device__ __forceinline__ void patch_at(_Float16* tile, uint32_t idx, uint32_t val, int ts, int nval) {
+  const uint32_t dd = idx - (uint32_t)ts * 128u;
+  const uint32_t at = dd < (uint32_t)nval * 128u ? tile_pos(dd) : (uint32_t)kHeadDim;
   tile[at] = outl_half<OUTL>(val);
 }
 
-template <int FMT, int OUTL>
-__global__ void __launch_bounds__(256) decode_mfma_kernel(DecodeLaunch d) {
+// DPP helpers (row = 16 lanes)
+template <int CTRL, int BANKS>
+__device__ __forceinline__ float dpp_f32(float old, float src) {
+  return as_f32((uint32_t)__builtin_amdgcn_update_dpp((int)as_u32(old), (int)as_u32(src), CTRL, 0xF,
+                                                      BANKS, false));
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t src) {   // lanes without a source: undefined
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)src, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float src) {
+  return as_f32(dpp_u32<CTRL>(as_u32(src)));
+}
+constexpr int kRowShl8 = 0x108;   // lane i <- lane i + 8 of its row
+constexpr int kRowShr8 = 0x118;   // lane i <- lane i - 8 of its row
+constexpr int kRowRor8 = 0x128;   // lane i <- lane (i + 8) mod 16 of its row
+
+// CMP: at most 8 query heads per KV head.  Score tiles then hold real query rows only in lanes
+// r < 8; the softmax runs on 4 scores per lane after moving tile 1's rows into lanes r >= 8.
+template <int FMT, int OUTL, bool CMP>
+__global__ void __launch_bounds__(256) KVQ_OCC decode_mfma_kernel(DecodeLaunch d) {
   __shared__ __attribute__((aligned(16))) _Float16 s_lds[kWaves * kWaveLds];
   __shared__ float s_ml[kWaves][16][2];
 
@@ -186,8 +223,10 @@ __global__ void __launch_bounds__(256) decode_mfma_kernel(DecodeLaunch d) {
   constexpr int VB = OUTL == KVQ_OUTL_FP16 ? 2 : 1;
   constexpr bool HAS_OUTL = OUTL != KVQ_OUTL_NONE;
 
+  // With one tile, K rows are expanded and read back as operands before V rows overwrite them
+  // (a wave's LDS operations complete in issue order).
   _Float16* ktile = s_lds + wave * kWaveLds;
-  _Float16* vtile = ktile + kTile;
+  _Float16* vtile = ktile + (KVQ_TILES - 1) * kTile;
 
   // query operand (B of S^T = K^ Q^T): lane (row r, k-group kg), positions 32*ks + 8*kg + e
   half8 qop[4];
@@ -198,8 +237,9 @@ __global__ void __launch_bounds__(256) decode_mfma_kernel(DecodeLaunch d) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) raw[ks][e] = qrow[chan_pos<FMT>(32 * ks + 8 * kg + e)];
-    const float keep = r < G ? 1.0f : 0.0f;
+      for (int e = 0; e < 8; ++e) raw[ks][e] = qrow[(32 * ks + 8 * kg + e)];
+    // a negative softmax scale is folded into the queries (exact), so the scale below is >= 0
+    const float keep = r < G ? (d.scale_log2 < 0.0f ? -1.0f : 1.0f) : 0.0f;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
@@ -213,6 +253,7 @@ __global__ void __launch_bounds__(256) decode_mfma_kernel(DecodeLaunch d) {
   const __amdgpu_buffer_rsrc_t rmK = make_rsrc((const uint8_t*)d.cache.meta[0] + rowbase * MB, (uint32_t)t1 * MB);
   const __amdgpu_buffer_rsrc_t rmV = make_rsrc((const uint8_t*)d.cache.meta[1] + rowbase * MB, (uint32_t)t1 * MB);
   const uint32_t coff = (uint32_t)(trow * CB + half * (CB / 2));
+  const uint32_t lane4 = (uint32_t)lane * 4u, laneVB = (uint32_t)lane * VB, laneVB8 = laneVB * 8u;
   const uint32_t moff = (uint32_t)(trow * MB + half * (MB / 2));
 
   const size_t lidK = list_id(L, b, h, 0);
@@ -223,16 +264,22 @@ __global__ void __launch_bounds__(256) decode_mfma_kernel(DecodeLaunch d) {
   const uint32_t* oidxV = nullptr;
   const uint8_t* ovalK = nullptr;
   const uint8_t* ovalV = nullptr;
+  uint32_t lv3 = 0;   // byte offset of the list's first value inside its aligned 32-bit word
   if constexpr (HAS_OUTL) {
     const size_t lbase = ((size_t)b * L.H + h) * (size_t)L.outl_cap;
     oidxK = d.cache.outl_idx[0] + lbase;
     oidxV = d.cache.outl_idx[1] + lbase;
     ovalK = (const uint8_t*)d.cache.outl_val[0] + lbase * VB;
     ovalV = (const uint8_t*)d.cache.outl_val[1] + lbase * VB;
+    // value words: ranges start at the aligned word holding the list's first value and end at
+    // the word holding its last (value buffers are padded to whole words)
+    const size_t lvb = lbase * VB, w0 = lvb & ~(size_t)3;
+    lv3 = (uint32_t)(lvb & 3);
+    const uint32_t vbytes = (uint32_t)(((lvb + (size_t)cap * VB + 3) & ~(size_t)3) - w0);
+    rvK = make_rsrc((const uint8_t*)d.cache.outl_val[0] + w0, vbytes);
+    rvV = make_rsrc((const uint8_t*)d.cache.outl_val[1] + w0, vbytes);
     riK = make_rsrc(oidxK, (uint32_t)cap * 4);
     riV = make_rsrc(oidxV, (uint32_t)cap * 4);
-    rvK = make_rsrc(ovalK, (uint32_t)cap * VB);
-    rvV = make_rsrc(ovalV, (uint32_t)cap * VB);
     rbs = make_rsrc(d.cache.outl_block_start + lidK * (size_t)L.nblk, (uint32_t)L.nblk * 8);
     cntK = max(0, min(d.cache.outl_count[lidK], cap));
     cntV = max(0, min(d.cache.outl_count[lidK + 1], cap));
@@ -240,7 +287,25 @@ __global__ void __launch_bounds__(256) decode_mfma_kernel(DecodeLaunch d) {
 
   const int nsteps = (t1 - t0 + kStep - 1) / kStep;
   const int nmine = wave < nsteps ? (nsteps - wave + kWaves - 1) / kWaves : 0;
-  auto step_ts = [&](int j) { return t0 + kStep * (wave + kWaves * j); };
+  // The chunk's ragged last step (if any) belongs to one wave and is processed last.
+  const bool ragged = (t1 - t0) % kStep != 0 && wave == (nsteps - 1) % kWaves;
+  const int nfull = nmine - (ragged ? 1 : 0);
+  // Workgroups walk their full steps in rotated order, starting at evenly spread points.  Every
+  // (sequence, head) slice starts at the same power-of-two-aligned offset; walking them in
+  // lockstep would send every workgroup to the same HBM channels at the same time.
+#if KVQ_ROTATE
+  const uint32_t n_wg = gridDim.x * gridDim.y * gridDim.z;
+  const uint32_t wg = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+  const int rot = nfull > 0 ? (int)(((uint64_t)wg * (uint64_t)nfull) / n_wg) : 0;
+#else
+  const int rot = 0;
+#endif
+  // token start of the wave's j-th processed step (j >= nmine: past the chunk)
+  auto step_ts = [&](int j) {
+    int jj = j;
+    if (j < nfull) { jj = j + rot; if (jj >= nfull) jj -= nfull; }
+    return t0 + kStep * (wave + kWaves * jj);
+  };
 
   auto issue_codes = [&](Buf<FMT>& bf, int j) {
     const uint32_t ts = (uint32_t)step_ts(j);
@@ -275,153 +340,231 @@ __global__ void __launch_bounds__(256) decode_mfma_kernel(DecodeLaunch d) {
       const int v1 = last ? cntV : max(0, min(__builtin_amdgcn_readlane((int)bnd, 3), cap));
       rc.kr0 = k0; rc.nk = max(k1 - k0, 0);
       rc.vr0 = v0; rc.nv = max(v1 - v0, 0);
-      const uint32_t a0 = (uint32_t)(k0 + lane), a1 = a0 + 64u;
-      const uint32_t c0 = (uint32_t)(v0 + lane), c1 = c0 + 64u;
-      rc.kidx0 = ld32(riK, a0 * 4);
-      rc.kidx1 = ld32(riK, a1 * 4);
-      rc.vidx0 = ld32(riV, c0 * 4);
-      rc.vidx1 = ld32(riV, c1 * 4);
-      if constexpr (VB == 2) {
-        rc.kval0 = ld16(rvK, a0 * 2); rc.kval1 = ld16(rvK, a1 * 2);
-        rc.vval0 = ld16(rvV, c0 * 2); rc.vval1 = ld16(rvV, c1 * 2);
-      } else {
-        rc.kval0 = ld8(rvK, a0); rc.kval1 = ld8(rvK, a1);
-        rc.vval0 = ld8(rvV, c0); rc.vval1 = ld8(rvV, c1);
-      }
+      // Slots past a list's records read past its range (zeros) or unused records.  Values are
+      // read as the aligned 32-bit word that holds them and extracted where they are used: a byte
+      // or short load would leave the compiler a narrow value that it re-extends at the loop
+      // back-edge, waiting for the load there.
+      const uint32_t oik = (uint32_t)k0 * 4u + lane4, oiv = (uint32_t)v0 * 4u + lane4;
+      rc.ik[0] = ld32(riK, oik);
+      rc.ik[1] = ld32(riK, oik + 256u);
+      rc.iv = ld32(riV, oiv);
+      const uint32_t obk = ((uint32_t)k0 * VB + lv3 + laneVB) & ~3u;
+      const uint32_t obv = ((uint32_t)v0 * VB + lv3 + laneVB) & ~3u;
+      rc.vk[0] = ld32(rvK, obk);
+      rc.vk[1] = ld32(rvK, obk + 64u * VB);
+      rc.vv = ld32(rvV, obv);
     }
   };
 
   floatx4 oacc[8];
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt) oacc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.0f;
-  const float sl2 = d.scale_log2;
+  float m_run = -INFINITY, l_run = 0.0f;   // -inf until the first step sets it
+  const float sl2 = fabsf(d.scale_log2);
 
-  auto consume = [&](const Buf<FMT>& bf, const Recs& rc, int j) {
+  // One 32-token step.  FULL: every token of the step is valid.  K records past the first 128 of
+  // a step and V records past the first 64 are written by rarely taken loops.  Otherwise the body is one
+  // branch-free block: K rows are expanded and written, the K^ operand reads are issued, V rows
+  // are expanded while those reads are in flight, the score MFMAs run, the V^T operand reads are
+  // issued before the softmax needs them.
+  auto consume = [&](const Buf<FMT>& bf, const Recs& rc, int j, auto full_tag) {
+    constexpr bool FULL = decltype(full_tag)::value;
     const int ts = step_ts(j);
-    const int nval = min(kStep, t1 - ts);
+    const int nval = FULL ? kStep : min(kStep, t1 - ts);
     _Float16* krow = ktile + trow * kRow + 64 * half;
     _Float16* vrow = vtile + trow * kRow + 64 * half;
-    if constexpr (FMT == FMT_C2) {
-      expand_c2(bf.kc, bf.km, krow);
-      expand_c2(bf.vc, bf.vm, vrow);
-    } else {
-      expand_fp4(bf.kc0, bf.kc1, bf.km, krow);
-      expand_fp4(bf.vc0, bf.vc1, bf.vm, vrow);
-    }
+    // tile positions of this lane's record slots (the pad slot where a slot is unused)
+    uint32_t posK[2], posV = kHeadDim;
+    _Float16 ovK[2], ovV;
     if constexpr (HAS_OUTL) {
-      patch<FMT, OUTL>(ktile, lane < rc.nk, rc.kidx0, rc.kval0, ts, nval);
-      patch<FMT, OUTL>(ktile, lane + 64 < rc.nk, rc.kidx1, rc.kval1, ts, nval);
-      patch<FMT, OUTL>(vtile, lane < rc.nv, rc.vidx0, rc.vval0, ts, nval);
-      patch<FMT, OUTL>(vtile, lane + 64 < rc.nv, rc.vidx1, rc.vval1, ts, nval);
-      if (rc.nk > 128 || rc.nv > 128) {  // rare: the rest of a crowded step, read directly
-        for (int a = 128 + lane; a < rc.nk; a += 64) {
+      // bit offsets of the values inside their words (bit-field extraction takes them modulo 32;
+      // slot K1 is 64 records on, a whole number of words)
+      const uint32_t bitK = laneVB8 + ((uint32_t)rc.kr0 * VB + lv3) * 8u;
+      const uint32_t bitV = laneVB8 + ((uint32_t)rc.vr0 * VB + lv3) * 8u;
+      const uint32_t lim = (uint32_t)nval * 128u;
+#pragma unroll
+      for (int sl = 0; sl < 2; ++sl) {
+        const uint32_t dd = rc.ik[sl] - (uint32_t)ts * 128u;
+        const bool ok = 64 * sl + lane < rc.nk && dd < lim;
+        posK[sl] = ok ? tile_pos(dd) : (uint32_t)kHeadDim;
+        ovK[sl] = outl_half<OUTL>(__builtin_amdgcn_ubfe(rc.vk[sl], bitK, VB * 8));
+      }
+      const uint32_t ddv = rc.iv - (uint32_t)ts * 128u;
+      posV = lane < rc.nv && ddv < lim ? tile_pos(ddv) : (uint32_t)kHeadDim;
+      ovV = outl_half<OUTL>(__builtin_amdgcn_ubfe(rc.vv, bitV, VB * 8));
+    }
+    if constexpr (FMT == FMT_C2) expand_c2(bf.kc, bf.km, krow);
+    else expand_fp4(bf.kc0, bf.kc1, bf.km, krow);
+    if constexpr (HAS_OUTL) {
+      ktile[posK[0]] = ovK[0];
+      ktile[posK[1]] = ovK[1];
+      if (rc.nk > 128) {
+        for (int a = 128 + lane; a < rc.nk; a += 64) {  // the rest of a crowded step
           const int at = rc.kr0 + a;
           const uint32_t v = VB == 2 ? ((const uint16_t*)ovalK)[at] : ovalK[at];
-          patch<FMT, OUTL>(ktile, true, oidxK[at], v, ts, nval);
-        }
-        for (int a = 128 + lane; a < rc.nv; a += 64) {
-          const int at = rc.vr0 + a;
-          const uint32_t v = VB == 2 ? ((const uint16_t*)ovalV)[at] : ovalV[at];
-          patch<FMT, OUTL>(vtile, true, oidxV[at], v, ts, nval);
+          patch_at<FMT, OUTL>(ktile, oidxK[at], v, ts, nval);
         }
       }
     }
-    // S^T for tokens 0..15 and 16..31 of the step
+    half8 ak[8];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      ak[ks] = *(const half8*)(ktile + r * kRow + 32 * ks + 8 * kg);
+      ak[4 + ks] = *(const half8*)(ktile + (16 + r) * kRow + 32 * ks + 8 * kg);
+    }
+    if constexpr (FMT == FMT_C2) expand_c2(bf.vc, bf.vm, vrow);
+    else expand_fp4(bf.vc0, bf.vc1, bf.vm, vrow);
+    if constexpr (HAS_OUTL) {
+      vtile[posV] = ovV;
+      if (rc.nv > 64) {
+        for (int i = 64 + lane; i < rc.nv; i += 64) {
+          const int at = rc.vr0 + i;
+          const uint32_t v = VB == 2 ? ((const uint16_t*)ovalV)[at] : ovalV[at];
+          patch_at<FMT, OUTL>(vtile, oidxV[at], v, ts, nval);
+        }
+      }
+    }
     floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const half8 a0 = *(const half8*)(ktile + r * kRow + 32 * ks + 8 * kg);
-      const half8 a1 = *(const half8*)(ktile + (16 + r) * kRow + 32 * ks + 8 * kg);
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, qop[ks], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, qop[ks], s1, 0, 0, 0);
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak[ks], qop[ks], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak[4 + ks], qop[ks], s1, 0, 0, 0);
     }
-    // online softmax: lane holds query row r, tokens 4kg+v (tile 0) and 16+4kg+v (tile 1)
-    float sc[8];
+    // V^T operands (16 channels x 32 tokens per M-tile) through transposing LDS reads
+    half8 av[8];
+    {
+      const lds_half* vbase = (const lds_half*)vtile;
+      const int col0 = 4 * (r & 3);
+      const int rowo = 4 * kg + (r >> 2);
 #pragma unroll
-    for (int v = 0; v < 4; ++v) { sc[v] = s0[v] * sl2; sc[4 + v] = s1[v] * sl2; }
-    if (nval < kStep) {
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        if (4 * kg + v >= nval) sc[v] = -INFINITY;
-        if (16 + 4 * kg + v >= nval) sc[4 + v] = -INFINITY;
+      for (int mt = 0; mt < 8; ++mt) {
+        const half4v t0v = read_tr16(vbase + rowo * kRow + 16 * mt + col0);
+        const half4v t1v = read_tr16(vbase + (16 + rowo) * kRow + 16 * mt + col0);
+        av[mt] = half8{t0v[0], t0v[1], t0v[2], t0v[3], t1v[0], t1v[1], t1v[2], t1v[3]};
       }
     }
-    float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
-                     fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    half8 phi, plo;
-    float psum = 0.0f;
+    // Online softmax in the exp2 domain.  Without CMP a lane holds query row r, tokens 4kg+v
+    // (tile 0) and 16+4kg+v (tile 1); with CMP lanes r < 8 hold tile 0 and lanes r >= 8 hold
+    // tile 1 of query r - 8.  The running maximum moves only when a scaled score exceeds it by
+    // more than 2^8 (lazy rescaling): probabilities stay below 256, exact in fp32 and in the
+    // fp16 hi + lo split.
+    constexpr int NS = CMP ? 4 : 8;
+    float sc[NS];
+    if constexpr (CMP) {
 #pragma unroll
-    for (int v = 0; v < 8; v += 2) {
-      const float p0 = __builtin_amdgcn_exp2f(sc[v] - m_new);
-      const float p1 = __builtin_amdgcn_exp2f(sc[v + 1] - m_new);
-      psum += p0 + p1;
-      const half2v hi = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(p0, p1));
-      const half2v lo = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(p0 - (float)hi[0], p1 - (float)hi[1]));
-      phi[v] = hi[0]; phi[v + 1] = hi[1];
-      plo[v] = lo[0]; plo[v + 1] = lo[1];
+      for (int v = 0; v < 4; ++v) sc[v] = dpp_f32<kRowShr8, 0xC>(s0[v], s1[v]);
+    } else {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) { sc[v] = s0[v]; sc[4 + v] = s1[v]; }
     }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+    bool valid[NS];
+#pragma unroll
+    for (int v = 0; v < NS; ++v) {
+      const int tok = CMP ? (r >= 8 ? 16 : 0) + 4 * kg + v : (v < 4 ? 4 * kg + v : 12 + 4 * kg + v);
+      valid[v] = FULL || tok < nval;
+      if constexpr (!FULL) sc[v] = valid[v] ? sc[v] : -INFINITY;
+    }
+    // Lane-local maximum first: the row maximum (across the lanes that hold the row) is formed
+    // only when some scaled score exceeds the running maximum by more than 2^8.
+    float mx = sc[0];
+#pragma unroll
+    for (int v = 1; v < NS; ++v) mx = fmaxf(mx, sc[v]);
+    if (__builtin_amdgcn_ballot_w64(mx * sl2 > m_run + 8.0f)) {
+      if constexpr (CMP) mx = fmaxf(mx, dpp_f32<kRowRor8>(mx));
+      const auto x16 = __builtin_amdgcn_permlane16_swap(as_u32(mx), as_u32(mx), false, false);
+      mx = fmaxf(as_f32(x16[0]), as_f32(x16[1]));
+      const auto x32 = __builtin_amdgcn_permlane32_swap(as_u32(mx), as_u32(mx), false, false);
+      mx = fmaxf(as_f32(x32[0]), as_f32(x32[1]));
+      const float m_new = fmaxf(m_run, mx * sl2);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) oacc[mt] *= alpha;
+      m_run = m_new;
     }
-    // O^T += V^T P^T: A = V^T (16 channels x 32 tokens) through transposing LDS reads
-    const lds_half* vbase = (const lds_half*)vtile;
-    const int col0 = 4 * (r & 3);
-    const int rowo = 4 * kg + (r >> 2);
+    uint32_t hw[NS / 2], lw[NS / 2];
+    float psum;
+#pragma unroll
+    for (int v = 0; v < NS; v += 2) {
+      float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[v], sl2, -m_run));
+      float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[v + 1], sl2, -m_run));
+      if constexpr (!FULL) { p0 = valid[v] ? p0 : 0.0f; p1 = valid[v + 1] ? p1 : 0.0f; }
+      psum = v == 0 ? p0 + p1 : psum + (p0 + p1);
+      const half2v hi = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(p0, p1));
+      hw[v / 2] = __builtin_bit_cast(uint32_t, hi);
+      lw[v / 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(p0 - (float)hi[0], p1 - (float)hi[1]));
+    }
+    l_run += psum;
+    uint4 hq, lq;
+    if constexpr (CMP) {
+      // B operand of lane (query r, kg): tile-0 tokens of its own, tile-1 tokens from lane r + 8
+      hq = make_uint4(hw[0], hw[1], dpp_u32<kRowShl8>(hw[0]), dpp_u32<kRowShl8>(hw[1]));
+      lq = make_uint4(lw[0], lw[1], dpp_u32<kRowShl8>(lw[0]), dpp_u32<kRowShl8>(lw[1]));
+    } else {
+      hq = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+      lq = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+    }
+    const half8 phi = __builtin_bit_cast(half8, hq), plo = __builtin_bit_cast(half8, lq);
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) {
-      const half4v t0v = read_tr16(vbase + rowo * kRow + 16 * mt + col0);
-      const half4v t1v = read_tr16(vbase + (16 + rowo) * kRow + 16 * mt + col0);
-      const half8 av = {t0v[0], t0v[1], t0v[2], t0v[3], t1v[0], t1v[1], t1v[2], t1v[3]};
-      oacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, phi, oacc[mt], 0, 0, 0);
-      oacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, plo, oacc[mt], 0, 0, 0);
+      oacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[mt], phi, oacc[mt], 0, 0, 0);
+      oacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[mt], plo, oacc[mt], 0, 0, 0);
     }
   };
+  auto run_step = [&](const Buf<FMT>& bf, const Recs& rc, int j) {
+    if (step_ts(j) + kStep <= t1) consume(bf, rc, j, std::true_type{});
+    else consume(bf, rc, j, std::false_type{});
+  };
 
-  // ---- software pipeline: codes and records two steps ahead, record bounds three ahead
-  Buf<FMT> buf[3];
-  Recs rec[3];
-  uint32_t bnd[3] = {0u, 0u, 0u};
+  // ---- software pipeline: codes and records kPF steps ahead, record bounds kPF + 1 ahead.
   // Loads for steps past the wave's last step are issued anyway: their offsets lie past the
   // buffer ranges (codes) or are clamped (records), so they return zeros or unused data without
   // touching memory, and keeping every load unconditional lets the wait counters stay exact.
+  constexpr int NB = kPF + 1;  // ring slots
+  Buf<FMT> buf[NB];
+  Recs rec[NB];
+  uint32_t bnd[NB];
   if (nmine > 0) {
-    bnd[0] = issue_bounds(0);
-    bnd[1] = issue_bounds(1);
-    bnd[2] = issue_bounds(2);
-    issue_recs(rec[0], bnd[0], 0);
-    issue_codes(buf[0], 0);
-    issue_recs(rec[1], bnd[1], 1);
-    issue_codes(buf[1], 1);
-  }
-  for (int j = 0; j < nmine; j += 3) {
 #pragma unroll
-    for (int u = 0; u < 3; ++u) {
-      const int jj = j + u;
-      if (jj < nmine) {
-        bnd[u] = issue_bounds(jj + 3);
-        issue_recs(rec[(u + 2) % 3], bnd[(u + 2) % 3], jj + 2);
-        issue_codes(buf[(u + 2) % 3], jj + 2);
-        consume(buf[u], rec[u], jj);
-      }
+    for (int k = 0; k < NB; ++k) bnd[k] = issue_bounds(k);
+#pragma unroll
+    for (int k = 0; k < kPF; ++k) { issue_recs(rec[k], bnd[k], k); issue_codes(buf[k], k); }
+  }
+  // Whole groups of NB full steps run without conditions (so every ring slot keeps its registers
+  // and the wait counters stay exact); the last group holds the remaining steps, the chunk's
+  // ragged last step among them.
+  const int ngroups = nfull / NB;
+  for (int g = 0; g < ngroups; ++g) {
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const int jj = g * NB + u;
+      bnd[u] = issue_bounds(jj + NB);
+      issue_recs(rec[(u + kPF) % NB], bnd[(u + kPF) % NB], jj + kPF);
+      issue_codes(buf[(u + kPF) % NB], jj + kPF);
+      consume(buf[u], rec[u], jj, std::true_type{});
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < NB; ++u) {
+    const int jj = ngroups * NB + u;
+    if (jj < nmine) {
+      bnd[u] = issue_bounds(jj + NB);
+      issue_recs(rec[(u + kPF) % NB], bnd[(u + kPF) % NB], jj + kPF);
+      issue_codes(buf[(u + kPF) % NB], jj + kPF);
+      run_step(buf[u], rec[u], jj);
     }
   }
 
   // ---- merge the waves of the workgroup
-  float l_row = l_run + __shfl_xor(l_run, 16, 64);
+  float l_row = l_run;
+  if constexpr (CMP) l_row += dpp_f32<kRowRor8>(l_row);
+  l_row += __shfl_xor(l_row, 16, 64);
   l_row += __shfl_xor(l_row, 32, 64);
   float* s_o = (float*)(s_lds + wave * kWaveLds);   // [16 rows][128 channels] of this wave
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) s_o[r * kHeadDim + chan_pos<FMT>(16 * mt + 4 * kg + v)] = oacc[mt][v];
+    for (int v = 0; v < 4; ++v) s_o[r * kHeadDim + (16 * mt + 4 * kg + v)] = oacc[mt][v];
   if (kg == 0) { s_ml[wave][r][0] = m_run; s_ml[wave][r][1] = l_row; }
   __syncthreads();
   for (int i = threadIdx.x; i < G * kHeadDim; i += 256) {
@@ -448,13 +591,19 @@ __global__ void __launch_bounds__(256) decode_mfma_kernel(DecodeLaunch d) {
   }
 }
 
+template <int FMT, bool CMP>
+void launch_cmp(const DecodeLaunch& d, dim3 grid, hipStream_t st) {
+  switch (d.outl) {
+    case KVQ_OUTL_NONE: decode_mfma_kernel<FMT, KVQ_OUTL_NONE, CMP><<<grid, 256, 0, st>>>(d); break;
+    case KVQ_OUTL_FP16: decode_mfma_kernel<FMT, KVQ_OUTL_FP16, CMP><<<grid, 256, 0, st>>>(d); break;
+    default: decode_mfma_kernel<FMT, KVQ_OUTL_FP8_E4M3, CMP><<<grid, 256, 0, st>>>(d); break;
+  }
+}
+
 template <int FMT>
 void launch_fmt(const DecodeLaunch& d, dim3 grid, hipStream_t st) {
-  switch (d.outl) {
-    case KVQ_OUTL_NONE: decode_mfma_kernel<FMT, KVQ_OUTL_NONE><<<grid, 256, 0, st>>>(d); break;
-    case KVQ_OUTL_FP16: decode_mfma_kernel<FMT, KVQ_OUTL_FP16><<<grid, 256, 0, st>>>(d); break;
-    default: decode_mfma_kernel<FMT, KVQ_OUTL_FP8_E4M3><<<grid, 256, 0, st>>>(d); break;
-  }
+  if (d.Hq / d.L.H <= 8) launch_cmp<FMT, true>(d, grid, st);
+  else launch_cmp<FMT, false>(d, grid, st);
 }
 
 }  // namespace

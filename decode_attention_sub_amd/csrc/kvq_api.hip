@@ -72,6 +72,7 @@ int32_t check_cache(const kvq_params* p, const kvq_cache* c) {
   }
   if (!c->outl_count || !c->outl_block_start) return KVQ_ERR_INVALID_ARG;
   if (p->outlier_dtype != KVQ_OUTL_NONE && c->outl_capacity < 1) return KVQ_ERR_INVALID_ARG;
+  if (c->outl_capacity > (int64_t(1) << 28)) return KVQ_ERR_INVALID_ARG;  // 32-bit record offsets
   return KVQ_OK;
 }
 
@@ -142,7 +143,7 @@ int32_t kvq_cache_sizes(const kvq_params* p, int64_t outl_capacity, kvq_cache_si
   }
   const uint64_t vb = p->outlier_dtype == KVQ_OUTL_FP16 ? 2 : 1;
   out->outl_idx = BH * (uint64_t)outl_capacity * 4;
-  out->outl_val = BH * (uint64_t)outl_capacity * vb;
+  out->outl_val = (BH * (uint64_t)outl_capacity * vb + 3) & ~3ull;  // whole 32-bit words
   out->outl_count = BH * 2 * 4;
   out->outl_block_start = BH * 2 * (uint64_t)((p->max_seq_len + kBlock - 1) / kBlock) * 4;
   return KVQ_OK;

@@ -378,9 +378,12 @@ __global__ void __launch_bounds__(64 * NW) quantize_append_kernel(QArgs a) {
       const int bits = tr ? 8 : code_bits(FMT);
       const int per_word = 32 / bits;
       if (lane < cb / 4) {
+        // 2-bit: channel 4s + j of the word's 16 goes to byte j, bit pair s; otherwise LSB first
         uint32_t w = 0;
-        for (int k = 0; k < per_word; ++k)
-          w |= (uint32_t)s_code[slot][lane * per_word + k] << (bits * k);
+        for (int k = 0; k < per_word; ++k) {
+          const int sh = bits == 2 ? 8 * (k & 3) + 2 * (k >> 2) : bits * k;
+          w |= (uint32_t)s_code[slot][lane * per_word + k] << sh;
+        }
         ((uint32_t*)codes_dst)[lane] = w;
       }
       if (lane < mb / 4) ((uint32_t*)meta_dst)[lane] = s_meta[slot][lane];

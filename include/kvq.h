@@ -106,9 +106,12 @@ typedef struct {
  *              meta[kv]   [num_pages][H][16][meta_bytes]
  *              codes8[kv] [num_pages_fp8][H][16][D]            FP8 tier-1 pool
  *              scale8[kv] [num_pages_fp8][H][16] float         per-row FP8 scales
- * Outliers:    outl_idx[kv] [B][H][outl_capacity] uint32, outl_val[kv] [B][H][outl_capacity]
+ * Outliers:    outl_idx[kv] [B][H][outl_capacity] uint32 (outl_capacity <= 2^28), outl_val[kv] [B][H][outl_capacity]
  *              (uint16 fp16 bits or uint8 E4M3), outl_count [B][H][2] int32,
  *              outl_block_start [B][H][2][ceil(max_seq_len/16)] int32.
+ *              outl_val buffers are 4-byte aligned and as large as kvq_cache_sizes reports
+ *              (rounded up to whole 32-bit words: the decoder reads the aligned word around
+ *              each value).
  * status: one int32 the kernels set (first error wins) to KVQ_ERR_CAPACITY or
  *         KVQ_ERR_INVALID_ARG when a device-side check fails; the library never clears it.
  * Buffers may be uninitialised except outl_count / status (zero before first use). */

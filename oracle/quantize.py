@@ -188,28 +188,33 @@ def _fit_fp8row(x):
 
 # ----------------------------------------------------------------------------- packing
 def pack_codes(codes: np.ndarray, bits: int) -> np.ndarray:
-    """LSB-first packing along the channel axis: a 2-bit byte k holds channels 4k..4k+3 with
-    channel 4k+r in bits 2r..2r+1; a 4-bit byte k holds channel 2k in bits 0-3 and 2k+1 in
-    bits 4-7; 8-bit codes are stored as they are."""
+    """Packing along the channel axis.  2-bit: every block of 16 channels fills 4 bytes; byte j
+    of a block holds channels j, 4+j, 8+j, 12+j in bit pairs 0, 1, 2, 3 (channel 4s+j in bits
+    2s..2s+1).  4-bit: byte k holds channel 2k in bits 0-3 and 2k+1 in bits 4-7.  8-bit codes are
+    stored as they are."""
     c = np.asarray(codes, dtype=np.uint8)
     if bits == 8:
         return c.copy()
-    per = 8 // bits
-    c = c.reshape(*c.shape[:-1], -1, per).astype(np.uint16)
-    out = np.zeros(c.shape[:-1], dtype=np.uint16)
-    for r in range(per):
-        out |= c[..., r] << (bits * r)
-    return out.astype(np.uint8)
+    if bits == 2:
+        blk = c.reshape(*c.shape[:-1], -1, 4, 4).astype(np.uint16)   # [..., block, s, j]
+        out = np.zeros(blk.shape[:-2] + (4,), dtype=np.uint16)       # [..., block, j]
+        for sp in range(4):
+            out |= blk[..., sp, :] << (2 * sp)
+        return out.reshape(*c.shape[:-1], -1).astype(np.uint8)
+    c = c.reshape(*c.shape[:-1], -1, 2).astype(np.uint16)
+    return (c[..., 0] | (c[..., 1] << 4)).astype(np.uint8)
 
 
 def unpack_codes(packed: np.ndarray, bits: int, D: int) -> np.ndarray:
+    """Inverse of pack_codes: [..., D * bits / 8] bytes -> [..., D] codes."""
     p = np.asarray(packed, dtype=np.uint8)
     if bits == 8:
         return p.copy()
-    per = 8 // bits
-    mask = (1 << bits) - 1
-    parts = [(p >> (bits * r)) & mask for r in range(per)]
-    return np.stack(parts, axis=-1).reshape(*p.shape[:-1], D).astype(np.uint8)
+    if bits == 2:
+        blk = p.reshape(*p.shape[:-1], -1, 4)                         # [..., block, j]
+        parts = [(blk >> (2 * sp)) & 3 for sp in range(4)]            # bit pair s
+        return np.stack(parts, axis=-2).reshape(*p.shape[:-1], D).astype(np.uint8)
+    return np.stack([p & 15, p >> 4], axis=-1).reshape(*p.shape[:-1], D).astype(np.uint8)
 
 
 # ----------------------------------------------------------------------------- rows

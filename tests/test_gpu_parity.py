@@ -78,6 +78,21 @@ def test_decode_matches_oracle(small, split):
             assert err <= ATOL, f"{name} b={b} hq={hq} split={split}: max-abs {err}"
 
 
+@pytest.mark.parametrize("sm", [-0.07, 0.0, 0.4])
+def test_decode_softmax_scale(sm):
+    """Negative, zero and large softmax scales (the kernel folds the sign into the queries)."""
+    for name in ("c2_small", "c2_g16_small", "fp4_small"):
+        w = SMALL[name]
+        log(f"[gpu] decode {name} sm_scale={sm}")
+        dc = WD.build(w)
+        got = run_decode(dc, split_chunk=0, sm_scale=sm)
+        for b in range(w.B):
+            ref = oracle_attention(dc, b, range(w.Hq), sm)
+            for hq, o in ref.items():
+                err = np.abs(got[b, hq] - o).max()
+                assert err <= ATOL, f"{name} b={b} hq={hq} sm={sm}: max-abs {err}"
+
+
 def test_decode_deterministic(small):
     name, dc = small
     a = run_decode(dc, split_chunk=256)

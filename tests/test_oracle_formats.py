@@ -122,6 +122,8 @@ def test_packing_known_vectors_and_roundtrip():
         codes = np.array([case["codes"]], dtype=np.uint8)
         got = pack_codes(codes, case["bits"])[0].tolist()
         assert got == case["bytes"], case
+        back = unpack_codes(np.array([case["bytes"]], dtype=np.uint8), case["bits"], codes.shape[1])
+        assert back[0].tolist() == case["codes"], case
     rng = np.random.default_rng(4)
     for bits in (2, 4, 8):
         c = rng.integers(0, 1 << bits, size=(7, 128)).astype(np.uint8)
