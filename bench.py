@@ -9,7 +9,7 @@ Prints one JSON line.  ``value`` is algorithmic KV bytes moved per second by the
 HIP events on the stream it runs on) against the 8 TB/s HBM peak; ``cpu_baseline`` is the oracle
 timed on a bounded sample of the same step on the host cores.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--workload c2_b64_s32k]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 40] [--workload c2_b64_s32k]
 """
 
 from __future__ import annotations
@@ -55,6 +55,33 @@ def algorithmic_bytes(dc, n_outliers: int, seq_lens: np.ndarray) -> int:
         kv = 2 * w.H * tokens * (sz.code_bytes_per_row + sz.meta_bytes_per_row)
         table = 0
     return kv + n_outliers * (vb + 4) + w.B * w.Hq * w.D * (2 + 4) + table
+
+
+KERNEL_SOURCES = ["decode_attention_sub_amd/csrc/decode_mfma.hip",
+                  "decode_attention_sub_amd/csrc/kvq_device.h",
+                  "decode_attention_sub_amd/csrc/kvq_launch.h"]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per decode launch from the committed counter record of this workload, or None
+    when there is none or the decode kernel's sources have changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"decode_mfma_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    for ln in open(path):
+        if ln.startswith("#") or ":" not in ln:
+            continue
+        k, v = ln.split(":", 1)
+        rec[k.strip()] = v.strip()
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    if rec.get("workload") != workload or rec.get("kernel_sources_sha256") != h.hexdigest():
+        return None
+    return int(rec["traffic_bytes_per_launch"])
 
 
 def read_ceiling_gbs(device="cuda") -> float:
@@ -131,7 +158,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default="c2_b64_s32k")
     ap.add_argument("--split", type=int, default=-1, help="split-K chunk (default: workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -232,7 +259,8 @@ def main():
         "outliers": n_out, "outlier_fraction": round(n_out / elems, 6),
         "decode_bytes": dec_bytes,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(w.name)},
     }
     if not args.no_cpu_baseline:
         log("timing the oracle on a sample of the step")

@@ -54,6 +54,10 @@ class kvq_cache_sizes_t(C.Structure):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with decode_attention_sub_amd/build.py")
+    # torch ships its own HIP runtime and asks for it by a different name than this library does;
+    # loading torch first makes the library bind to that same runtime.  Loaded the other way
+    # round, the process holds two runtimes and torch's streams are foreign to the library.
+    import torch  # noqa: F401
     lib = C.CDLL(LIB_PATH)
     P, Pc, vp = C.POINTER(kvq_params), C.POINTER(kvq_cache), C.c_void_p
     sig = {

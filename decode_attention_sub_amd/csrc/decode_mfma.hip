@@ -10,16 +10,17 @@
 // section "2. FP4/INT4 KV-Cache Quantization", item 3 (dequantize into fp16 operand space inside
 // the flash-attention reduction).
 //
-// Work unit: a workgroup of 4 waves per (split-K chunk, KV head, sequence).  Waves take 32-token
-// steps of the chunk in turn.  Per step a lane owns (token, 64-channel half row): it loads the
-// packed codes and group metadata with 128-bit loads (prefetched two steps ahead), expands them
-// to fp16 in registers and writes the rows into the wave's LDS tile; outlier records of the step
-// are written over their positions.  Scores are computed transposed, S^T = K^ Q^T, with
-// v_mfma_f32_16x16x32_f16 (16 tokens x 16 padded query rows), which leaves every lane holding
-// the probabilities of one query row for 4+4 tokens - exactly the B operand of O^T = V^T P^T.
-// V^T operands come out of the LDS tile with ds_read_b64_tr_b16.  P is split into fp16 hi + lo
-// parts so that large outlier values in V see fp32-grade probabilities.  The 4 waves' states are
-// merged in LDS; a chunk writes either the final output or a (max, sum, output) partial.
+// Work unit: a workgroup of 8 waves (two per SIMD) per (split-K chunk, KV head, sequence).
+// Waves take 32-token steps of the chunk in turn.  Per step a lane owns (token, 64-channel half
+// row): it loads the packed codes and group metadata with 128-bit loads (prefetched two steps
+// ahead), expands them to fp16 in registers and writes the rows into the wave's LDS tile; outlier
+// records of the step are written over their positions.  Scores are computed transposed,
+// S^T = K^ Q^T, with v_mfma_f32_16x16x32_f16 (16 tokens x 16 padded query rows), which leaves
+// every lane holding the probabilities of one query row for 4+4 tokens - exactly the B operand of
+// O^T = V^T P^T.  V^T operands come out of the LDS tile with ds_read_b64_tr_b16.  P is split into
+// fp16 hi + lo parts so that large outlier values in V see fp32-grade probabilities.  The waves'
+// states are merged in LDS; a chunk writes either the final output or a (max, sum, output)
+// partial.  The two waves of a SIMD keep pace with each other through their issue priority.
 //
 // 2-bit expansion: per 64-bit centroid word, two byte tables (low bytes and high bytes of the 4
 // fp16 centroids) are built once; the four codes of one bit pair of a 32-bit code word (one per
@@ -48,7 +49,7 @@ __device__ __forceinline__ half4v read_tr16(const lds_half* p) {
   return __builtin_bit_cast(half4v, v);
 }
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;                  // one workgroup of 8 waves per (chunk, KV head, sequence)
 #ifndef KVQ_PREFETCH_STEPS
 #define KVQ_PREFETCH_STEPS 2
 #endif
@@ -65,6 +66,9 @@ constexpr int kRow = KVQ_TILE_ROW;         // LDS row stride in halfs (272 bytes
 #endif
 #ifndef KVQ_ROTATE
 #define KVQ_ROTATE 1
+#endif
+#ifndef KVQ_PRIO
+#define KVQ_PRIO 1
 #endif
 #ifndef KVQ_TILES
 #define KVQ_TILES 2
@@ -169,12 +173,22 @@ __device__ __forceinline__ uint32_t tile_pos(uint32_t dd) {
   return dd + ((dd >> 7) << 3);   // t * kRow + c = dd + 8 t
 }
 
+// V tiles keep token t in row 2 (t % 16) + t / 16: the four rows that one transposing read
+// touches (tokens 4i .. 4i+3) are then 8 banks apart, and the rows written by lanes 0..7 of a
+// 128-bit store are still 4 banks apart.  Lane row r therefore loads V of token vtok(r).
+__device__ __forceinline__ int vrow_of(int t) { return 2 * (t & 15) + (t >> 4); }
+__device__ __forceinline__ int vtok(int row) { return 16 * (row & 1) + (row >> 1); }
+__device__ __forceinline__ uint32_t tile_pos_v(uint32_t dd) {
+  const uint32_t t = dd >> 7;
+  return (uint32_t)vrow_of((int)t) * (uint32_t)kRow + (dd & 127u);
+}
+
 // Overwrite one outlier position of a tile straight from the record (crowded or ragged steps).
 // A record outside the step goes to a pad slot (row 0, column 128) that no operand read touches.
-template <int FMT, int OUTL>
+template <int FMT, int OUTL, bool VT>
 __device__ __forceinline__ void patch_at(_Float16* tile, uint32_t idx, uint32_t val, int ts, int nval) {
   const uint32_t dd = idx - (uint32_t)ts * 128u;
-  const uint32_t at = dd < (uint32_t)nval * 128u ? tile_pos(dd) : (uint32_t)kHeadDim;
+  const uint32_t at = dd < (uint32_t)nval * 128u ? (VT ? tile_pos_v(dd) : tile_pos(dd)) : (uint32_t)kHeadDim;
   tile[at] = outl_half<OUTL>(val);
 }
 
@@ -199,9 +213,10 @@ constexpr int kRowRor8 = 0x128;   // lane i <- lane (i + 8) mod 16 of its row
 // CMP: at most 8 query heads per KV head.  Score tiles then hold real query rows only in lanes
 // r < 8; the softmax runs on 4 scores per lane after moving tile 1's rows into lanes r >= 8.
 template <int FMT, int OUTL, bool CMP>
-__global__ void __launch_bounds__(256) KVQ_OCC decode_mfma_kernel(DecodeLaunch d) {
+__global__ void __launch_bounds__(kWaves * 64) KVQ_OCC decode_mfma_kernel(DecodeLaunch d) {
   __shared__ __attribute__((aligned(16))) _Float16 s_lds[kWaves * kWaveLds];
   __shared__ float s_ml[kWaves][16][2];
+  __shared__ int s_simd[kWaves], s_prog[kWaves];   // SIMD of each wave, groups done
 
   const Layout& L = d.L;
   const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -253,8 +268,10 @@ __global__ void __launch_bounds__(256) KVQ_OCC decode_mfma_kernel(DecodeLaunch d
   const __amdgpu_buffer_rsrc_t rmK = make_rsrc((const uint8_t*)d.cache.meta[0] + rowbase * MB, (uint32_t)t1 * MB);
   const __amdgpu_buffer_rsrc_t rmV = make_rsrc((const uint8_t*)d.cache.meta[1] + rowbase * MB, (uint32_t)t1 * MB);
   const uint32_t coff = (uint32_t)(trow * CB + half * (CB / 2));
+  const uint32_t coffv = (uint32_t)(vtok(trow) * CB + half * (CB / 2));
   const uint32_t lane4 = (uint32_t)lane * 4u, laneVB = (uint32_t)lane * VB, laneVB8 = laneVB * 8u;
   const uint32_t moff = (uint32_t)(trow * MB + half * (MB / 2));
+  const uint32_t moffv = (uint32_t)(vtok(trow) * MB + half * (MB / 2));
 
   const size_t lidK = list_id(L, b, h, 0);
   const int cap = (int)min(L.outl_cap, (int64_t)INT32_MAX);
@@ -285,11 +302,11 @@ __global__ void __launch_bounds__(256) KVQ_OCC decode_mfma_kernel(DecodeLaunch d
     cntV = max(0, min(d.cache.outl_count[lidK + 1], cap));
   }
 
+  // The chunk's full 32-token steps are spread over the waves; its ragged last step (if any) is
+  // left to wave 0 after the others.
   const int nsteps = (t1 - t0 + kStep - 1) / kStep;
-  const int nmine = wave < nsteps ? (nsteps - wave + kWaves - 1) / kWaves : 0;
-  // The chunk's ragged last step (if any) belongs to one wave and is processed last.
-  const bool ragged = (t1 - t0) % kStep != 0 && wave == (nsteps - 1) % kWaves;
-  const int nfull = nmine - (ragged ? 1 : 0);
+  const bool ragged = (t1 - t0) % kStep != 0;
+  const int nfull = nsteps - (ragged ? 1 : 0);
   // Workgroups walk their full steps in rotated order, starting at evenly spread points.  Every
   // (sequence, head) slice starts at the same power-of-two-aligned offset; walking them in
   // lockstep would send every workgroup to the same HBM channels at the same time.
@@ -300,40 +317,41 @@ __global__ void __launch_bounds__(256) KVQ_OCC decode_mfma_kernel(DecodeLaunch d
 #else
   const int rot = 0;
 #endif
-  // token start of the wave's j-th processed step (j >= nmine: past the chunk)
-  auto step_ts = [&](int j) {
-    int jj = j;
-    if (j < nfull) { jj = j + rot; if (jj >= nfull) jj -= nfull; }
-    return t0 + kStep * (wave + kWaves * jj);
+  // token start of full step number c (c >= nfull: past the chunk, every load reads zeros)
+  auto step_ts = [&](int c) {
+    if (c >= nfull) return t1 + 2 * kStep;
+    int a = c + rot;
+    if (a >= nfull) a -= nfull;
+    return t0 + kStep * a;
   };
 
-  auto issue_codes = [&](Buf<FMT>& bf, int j) {
-    const uint32_t ts = (uint32_t)step_ts(j);
+  auto issue_codes = [&](Buf<FMT>& bf, int tsi) {
+    const uint32_t ts = (uint32_t)tsi;
     if constexpr (FMT == FMT_C2) {
       bf.kc = ld128(rcK, ts * CB + coff);
-      bf.vc = ld128(rcV, ts * CB + coff);
+      bf.vc = ld128(rcV, ts * CB + coffv);
       bf.km = ld64(rmK, ts * MB + moff);
-      bf.vm = ld64(rmV, ts * MB + moff);
+      bf.vm = ld64(rmV, ts * MB + moffv);
     } else {
       bf.kc0 = ld128(rcK, ts * CB + coff);
       bf.kc1 = ld128(rcK, ts * CB + coff + 16);
-      bf.vc0 = ld128(rcV, ts * CB + coff);
-      bf.vc1 = ld128(rcV, ts * CB + coff + 16);
+      bf.vc0 = ld128(rcV, ts * CB + coffv);
+      bf.vc1 = ld128(rcV, ts * CB + coffv + 16);
       bf.km = ld16(rmK, ts * MB + moff);
-      bf.vm = ld16(rmV, ts * MB + moff);
+      bf.vm = ld16(rmV, ts * MB + moffv);
     }
   };
   // lanes 0..3 load {K start, K end, V start, V end} of step j's records (block starts)
-  auto issue_bounds = [&](int j) -> uint32_t {
+  auto issue_bounds = [&](int ts) -> uint32_t {
     if constexpr (!HAS_OUTL) return 0u;
-    const int blk = step_ts(j) >> 4;
+    const int blk = ts >> 4;
     const int which = lane & 3;  // 0: K blk, 1: K blk+2, 2: V blk, 3: V blk+2
     const uint32_t off = (uint32_t)(((which >> 1) * L.nblk + blk + 2 * (which & 1)) * 4);
     return ld32(rbs, off);
   };
-  auto issue_recs = [&](Recs& rc, uint32_t bnd, int j) {
+  auto issue_recs = [&](Recs& rc, uint32_t bnd, int ts) {
     if constexpr (HAS_OUTL) {
-      const bool last = step_ts(j) + kStep >= S;
+      const bool last = ts + kStep >= S;
       const int k0 = max(0, min(__builtin_amdgcn_readlane((int)bnd, 0), cap));
       const int k1 = last ? cntK : max(0, min(__builtin_amdgcn_readlane((int)bnd, 1), cap));
       const int v0 = max(0, min(__builtin_amdgcn_readlane((int)bnd, 2), cap));
@@ -367,9 +385,8 @@ __global__ void __launch_bounds__(256) KVQ_OCC decode_mfma_kernel(DecodeLaunch d
   // branch-free block: K rows are expanded and written, the K^ operand reads are issued, V rows
   // are expanded while those reads are in flight, the score MFMAs run, the V^T operand reads are
   // issued before the softmax needs them.
-  auto consume = [&](const Buf<FMT>& bf, const Recs& rc, int j, auto full_tag) {
+  auto consume = [&](const Buf<FMT>& bf, const Recs& rc, int ts, auto full_tag) {
     constexpr bool FULL = decltype(full_tag)::value;
-    const int ts = step_ts(j);
     const int nval = FULL ? kStep : min(kStep, t1 - ts);
     _Float16* krow = ktile + trow * kRow + 64 * half;
     _Float16* vrow = vtile + trow * kRow + 64 * half;
@@ -390,7 +407,7 @@ __global__ void __launch_bounds__(256) KVQ_OCC decode_mfma_kernel(DecodeLaunch d
         ovK[sl] = outl_half<OUTL>(__builtin_amdgcn_ubfe(rc.vk[sl], bitK, VB * 8));
       }
       const uint32_t ddv = rc.iv - (uint32_t)ts * 128u;
-      posV = lane < rc.nv && ddv < lim ? tile_pos(ddv) : (uint32_t)kHeadDim;
+      posV = lane < rc.nv && ddv < lim ? tile_pos_v(ddv) : (uint32_t)kHeadDim;
       ovV = outl_half<OUTL>(__builtin_amdgcn_ubfe(rc.vv, bitV, VB * 8));
     }
     if constexpr (FMT == FMT_C2) expand_c2(bf.kc, bf.km, krow);
@@ -402,7 +419,7 @@ __global__ void __launch_bounds__(256) KVQ_OCC decode_mfma_kernel(DecodeLaunch d
         for (int a = 128 + lane; a < rc.nk; a += 64) {  // the rest of a crowded step
           const int at = rc.kr0 + a;
           const uint32_t v = VB == 2 ? ((const uint16_t*)ovalK)[at] : ovalK[at];
-          patch_at<FMT, OUTL>(ktile, oidxK[at], v, ts, nval);
+          patch_at<FMT, OUTL, false>(ktile, oidxK[at], v, ts, nval);
         }
       }
     }
@@ -420,7 +437,7 @@ __global__ void __launch_bounds__(256) KVQ_OCC decode_mfma_kernel(DecodeLaunch d
         for (int i = 64 + lane; i < rc.nv; i += 64) {
           const int at = rc.vr0 + i;
           const uint32_t v = VB == 2 ? ((const uint16_t*)ovalV)[at] : ovalV[at];
-          patch_at<FMT, OUTL>(vtile, oidxV[at], v, ts, nval);
+          patch_at<FMT, OUTL, true>(vtile, oidxV[at], v, ts, nval);
         }
       }
     }
@@ -435,11 +452,11 @@ __global__ void __launch_bounds__(256) KVQ_OCC decode_mfma_kernel(DecodeLaunch d
     {
       const lds_half* vbase = (const lds_half*)vtile;
       const int col0 = 4 * (r & 3);
-      const int rowo = 4 * kg + (r >> 2);
+      const int rowo = vrow_of(4 * kg + (r >> 2));   // token 4 kg + r / 4; its tile-1 partner is the next row
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) {
         const half4v t0v = read_tr16(vbase + rowo * kRow + 16 * mt + col0);
-        const half4v t1v = read_tr16(vbase + (16 + rowo) * kRow + 16 * mt + col0);
+        const half4v t1v = read_tr16(vbase + (rowo + 1) * kRow + 16 * mt + col0);
         av[mt] = half8{t0v[0], t0v[1], t0v[2], t0v[3], t1v[0], t1v[1], t1v[2], t1v[3]};
       }
     }
@@ -511,48 +528,75 @@ __global__ void __launch_bounds__(256) KVQ_OCC decode_mfma_kernel(DecodeLaunch d
       oacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[mt], plo, oacc[mt], 0, 0, 0);
     }
   };
-  auto run_step = [&](const Buf<FMT>& bf, const Recs& rc, int j) {
-    if (step_ts(j) + kStep <= t1) consume(bf, rc, j, std::true_type{});
-    else consume(bf, rc, j, std::false_type{});
-  };
-
-  // ---- software pipeline: codes and records kPF steps ahead, record bounds kPF + 1 ahead.
-  // Loads for steps past the wave's last step are issued anyway: their offsets lie past the
-  // buffer ranges (codes) or are clamped (records), so they return zeros or unused data without
-  // touching memory, and keeping every load unconditional lets the wait counters stay exact.
+  // ---- software pipeline: codes and records of the next kPF steps in flight, the record
+  // bounds of the step after them too.  Wave w takes full steps w, w + kWaves, ...; whole groups
+  // of NB steps run without conditions, so every ring slot keeps its registers and the wait
+  // counters stay exact.  Loads for steps past the chunk return zeros without touching memory.
+  //
+  // Two waves share each SIMD and the scheduler favours the older one; every group, a wave that
+  // is ahead of its SIMD partner lowers its priority, so both finish together.
   constexpr int NB = kPF + 1;  // ring slots
   Buf<FMT> buf[NB];
   Recs rec[NB];
   uint32_t bnd[NB];
-  if (nmine > 0) {
+  const int nmine = wave < nfull ? (nfull - wave + kWaves - 1) / kWaves : 0;
+  auto wts = [&](int j) { return step_ts(j < nmine ? wave + kWaves * j : nfull); };
+#if KVQ_PRIO
+  const int mysimd = (int)((__builtin_amdgcn_s_getreg((31 << 11) | 4) >> 4) & 3);   // HW_ID.simd
+  if (lane == 0) { s_simd[wave] = mysimd; s_prog[wave] = 0; }
+  __syncthreads();
+  int partner = wave;
+  for (int w2 = 0; w2 < kWaves; ++w2)
+    if (w2 != wave && __builtin_amdgcn_readfirstlane(s_simd[w2]) == mysimd) partner = w2;
+  int* const prog_mine = &s_prog[wave];
+  const int* const prog_partner = &s_prog[partner];
+  int partner_seen = 0;
+#endif
 #pragma unroll
-    for (int k = 0; k < NB; ++k) bnd[k] = issue_bounds(k);
+  for (int k = 0; k < NB; ++k) bnd[k] = issue_bounds(wts(k));
 #pragma unroll
-    for (int k = 0; k < kPF; ++k) { issue_recs(rec[k], bnd[k], k); issue_codes(buf[k], k); }
+  for (int k = 0; k < kPF; ++k) {
+    issue_recs(rec[k], bnd[k], wts(k));
+    issue_codes(buf[k], wts(k));
   }
-  // Whole groups of NB full steps run without conditions (so every ring slot keeps its registers
-  // and the wait counters stay exact); the last group holds the remaining steps, the chunk's
-  // ragged last step among them.
-  const int ngroups = nfull / NB;
+  const int ngroups = nmine / NB;
   for (int g = 0; g < ngroups; ++g) {
+#if KVQ_PRIO
+    if (g > partner_seen) __builtin_amdgcn_s_setprio(0);
+    else __builtin_amdgcn_s_setprio(1);
+    if (lane == 0) *prog_mine = g;
+#endif
 #pragma unroll
     for (int u = 0; u < NB; ++u) {
       const int jj = g * NB + u;
-      bnd[u] = issue_bounds(jj + NB);
-      issue_recs(rec[(u + kPF) % NB], bnd[(u + kPF) % NB], jj + kPF);
-      issue_codes(buf[(u + kPF) % NB], jj + kPF);
-      consume(buf[u], rec[u], jj, std::true_type{});
+      bnd[u] = issue_bounds(wts(jj + NB));
+      issue_recs(rec[(u + kPF) % NB], bnd[(u + kPF) % NB], wts(jj + kPF));
+      issue_codes(buf[(u + kPF) % NB], wts(jj + kPF));
+      consume(buf[u], rec[u], wts(jj), std::true_type{});
     }
+#if KVQ_PRIO
+    partner_seen = __builtin_amdgcn_readfirstlane(*prog_partner);
+#endif
   }
+#if KVQ_PRIO
+  __builtin_amdgcn_s_setprio(0);
+#endif
 #pragma unroll
   for (int u = 0; u < NB; ++u) {
     const int jj = ngroups * NB + u;
     if (jj < nmine) {
-      bnd[u] = issue_bounds(jj + NB);
-      issue_recs(rec[(u + kPF) % NB], bnd[(u + kPF) % NB], jj + kPF);
-      issue_codes(buf[(u + kPF) % NB], jj + kPF);
-      run_step(buf[u], rec[u], jj);
+      bnd[u] = issue_bounds(wts(jj + NB));
+      issue_recs(rec[(u + kPF) % NB], bnd[(u + kPF) % NB], wts(jj + kPF));
+      issue_codes(buf[(u + kPF) % NB], wts(jj + kPF));
+      consume(buf[u], rec[u], wts(jj), std::true_type{});
     }
+  }
+  if (ragged && wave == 0) {
+    const int ts = t0 + kStep * (nsteps - 1);
+    const uint32_t b0 = issue_bounds(ts);
+    issue_recs(rec[0], b0, ts);
+    issue_codes(buf[0], ts);
+    consume(buf[0], rec[0], ts, std::false_type{});
   }
 
   // ---- merge the waves of the workgroup
@@ -594,9 +638,9 @@ __global__ void __launch_bounds__(256) KVQ_OCC decode_mfma_kernel(DecodeLaunch d
 template <int FMT, bool CMP>
 void launch_cmp(const DecodeLaunch& d, dim3 grid, hipStream_t st) {
   switch (d.outl) {
-    case KVQ_OUTL_NONE: decode_mfma_kernel<FMT, KVQ_OUTL_NONE, CMP><<<grid, 256, 0, st>>>(d); break;
-    case KVQ_OUTL_FP16: decode_mfma_kernel<FMT, KVQ_OUTL_FP16, CMP><<<grid, 256, 0, st>>>(d); break;
-    default: decode_mfma_kernel<FMT, KVQ_OUTL_FP8_E4M3, CMP><<<grid, 256, 0, st>>>(d); break;
+    case KVQ_OUTL_NONE: decode_mfma_kernel<FMT, KVQ_OUTL_NONE, CMP><<<grid, kWaves * 64, 0, st>>>(d); break;
+    case KVQ_OUTL_FP16: decode_mfma_kernel<FMT, KVQ_OUTL_FP16, CMP><<<grid, kWaves * 64, 0, st>>>(d); break;
+    default: decode_mfma_kernel<FMT, KVQ_OUTL_FP8_E4M3, CMP><<<grid, kWaves * 64, 0, st>>>(d); break;
   }
 }
 
