@@ -49,10 +49,10 @@ __device__ __forceinline__ half4v read_tr16(const lds_half* p) {
   return __builtin_bit_cast(half4v, v);
 }
 
-constexpr int kWaves = 8;                  // one workgroup of 8 waves per (chunk, KV head, sequence)
 #ifndef KVQ_PREFETCH_STEPS
 #define KVQ_PREFETCH_STEPS 2
 #endif
+constexpr int kWaves = 8;                  // waves per workgroup, two per SIMD
 constexpr int kPF = KVQ_PREFETCH_STEPS;    // steps of codes / records in flight per wave
 constexpr int kStep = 32;                  // tokens per wave step
 #ifndef KVQ_TILE_ROW
@@ -219,17 +219,21 @@ __global__ void __launch_bounds__(kWaves * 64) KVQ_OCC decode_mfma_kernel(Decode
   __shared__ int s_simd[kWaves], s_prog[kWaves];   // SIMD of each wave, groups done
 
   const Layout& L = d.L;
-  const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int h = blockIdx.y, b = blockIdx.z;
   const int S = d.seq_lens[b];
   if (S < 1 || S > L.S_cap) {
-    if (threadIdx.x == 0 && chunk == 0 && h == 0) report(d.cache.status, KVQ_ERR_INVALID_ARG);
+    if (threadIdx.x == 0 && blockIdx.x == 0 && h == 0) report(d.cache.status, KVQ_ERR_INVALID_ARG);
     return;
   }
-  const int t0 = chunk * d.chunk;
-  if (t0 >= S) return;
-  const int t1 = min(t0 + d.chunk, S);
-  const int G = d.Hq / L.H;
+  // The workgroup covers chunks cpw * blockIdx.x .. + cpw - 1, wpc waves each.
+  const int cpw = d.cpw, wpc = kWaves / cpw;
+  if (blockIdx.x * cpw * d.chunk >= S) return;
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int ci = wave / wpc, wi = wave - ci * wpc;   // chunk of this wave, its place in the chunk
+  const int chunk = blockIdx.x * cpw + ci;
+  const int t0 = chunk * d.chunk;
+  const int t1 = chunk < d.n_chunks && t0 < S ? min(t0 + d.chunk, S) : t0;   // empty: past S
+  const int G = d.Hq / L.H;
   const int lane = threadIdx.x & 63;
   const int r = lane & 15, kg = lane >> 4;           // MFMA lane coordinates
   const int trow = lane & 31, half = lane >> 5;      // dequant lane coordinates
@@ -302,8 +306,8 @@ __global__ void __launch_bounds__(kWaves * 64) KVQ_OCC decode_mfma_kernel(Decode
     cntV = max(0, min(d.cache.outl_count[lidK + 1], cap));
   }
 
-  // The chunk's full 32-token steps are spread over the waves; its ragged last step (if any) is
-  // left to wave 0 after the others.
+  // The chunk's full 32-token steps are spread over its waves; its ragged last step (if any) is
+  // left to the chunk's first wave after the others.
   const int nsteps = (t1 - t0 + kStep - 1) / kStep;
   const bool ragged = (t1 - t0) % kStep != 0;
   const int nfull = nsteps - (ragged ? 1 : 0);
@@ -311,9 +315,9 @@ __global__ void __launch_bounds__(kWaves * 64) KVQ_OCC decode_mfma_kernel(Decode
   // (sequence, head) slice starts at the same power-of-two-aligned offset; walking them in
   // lockstep would send every workgroup to the same HBM channels at the same time.
 #if KVQ_ROTATE
-  const uint32_t n_wg = gridDim.x * gridDim.y * gridDim.z;
-  const uint32_t wg = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
-  const int rot = nfull > 0 ? (int)(((uint64_t)wg * (uint64_t)nfull) / n_wg) : 0;
+  const uint32_t n_units = (uint32_t)d.n_chunks * gridDim.y * gridDim.z;
+  const uint32_t unit = (uint32_t)chunk + (uint32_t)d.n_chunks * (blockIdx.y + gridDim.y * blockIdx.z);
+  const int rot = nfull > 0 ? (int)(((uint64_t)unit * (uint64_t)nfull) / n_units) : 0;
 #else
   const int rot = 0;
 #endif
@@ -529,7 +533,8 @@ __global__ void __launch_bounds__(kWaves * 64) KVQ_OCC decode_mfma_kernel(Decode
     }
   };
   // ---- software pipeline: codes and records of the next kPF steps in flight, the record
-  // bounds of the step after them too.  Wave w takes full steps w, w + kWaves, ...; whole groups
+  // bounds of the step after them too.  Wave wi of a chunk takes its full steps wi, wi + wpc, ...;
+  // whole groups
   // of NB steps run without conditions, so every ring slot keeps its registers and the wait
   // counters stay exact.  Loads for steps past the chunk return zeros without touching memory.
   //
@@ -539,8 +544,8 @@ __global__ void __launch_bounds__(kWaves * 64) KVQ_OCC decode_mfma_kernel(Decode
   Buf<FMT> buf[NB];
   Recs rec[NB];
   uint32_t bnd[NB];
-  const int nmine = wave < nfull ? (nfull - wave + kWaves - 1) / kWaves : 0;
-  auto wts = [&](int j) { return step_ts(j < nmine ? wave + kWaves * j : nfull); };
+  const int nmine = wi < nfull ? (nfull - wi + wpc - 1) / wpc : 0;
+  auto wts = [&](int j) { return step_ts(j < nmine ? wi + wpc * j : nfull); };
 #if KVQ_PRIO
   const int mysimd = (int)((__builtin_amdgcn_s_getreg((31 << 11) | 4) >> 4) & 3);   // HW_ID.simd
   if (lane == 0) { s_simd[wave] = mysimd; s_prog[wave] = 0; }
@@ -591,7 +596,7 @@ __global__ void __launch_bounds__(kWaves * 64) KVQ_OCC decode_mfma_kernel(Decode
       consume(buf[u], rec[u], wts(jj), std::true_type{});
     }
   }
-  if (ragged && wave == 0) {
+  if (ragged && wi == 0) {
     const int ts = t0 + kStep * (nsteps - 1);
     const uint32_t b0 = issue_bounds(ts);
     issue_recs(rec[0], b0, ts);
@@ -611,14 +616,15 @@ __global__ void __launch_bounds__(kWaves * 64) KVQ_OCC decode_mfma_kernel(Decode
     for (int v = 0; v < 4; ++v) s_o[r * kHeadDim + (16 * mt + 4 * kg + v)] = oacc[mt][v];
   if (kg == 0) { s_ml[wave][r][0] = m_run; s_ml[wave][r][1] = l_row; }
   __syncthreads();
-  for (int i = threadIdx.x; i < G * kHeadDim; i += 256) {
-    const int row = i / kHeadDim, ch = i % kHeadDim;
+  for (int i = threadIdx.x; i < cpw * G * kHeadDim; i += kWaves * 64) {
+    const int c2 = i / (G * kHeadDim), row = (i / kHeadDim) % G, ch = i % kHeadDim;
+    const int chunk2 = blockIdx.x * cpw + c2;
+    if (chunk2 >= d.n_chunks || chunk2 * d.chunk >= S) continue;
+    const int w0 = c2 * wpc;
     float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_ml[w][row][0]);
+    for (int w = w0; w < w0 + wpc; ++w) M = fmaxf(M, s_ml[w][row][0]);
     float num = 0.0f, den = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = w0; w < w0 + wpc; ++w) {
       const float mw = s_ml[w][row][0];
       const float f = mw == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
       den += f * s_ml[w][row][1];
@@ -628,7 +634,7 @@ __global__ void __launch_bounds__(kWaves * 64) KVQ_OCC decode_mfma_kernel(Decode
     if (d.n_chunks == 1) {
       d.out[((size_t)b * d.Hq + hq) * kHeadDim + ch] = num / den;
     } else {
-      float* pp = d.partials + (((size_t)b * d.Hq + hq) * d.n_chunks + chunk) * (kHeadDim + 2);
+      float* pp = d.partials + (((size_t)b * d.Hq + hq) * d.n_chunks + chunk2) * (kHeadDim + 2);
       if (ch == 0) { pp[0] = M; pp[1] = den; }
       pp[2 + ch] = num;
     }
@@ -657,9 +663,13 @@ hipError_t launch_decode_mfma(const DecodeLaunch& d, hipStream_t st, bool* handl
   if (d.L.paged) return hipSuccess;
   if (d.fmt != FMT_C2 && !(d.fmt == FMT_FP4 && d.group == 32)) return hipSuccess;
   if (d.chunk % kStep) return hipSuccess;
-  dim3 grid(d.n_chunks, d.L.H, d.L.B);
-  if (d.fmt == FMT_C2) launch_fmt<FMT_C2>(d, grid, st);
-  else launch_fmt<FMT_FP4>(d, grid, st);
+  // Short chunks are packed several to a workgroup so that every wave keeps >= 16 steps.
+  DecodeLaunch dd = d;
+  dd.cpw = 1;
+  while (dd.cpw < kWaves && d.chunk * dd.cpw * 2 <= 16 * kStep * kWaves) dd.cpw *= 2;
+  dim3 grid((d.n_chunks + dd.cpw - 1) / dd.cpw, d.L.H, d.L.B);
+  if (d.fmt == FMT_C2) launch_fmt<FMT_C2>(dd, grid, st);
+  else launch_fmt<FMT_FP4>(dd, grid, st);
   *handled = true;
   return hipGetLastError();
 }

@@ -83,7 +83,7 @@ int resolve_chunk(const kvq_params* p, int32_t split_chunk) {
   if (split_chunk == 0) {
     if (p->page_size) return kDefaultPagedChunk;
     const int64_t units = (int64_t)p->batch * p->num_kv_heads;
-    const int64_t want = 512;
+    const int64_t want = 256;   // one 8-wave MFMA workgroup per compute unit
     int64_t nchunks = units >= want ? 1 : (want + units - 1) / units;
     int64_t chunk = (p->max_seq_len + nchunks - 1) / nchunks;
     chunk = chunk < 512 ? 512 : chunk;
@@ -217,6 +217,7 @@ int32_t kvq_decode_attention(const kvq_params* p, const kvq_cache* cache, const 
   d.n_chunks = (p->max_seq_len + chunk - 1) / chunk;
   d.partials = d.n_chunks > 1 ? (float*)workspace : nullptr;
   d.scale_log2 = sm_scale * 1.4426950408889634f;
+  d.cpw = 1;
   hipStream_t s = (hipStream_t)stream;
   bool handled = false;
   if (launch_decode_mfma(d, s, &handled) != hipSuccess) return KVQ_ERR_HIP;

@@ -38,6 +38,7 @@ struct DecodeLaunch {
   int chunk;                  // tokens per split-K chunk (multiple of 64)
   int n_chunks;               // ceil(S_cap / chunk)
   float scale_log2;           // sm_scale * log2(e)
+  int cpw;                    // MFMA decoder: chunks per workgroup (set by its launcher)
 };
 
 hipError_t launch_quantize_append(const QuantizeLaunch& q, hipStream_t st);

@@ -62,7 +62,7 @@ def test_quantize_bit_exact(small):
                 assert_list_equal(got, ref, f"{name} b={b} h={h} kv={kv}")
 
 
-@pytest.mark.parametrize("split", [0, 128, 512])
+@pytest.mark.parametrize("split", [0, 128, 512, 16384])
 def test_decode_matches_oracle(small, split):
     name, dc = small
     w = dc.w
