@@ -78,8 +78,31 @@ constexpr int kWaveLds = KVQ_TILES * kTile; // K tile + V tile (or one tile for 
 
 
 template <int FMT> struct Buf;
-template <> struct Buf<FMT_C2> { uint4 kc, vc; uint2 km, vm; };
-template <> struct Buf<FMT_FP4> { uint4 kc0, kc1, vc0, vc1; uint32_t km, vm; };
+// ea, eb: block-table entries of the step's two pages (paged caches)
+template <> struct Buf<FMT_C2> { uint4 kc, vc; uint2 km, vm; uint32_t ea, eb; };
+template <> struct Buf<FMT_FP4> { uint4 kc0, kc1, vc0, vc1; uint32_t km, vm, ea, eb; };
+// record bounds of a step (lanes 0..3) and, for paged caches, its block-table entries (lanes 0, 1)
+struct Bnd { uint32_t rec, bt; };
+// FP8-tier rows of a step (paged caches): a lane's K and V half rows and their rows' scales;
+// fk / fv tell whether the lane's K / V token sits on an FP8 page, slow whether any token does
+struct F8 { uint4 k[4], v[4]; uint32_t ks, vs; bool fk, fv, slow; };
+
+// FP8 row codes -> fp16 in channel order (E4M3 values are exact in fp16)
+__device__ __forceinline__ void expand_fp8(const uint4 (&c)[4], _Float16* dst) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t w[4] = {c[k].x, c[k].y, c[k].z, c[k].w};
+    uint32_t o[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      o[2 * j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[j], 1.0f, false));
+      o[2 * j + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[j], 1.0f, true));
+    }
+    uint4* dd = (uint4*)(dst + 16 * k);
+    dd[0] = make_uint4(o[0], o[1], o[2], o[3]);
+    dd[1] = make_uint4(o[4], o[5], o[6], o[7]);
+  }
+}
 
 // Outlier records of one step: lane slots K0, K1 hold K records kr0 + lane and kr0 + 64 + lane,
 // slot V holds V record vr0 + lane.  Values are kept as the aligned 32-bit words that hold them.
@@ -109,7 +132,7 @@ __device__ __forceinline__ uint32_t ld8(__amdgpu_buffer_rsrc_t r, uint32_t off) 
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, (int)off, 0, 0);
 }
 
-// 64 channels of one 2-bit row -> 64 fp16 in transposed-block order at dst
+// 64 channels of one 2-bit row -> 64 fp16 in channel order at dst
 __device__ __forceinline__ void expand_c2(uint4 c, uint2 m, _Float16* dst) {
   const uint32_t tl = __builtin_amdgcn_perm(m.y, m.x, 0x06040200u);  // low bytes of C0..C3
   const uint32_t th = __builtin_amdgcn_perm(m.y, m.x, 0x07050301u);  // high bytes
@@ -212,11 +235,13 @@ constexpr int kRowRor8 = 0x128;   // lane i <- lane (i + 8) mod 16 of its row
 
 // CMP: at most 8 query heads per KV head.  Score tiles then hold real query rows only in lanes
 // r < 8; the softmax runs on 4 scores per lane after moving tile 1's rows into lanes r >= 8.
-template <int FMT, int OUTL, bool CMP>
+// PAGED: 2-bit pages behind a block table, some of them (tier 1) FP8 rows with a per-row scale.
+template <int FMT, int OUTL, bool CMP, bool PAGED>
 __global__ void __launch_bounds__(kWaves * 64) KVQ_OCC decode_mfma_kernel(DecodeLaunch d) {
   __shared__ __attribute__((aligned(16))) _Float16 s_lds[kWaves * kWaveLds];
   __shared__ float s_ml[kWaves][16][2];
   __shared__ int s_simd[kWaves], s_prog[kWaves];   // SIMD of each wave, groups done
+  __shared__ __attribute__((aligned(16))) float s_rs[PAGED ? kWaves : 1][2][kStep];   // FP8-tier row scales (K, V)
 
   const Layout& L = d.L;
   const int h = blockIdx.y, b = blockIdx.z;
@@ -265,12 +290,23 @@ __global__ void __launch_bounds__(kWaves * 64) KVQ_OCC decode_mfma_kernel(Decode
       for (int e = 0; e < 8; ++e) qop[ks][e] = (_Float16)(as_f32((uint32_t)raw[ks][e] << 16) * keep);
   }
 
-  // buffer resources: rows [0, t1) of this (sequence, KV head); rows past t1 read as zero
-  const size_t rowbase = ((size_t)b * L.H + h) * (size_t)L.S_cap;
-  const __amdgpu_buffer_rsrc_t rcK = make_rsrc((const uint8_t*)d.cache.codes[0] + rowbase * CB, (uint32_t)t1 * CB);
-  const __amdgpu_buffer_rsrc_t rcV = make_rsrc((const uint8_t*)d.cache.codes[1] + rowbase * CB, (uint32_t)t1 * CB);
-  const __amdgpu_buffer_rsrc_t rmK = make_rsrc((const uint8_t*)d.cache.meta[0] + rowbase * MB, (uint32_t)t1 * MB);
-  const __amdgpu_buffer_rsrc_t rmV = make_rsrc((const uint8_t*)d.cache.meta[1] + rowbase * MB, (uint32_t)t1 * MB);
+  // buffer resources.  Contiguous: rows [0, t1) of this (sequence, KV head); rows past t1 read as
+  // zero.  Paged: the whole page pools (rows past t1 get out-of-range offsets).
+  const size_t rowbase = PAGED ? 0 : ((size_t)b * L.H + h) * (size_t)L.S_cap;
+  const uint32_t nrows = PAGED ? (uint32_t)L.num_pages * (uint32_t)L.H * kBlock : (uint32_t)t1;
+  const __amdgpu_buffer_rsrc_t rcK = make_rsrc((const uint8_t*)d.cache.codes[0] + rowbase * CB, nrows * CB);
+  const __amdgpu_buffer_rsrc_t rcV = make_rsrc((const uint8_t*)d.cache.codes[1] + rowbase * CB, nrows * CB);
+  const __amdgpu_buffer_rsrc_t rmK = make_rsrc((const uint8_t*)d.cache.meta[0] + rowbase * MB, nrows * MB);
+  const __amdgpu_buffer_rsrc_t rmV = make_rsrc((const uint8_t*)d.cache.meta[1] + rowbase * MB, nrows * MB);
+  __amdgpu_buffer_rsrc_t r8K, r8V, rsK, rsV, rbt;
+  if constexpr (PAGED) {
+    const uint32_t n8 = (uint32_t)L.num_pages_fp8 * (uint32_t)L.H * kBlock;
+    r8K = make_rsrc(d.cache.codes8[0], n8 * kHeadDim);
+    r8V = make_rsrc(d.cache.codes8[1], n8 * kHeadDim);
+    rsK = make_rsrc(d.cache.scale8[0], n8 * 4);
+    rsV = make_rsrc(d.cache.scale8[1], n8 * 4);
+    rbt = make_rsrc(d.block_table + (size_t)b * L.max_pages, (uint32_t)L.max_pages * 4);
+  }
   const uint32_t coff = (uint32_t)(trow * CB + half * (CB / 2));
   const uint32_t coffv = (uint32_t)(vtok(trow) * CB + half * (CB / 2));
   const uint32_t lane4 = (uint32_t)lane * 4u, laneVB = (uint32_t)lane * VB, laneVB8 = laneVB * 8u;
@@ -329,9 +365,34 @@ __global__ void __launch_bounds__(kWaves * 64) KVQ_OCC decode_mfma_kernel(Decode
     return t0 + kStep * a;
   };
 
-  auto issue_codes = [&](Buf<FMT>& bf, int tsi) {
+  constexpr uint32_t kOOB = 0xFFFFFFF0u;   // an offset past every buffer range
+  // paged: pool row of logical token ts + t (t < 32) of page entry ea (t < 16) or eb, or kOOB
+  // when the token is past t1, its page is FP8 (fp8 = false) / 2-bit (fp8 = true), or the slot
+  // is outside its pool (reported)
+  auto page_row = [&](uint32_t ea, uint32_t eb, int ts, int t, bool fp8) -> uint32_t {
+    const uint32_t e = t < 16 ? ea : eb;
+    const uint32_t slot = e & 0x7FFFFFFFu;
+    const bool t1page = (e >> 31) != 0;
+    const bool in_pool = slot < (uint32_t)(t1page ? L.num_pages_fp8 : L.num_pages);
+    const bool want = ts + t < t1 && t1page == fp8;
+    return want && in_pool ? (slot * (uint32_t)L.H + (uint32_t)h) * kBlock + (uint32_t)(t & 15) : kOOB;
+  };
+  auto issue_codes = [&](Buf<FMT>& bf, const Bnd& bd, int tsi) {
     const uint32_t ts = (uint32_t)tsi;
-    if constexpr (FMT == FMT_C2) {
+    if constexpr (PAGED) {
+      bf.ea = (uint32_t)__builtin_amdgcn_readlane((int)bd.bt, 0);
+      bf.eb = (uint32_t)__builtin_amdgcn_readlane((int)bd.bt, 1);
+      const uint32_t rk = page_row(bf.ea, bf.eb, tsi, trow, false);
+      const uint32_t rv = page_row(bf.ea, bf.eb, tsi, vtok(trow), false);
+      const uint32_t ok = rk == kOOB ? kOOB : rk * CB + half * (CB / 2);
+      const uint32_t ov = rv == kOOB ? kOOB : rv * CB + half * (CB / 2);
+      const uint32_t mk = rk == kOOB ? kOOB : rk * MB + half * (MB / 2);
+      const uint32_t mv = rv == kOOB ? kOOB : rv * MB + half * (MB / 2);
+      bf.kc = ld128(rcK, ok);
+      bf.vc = ld128(rcV, ov);
+      bf.km = ld64(rmK, mk);
+      bf.vm = ld64(rmV, mv);
+    } else if constexpr (FMT == FMT_C2) {
       bf.kc = ld128(rcK, ts * CB + coff);
       bf.vc = ld128(rcV, ts * CB + coffv);
       bf.km = ld64(rmK, ts * MB + moff);
@@ -345,16 +406,22 @@ __global__ void __launch_bounds__(kWaves * 64) KVQ_OCC decode_mfma_kernel(Decode
       bf.vm = ld16(rmV, ts * MB + moffv);
     }
   };
-  // lanes 0..3 load {K start, K end, V start, V end} of step j's records (block starts)
-  auto issue_bounds = [&](int ts) -> uint32_t {
-    if constexpr (!HAS_OUTL) return 0u;
+  // lanes 0..3 load {K start, K end, V start, V end} of the step's records (block starts); for
+  // paged caches lanes 0, 1 also load the block-table entries of its two pages
+  auto issue_bounds = [&](int ts) -> Bnd {
+    Bnd bd{0u, 0u};
     const int blk = ts >> 4;
-    const int which = lane & 3;  // 0: K blk, 1: K blk+2, 2: V blk, 3: V blk+2
-    const uint32_t off = (uint32_t)(((which >> 1) * L.nblk + blk + 2 * (which & 1)) * 4);
-    return ld32(rbs, off);
-  };
-  auto issue_recs = [&](Recs& rc, uint32_t bnd, int ts) {
     if constexpr (HAS_OUTL) {
+      const int which = lane & 3;  // 0: K blk, 1: K blk+2, 2: V blk, 3: V blk+2
+      const uint32_t off = (uint32_t)(((which >> 1) * L.nblk + blk + 2 * (which & 1)) * 4);
+      bd.rec = ld32(rbs, off);
+    }
+    if constexpr (PAGED) bd.bt = ld32(rbt, (uint32_t)(blk + (lane & 1)) * 4u);
+    return bd;
+  };
+  auto issue_recs = [&](Recs& rc, const Bnd& bd, int ts) {
+    if constexpr (HAS_OUTL) {
+      const uint32_t bnd = bd.rec;
       const bool last = ts + kStep >= S;
       const int k0 = max(0, min(__builtin_amdgcn_readlane((int)bnd, 0), cap));
       const int k1 = last ? cntK : max(0, min(__builtin_amdgcn_readlane((int)bnd, 1), cap));
@@ -377,6 +444,35 @@ __global__ void __launch_bounds__(kWaves * 64) KVQ_OCC decode_mfma_kernel(Decode
       rc.vv = ld32(rvV, obv);
     }
   };
+  // paged: FP8-tier rows of a step, loaded one step before it is consumed (only when one of the
+  // step's pages is FP8); a block-table entry naming a slot outside its pool is reported and
+  // its rows read as zeros
+  auto issue_fp8 = [&](F8& f, const Buf<FMT>& bf, int ts) {
+    if constexpr (PAGED) {
+      const bool live_b = ts + 16 < t1;
+      const auto bad = [&](uint32_t e) {
+        return (e & 0x7FFFFFFFu) >= (uint32_t)((e >> 31) ? L.num_pages_fp8 : L.num_pages);
+      };
+      if (ts < t1 && (bad(bf.ea) || (live_b && bad(bf.eb))) && lane == 0)
+        report(d.cache.status, KVQ_ERR_INVALID_ARG);
+      f.slow = ts < t1 && ((bf.ea >> 31) != 0 || (live_b && (bf.eb >> 31) != 0));
+      if (f.slow) {
+        const uint32_t rk = page_row(bf.ea, bf.eb, ts, trow, true);
+        const uint32_t rv = page_row(bf.ea, bf.eb, ts, vtok(trow), true);
+        f.fk = rk != kOOB;
+        f.fv = rv != kOOB;
+        // (each skipped load gets kOOB itself: kOOB + 16 k would wrap into range)
+        const uint32_t ok = rk * kHeadDim + 64u * half, ov = rv * kHeadDim + 64u * half;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          f.k[k] = ld128(r8K, f.fk ? ok + 16u * k : kOOB);
+          f.v[k] = ld128(r8V, f.fv ? ov + 16u * k : kOOB);
+        }
+        f.ks = ld32(rsK, f.fk ? rk * 4u : kOOB);
+        f.vs = ld32(rsV, f.fv ? rv * 4u : kOOB);
+      }
+    }
+  };
 
   floatx4 oacc[8];
 #pragma unroll
@@ -389,7 +485,7 @@ __global__ void __launch_bounds__(kWaves * 64) KVQ_OCC decode_mfma_kernel(Decode
   // branch-free block: K rows are expanded and written, the K^ operand reads are issued, V rows
   // are expanded while those reads are in flight, the score MFMAs run, the V^T operand reads are
   // issued before the softmax needs them.
-  auto consume = [&](const Buf<FMT>& bf, const Recs& rc, int ts, auto full_tag) {
+  auto consume = [&](const Buf<FMT>& bf, const Recs& rc, const F8& f8, int ts, auto full_tag) {
     constexpr bool FULL = decltype(full_tag)::value;
     const int nval = FULL ? kStep : min(kStep, t1 - ts);
     _Float16* krow = ktile + trow * kRow + 64 * half;
@@ -416,6 +512,19 @@ __global__ void __launch_bounds__(kWaves * 64) KVQ_OCC decode_mfma_kernel(Decode
     }
     if constexpr (FMT == FMT_C2) expand_c2(bf.kc, bf.km, krow);
     else expand_fp4(bf.kc0, bf.kc1, bf.km, krow);
+    float* const rsk = PAGED ? s_rs[wave][0] : nullptr;
+    float* const rsv = PAGED ? s_rs[wave][1] : nullptr;
+    if constexpr (PAGED) {
+      // FP8 rows replace the (zero) 2-bit rows of their tokens; the row scales multiply the
+      // scores (K) and the probabilities (V); tier-2 rows have scale 1
+      if (f8.slow) {
+        if (f8.fk) expand_fp8(f8.k, krow);
+        if (half == 0) {
+          rsk[trow] = f8.fk ? as_f32(f8.ks) : 1.0f;
+          rsv[vtok(trow)] = f8.fv ? as_f32(f8.vs) : 1.0f;
+        }
+      }
+    }
     if constexpr (HAS_OUTL) {
       ktile[posK[0]] = ovK[0];
       ktile[posK[1]] = ovK[1];
@@ -435,6 +544,9 @@ __global__ void __launch_bounds__(kWaves * 64) KVQ_OCC decode_mfma_kernel(Decode
     }
     if constexpr (FMT == FMT_C2) expand_c2(bf.vc, bf.vm, vrow);
     else expand_fp4(bf.vc0, bf.vc1, bf.vm, vrow);
+    if constexpr (PAGED) {
+      if (f8.slow && f8.fv) expand_fp8(f8.v, vrow);
+    }
     if constexpr (HAS_OUTL) {
       vtile[posV] = ovV;
       if (rc.nv > 64) {
@@ -478,6 +590,20 @@ __global__ void __launch_bounds__(kWaves * 64) KVQ_OCC decode_mfma_kernel(Decode
 #pragma unroll
       for (int v = 0; v < 4; ++v) { sc[v] = s0[v]; sc[4 + v] = s1[v]; }
     }
+    // tokens of the lane's scores: 4 kg + v (+16 for tile 1)
+    const int tb0 = CMP ? (r >= 8 ? 16 : 0) + 4 * kg : 4 * kg;
+    floatx4 vsc[NS / 4];
+    if constexpr (PAGED) {
+      if (f8.slow) {
+#pragma unroll
+        for (int i = 0; i < NS / 4; ++i) {
+          const floatx4 ksc = *(const floatx4*)(rsk + tb0 + 16 * i);
+          vsc[i] = *(const floatx4*)(rsv + tb0 + 16 * i);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) sc[4 * i + v] *= ksc[v];
+        }
+      }
+    }
     bool valid[NS];
 #pragma unroll
     for (int v = 0; v < NS; ++v) {
@@ -511,6 +637,9 @@ __global__ void __launch_bounds__(kWaves * 64) KVQ_OCC decode_mfma_kernel(Decode
       float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[v + 1], sl2, -m_run));
       if constexpr (!FULL) { p0 = valid[v] ? p0 : 0.0f; p1 = valid[v + 1] ? p1 : 0.0f; }
       psum = v == 0 ? p0 + p1 : psum + (p0 + p1);
+      if constexpr (PAGED) {
+        if (f8.slow) { p0 *= vsc[v / 4][v % 4]; p1 *= vsc[v / 4][v % 4 + 1]; }
+      }
       const half2v hi = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(p0, p1));
       hw[v / 2] = __builtin_bit_cast(uint32_t, hi);
       lw[v / 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(p0 - (float)hi[0], p1 - (float)hi[1]));
@@ -543,7 +672,9 @@ __global__ void __launch_bounds__(kWaves * 64) KVQ_OCC decode_mfma_kernel(Decode
   constexpr int NB = kPF + 1;  // ring slots
   Buf<FMT> buf[NB];
   Recs rec[NB];
-  uint32_t bnd[NB];
+  Bnd bnd[NB];
+  F8 f8;
+  f8.slow = false;
   const int nmine = wi < nfull ? (nfull - wi + wpc - 1) / wpc : 0;
   auto wts = [&](int j) { return step_ts(j < nmine ? wi + wpc * j : nfull); };
 #if KVQ_PRIO
@@ -562,8 +693,9 @@ __global__ void __launch_bounds__(kWaves * 64) KVQ_OCC decode_mfma_kernel(Decode
 #pragma unroll
   for (int k = 0; k < kPF; ++k) {
     issue_recs(rec[k], bnd[k], wts(k));
-    issue_codes(buf[k], wts(k));
+    issue_codes(buf[k], bnd[k], wts(k));
   }
+  issue_fp8(f8, buf[0], wts(0));
   const int ngroups = nmine / NB;
   for (int g = 0; g < ngroups; ++g) {
 #if KVQ_PRIO
@@ -576,8 +708,9 @@ __global__ void __launch_bounds__(kWaves * 64) KVQ_OCC decode_mfma_kernel(Decode
       const int jj = g * NB + u;
       bnd[u] = issue_bounds(wts(jj + NB));
       issue_recs(rec[(u + kPF) % NB], bnd[(u + kPF) % NB], wts(jj + kPF));
-      issue_codes(buf[(u + kPF) % NB], wts(jj + kPF));
-      consume(buf[u], rec[u], wts(jj), std::true_type{});
+      issue_codes(buf[(u + kPF) % NB], bnd[(u + kPF) % NB], wts(jj + kPF));
+      consume(buf[u], rec[u], f8, wts(jj), std::true_type{});
+      issue_fp8(f8, buf[(u + 1) % NB], wts(jj + 1));
     }
 #if KVQ_PRIO
     partner_seen = __builtin_amdgcn_readfirstlane(*prog_partner);
@@ -592,16 +725,18 @@ __global__ void __launch_bounds__(kWaves * 64) KVQ_OCC decode_mfma_kernel(Decode
     if (jj < nmine) {
       bnd[u] = issue_bounds(wts(jj + NB));
       issue_recs(rec[(u + kPF) % NB], bnd[(u + kPF) % NB], wts(jj + kPF));
-      issue_codes(buf[(u + kPF) % NB], wts(jj + kPF));
-      consume(buf[u], rec[u], wts(jj), std::true_type{});
+      issue_codes(buf[(u + kPF) % NB], bnd[(u + kPF) % NB], wts(jj + kPF));
+      consume(buf[u], rec[u], f8, wts(jj), std::true_type{});
+      issue_fp8(f8, buf[(u + 1) % NB], wts(jj + 1));
     }
   }
   if (ragged && wi == 0) {
     const int ts = t0 + kStep * (nsteps - 1);
-    const uint32_t b0 = issue_bounds(ts);
+    const Bnd b0 = issue_bounds(ts);
     issue_recs(rec[0], b0, ts);
-    issue_codes(buf[0], ts);
-    consume(buf[0], rec[0], ts, std::false_type{});
+    issue_codes(buf[0], b0, ts);
+    issue_fp8(f8, buf[0], ts);
+    consume(buf[0], rec[0], f8, ts, std::false_type{});
   }
 
   // ---- merge the waves of the workgroup
@@ -641,35 +776,43 @@ __global__ void __launch_bounds__(kWaves * 64) KVQ_OCC decode_mfma_kernel(Decode
   }
 }
 
-template <int FMT, bool CMP>
+template <int FMT, bool CMP, bool PAGED>
 void launch_cmp(const DecodeLaunch& d, dim3 grid, hipStream_t st) {
   switch (d.outl) {
-    case KVQ_OUTL_NONE: decode_mfma_kernel<FMT, KVQ_OUTL_NONE, CMP><<<grid, kWaves * 64, 0, st>>>(d); break;
-    case KVQ_OUTL_FP16: decode_mfma_kernel<FMT, KVQ_OUTL_FP16, CMP><<<grid, kWaves * 64, 0, st>>>(d); break;
-    default: decode_mfma_kernel<FMT, KVQ_OUTL_FP8_E4M3, CMP><<<grid, kWaves * 64, 0, st>>>(d); break;
+    case KVQ_OUTL_NONE: decode_mfma_kernel<FMT, KVQ_OUTL_NONE, CMP, PAGED><<<grid, kWaves * 64, 0, st>>>(d); break;
+    case KVQ_OUTL_FP16: decode_mfma_kernel<FMT, KVQ_OUTL_FP16, CMP, PAGED><<<grid, kWaves * 64, 0, st>>>(d); break;
+    default: decode_mfma_kernel<FMT, KVQ_OUTL_FP8_E4M3, CMP, PAGED><<<grid, kWaves * 64, 0, st>>>(d); break;
   }
 }
 
-template <int FMT>
+template <int FMT, bool PAGED>
 void launch_fmt(const DecodeLaunch& d, dim3 grid, hipStream_t st) {
-  if (d.Hq / d.L.H <= 8) launch_cmp<FMT, true>(d, grid, st);
-  else launch_cmp<FMT, false>(d, grid, st);
+  if (d.Hq / d.L.H <= 8) launch_cmp<FMT, true, PAGED>(d, grid, st);
+  else launch_cmp<FMT, false, PAGED>(d, grid, st);
 }
 
 }  // namespace
 
 hipError_t launch_decode_mfma(const DecodeLaunch& d, hipStream_t st, bool* handled) {
   *handled = false;
-  if (d.L.paged) return hipSuccess;
   if (d.fmt != FMT_C2 && !(d.fmt == FMT_FP4 && d.group == 32)) return hipSuccess;
   if (d.chunk % kStep) return hipSuccess;
+  if (d.L.paged) {
+    // pools are addressed with 32-bit byte offsets (the largest must stay below the offset that
+    // marks a skipped row); FP4 pages take the generic kernel
+    const uint64_t rows2 = (uint64_t)d.L.num_pages * d.L.H * kBlock;
+    const uint64_t rows8 = (uint64_t)d.L.num_pages_fp8 * d.L.H * kBlock;
+    if (d.fmt != FMT_C2 || rows2 * 32 >= 0xFFFFFF00ull || rows8 * kHeadDim >= 0xFFFFFF00ull)
+      return hipSuccess;
+  }
   // Short chunks are packed several to a workgroup so that every wave keeps >= 16 steps.
   DecodeLaunch dd = d;
   dd.cpw = 1;
   while (dd.cpw < kWaves && d.chunk * dd.cpw * 2 <= 16 * kStep * kWaves) dd.cpw *= 2;
   dim3 grid((d.n_chunks + dd.cpw - 1) / dd.cpw, d.L.H, d.L.B);
-  if (d.fmt == FMT_C2) launch_fmt<FMT_C2>(dd, grid, st);
-  else launch_fmt<FMT_FP4>(dd, grid, st);
+  if (d.L.paged) launch_fmt<FMT_C2, true>(dd, grid, st);
+  else if (d.fmt == FMT_C2) launch_fmt<FMT_C2, false>(dd, grid, st);
+  else launch_fmt<FMT_FP4, false>(dd, grid, st);
   *handled = true;
   return hipGetLastError();
 }

@@ -178,7 +178,9 @@ int32_t kvq_workspace_bytes(const kvq_params* p, int32_t split_chunk, uint64_t* 
  * merged by log-sum-exp.  q_bf16: device bfloat16 [B][Hq][D] (values must be finite and
  * within fp16 range); seq_lens: device int32 [B], 1 <= seq_lens[b] <= max_seq_len and no more
  * than the tokens appended; block_table as above (paged) or NULL; out: device float32
- * [B][Hq][D]; workspace: device, ws_bytes >= kvq_workspace_bytes. */
+ * [B][Hq][D]; workspace: device, ws_bytes >= kvq_workspace_bytes.  A block-table entry of a
+ * live page that names a slot outside its tier's pool sets *status to KVQ_ERR_INVALID_ARG;
+ * that page's rows then read as zeros (nothing outside the pools is read). */
 int32_t kvq_decode_attention(const kvq_params* p, const kvq_cache* cache, const void* q_bf16,
                              const int32_t* seq_lens, const int32_t* block_table,
                              float sm_scale, int32_t split_chunk, float* out, void* workspace,

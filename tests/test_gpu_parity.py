@@ -38,6 +38,9 @@ SMALL = {
     # tiered paged cache, variable lengths
     "tiered_small": WD.variant(CONFIGS["tiered_b32_paged"], B=3, H=2, Hq=8, S=3000,
                                S_range=(90, 3000), fp8_page_frac=0.3),
+    # tiered paged cache with GQA 16 and mostly FP8 pages
+    "tiered_g16_small": WD.variant(CONFIGS["tiered_b32_paged"], B=2, H=1, Hq=16, S=1500,
+                                   S_range=(40, 1500), fp8_page_frac=0.7),
 }
 
 
@@ -181,3 +184,23 @@ def test_out_of_range_position_reports_status():
     K.kvq_quantize_append(p, cache, k, k, pos, cnt)
     torch.cuda.synchronize()
     assert cache.status() == K.KVQ_ERR_INVALID_ARG
+
+
+def test_paged_bad_slot_reports_status():
+    """A block-table entry naming a slot outside its pool is reported by the decoder (the rows
+    of that page read as zeros; nothing is read outside the pools)."""
+    import decode_attention_sub_amd as K
+    w = SMALL["tiered_small"]
+    dc = WD.build(w)
+    p = dc.params
+    for entry in (p.num_pages + 5, (1 << 31) | (p.num_pages_fp8 + 3)):
+        bt = dc.block_table_host.copy()
+        bt[0, 1] = np.uint32(entry).view(np.int32)
+        dc.cache.tensors["status"].zero_()
+        dcb = WD.DeviceCache(w, p, dc.cache, dc.seq_lens_host, dc.seq_lens, bt,
+                             torch.from_numpy(bt).cuda(), dc.q_host, dc.q)
+        for split in (0, 128):
+            log(f"[gpu] decode with bad block-table entry {entry:#x} split={split}")
+            dc.cache.tensors["status"].zero_()
+            run_decode(dcb, split_chunk=split)
+            assert dc.cache.status() == K.KVQ_ERR_INVALID_ARG
