@@ -244,18 +244,20 @@ __global__ void __launch_bounds__(kWaves * 64) KVQ_OCC decode_mfma_kernel(Decode
   __shared__ __attribute__((aligned(16))) float s_rs[PAGED ? kWaves : 1][2][kStep];   // FP8-tier row scales (K, V)
 
   const Layout& L = d.L;
-  const int h = blockIdx.y, b = blockIdx.z;
+  // KV head fastest: consecutive workgroups (dealt round-robin to the XCDs) then carry the same
+  // amount of work, whatever the mix of sequence lengths
+  const int h = blockIdx.x, grp = blockIdx.y, b = blockIdx.z;
   const int S = d.seq_lens[b];
   if (S < 1 || S > L.S_cap) {
-    if (threadIdx.x == 0 && blockIdx.x == 0 && h == 0) report(d.cache.status, KVQ_ERR_INVALID_ARG);
+    if (threadIdx.x == 0 && grp == 0 && h == 0) report(d.cache.status, KVQ_ERR_INVALID_ARG);
     return;
   }
-  // The workgroup covers chunks cpw * blockIdx.x .. + cpw - 1, wpc waves each.
+  // The workgroup covers chunks cpw * grp .. + cpw - 1, wpc waves each.
   const int cpw = d.cpw, wpc = kWaves / cpw;
-  if (blockIdx.x * cpw * d.chunk >= S) return;
+  if (grp * cpw * d.chunk >= S) return;
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int ci = wave / wpc, wi = wave - ci * wpc;   // chunk of this wave, its place in the chunk
-  const int chunk = blockIdx.x * cpw + ci;
+  const int chunk = grp * cpw + ci;
   const int t0 = chunk * d.chunk;
   const int t1 = chunk < d.n_chunks && t0 < S ? min(t0 + d.chunk, S) : t0;   // empty: past S
   const int G = d.Hq / L.H;
@@ -351,8 +353,8 @@ __global__ void __launch_bounds__(kWaves * 64) KVQ_OCC decode_mfma_kernel(Decode
   // (sequence, head) slice starts at the same power-of-two-aligned offset; walking them in
   // lockstep would send every workgroup to the same HBM channels at the same time.
 #if KVQ_ROTATE
-  const uint32_t n_units = (uint32_t)d.n_chunks * gridDim.y * gridDim.z;
-  const uint32_t unit = (uint32_t)chunk + (uint32_t)d.n_chunks * (blockIdx.y + gridDim.y * blockIdx.z);
+  const uint32_t n_units = (uint32_t)d.n_chunks * (uint32_t)L.H * (uint32_t)L.B;
+  const uint32_t unit = (uint32_t)chunk + (uint32_t)d.n_chunks * ((uint32_t)h + (uint32_t)L.H * (uint32_t)b);
   const int rot = nfull > 0 ? (int)(((uint64_t)unit * (uint64_t)nfull) / n_units) : 0;
 #else
   const int rot = 0;
@@ -366,28 +368,42 @@ __global__ void __launch_bounds__(kWaves * 64) KVQ_OCC decode_mfma_kernel(Decode
   };
 
   constexpr uint32_t kOOB = 0xFFFFFFF0u;   // an offset past every buffer range
-  // paged: pool row of logical token ts + t (t < 32) of page entry ea (t < 16) or eb, or kOOB
-  // when the token is past t1, its page is FP8 (fp8 = false) / 2-bit (fp8 = true), or the slot
-  // is outside its pool (reported)
-  auto page_row = [&](uint32_t ea, uint32_t eb, int ts, int t, bool fp8) -> uint32_t {
-    const uint32_t e = t < 16 ? ea : eb;
+  // Paged caches: a page entry is turned into the pool row of the page's first row for this KV
+  // head, (slot * H + h) * 16, or'ed with 2^31 for an FP8 page, or kDead when the page holds no
+  // token < t1 or its slot lies outside its pool (flagged in bad_page, reported at the end).
+  // Rows of 2-bit pages lie below 2^27 (pools below 4 GiB), FP8 rows below 2^25.
+  constexpr uint32_t kDead = 0xFFFFFFFFu;
+  bool bad_page = false;
+  auto enc_page = [&](uint32_t e, bool live) -> uint32_t {
     const uint32_t slot = e & 0x7FFFFFFFu;
-    const bool t1page = (e >> 31) != 0;
-    const bool in_pool = slot < (uint32_t)(t1page ? L.num_pages_fp8 : L.num_pages);
-    const bool want = ts + t < t1 && t1page == fp8;
-    return want && in_pool ? (slot * (uint32_t)L.H + (uint32_t)h) * kBlock + (uint32_t)(t & 15) : kOOB;
+    const bool in_pool = slot < (uint32_t)((e >> 31) ? L.num_pages_fp8 : L.num_pages);
+    bad_page = bad_page || (live && !in_pool);
+    return live && in_pool ? ((slot * (uint32_t)L.H + (uint32_t)h) * kBlock) | (e & 0x80000000u) : kDead;
   };
-  auto issue_codes = [&](Buf<FMT>& bf, const Bnd& bd, int tsi) {
+  // lane constants: a lane's K token is trow (page A below 16), its V token vtok(trow)
+  const bool kpageB = trow >= 16, vpageB = (trow & 1) != 0;
+  const uint32_t lcK = (uint32_t)(trow & 15) * CB + half * (CB / 2);
+  const uint32_t lcV = (uint32_t)(trow >> 1) * CB + half * (CB / 2);
+  const uint32_t lmK = (uint32_t)(trow & 15) * MB + half * (MB / 2);
+  const uint32_t lmV = (uint32_t)(trow >> 1) * MB + half * (MB / 2);
+  // RAGGED: the step may hold tokens >= t1 (only the chunk's last step)
+  auto issue_codes = [&](Buf<FMT>& bf, const Bnd& bd, int tsi, auto ragged_tag) {
     const uint32_t ts = (uint32_t)tsi;
     if constexpr (PAGED) {
-      bf.ea = (uint32_t)__builtin_amdgcn_readlane((int)bd.bt, 0);
-      bf.eb = (uint32_t)__builtin_amdgcn_readlane((int)bd.bt, 1);
-      const uint32_t rk = page_row(bf.ea, bf.eb, tsi, trow, false);
-      const uint32_t rv = page_row(bf.ea, bf.eb, tsi, vtok(trow), false);
-      const uint32_t ok = rk == kOOB ? kOOB : rk * CB + half * (CB / 2);
-      const uint32_t ov = rv == kOOB ? kOOB : rv * CB + half * (CB / 2);
-      const uint32_t mk = rk == kOOB ? kOOB : rk * MB + half * (MB / 2);
-      const uint32_t mv = rv == kOOB ? kOOB : rv * MB + half * (MB / 2);
+      constexpr bool RAGGED = decltype(ragged_tag)::value;
+      bf.ea = enc_page((uint32_t)__builtin_amdgcn_readlane((int)bd.bt, 0), tsi < t1);
+      bf.eb = enc_page((uint32_t)__builtin_amdgcn_readlane((int)bd.bt, 1), tsi + 16 < t1);
+      const uint32_t ek = kpageB ? bf.eb : bf.ea;
+      const uint32_t ev = vpageB ? bf.eb : bf.ea;
+      bool okk = ek < (1u << 27), okv = ev < (1u << 27);
+      if constexpr (RAGGED) {
+        okk = okk && tsi + trow < t1;
+        okv = okv && tsi + vtok(trow) < t1;
+      }
+      const uint32_t ok = okk ? ek * CB + lcK : kOOB;
+      const uint32_t ov = okv ? ev * CB + lcV : kOOB;
+      const uint32_t mk = okk ? ek * MB + lmK : kOOB;
+      const uint32_t mv = okv ? ev * MB + lmV : kOOB;
       bf.kc = ld128(rcK, ok);
       bf.vc = ld128(rcV, ov);
       bf.km = ld64(rmK, mk);
@@ -445,22 +461,18 @@ __global__ void __launch_bounds__(kWaves * 64) KVQ_OCC decode_mfma_kernel(Decode
     }
   };
   // paged: FP8-tier rows of a step, loaded one step before it is consumed (only when one of the
-  // step's pages is FP8); a block-table entry naming a slot outside its pool is reported and
-  // its rows read as zeros
+  // step's pages is FP8)
   auto issue_fp8 = [&](F8& f, const Buf<FMT>& bf, int ts) {
     if constexpr (PAGED) {
-      const bool live_b = ts + 16 < t1;
-      const auto bad = [&](uint32_t e) {
-        return (e & 0x7FFFFFFFu) >= (uint32_t)((e >> 31) ? L.num_pages_fp8 : L.num_pages);
-      };
-      if (ts < t1 && (bad(bf.ea) || (live_b && bad(bf.eb))) && lane == 0)
-        report(d.cache.status, KVQ_ERR_INVALID_ARG);
-      f.slow = ts < t1 && ((bf.ea >> 31) != 0 || (live_b && (bf.eb >> 31) != 0));
+      const auto is8 = [](uint32_t e) { return (e >> 31) != 0 && e != kDead; };
+      f.slow = is8(bf.ea) || is8(bf.eb);
       if (f.slow) {
-        const uint32_t rk = page_row(bf.ea, bf.eb, ts, trow, true);
-        const uint32_t rv = page_row(bf.ea, bf.eb, ts, vtok(trow), true);
-        f.fk = rk != kOOB;
-        f.fv = rv != kOOB;
+        const uint32_t ek = kpageB ? bf.eb : bf.ea;
+        const uint32_t ev = vpageB ? bf.eb : bf.ea;
+        f.fk = is8(ek) && ts + trow < t1;
+        f.fv = is8(ev) && ts + vtok(trow) < t1;
+        const uint32_t rk = (ek & 0x7FFFFFFFu) + (uint32_t)(trow & 15);
+        const uint32_t rv = (ev & 0x7FFFFFFFu) + (uint32_t)(trow >> 1);
         // (each skipped load gets kOOB itself: kOOB + 16 k would wrap into range)
         const uint32_t ok = rk * kHeadDim + 64u * half, ov = rv * kHeadDim + 64u * half;
 #pragma unroll
@@ -693,7 +705,7 @@ __global__ void __launch_bounds__(kWaves * 64) KVQ_OCC decode_mfma_kernel(Decode
 #pragma unroll
   for (int k = 0; k < kPF; ++k) {
     issue_recs(rec[k], bnd[k], wts(k));
-    issue_codes(buf[k], bnd[k], wts(k));
+    issue_codes(buf[k], bnd[k], wts(k), std::false_type{});
   }
   issue_fp8(f8, buf[0], wts(0));
   const int ngroups = nmine / NB;
@@ -708,7 +720,7 @@ __global__ void __launch_bounds__(kWaves * 64) KVQ_OCC decode_mfma_kernel(Decode
       const int jj = g * NB + u;
       bnd[u] = issue_bounds(wts(jj + NB));
       issue_recs(rec[(u + kPF) % NB], bnd[(u + kPF) % NB], wts(jj + kPF));
-      issue_codes(buf[(u + kPF) % NB], bnd[(u + kPF) % NB], wts(jj + kPF));
+      issue_codes(buf[(u + kPF) % NB], bnd[(u + kPF) % NB], wts(jj + kPF), std::false_type{});
       consume(buf[u], rec[u], f8, wts(jj), std::true_type{});
       issue_fp8(f8, buf[(u + 1) % NB], wts(jj + 1));
     }
@@ -725,7 +737,7 @@ __global__ void __launch_bounds__(kWaves * 64) KVQ_OCC decode_mfma_kernel(Decode
     if (jj < nmine) {
       bnd[u] = issue_bounds(wts(jj + NB));
       issue_recs(rec[(u + kPF) % NB], bnd[(u + kPF) % NB], wts(jj + kPF));
-      issue_codes(buf[(u + kPF) % NB], bnd[(u + kPF) % NB], wts(jj + kPF));
+      issue_codes(buf[(u + kPF) % NB], bnd[(u + kPF) % NB], wts(jj + kPF), std::false_type{});
       consume(buf[u], rec[u], f8, wts(jj), std::true_type{});
       issue_fp8(f8, buf[(u + 1) % NB], wts(jj + 1));
     }
@@ -734,9 +746,13 @@ __global__ void __launch_bounds__(kWaves * 64) KVQ_OCC decode_mfma_kernel(Decode
     const int ts = t0 + kStep * (nsteps - 1);
     const Bnd b0 = issue_bounds(ts);
     issue_recs(rec[0], b0, ts);
-    issue_codes(buf[0], b0, ts);
+    issue_codes(buf[0], b0, ts, std::true_type{});
     issue_fp8(f8, buf[0], ts);
     consume(buf[0], rec[0], f8, ts, std::false_type{});
+  }
+
+  if constexpr (PAGED) {
+    if (bad_page && lane == 0) report(d.cache.status, KVQ_ERR_INVALID_ARG);
   }
 
   // ---- merge the waves of the workgroup
@@ -753,7 +769,7 @@ __global__ void __launch_bounds__(kWaves * 64) KVQ_OCC decode_mfma_kernel(Decode
   __syncthreads();
   for (int i = threadIdx.x; i < cpw * G * kHeadDim; i += kWaves * 64) {
     const int c2 = i / (G * kHeadDim), row = (i / kHeadDim) % G, ch = i % kHeadDim;
-    const int chunk2 = blockIdx.x * cpw + c2;
+    const int chunk2 = grp * cpw + c2;
     if (chunk2 >= d.n_chunks || chunk2 * d.chunk >= S) continue;
     const int w0 = c2 * wpc;
     float M = -INFINITY;
@@ -802,14 +818,15 @@ hipError_t launch_decode_mfma(const DecodeLaunch& d, hipStream_t st, bool* handl
     // marks a skipped row); FP4 pages take the generic kernel
     const uint64_t rows2 = (uint64_t)d.L.num_pages * d.L.H * kBlock;
     const uint64_t rows8 = (uint64_t)d.L.num_pages_fp8 * d.L.H * kBlock;
-    if (d.fmt != FMT_C2 || rows2 * 32 >= 0xFFFFFF00ull || rows8 * kHeadDim >= 0xFFFFFF00ull)
+    if (d.fmt != FMT_C2 || rows2 * 32 > 0xFFFFF000ull || rows8 * kHeadDim > 0xFFFFF000ull)
       return hipSuccess;
   }
   // Short chunks are packed several to a workgroup so that every wave keeps >= 16 steps.
   DecodeLaunch dd = d;
   dd.cpw = 1;
   while (dd.cpw < kWaves && d.chunk * dd.cpw * 2 <= 16 * kStep * kWaves) dd.cpw *= 2;
-  dim3 grid((d.n_chunks + dd.cpw - 1) / dd.cpw, d.L.H, d.L.B);
+  dim3 grid(d.L.H, (d.n_chunks + dd.cpw - 1) / dd.cpw, d.L.B);
+  if (grid.y > 65535u) return hipSuccess;
   if (d.L.paged) launch_fmt<FMT_C2, true>(dd, grid, st);
   else if (d.fmt == FMT_C2) launch_fmt<FMT_C2, false>(dd, grid, st);
   else launch_fmt<FMT_FP4, false>(dd, grid, st);
