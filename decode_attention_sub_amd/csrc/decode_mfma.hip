@@ -18,7 +18,9 @@
 // S^T = K^ Q^T, with v_mfma_f32_16x16x32_f16 (16 tokens x 16 padded query rows), which leaves
 // every lane holding the probabilities of one query row for 4+4 tokens - exactly the B operand of
 // O^T = V^T P^T.  V^T operands come out of the LDS tile with ds_read_b64_tr_b16.  P is split into
-// fp16 hi + lo parts so that large outlier values in V see fp32-grade probabilities.  The waves'
+// fp16 hi + lo parts so that large outlier values in V see fp32-grade probabilities; with at most
+// 8 query rows both parts ride in one B operand (hi parts in columns 0-7, lo parts in the padding
+// columns 8-15), otherwise they take two MFMAs.  The waves'
 // states are merged in LDS; a chunk writes either the final output or a (max, sum, output)
 // partial.  The two waves of a SIMD keep pace with each other through their issue priority.
 //
@@ -104,10 +106,10 @@ __device__ __forceinline__ void expand_fp8(const uint4 (&c)[4], _Float16* dst) {
   }
 }
 
-// Outlier records of one step: lane slots K0, K1 hold K records kr0 + lane and kr0 + 64 + lane,
-// slot V holds V record vr0 + lane.  Values are kept as the aligned 32-bit words that hold them.
+// Outlier records of one step: lane slots K and V hold records kr0 + lane and vr0 + lane.
+// Values are kept as the aligned 32-bit words that hold them.
 struct Recs {
-  uint32_t ik[2], vk[2];   // K: index words, value words
+  uint32_t ik, vk;         // K: index word, value word
   uint32_t iv, vv;         // V: index word, value word
   int kr0, nk, vr0, nv;    // first record and record count of each list (uniform)
 };
@@ -189,6 +191,17 @@ __device__ __forceinline__ _Float16 outl_half(uint32_t v) {
   }
 }
 
+// outlier value stored at bit offset `bit` (mod 32) of word w -> fp16
+template <int OUTL>
+__device__ __forceinline__ _Float16 outl_from_word(uint32_t w, uint32_t bit) {
+  if constexpr (OUTL == KVQ_OUTL_FP16) {
+    return __builtin_bit_cast(_Float16, (uint16_t)__builtin_amdgcn_ubfe(w, bit, 16));
+  } else {
+    const uint32_t code = __builtin_amdgcn_ubfe(w, bit, 8);
+    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)code, 1.0f, false)[0];
+  }
+}
+
 // LDS tile position of record offset dd = 128 * t + c (token t of the step, channel c < 128);
 // the caller guarantees t < 32.
 __device__ __forceinline__ uint32_t tile_pos(uint32_t dd) {
@@ -220,6 +233,10 @@ template <int CTRL, int BANKS>
 __device__ __forceinline__ float dpp_f32(float old, float src) {
   return as_f32((uint32_t)__builtin_amdgcn_update_dpp((int)as_u32(old), (int)as_u32(src), CTRL, 0xF,
                                                       BANKS, false));
+}
+template <int CTRL, int BANKS>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t src) {   // banks not written keep old
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)src, CTRL, 0xF, BANKS, false);
 }
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t src) {   // lanes without a source: undefined
@@ -450,13 +467,11 @@ __global__ void __launch_bounds__(kWaves * 64) KVQ_OCC decode_mfma_kernel(Decode
       // or short load would leave the compiler a narrow value that it re-extends at the loop
       // back-edge, waiting for the load there.
       const uint32_t oik = (uint32_t)k0 * 4u + lane4, oiv = (uint32_t)v0 * 4u + lane4;
-      rc.ik[0] = ld32(riK, oik);
-      rc.ik[1] = ld32(riK, oik + 256u);
+      rc.ik = ld32(riK, oik);
       rc.iv = ld32(riV, oiv);
       const uint32_t obk = ((uint32_t)k0 * VB + lv3 + laneVB) & ~3u;
       const uint32_t obv = ((uint32_t)v0 * VB + lv3 + laneVB) & ~3u;
-      rc.vk[0] = ld32(rvK, obk);
-      rc.vk[1] = ld32(rvK, obk + 64u * VB);
+      rc.vk = ld32(rvK, obk);
       rc.vv = ld32(rvV, obv);
     }
   };
@@ -490,10 +505,13 @@ __global__ void __launch_bounds__(kWaves * 64) KVQ_OCC decode_mfma_kernel(Decode
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt) oacc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.0f;   // -inf until the first step sets it
+  // raw-score threshold of the lazy rescale: scores above it exceed m_run + 8 once scaled
+  // (+inf when the scale is 0 and m_run is set: scaled scores are then all 0)
+  float m_thr = -INFINITY;
   const float sl2 = fabsf(d.scale_log2);
 
-  // One 32-token step.  FULL: every token of the step is valid.  K records past the first 128 of
-  // a step and V records past the first 64 are written by rarely taken loops.  Otherwise the body is one
+  // One 32-token step.  FULL: every token of the step is valid.  Records past the first 64 of a
+  // step (per list) are written by rarely taken loops.  Otherwise the body is one
   // branch-free block: K rows are expanded and written, the K^ operand reads are issued, V rows
   // are expanded while those reads are in flight, the score MFMAs run, the V^T operand reads are
   // issued before the softmax needs them.
@@ -503,24 +521,19 @@ __global__ void __launch_bounds__(kWaves * 64) KVQ_OCC decode_mfma_kernel(Decode
     _Float16* krow = ktile + trow * kRow + 64 * half;
     _Float16* vrow = vtile + trow * kRow + 64 * half;
     // tile positions of this lane's record slots (the pad slot where a slot is unused)
-    uint32_t posK[2], posV = kHeadDim;
-    _Float16 ovK[2], ovV;
+    uint32_t posK = kHeadDim, posV = kHeadDim;
+    _Float16 ovK, ovV;
     if constexpr (HAS_OUTL) {
-      // bit offsets of the values inside their words (bit-field extraction takes them modulo 32;
-      // slot K1 is 64 records on, a whole number of words)
+      // bit offsets of the values inside their words (bit-field extraction takes them modulo 32)
       const uint32_t bitK = laneVB8 + ((uint32_t)rc.kr0 * VB + lv3) * 8u;
       const uint32_t bitV = laneVB8 + ((uint32_t)rc.vr0 * VB + lv3) * 8u;
       const uint32_t lim = (uint32_t)nval * 128u;
-#pragma unroll
-      for (int sl = 0; sl < 2; ++sl) {
-        const uint32_t dd = rc.ik[sl] - (uint32_t)ts * 128u;
-        const bool ok = 64 * sl + lane < rc.nk && dd < lim;
-        posK[sl] = ok ? tile_pos(dd) : (uint32_t)kHeadDim;
-        ovK[sl] = outl_half<OUTL>(__builtin_amdgcn_ubfe(rc.vk[sl], bitK, VB * 8));
-      }
+      const uint32_t ddk = rc.ik - (uint32_t)ts * 128u;
+      posK = lane < rc.nk && ddk < lim ? tile_pos(ddk) : (uint32_t)kHeadDim;
+      ovK = outl_from_word<OUTL>(rc.vk, bitK);
       const uint32_t ddv = rc.iv - (uint32_t)ts * 128u;
       posV = lane < rc.nv && ddv < lim ? tile_pos_v(ddv) : (uint32_t)kHeadDim;
-      ovV = outl_half<OUTL>(__builtin_amdgcn_ubfe(rc.vv, bitV, VB * 8));
+      ovV = outl_from_word<OUTL>(rc.vv, bitV);
     }
     if constexpr (FMT == FMT_C2) expand_c2(bf.kc, bf.km, krow);
     else expand_fp4(bf.kc0, bf.kc1, bf.km, krow);
@@ -538,10 +551,9 @@ __global__ void __launch_bounds__(kWaves * 64) KVQ_OCC decode_mfma_kernel(Decode
       }
     }
     if constexpr (HAS_OUTL) {
-      ktile[posK[0]] = ovK[0];
-      ktile[posK[1]] = ovK[1];
-      if (rc.nk > 128) {
-        for (int a = 128 + lane; a < rc.nk; a += 64) {  // the rest of a crowded step
+      ktile[posK] = ovK;
+      if (rc.nk > 64) {
+        for (int a = 64 + lane; a < rc.nk; a += 64) {  // the rest of a crowded step
           const int at = rc.kr0 + a;
           const uint32_t v = VB == 2 ? ((const uint16_t*)ovalK)[at] : ovalK[at];
           patch_at<FMT, OUTL, false>(ktile, oidxK[at], v, ts, nval);
@@ -628,7 +640,7 @@ __global__ void __launch_bounds__(kWaves * 64) KVQ_OCC decode_mfma_kernel(Decode
     float mx = sc[0];
 #pragma unroll
     for (int v = 1; v < NS; ++v) mx = fmaxf(mx, sc[v]);
-    if (__builtin_amdgcn_ballot_w64(mx * sl2 > m_run + 8.0f)) {
+    if (__builtin_amdgcn_ballot_w64(mx > m_thr)) {
       if constexpr (CMP) mx = fmaxf(mx, dpp_f32<kRowRor8>(mx));
       const auto x16 = __builtin_amdgcn_permlane16_swap(as_u32(mx), as_u32(mx), false, false);
       mx = fmaxf(as_f32(x16[0]), as_f32(x16[1]));
@@ -640,6 +652,7 @@ __global__ void __launch_bounds__(kWaves * 64) KVQ_OCC decode_mfma_kernel(Decode
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) oacc[mt] *= alpha;
       m_run = m_new;
+      m_thr = sl2 > 0.0f ? (m_run + 8.0f) / sl2 : (m_run == -INFINITY ? -INFINITY : INFINITY);
     }
     uint32_t hw[NS / 2], lw[NS / 2];
     float psum;
@@ -654,23 +667,29 @@ __global__ void __launch_bounds__(kWaves * 64) KVQ_OCC decode_mfma_kernel(Decode
       }
       const half2v hi = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(p0, p1));
       hw[v / 2] = __builtin_bit_cast(uint32_t, hi);
-      lw[v / 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(p0 - (float)hi[0], p1 - (float)hi[1]));
+      lw[v / 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__builtin_fmaf((float)hi[0], -1.0f, p0),
+                                                                        __builtin_fmaf((float)hi[1], -1.0f, p1)));
     }
     l_run += psum;
-    uint4 hq, lq;
     if constexpr (CMP) {
-      // B operand of lane (query r, kg): tile-0 tokens of its own, tile-1 tokens from lane r + 8
-      hq = make_uint4(hw[0], hw[1], dpp_u32<kRowShl8>(hw[0]), dpp_u32<kRowShl8>(hw[1]));
-      lq = make_uint4(lw[0], lw[1], dpp_u32<kRowShl8>(lw[0]), dpp_u32<kRowShl8>(lw[1]));
-    } else {
-      hq = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-      lq = make_uint4(lw[0], lw[1], lw[2], lw[3]);
-    }
-    const half8 phi = __builtin_bit_cast(half8, hq), plo = __builtin_bit_cast(half8, lq);
+      // One B operand carries both parts: column r < 8 the hi parts of query r (tile-0 tokens of
+      // its own lane, tile-1 tokens from lane r + 8), column r + 8 the lo parts of query r
+      // (tile-0 tokens from lane r, tile-1 tokens of its own lane).  The two columns of a query
+      // are summed once, after the last step.
+      const uint4 pq = make_uint4(dpp_u32<kRowShr8, 0xC>(hw[0], lw[0]), dpp_u32<kRowShr8, 0xC>(hw[1], lw[1]),
+                                  dpp_u32<kRowShl8, 0x3>(lw[0], hw[0]), dpp_u32<kRowShl8, 0x3>(lw[1], hw[1]));
+      const half8 pb = __builtin_bit_cast(half8, pq);
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
-      oacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[mt], phi, oacc[mt], 0, 0, 0);
-      oacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[mt], plo, oacc[mt], 0, 0, 0);
+      for (int mt = 0; mt < 8; ++mt)
+        oacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[mt], pb, oacc[mt], 0, 0, 0);
+    } else {
+      const half8 phi = __builtin_bit_cast(half8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+      const half8 plo = __builtin_bit_cast(half8, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) {
+        oacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[mt], phi, oacc[mt], 0, 0, 0);
+        oacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[mt], plo, oacc[mt], 0, 0, 0);
+      }
     }
   };
   // ---- software pipeline: codes and records of the next kPF steps in flight, the record
@@ -756,6 +775,12 @@ __global__ void __launch_bounds__(kWaves * 64) KVQ_OCC decode_mfma_kernel(Decode
   }
 
   // ---- merge the waves of the workgroup
+  if constexpr (CMP) {   // column r of query r < 8 += its lo column r + 8
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) oacc[mt][v] += dpp_f32<kRowShl8>(oacc[mt][v]);
+  }
   float l_row = l_run;
   if constexpr (CMP) l_row += dpp_f32<kRowRor8>(l_row);
   l_row += __shfl_xor(l_row, 16, 64);
