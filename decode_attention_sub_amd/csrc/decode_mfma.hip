@@ -10,10 +10,11 @@
 // section "2. FP4/INT4 KV-Cache Quantization", item 3 (dequantize into fp16 operand space inside
 // the flash-attention reduction).
 //
-// Work unit: a workgroup of 8 waves (two per SIMD) per (split-K chunk, KV head, sequence).
-// Waves take 32-token steps of the chunk in turn.  Per step a lane owns (token, 64-channel half
-// row): it loads the packed codes and group metadata with 128-bit loads (prefetched two steps
-// ahead), expands them to fp16 in registers and writes the rows into the wave's LDS tile; outlier
+// Work unit: a workgroup of 12 waves (three per SIMD; 8 for paged caches) per (split-K chunk, KV
+// head, sequence).  Waves take 32-token steps of the chunk in turn.  Per step a lane owns (token,
+// 64-channel half row): it loads the packed codes and group metadata with 128-bit loads
+// (prefetched one or two steps ahead), expands them to fp16 in registers and writes the rows into
+// the wave's LDS tile; outlier
 // records of the step are written over their positions.  Scores are computed transposed,
 // S^T = K^ Q^T, with v_mfma_f32_16x16x32_f16 (16 tokens x 16 padded query rows), which leaves
 // every lane holding the probabilities of one query row for 4+4 tokens - exactly the B operand of
@@ -22,7 +23,7 @@
 // 8 query rows both parts ride in one B operand (hi parts in columns 0-7, lo parts in the padding
 // columns 8-15), otherwise they take two MFMAs.  The waves'
 // states are merged in LDS; a chunk writes either the final output or a (max, sum, output)
-// partial.  The two waves of a SIMD keep pace with each other through their issue priority.
+// partial.  The waves of a SIMD keep pace with each other through their issue priority.
 //
 // 2-bit expansion: per 64-bit centroid word, two byte tables (low bytes and high bytes of the 4
 // fp16 centroids) are built once; the four codes of one bit pair of a 32-bit code word (one per
@@ -51,11 +52,6 @@ __device__ __forceinline__ half4v read_tr16(const lds_half* p) {
   return __builtin_bit_cast(half4v, v);
 }
 
-#ifndef KVQ_PREFETCH_STEPS
-#define KVQ_PREFETCH_STEPS 2
-#endif
-constexpr int kWaves = 8;                  // waves per workgroup, two per SIMD
-constexpr int kPF = KVQ_PREFETCH_STEPS;    // steps of codes / records in flight per wave
 constexpr int kStep = 32;                  // tokens per wave step
 #ifndef KVQ_TILE_ROW
 #define KVQ_TILE_ROW 136
@@ -72,11 +68,20 @@ constexpr int kRow = KVQ_TILE_ROW;         // LDS row stride in halfs (272 bytes
 #ifndef KVQ_PRIO
 #define KVQ_PRIO 1
 #endif
-#ifndef KVQ_TILES
-#define KVQ_TILES 2
-#endif
 constexpr int kTile = kStep * kRow;        // halfs per tile
-constexpr int kWaveLds = KVQ_TILES * kTile; // K tile + V tile (or one tile for both)
+
+// Workgroup shape.  Contiguous caches: 12 waves (three per SIMD), one LDS tile per wave for both
+// K and V rows, one step of loads in flight, score MFMAs issued before the V rows are expanded
+// (their operands then die early): the registers fit three waves per SIMD.  Paged caches keep
+// 8 waves with separate K and V tiles and two steps in flight; their extra addressing state
+// does not fit three waves per SIMD.
+template <bool PAGED> struct Shape {
+  static constexpr int kWaves = PAGED ? 8 : 12;
+  static constexpr int kTiles = PAGED ? 2 : 1;
+  static constexpr int kPF = PAGED ? 2 : 1;       // steps of codes / records in flight per wave
+  static constexpr bool kEarlyS = !PAGED;
+  static constexpr int kWaveLds = kTiles * kTile; // halfs of LDS per wave
+};
 
 
 template <int FMT> struct Buf;
@@ -254,7 +259,10 @@ constexpr int kRowRor8 = 0x128;   // lane i <- lane (i + 8) mod 16 of its row
 // r < 8; the softmax runs on 4 scores per lane after moving tile 1's rows into lanes r >= 8.
 // PAGED: 2-bit pages behind a block table, some of them (tier 1) FP8 rows with a per-row scale.
 template <int FMT, int OUTL, bool CMP, bool PAGED>
-__global__ void __launch_bounds__(kWaves * 64) KVQ_OCC decode_mfma_kernel(DecodeLaunch d) {
+__global__ void __launch_bounds__(Shape<PAGED>::kWaves * 64) KVQ_OCC decode_mfma_kernel(DecodeLaunch d) {
+  constexpr int kWaves = Shape<PAGED>::kWaves;
+  constexpr int kWaveLds = Shape<PAGED>::kWaveLds;
+  constexpr int kPF = Shape<PAGED>::kPF;
   __shared__ __attribute__((aligned(16))) _Float16 s_lds[kWaves * kWaveLds];
   __shared__ float s_ml[kWaves][16][2];
   __shared__ int s_simd[kWaves], s_prog[kWaves];   // SIMD of each wave, groups done
@@ -289,7 +297,7 @@ __global__ void __launch_bounds__(kWaves * 64) KVQ_OCC decode_mfma_kernel(Decode
   // With one tile, K rows are expanded and read back as operands before V rows overwrite them
   // (a wave's LDS operations complete in issue order).
   _Float16* ktile = s_lds + wave * kWaveLds;
-  _Float16* vtile = ktile + (KVQ_TILES - 1) * kTile;
+  _Float16* vtile = ktile + (Shape<PAGED>::kTiles - 1) * kTile;
 
   // query operand (B of S^T = K^ Q^T): lane (row r, k-group kg), positions 32*ks + 8*kg + e
   half8 qop[4];
@@ -566,6 +574,14 @@ __global__ void __launch_bounds__(kWaves * 64) KVQ_OCC decode_mfma_kernel(Decode
       ak[ks] = *(const half8*)(ktile + r * kRow + 32 * ks + 8 * kg);
       ak[4 + ks] = *(const half8*)(ktile + (16 + r) * kRow + 32 * ks + 8 * kg);
     }
+    floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (Shape<PAGED>::kEarlyS) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak[ks], qop[ks], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak[4 + ks], qop[ks], s1, 0, 0, 0);
+      }
+    }
     if constexpr (FMT == FMT_C2) expand_c2(bf.vc, bf.vm, vrow);
     else expand_fp4(bf.vc0, bf.vc1, bf.vm, vrow);
     if constexpr (PAGED) {
@@ -581,11 +597,12 @@ __global__ void __launch_bounds__(kWaves * 64) KVQ_OCC decode_mfma_kernel(Decode
         }
       }
     }
-    floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (!Shape<PAGED>::kEarlyS) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak[ks], qop[ks], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak[4 + ks], qop[ks], s1, 0, 0, 0);
+      for (int ks = 0; ks < 4; ++ks) {
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak[ks], qop[ks], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak[4 + ks], qop[ks], s1, 0, 0, 0);
+      }
     }
     // V^T operands (16 channels x 32 tokens per M-tile) through transposing LDS reads
     half8 av[8];
@@ -712,11 +729,18 @@ __global__ void __launch_bounds__(kWaves * 64) KVQ_OCC decode_mfma_kernel(Decode
   const int mysimd = (int)((__builtin_amdgcn_s_getreg((31 << 11) | 4) >> 4) & 3);   // HW_ID.simd
   if (lane == 0) { s_simd[wave] = mysimd; s_prog[wave] = 0; }
   __syncthreads();
-  int partner = wave;
-  for (int w2 = 0; w2 < kWaves; ++w2)
-    if (w2 != wave && __builtin_amdgcn_readfirstlane(s_simd[w2]) == mysimd) partner = w2;
+  // the (up to two) other waves of this SIMD; a wave ahead of the slower of them yields
+  int peer1 = wave, peer2 = wave;
+  for (int w2 = 0; w2 < kWaves; ++w2) {
+    if (w2 != wave && __builtin_amdgcn_readfirstlane(s_simd[w2]) == mysimd) {
+      if (peer1 == wave) peer1 = w2;
+      else peer2 = w2;
+    }
+  }
+  if (peer2 == wave) peer2 = peer1;
   int* const prog_mine = &s_prog[wave];
-  const int* const prog_partner = &s_prog[partner];
+  const int* const prog_p1 = &s_prog[peer1];
+  const int* const prog_p2 = &s_prog[peer2];
   int partner_seen = 0;
 #endif
 #pragma unroll
@@ -744,7 +768,7 @@ __global__ void __launch_bounds__(kWaves * 64) KVQ_OCC decode_mfma_kernel(Decode
       issue_fp8(f8, buf[(u + 1) % NB], wts(jj + 1));
     }
 #if KVQ_PRIO
-    partner_seen = __builtin_amdgcn_readfirstlane(*prog_partner);
+    partner_seen = min(__builtin_amdgcn_readfirstlane(*prog_p1), __builtin_amdgcn_readfirstlane(*prog_p2));
 #endif
   }
 #if KVQ_PRIO
@@ -820,9 +844,9 @@ __global__ void __launch_bounds__(kWaves * 64) KVQ_OCC decode_mfma_kernel(Decode
 template <int FMT, bool CMP, bool PAGED>
 void launch_cmp(const DecodeLaunch& d, dim3 grid, hipStream_t st) {
   switch (d.outl) {
-    case KVQ_OUTL_NONE: decode_mfma_kernel<FMT, KVQ_OUTL_NONE, CMP, PAGED><<<grid, kWaves * 64, 0, st>>>(d); break;
-    case KVQ_OUTL_FP16: decode_mfma_kernel<FMT, KVQ_OUTL_FP16, CMP, PAGED><<<grid, kWaves * 64, 0, st>>>(d); break;
-    default: decode_mfma_kernel<FMT, KVQ_OUTL_FP8_E4M3, CMP, PAGED><<<grid, kWaves * 64, 0, st>>>(d); break;
+    case KVQ_OUTL_NONE: decode_mfma_kernel<FMT, KVQ_OUTL_NONE, CMP, PAGED><<<grid, Shape<PAGED>::kWaves * 64, 0, st>>>(d); break;
+    case KVQ_OUTL_FP16: decode_mfma_kernel<FMT, KVQ_OUTL_FP16, CMP, PAGED><<<grid, Shape<PAGED>::kWaves * 64, 0, st>>>(d); break;
+    default: decode_mfma_kernel<FMT, KVQ_OUTL_FP8_E4M3, CMP, PAGED><<<grid, Shape<PAGED>::kWaves * 64, 0, st>>>(d); break;
   }
 }
 
@@ -846,10 +870,12 @@ hipError_t launch_decode_mfma(const DecodeLaunch& d, hipStream_t st, bool* handl
     if (d.fmt != FMT_C2 || rows2 * 32 > 0xFFFFF000ull || rows8 * kHeadDim > 0xFFFFF000ull)
       return hipSuccess;
   }
-  // Short chunks are packed several to a workgroup so that every wave keeps >= 16 steps.
+  // Short chunks are packed several to a workgroup (a divisor of its wave count) so that every
+  // wave keeps >= 16 steps.
+  const int waves = d.L.paged ? Shape<true>::kWaves : Shape<false>::kWaves;
   DecodeLaunch dd = d;
   dd.cpw = 1;
-  while (dd.cpw < kWaves && d.chunk * dd.cpw * 2 <= 16 * kStep * kWaves) dd.cpw *= 2;
+  while (waves % (dd.cpw * 2) == 0 && d.chunk * dd.cpw * 2 <= 16 * kStep * waves) dd.cpw *= 2;
   dim3 grid(d.L.H, (d.n_chunks + dd.cpw - 1) / dd.cpw, d.L.B);
   if (grid.y > 65535u) return hipSuccess;
   if (d.L.paged) launch_fmt<FMT_C2, true>(dd, grid, st);
