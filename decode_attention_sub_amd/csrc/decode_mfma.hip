@@ -132,6 +132,19 @@ __device__ __forceinline__ uint2 ld64(__amdgpu_buffer_rsrc_t r, uint32_t off) {
 __device__ __forceinline__ uint32_t ld32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
 }
+// with a uniform part of the offset in the scalar offset (the range check covers the sum)
+__device__ __forceinline__ uint4 ld128s(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+__device__ __forceinline__ uint2 ld64s(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0));
+}
+__device__ __forceinline__ uint32_t ld32s(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
+}
+__device__ __forceinline__ uint32_t ld16s(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, (int)soff, 0);
+}
 __device__ __forceinline__ uint32_t ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
 }
@@ -231,6 +244,19 @@ __device__ __forceinline__ void patch_at(_Float16* tile, uint32_t idx, uint32_t 
   const uint32_t dd = idx - (uint32_t)ts * 128u;
   const uint32_t at = dd < (uint32_t)nval * 128u ? (VT ? tile_pos_v(dd) : tile_pos(dd)) : (uint32_t)kHeadDim;
   tile[at] = outl_half<OUTL>(val);
+}
+
+// p - (float)h for the low / high fp16 half h of pair, one mixed-precision FMA each (the exact
+// remainder of the fp16 split: both values are fp32 and h is p rounded toward zero)
+__device__ __forceinline__ float rem_lo(uint32_t pair, float p) {
+  float r;
+  asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(pair), "v"(p));
+  return r;
+}
+__device__ __forceinline__ float rem_hi(uint32_t pair, float p) {
+  float r;
+  asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(pair), "v"(p));
+  return r;
 }
 
 // DPP helpers (row = 16 lanes)
@@ -434,17 +460,17 @@ __global__ void __launch_bounds__(Shape<PAGED>::kWaves * 64) KVQ_OCC decode_mfma
       bf.km = ld64(rmK, mk);
       bf.vm = ld64(rmV, mv);
     } else if constexpr (FMT == FMT_C2) {
-      bf.kc = ld128(rcK, ts * CB + coff);
-      bf.vc = ld128(rcV, ts * CB + coffv);
-      bf.km = ld64(rmK, ts * MB + moff);
-      bf.vm = ld64(rmV, ts * MB + moffv);
+      bf.kc = ld128s(rcK, coff, ts * CB);
+      bf.vc = ld128s(rcV, coffv, ts * CB);
+      bf.km = ld64s(rmK, moff, ts * MB);
+      bf.vm = ld64s(rmV, moffv, ts * MB);
     } else {
-      bf.kc0 = ld128(rcK, ts * CB + coff);
-      bf.kc1 = ld128(rcK, ts * CB + coff + 16);
-      bf.vc0 = ld128(rcV, ts * CB + coffv);
-      bf.vc1 = ld128(rcV, ts * CB + coffv + 16);
-      bf.km = ld16(rmK, ts * MB + moff);
-      bf.vm = ld16(rmV, ts * MB + moffv);
+      bf.kc0 = ld128s(rcK, coff, ts * CB);
+      bf.kc1 = ld128s(rcK, coff + 16, ts * CB);
+      bf.vc0 = ld128s(rcV, coffv, ts * CB);
+      bf.vc1 = ld128s(rcV, coffv + 16, ts * CB);
+      bf.km = ld16s(rmK, moff, ts * MB);
+      bf.vm = ld16s(rmV, moffv, ts * MB);
     }
   };
   // lanes 0..3 load {K start, K end, V start, V end} of the step's records (block starts); for
@@ -474,13 +500,13 @@ __global__ void __launch_bounds__(Shape<PAGED>::kWaves * 64) KVQ_OCC decode_mfma
       // read as the aligned 32-bit word that holds them and extracted where they are used: a byte
       // or short load would leave the compiler a narrow value that it re-extends at the loop
       // back-edge, waiting for the load there.
-      const uint32_t oik = (uint32_t)k0 * 4u + lane4, oiv = (uint32_t)v0 * 4u + lane4;
-      rc.ik = ld32(riK, oik);
-      rc.iv = ld32(riV, oiv);
-      const uint32_t obk = ((uint32_t)k0 * VB + lv3 + laneVB) & ~3u;
-      const uint32_t obv = ((uint32_t)v0 * VB + lv3 + laneVB) & ~3u;
-      rc.vk = ld32(rvK, obk);
-      rc.vv = ld32(rvV, obv);
+      rc.ik = ld32s(riK, lane4, (uint32_t)k0 * 4u);
+      rc.iv = ld32s(riV, lane4, (uint32_t)v0 * 4u);
+      // value word of a lane's record: the list's byte offset k0 * VB + lv3 (uniform) split into
+      // its word-aligned part (scalar offset) and its remainder, which joins the lane's bytes
+      const uint32_t bk = (uint32_t)k0 * VB + lv3, bv = (uint32_t)v0 * VB + lv3;
+      rc.vk = ld32s(rvK, ((bk & 3u) + laneVB) & ~3u, bk & ~3u);
+      rc.vv = ld32s(rvV, ((bv & 3u) + laneVB) & ~3u, bv & ~3u);
     }
   };
   // paged: FP8-tier rows of a step, loaded one step before it is consumed (only when one of the
@@ -684,8 +710,7 @@ __global__ void __launch_bounds__(Shape<PAGED>::kWaves * 64) KVQ_OCC decode_mfma
       }
       const half2v hi = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(p0, p1));
       hw[v / 2] = __builtin_bit_cast(uint32_t, hi);
-      lw[v / 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__builtin_fmaf((float)hi[0], -1.0f, p0),
-                                                                        __builtin_fmaf((float)hi[1], -1.0f, p1)));
+      lw[v / 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(rem_lo(hw[v / 2], p0), rem_hi(hw[v / 2], p1)));
     }
     l_run += psum;
     if constexpr (CMP) {
