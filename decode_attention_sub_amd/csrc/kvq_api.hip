@@ -76,17 +76,22 @@ int32_t check_cache(const kvq_params* p, const kvq_cache* c) {
   return KVQ_OK;
 }
 
-// Default split: enough (sequence, KV head, chunk) units to give every CU of an MI355X (256)
-// two workgroups, the number that fit at once; never chunks shorter than 512 tokens.
+// Default split.  Formats on the MFMA decoder (2-bit, FP4 with groups of 32): enough
+// (sequence, KV head, chunk) units for one workgroup per CU of an MI355X (256), never chunks
+// shorter than 512 tokens (each wave keeps a run of steps).  Formats on the generic decoder
+// (INT4, FP4 with groups of 64): its 4-wave workgroups take one 64-token step at a time, so
+// short contexts are split down to 64-token chunks across ~1024 units (latency).
 int resolve_chunk(const kvq_params* p, int32_t split_chunk) {
   if (split_chunk < 0) return -1;
   if (split_chunk == 0) {
     if (p->page_size) return kDefaultPagedChunk;
+    const bool mfma = p->format == FMT_C2 || (p->format == FMT_FP4 && p->group_size == 32);
     const int64_t units = (int64_t)p->batch * p->num_kv_heads;
-    const int64_t want = 256;   // one 8-wave MFMA workgroup per compute unit
+    const int64_t want = mfma ? 256 : 1024;
+    const int64_t min_chunk = mfma ? 512 : 64;
     int64_t nchunks = units >= want ? 1 : (want + units - 1) / units;
     int64_t chunk = (p->max_seq_len + nchunks - 1) / nchunks;
-    chunk = chunk < 512 ? 512 : chunk;
+    chunk = chunk < min_chunk ? min_chunk : chunk;
     return (int)(((chunk + 63) / 64) * 64);
   }
   if (split_chunk % 64) return -1;

@@ -80,14 +80,32 @@ __device__ __forceinline__ uint32_t f32_to_e2m1(float y) {
 }
 
 // ------------------------------------------------------------------ wave helpers
-// lane i reads lane i ^ w within its 32-lane half (ds_swizzle bit mode)
-template <int W>
-__device__ __forceinline__ float xor_f32(float v) {
-  return as_f32((uint32_t)__builtin_amdgcn_ds_swizzle((int)as_u32(v), (W << 10) | 0x1F));
-}
+// lane i reads lane i ^ w.  w < 16 stays inside a 16-lane DPP row and takes DPP moves (a few
+// cycles): quad permutes for 1 and 2, row shifts for 4 (two moves, one per pair of banks) and
+// a row rotation for 8; w = 16 goes through ds_swizzle (within the 32-lane half).
 template <int W>
 __device__ __forceinline__ int xor_i32(int v) {
-  return __builtin_amdgcn_ds_swizzle(v, (W << 10) | 0x1F);
+  if constexpr (W == 1) {
+    return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);        // quad_perm [1,0,3,2]
+  } else if constexpr (W == 2) {
+    return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);        // quad_perm [2,3,0,1]
+  } else if constexpr (W == 4) {
+    const int t = __builtin_amdgcn_update_dpp(v, v, 0x104, 0xF, 0x5, false);   // banks 0, 2: lane + 4
+    return __builtin_amdgcn_update_dpp(t, v, 0x114, 0xF, 0xA, false);         // banks 1, 3: lane - 4
+  } else if constexpr (W == 8) {
+    return __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, false);       // row_ror 8
+  } else {
+    return __builtin_amdgcn_ds_swizzle(v, (W << 10) | 0x1F);
+  }
+}
+template <int W>
+__device__ __forceinline__ float xor_f32(float v) {
+  return as_f32((uint32_t)xor_i32<W>((int)as_u32(v)));
+}
+// lane S of the lane's 16-lane DPP row
+template <int S>
+__device__ __forceinline__ int row_bcast_i32(int v) {
+  return __builtin_amdgcn_mov_dpp(v, 0x150 + S, 0xF, 0xF, false);    // row_newbcast S
 }
 
 // ------------------------------------------------------------------ cache addressing

@@ -16,6 +16,8 @@
 // exchanges between lanes (every lane then holds the root by commutativity of addition).
 #pragma clang fp contract(off)
 
+#include <type_traits>
+
 #include "kvq_device.h"
 #include "kvq_launch.h"
 
@@ -37,6 +39,15 @@ struct QArgs {
   float tau2;        // fl32(tau * tau)
   int lloyd;
 };
+
+// compile-time loop: f(std::integral_constant<int, I>) for I = 0 .. N-1
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
+}
 
 // ---------------------------------------------------------------- group reductions
 template <int L>
@@ -173,31 +184,29 @@ __device__ void fit_c2(const float x[4], const bool keep[4], int jg, int iters, 
 #pragma unroll
   for (int i = 0; i < 4; ++i) nloc += keep[i] ? 1 : 0;
   const int n = group_isum<L>(nloc);
-  // stable rank of each kept element among the kept elements of the group
+  // stable rank of each kept element among the kept elements of the group: element (src, e)
+  // of the group (index src + L e, broadcast from lane src of the 16-lane row that holds the
+  // group) precedes my element i (index jg + L i) when it is smaller, or equal with a lower
+  // index.  Outliers compare as +inf, which precedes no kept element.
+  static_assert(G == 64, "one group per 16-lane DPP row");
+  float xs[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) xs[i] = keep[i] ? x[i] : INFINITY;
   int rank[4] = {0, 0, 0, 0};
   const uint32_t xb[4] = {as_u32(x[0]), as_u32(x[1]), as_u32(x[2]), as_u32(x[3])};
-  const uint32_t kb = (keep[0] ? 1u : 0u) | (keep[1] ? 2u : 0u) | (keep[2] ? 4u : 0u) |
-                      (keep[3] ? 8u : 0u);
-  const int lane32 = (int)(threadIdx.x & 31);
-  const int gbase = lane32 - jg;  // first lane of this group within the 32-lane half
-#pragma unroll
-  for (int src = 0; src < L; ++src) {
-    // broadcast lane gbase + src of this group (bpermute within the wave)
-    const int srcl = ((int)threadIdx.x & 32) + gbase + src;  // lane within the wave
-    const uint32_t kbs = (uint32_t)__shfl((int)kb, srcl, 64);
+  static_for<L>([&](auto src_c) {
+    constexpr int src = decltype(src_c)::value;
+    const bool before_me = src < jg;   // same e: the source's index is lower when src < jg
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float v = as_f32((uint32_t)__shfl((int)xb[e], srcl, 64));
-      const bool vk = (kbs >> e) & 1u;
-      const int vidx = src + L * e;
+      const float v = as_f32((uint32_t)row_bcast_i32<src>((int)as_u32(xs[e])));
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int myidx = jg + L * i;
-        const bool less = v < x[i] || (v == x[i] && vidx < myidx);
-        rank[i] += (vk && less) ? 1 : 0;
+        const bool less = e < i ? v <= xs[i] : e > i ? v < xs[i] : (before_me ? v <= xs[i] : v < xs[i]);
+        rank[i] += less ? 1 : 0;
       }
     }
-  }
+  });
   float c[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -289,6 +298,13 @@ __global__ void __launch_bounds__(64 * NW) quantize_append_kernel(QArgs a) {
   uint8_t* oval = (uint8_t*)a.cache.outl_val[kv] +
                   ((size_t)b * Lo.H + h) * (size_t)Lo.outl_cap * (a.outl == KVQ_OUTL_FP16 ? 2 : 1);
 
+  // the first rows' values are loaded before the list truncation, which waits on memory too
+  const float* src = (kv == 0 ? a.k_new : a.v_new) + ((size_t)b * Lo.H + h) * (size_t)a.max_new * kHeadDim;
+  float x0[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    x0[e] = slot < n ? src[(size_t)slot * kHeadDim + gi * G + jg + L * e] : 0.0f;
+
   // truncate the list to the records of tokens < p
   if (tid == 0) s_trunc = 0;
   __syncthreads();
@@ -304,8 +320,6 @@ __global__ void __launch_bounds__(64 * NW) quantize_append_kernel(QArgs a) {
     running = start + s_trunc;
   }
 
-  const float* src = (kv == 0 ? a.k_new : a.v_new) + ((size_t)b * Lo.H + h) * (size_t)a.max_new * kHeadDim;
-
   for (int i0 = 0; i0 < n; i0 += RPI) {
     const int r = i0 + slot;
     const bool valid = r < n;
@@ -313,7 +327,7 @@ __global__ void __launch_bounds__(64 * NW) quantize_append_kernel(QArgs a) {
     float x[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      x[e] = valid ? src[(size_t)r * kHeadDim + gi * G + jg + L * e] : 0.0f;
+      x[e] = i0 == 0 ? x0[e] : valid ? src[(size_t)r * kHeadDim + gi * G + jg + L * e] : 0.0f;
     int tier1 = 0;
     size_t pslot = 0;
     bool row_ok = valid;

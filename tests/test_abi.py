@@ -44,6 +44,11 @@ def test_cache_sizes_and_workspace():
     assert s.outl_block_start == 64 * 8 * 2 * 2048 * 4
     assert K.kvq_workspace_bytes(p) == 0                       # 512 (b, h) units: one chunk
     assert K.kvq_workspace_bytes(p, 2048) == 64 * 64 * 16 * 130 * 4
+    # default split of formats on the generic decoder: 64-token chunks for a short context
+    pi = K.make_params(1, 8, 2, 1024, "int4", 32, "fp16")
+    assert K.kvq_workspace_bytes(pi) == 1 * 8 * 16 * 130 * 4
+    # FP4 g32 (MFMA decoder): 32 (b, h) units -> 8 chunks of 16384 tokens
+    assert K.kvq_workspace_bytes(K.make_params(4, 64, 8, 131072, "fp4", 32, "fp16")) == 4 * 64 * 8 * 130 * 4
     p4 = K.make_params(4, 64, 8, 131072, "fp4", 32, "fp16")
     s4 = K.kvq_cache_sizes(p4, 10)
     assert (s4.code_bytes_per_row, s4.meta_bytes_per_row) == (64, 4)
