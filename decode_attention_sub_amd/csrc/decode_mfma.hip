@@ -554,8 +554,11 @@ __global__ void __launch_bounds__(Shape<PAGED>::kWaves * 64) KVQ_OCC decode_mfma
     const int nval = FULL ? kStep : min(kStep, t1 - ts);
     _Float16* krow = ktile + trow * kRow + 64 * half;
     _Float16* vrow = vtile + trow * kRow + 64 * half;
-    // tile positions of this lane's record slots (the pad slot where a slot is unused)
-    uint32_t posK = kHeadDim, posV = kHeadDim;
+    // tile positions of this lane's record slots; an unused slot writes the lane's own pad slot
+    // (row trow, column 128 + 4 half: no operand read touches it, and the unused slots of a
+    // wave spread over the banks instead of all hitting one address)
+    const uint32_t pad = (uint32_t)(trow * kRow + kHeadDim + 4 * half);
+    uint32_t posK = pad, posV = pad;
     _Float16 ovK, ovV;
     if constexpr (HAS_OUTL) {
       // bit offsets of the values inside their words (bit-field extraction takes them modulo 32)
@@ -563,10 +566,10 @@ __global__ void __launch_bounds__(Shape<PAGED>::kWaves * 64) KVQ_OCC decode_mfma
       const uint32_t bitV = laneVB8 + ((uint32_t)rc.vr0 * VB + lv3) * 8u;
       const uint32_t lim = (uint32_t)nval * 128u;
       const uint32_t ddk = rc.ik - (uint32_t)ts * 128u;
-      posK = lane < rc.nk && ddk < lim ? tile_pos(ddk) : (uint32_t)kHeadDim;
+      posK = lane < rc.nk && ddk < lim ? tile_pos(ddk) : pad;
       ovK = outl_from_word<OUTL>(rc.vk, bitK);
       const uint32_t ddv = rc.iv - (uint32_t)ts * 128u;
-      posV = lane < rc.nv && ddv < lim ? tile_pos_v(ddv) : (uint32_t)kHeadDim;
+      posV = lane < rc.nv && ddv < lim ? tile_pos_v(ddv) : pad;
       ovV = outl_from_word<OUTL>(rc.vv, bitV);
     }
     if constexpr (FMT == FMT_C2) expand_c2(bf.kc, bf.km, krow);
@@ -896,11 +899,17 @@ hipError_t launch_decode_mfma(const DecodeLaunch& d, hipStream_t st, bool* handl
       return hipSuccess;
   }
   // Short chunks are packed several to a workgroup (a divisor of its wave count) so that every
-  // wave keeps >= 16 steps.
+  // wave keeps a run of steps: up to 32 for contiguous caches (FP4 at 2048-token chunks: 206 ->
+  // 180 us), 16 for paged ones, whose variable sequence lengths leave larger workgroups unevenly
+  // loaded; never below one workgroup per CU (256).
   const int waves = d.L.paged ? Shape<true>::kWaves : Shape<false>::kWaves;
+  const int run = d.L.paged ? 16 : 32;
+  const int64_t units = (int64_t)d.L.H * d.L.B;
   DecodeLaunch dd = d;
   dd.cpw = 1;
-  while (waves % (dd.cpw * 2) == 0 && d.chunk * dd.cpw * 2 <= 16 * kStep * waves) dd.cpw *= 2;
+  while (waves % (dd.cpw * 2) == 0 && d.chunk * dd.cpw * 2 <= run * kStep * waves &&
+         units * ((d.n_chunks + dd.cpw * 2 - 1) / (dd.cpw * 2)) >= 256)
+    dd.cpw *= 2;
   dim3 grid(d.L.H, (d.n_chunks + dd.cpw - 1) / dd.cpw, d.L.B);
   if (grid.y > 65535u) return hipSuccess;
   if (d.L.paged) launch_fmt<FMT_C2, true>(dd, grid, st);

@@ -10,7 +10,7 @@ using namespace kvq;
 
 namespace {
 
-constexpr int kDefaultPagedChunk = 2048;
+constexpr int kDefaultPagedChunk = 4096;
 
 bool is_quant_fmt(int f) { return f == FMT_INT4 || f == FMT_FP4 || f == FMT_C2; }
 

@@ -167,7 +167,7 @@ int32_t kvq_quantize_append(const kvq_params* p, const kvq_cache* cache, const f
 
 /* Workspace for kvq_decode_attention: split-K partials B * Hq * ceil(max_seq_len/chunk) *
  * (D + 2) floats (0 when a single chunk covers max_seq_len).  split_chunk 0 selects the
- * default: 2048 for paged caches; for contiguous caches enough chunks for 256 (2-bit, FP4 g32)
+ * default: 4096 for paged caches; for contiguous caches enough chunks for 256 (2-bit, FP4 g32)
  * or 1024 (INT4, FP4 g64) (sequence, KV head, chunk) units, chunks of at least 512 / 64 tokens,
  * rounded up to a multiple of 64. */
 int32_t kvq_workspace_bytes(const kvq_params* p, int32_t split_chunk, uint64_t* out_bytes);
