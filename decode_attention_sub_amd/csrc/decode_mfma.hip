@@ -73,23 +73,24 @@ constexpr int kTile = kStep * kRow;        // halfs per tile
 // Workgroup shape.  Contiguous caches: 12 waves (three per SIMD), one LDS tile per wave for both
 // K and V rows, one step of loads in flight, score MFMAs issued before the V rows are expanded
 // (their operands then die early): the registers fit three waves per SIMD.  Paged caches keep
-// 8 waves with separate K and V tiles and two steps in flight; their extra addressing state
+// 8 waves with separate K and V tiles and one step in flight; their extra addressing state
 // does not fit three waves per SIMD.
 template <bool PAGED> struct Shape {
   static constexpr int kWaves = PAGED ? 8 : 12;
   static constexpr int kTiles = PAGED ? 2 : 1;
-  static constexpr int kPF = PAGED ? 2 : 1;       // steps of codes / records in flight per wave
+  static constexpr int kPF = 1;                   // steps of codes / records in flight per wave
   static constexpr bool kEarlyS = !PAGED;
   static constexpr int kWaveLds = kTiles * kTile; // halfs of LDS per wave
 };
 
 
 template <int FMT> struct Buf;
-// ea, eb: block-table entries of the step's two pages (paged caches)
-template <> struct Buf<FMT_C2> { uint4 kc, vc; uint2 km, vm; uint32_t ea, eb; };
-template <> struct Buf<FMT_FP4> { uint4 kc0, kc1, vc0, vc1; uint32_t km, vm, ea, eb; };
-// record bounds of a step (lanes 0..3) and, for paged caches, its block-table entries (lanes 0, 1)
-struct Bnd { uint32_t rec, bt; };
+// ek, ev: pool-row bases of the pages of the lane's K and V tokens (paged caches)
+template <> struct Buf<FMT_C2> { uint4 kc, vc; uint2 km, vm; uint32_t ek, ev; };
+template <> struct Buf<FMT_FP4> { uint4 kc0, kc1, vc0, vc1; uint32_t km, vm, ek, ev; };
+// record bounds of a step (lanes 0..3) and, for paged caches, the block-table entries of the
+// pages of the lane's K and V tokens (per lane: the page state stays out of scalar registers)
+struct Bnd { uint32_t rec, pk, pv; };
 // FP8-tier rows of a step (paged caches): a lane's K and V half rows and their rows' scales;
 // fk / fv tell whether the lane's K / V token sits on an FP8 page, slow whether any token does
 struct F8 { uint4 k[4], v[4]; uint32_t ks, vs; bool fk, fv, slow; };
@@ -351,15 +352,9 @@ __global__ void __launch_bounds__(Shape<PAGED>::kWaves * 64) KVQ_OCC decode_mfma
   const __amdgpu_buffer_rsrc_t rcV = make_rsrc((const uint8_t*)d.cache.codes[1] + rowbase * CB, nrows * CB);
   const __amdgpu_buffer_rsrc_t rmK = make_rsrc((const uint8_t*)d.cache.meta[0] + rowbase * MB, nrows * MB);
   const __amdgpu_buffer_rsrc_t rmV = make_rsrc((const uint8_t*)d.cache.meta[1] + rowbase * MB, nrows * MB);
-  __amdgpu_buffer_rsrc_t r8K, r8V, rsK, rsV, rbt;
-  if constexpr (PAGED) {
-    const uint32_t n8 = (uint32_t)L.num_pages_fp8 * (uint32_t)L.H * kBlock;
-    r8K = make_rsrc(d.cache.codes8[0], n8 * kHeadDim);
-    r8V = make_rsrc(d.cache.codes8[1], n8 * kHeadDim);
-    rsK = make_rsrc(d.cache.scale8[0], n8 * 4);
-    rsV = make_rsrc(d.cache.scale8[1], n8 * 4);
-    rbt = make_rsrc(d.block_table + (size_t)b * L.max_pages, (uint32_t)L.max_pages * 4);
-  }
+  // paged: this sequence's block-table row (FP8-tier rows are read through plain pointers on the
+  // rare steps that have them, keeping their descriptors out of the scalar registers)
+  const int32_t* __restrict__ btrow = PAGED ? d.block_table + (size_t)b * L.max_pages : nullptr;
   const uint32_t coff = (uint32_t)(trow * CB + half * (CB / 2));
   const uint32_t coffv = (uint32_t)(vtok(trow) * CB + half * (CB / 2));
   const uint32_t lane4 = (uint32_t)lane * 4u, laneVB = (uint32_t)lane * VB, laneVB8 = laneVB * 8u;
@@ -428,10 +423,10 @@ __global__ void __launch_bounds__(Shape<PAGED>::kWaves * 64) KVQ_OCC decode_mfma
   auto enc_page = [&](uint32_t e, bool live) -> uint32_t {
     const uint32_t slot = e & 0x7FFFFFFFu;
     const bool in_pool = slot < (uint32_t)((e >> 31) ? L.num_pages_fp8 : L.num_pages);
-    bad_page = bad_page || (live && !in_pool);
+    bad_page = bad_page || __builtin_amdgcn_ballot_w64(live && !in_pool) != 0;
     return live && in_pool ? ((slot * (uint32_t)L.H + (uint32_t)h) * kBlock) | (e & 0x80000000u) : kDead;
   };
-  // lane constants: a lane's K token is trow (page A below 16), its V token vtok(trow)
+  // lane constants: a lane's K token is trow (second page from 16 on), its V token vtok(trow)
   const bool kpageB = trow >= 16, vpageB = (trow & 1) != 0;
   const uint32_t lcK = (uint32_t)(trow & 15) * CB + half * (CB / 2);
   const uint32_t lcV = (uint32_t)(trow >> 1) * CB + half * (CB / 2);
@@ -442,10 +437,9 @@ __global__ void __launch_bounds__(Shape<PAGED>::kWaves * 64) KVQ_OCC decode_mfma
     const uint32_t ts = (uint32_t)tsi;
     if constexpr (PAGED) {
       constexpr bool RAGGED = decltype(ragged_tag)::value;
-      bf.ea = enc_page((uint32_t)__builtin_amdgcn_readlane((int)bd.bt, 0), tsi < t1);
-      bf.eb = enc_page((uint32_t)__builtin_amdgcn_readlane((int)bd.bt, 1), tsi + 16 < t1);
-      const uint32_t ek = kpageB ? bf.eb : bf.ea;
-      const uint32_t ev = vpageB ? bf.eb : bf.ea;
+      bf.ek = enc_page(bd.pk, tsi + (kpageB ? 16 : 0) < t1);
+      bf.ev = enc_page(bd.pv, tsi + (vpageB ? 16 : 0) < t1);
+      const uint32_t ek = bf.ek, ev = bf.ev;
       bool okk = ek < (1u << 27), okv = ev < (1u << 27);
       if constexpr (RAGGED) {
         okk = okk && tsi + trow < t1;
@@ -476,14 +470,18 @@ __global__ void __launch_bounds__(Shape<PAGED>::kWaves * 64) KVQ_OCC decode_mfma
   // lanes 0..3 load {K start, K end, V start, V end} of the step's records (block starts); for
   // paged caches lanes 0, 1 also load the block-table entries of its two pages
   auto issue_bounds = [&](int ts) -> Bnd {
-    Bnd bd{0u, 0u};
+    Bnd bd{0u, 0u, 0u};
     const int blk = ts >> 4;
     if constexpr (HAS_OUTL) {
       const int which = lane & 3;  // 0: K blk, 1: K blk+2, 2: V blk, 3: V blk+2
       const uint32_t off = (uint32_t)(((which >> 1) * L.nblk + blk + 2 * (which & 1)) * 4);
       bd.rec = ld32(rbs, off);
     }
-    if constexpr (PAGED) bd.bt = ld32(rbt, (uint32_t)(blk + (lane & 1)) * 4u);
+    if constexpr (PAGED) {   // entries past the row are clamped to its last (their pages are dead)
+      const int last = L.max_pages - 1;
+      bd.pk = (uint32_t)btrow[min(blk + (kpageB ? 1 : 0), last)];
+      bd.pv = (uint32_t)btrow[min(blk + (vpageB ? 1 : 0), last)];
+    }
     return bd;
   };
   auto issue_recs = [&](Recs& rc, const Bnd& bd, int ts) {
@@ -509,28 +507,32 @@ __global__ void __launch_bounds__(Shape<PAGED>::kWaves * 64) KVQ_OCC decode_mfma
       rc.vv = ld32s(rvV, ((bv & 3u) + laneVB) & ~3u, bv & ~3u);
     }
   };
-  // paged: FP8-tier rows of a step, loaded one step before it is consumed (only when one of the
-  // step's pages is FP8)
-  auto issue_fp8 = [&](F8& f, const Buf<FMT>& bf, int ts) {
+  // paged: FP8-tier rows of a step, loaded when the step is consumed (only when one of its pages
+  // is FP8, one step in five; holding them a step ahead cost more in registers than their
+  // latency costs here)
+  auto load_fp8 = [&](F8& f, const Buf<FMT>& bf, int ts) {
     if constexpr (PAGED) {
       const auto is8 = [](uint32_t e) { return (e >> 31) != 0 && e != kDead; };
-      f.slow = is8(bf.ea) || is8(bf.eb);
+      f.slow = __builtin_amdgcn_ballot_w64(is8(bf.ek) || is8(bf.ev)) != 0;
       if (f.slow) {
-        const uint32_t ek = kpageB ? bf.eb : bf.ea;
-        const uint32_t ev = vpageB ? bf.eb : bf.ea;
+        const uint32_t ek = bf.ek, ev = bf.ev;
         f.fk = is8(ek) && ts + trow < t1;
         f.fv = is8(ev) && ts + vtok(trow) < t1;
         const uint32_t rk = (ek & 0x7FFFFFFFu) + (uint32_t)(trow & 15);
         const uint32_t rv = (ev & 0x7FFFFFFFu) + (uint32_t)(trow >> 1);
-        // (each skipped load gets kOOB itself: kOOB + 16 k would wrap into range)
-        const uint32_t ok = rk * kHeadDim + 64u * half, ov = rv * kHeadDim + 64u * half;
+        // only lanes whose row lies on a live FP8 page (inside its pool) load
+        if (f.fk) {
+          const uint4* src = (const uint4*)((const uint8_t*)d.cache.codes8[0] + (size_t)rk * kHeadDim + 64u * half);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          f.k[k] = ld128(r8K, f.fk ? ok + 16u * k : kOOB);
-          f.v[k] = ld128(r8V, f.fv ? ov + 16u * k : kOOB);
+          for (int k = 0; k < 4; ++k) f.k[k] = src[k];
+          f.ks = as_u32(d.cache.scale8[0][rk]);
         }
-        f.ks = ld32(rsK, f.fk ? rk * 4u : kOOB);
-        f.vs = ld32(rsV, f.fv ? rv * 4u : kOOB);
+        if (f.fv) {
+          const uint4* src = (const uint4*)((const uint8_t*)d.cache.codes8[1] + (size_t)rv * kHeadDim + 64u * half);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) f.v[k] = src[k];
+          f.vs = as_u32(d.cache.scale8[1][rv]);
+        }
       }
     }
   };
@@ -549,8 +551,11 @@ __global__ void __launch_bounds__(Shape<PAGED>::kWaves * 64) KVQ_OCC decode_mfma
   // branch-free block: K rows are expanded and written, the K^ operand reads are issued, V rows
   // are expanded while those reads are in flight, the score MFMAs run, the V^T operand reads are
   // issued before the softmax needs them.
-  auto consume = [&](const Buf<FMT>& bf, const Recs& rc, const F8& f8, int ts, auto full_tag) {
+  auto consume = [&](const Buf<FMT>& bf, const Recs& rc, int ts, auto full_tag) {
     constexpr bool FULL = decltype(full_tag)::value;
+    F8 f8;
+    f8.slow = false;
+    load_fp8(f8, bf, ts);
     const int nval = FULL ? kStep : min(kStep, t1 - ts);
     _Float16* krow = ktile + trow * kRow + 64 * half;
     _Float16* vrow = vtile + trow * kRow + 64 * half;
@@ -749,8 +754,6 @@ __global__ void __launch_bounds__(Shape<PAGED>::kWaves * 64) KVQ_OCC decode_mfma
   Buf<FMT> buf[NB];
   Recs rec[NB];
   Bnd bnd[NB];
-  F8 f8;
-  f8.slow = false;
   const int nmine = wi < nfull ? (nfull - wi + wpc - 1) / wpc : 0;
   auto wts = [&](int j) { return step_ts(j < nmine ? wi + wpc * j : nfull); };
 #if KVQ_PRIO
@@ -778,7 +781,6 @@ __global__ void __launch_bounds__(Shape<PAGED>::kWaves * 64) KVQ_OCC decode_mfma
     issue_recs(rec[k], bnd[k], wts(k));
     issue_codes(buf[k], bnd[k], wts(k), std::false_type{});
   }
-  issue_fp8(f8, buf[0], wts(0));
   const int ngroups = nmine / NB;
   for (int g = 0; g < ngroups; ++g) {
 #if KVQ_PRIO
@@ -792,8 +794,7 @@ __global__ void __launch_bounds__(Shape<PAGED>::kWaves * 64) KVQ_OCC decode_mfma
       bnd[u] = issue_bounds(wts(jj + NB));
       issue_recs(rec[(u + kPF) % NB], bnd[(u + kPF) % NB], wts(jj + kPF));
       issue_codes(buf[(u + kPF) % NB], bnd[(u + kPF) % NB], wts(jj + kPF), std::false_type{});
-      consume(buf[u], rec[u], f8, wts(jj), std::true_type{});
-      issue_fp8(f8, buf[(u + 1) % NB], wts(jj + 1));
+      consume(buf[u], rec[u], wts(jj), std::true_type{});
     }
 #if KVQ_PRIO
     partner_seen = min(__builtin_amdgcn_readfirstlane(*prog_p1), __builtin_amdgcn_readfirstlane(*prog_p2));
@@ -809,8 +810,7 @@ __global__ void __launch_bounds__(Shape<PAGED>::kWaves * 64) KVQ_OCC decode_mfma
       bnd[u] = issue_bounds(wts(jj + NB));
       issue_recs(rec[(u + kPF) % NB], bnd[(u + kPF) % NB], wts(jj + kPF));
       issue_codes(buf[(u + kPF) % NB], bnd[(u + kPF) % NB], wts(jj + kPF), std::false_type{});
-      consume(buf[u], rec[u], f8, wts(jj), std::true_type{});
-      issue_fp8(f8, buf[(u + 1) % NB], wts(jj + 1));
+      consume(buf[u], rec[u], wts(jj), std::true_type{});
     }
   }
   if (ragged && wi == 0) {
@@ -818,8 +818,7 @@ __global__ void __launch_bounds__(Shape<PAGED>::kWaves * 64) KVQ_OCC decode_mfma
     const Bnd b0 = issue_bounds(ts);
     issue_recs(rec[0], b0, ts);
     issue_codes(buf[0], b0, ts, std::true_type{});
-    issue_fp8(f8, buf[0], ts);
-    consume(buf[0], rec[0], f8, ts, std::false_type{});
+    consume(buf[0], rec[0], ts, std::false_type{});
   }
 
   if constexpr (PAGED) {
