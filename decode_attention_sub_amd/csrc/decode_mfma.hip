@@ -365,17 +365,9 @@ __global__ void __launch_bounds__(Shape<PAGED>::kWaves * 64) KVQ_OCC decode_mfma
   const int cap = (int)min(L.outl_cap, (int64_t)INT32_MAX);
   __amdgpu_buffer_rsrc_t riK, riV, rvK, rvV, rbs;
   int cntK = 0, cntV = 0;
-  const uint32_t* oidxK = nullptr;
-  const uint32_t* oidxV = nullptr;
-  const uint8_t* ovalK = nullptr;
-  const uint8_t* ovalV = nullptr;
   uint32_t lv3 = 0;   // byte offset of the list's first value inside its aligned 32-bit word
   if constexpr (HAS_OUTL) {
     const size_t lbase = ((size_t)b * L.H + h) * (size_t)L.outl_cap;
-    oidxK = d.cache.outl_idx[0] + lbase;
-    oidxV = d.cache.outl_idx[1] + lbase;
-    ovalK = (const uint8_t*)d.cache.outl_val[0] + lbase * VB;
-    ovalV = (const uint8_t*)d.cache.outl_val[1] + lbase * VB;
     // value words: ranges start at the aligned word holding the list's first value and end at
     // the word holding its last (value buffers are padded to whole words)
     const size_t lvb = lbase * VB, w0 = lvb & ~(size_t)3;
@@ -383,8 +375,8 @@ __global__ void __launch_bounds__(Shape<PAGED>::kWaves * 64) KVQ_OCC decode_mfma
     const uint32_t vbytes = (uint32_t)(((lvb + (size_t)cap * VB + 3) & ~(size_t)3) - w0);
     rvK = make_rsrc((const uint8_t*)d.cache.outl_val[0] + w0, vbytes);
     rvV = make_rsrc((const uint8_t*)d.cache.outl_val[1] + w0, vbytes);
-    riK = make_rsrc(oidxK, (uint32_t)cap * 4);
-    riV = make_rsrc(oidxV, (uint32_t)cap * 4);
+    riK = make_rsrc(d.cache.outl_idx[0] + lbase, (uint32_t)cap * 4);
+    riV = make_rsrc(d.cache.outl_idx[1] + lbase, (uint32_t)cap * 4);
     rbs = make_rsrc(d.cache.outl_block_start + lidK * (size_t)L.nblk, (uint32_t)L.nblk * 8);
     cntK = max(0, min(d.cache.outl_count[lidK], cap));
     cntV = max(0, min(d.cache.outl_count[lidK + 1], cap));
@@ -596,9 +588,9 @@ __global__ void __launch_bounds__(Shape<PAGED>::kWaves * 64) KVQ_OCC decode_mfma
       ktile[posK] = ovK;
       if (rc.nk > 64) {
         for (int a = 64 + lane; a < rc.nk; a += 64) {  // the rest of a crowded step
-          const int at = rc.kr0 + a;
-          const uint32_t v = VB == 2 ? ((const uint16_t*)ovalK)[at] : ovalK[at];
-          patch_at<FMT, OUTL, false>(ktile, oidxK[at], v, ts, nval);
+          const uint32_t at = (uint32_t)(rc.kr0 + a), byte = at * VB + lv3;
+          const uint32_t v = __builtin_amdgcn_ubfe(ld32(rvK, byte & ~3u), (byte & 3u) * 8u, VB * 8);
+          patch_at<FMT, OUTL, false>(ktile, ld32(riK, at * 4u), v, ts, nval);
         }
       }
     }
@@ -625,9 +617,9 @@ __global__ void __launch_bounds__(Shape<PAGED>::kWaves * 64) KVQ_OCC decode_mfma
       vtile[posV] = ovV;
       if (rc.nv > 64) {
         for (int i = 64 + lane; i < rc.nv; i += 64) {
-          const int at = rc.vr0 + i;
-          const uint32_t v = VB == 2 ? ((const uint16_t*)ovalV)[at] : ovalV[at];
-          patch_at<FMT, OUTL, true>(vtile, oidxV[at], v, ts, nval);
+          const uint32_t at = (uint32_t)(rc.vr0 + i), byte = at * VB + lv3;
+          const uint32_t v = __builtin_amdgcn_ubfe(ld32(rvV, byte & ~3u), (byte & 3u) * 8u, VB * 8);
+          patch_at<FMT, OUTL, true>(vtile, ld32(riV, at * 4u), v, ts, nval);
         }
       }
     }
