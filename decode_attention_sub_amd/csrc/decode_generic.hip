@@ -217,21 +217,45 @@ __global__ void __launch_bounds__(256) decode_generic_kernel(DecodeLaunch d) {
   }
 }
 
-// out[b][hq] = sum_c 2^(m_c - M) o_c / sum_c 2^(m_c - M) l_c over the chunks holding tokens
+// out[b][hq] = sum_c 2^(m_c - M) o_c / sum_c 2^(m_c - M) l_c over the chunks holding tokens.
+// Latency-bound (one small workgroup per query head): the chunk maxima and weights are taken by
+// the 128 threads in parallel, 128 chunks at a time, and each channel thread then sums its
+// column with the weights from LDS, eight chunk rows in flight.  The order of every sum is fixed.
 __global__ void __launch_bounds__(128) lse_merge_kernel(DecodeLaunch d) {
-  const int hq = blockIdx.x, b = blockIdx.y, ch = threadIdx.x;
+  __shared__ float s_w[128];
+  __shared__ float s_red[2];
+  const int hq = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, ch = tid;
   const int S = d.seq_lens[b];
   const int nc = min((S + d.chunk - 1) / d.chunk, d.n_chunks);
   const float* pp = d.partials + ((size_t)b * d.Hq + hq) * d.n_chunks * (kHeadDim + 2);
-  float M = -INFINITY;
-  for (int c = 0; c < nc; ++c) M = fmaxf(M, pp[(size_t)c * (kHeadDim + 2)]);
-  float num = 0.0f, den = 0.0f;
-  for (int c = 0; c < nc; ++c) {
-    const float* q = pp + (size_t)c * (kHeadDim + 2);
-    const float w = exp2f(q[0] - M);
-    den = fmaf(w, q[1], den);
-    num = fmaf(w, q[2 + ch], num);
+  float m = -INFINITY;
+  for (int c = tid; c < nc; c += 128) m = fmaxf(m, pp[(size_t)c * (kHeadDim + 2)]);
+  m = wave_max(m);
+  if ((tid & 63) == 0) s_red[tid >> 6] = m;
+  __syncthreads();
+  const float M = fmaxf(s_red[0], s_red[1]);
+  float num = 0.0f, lsum = 0.0f;
+  for (int c0 = 0; c0 < nc; c0 += 128) {
+    const int c = c0 + tid;
+    float w = 0.0f;
+    if (c < nc) {
+      const float* q = pp + (size_t)c * (kHeadDim + 2);
+      w = exp2f(q[0] - M);
+      lsum = fmaf(w, q[1], lsum);
+    }
+    __syncthreads();   // the previous block's weights are consumed
+    s_w[tid] = w;
+    __syncthreads();
+    const int n = min(128, nc - c0);
+    const float* col = pp + (size_t)c0 * (kHeadDim + 2) + 2 + ch;
+#pragma unroll 8
+    for (int k = 0; k < n; ++k) num = fmaf(s_w[k], col[(size_t)k * (kHeadDim + 2)], num);
   }
+  lsum = wave_sum(lsum);
+  __syncthreads();
+  if ((tid & 63) == 0) s_red[tid >> 6] = lsum;
+  __syncthreads();
+  const float den = s_red[0] + s_red[1];
   d.out[((size_t)b * d.Hq + hq) * kHeadDim + ch] = num / den;
 }
 
