@@ -204,3 +204,27 @@ def test_paged_bad_slot_reports_status():
             dc.cache.tensors["status"].zero_()
             run_decode(dcb, split_chunk=split)
             assert dc.cache.status() == K.KVQ_ERR_INVALID_ARG
+
+
+# Many (sequence, KV head) units with short chunks: the launcher packs several chunks into one
+# workgroup (4 chunks of 3 waves for 2-bit, 2 chunks of 6 waves for FP4 g32) and the merge sums
+# 12 / 10 chunk partials.
+PACKED = {
+    "c2_packed": (WD.variant(CONFIGS["c2_b16_s8k"], B=32, Hq=32, H=8, S=1500), 128),
+    "fp4_packed": (WD.variant(CONFIGS["fp4_b4_s128k"], B=8, Hq=64, H=8, S=2500, split_chunk=256), 256),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PACKED))
+def test_decode_packed_chunks(name):
+    w, split = PACKED[name]
+    log(f"[gpu] packed chunks {name}: building the cache")
+    dc = WD.build(w)
+    assert dc.cache.status() == 0
+    got = run_decode(dc, split_chunk=split)
+    sm = 1.0 / math.sqrt(w.D)
+    for b in (0, w.B // 2 + 1, w.B - 1):
+        ref = oracle_attention(dc, b, range(w.Hq), sm)
+        for hq, o in ref.items():
+            err = np.abs(got[b, hq] - o).max()
+            assert err <= ATOL, f"{name} b={b} hq={hq} split={split}: max-abs {err}"
