@@ -227,7 +227,8 @@ def main():
     g1.record(stream)
     torch.cuda.synchronize()
     ms_step = g0.elapsed_time(g1) / args.steps
-    dec_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    dec_all = np.array([a.elapsed_time(b) for a, b in evs])
+    dec_ms = float(np.mean(dec_all))
     status = cache.status()
     if status != 0:
         raise RuntimeError(f"device status {status}: {K.kvq_status_string(status)}")
@@ -251,6 +252,7 @@ def main():
                    "outliers": w.outlier, "tau": w.sigma, "split_chunk": split if split else "default",
                    "layers": 1},
         "us_per_step_decode": round(dec_ms * 1e3, 2),
+        "us_decode_p10_p50_p90": [round(float(np.percentile(dec_all, q)) * 1e3, 2) for q in (10, 50, 90)],
         "us_per_step": round(ms_step * 1e3, 2),
         "pct_hbm_peak": round(100 * achieved / HBM_PEAK_GBS, 2),
         "pct_read_ceiling": round(100 * achieved / ceiling, 2),
