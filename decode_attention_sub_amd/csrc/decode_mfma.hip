@@ -390,12 +390,15 @@ __global__ void __launch_bounds__(Shape<PAGED>::kWaves * 64) KVQ_OCC decode_mfma
   // Workgroups walk their full steps in rotated order, starting at evenly spread points.  Every
   // (sequence, head) slice starts at the same power-of-two-aligned offset; walking them in
   // lockstep would send every workgroup to the same HBM channels at the same time.
+  // (Paged caches scatter their pages anyway, and the scalar registers the rotation takes are
+  // worth more there.)
+  int rot = 0;
 #if KVQ_ROTATE
-  const uint32_t n_units = (uint32_t)d.n_chunks * (uint32_t)L.H * (uint32_t)L.B;
-  const uint32_t unit = (uint32_t)chunk + (uint32_t)d.n_chunks * ((uint32_t)h + (uint32_t)L.H * (uint32_t)b);
-  const int rot = nfull > 0 ? (int)(((uint64_t)unit * (uint64_t)nfull) / n_units) : 0;
-#else
-  const int rot = 0;
+  if constexpr (!PAGED) {
+    const uint32_t n_units = (uint32_t)d.n_chunks * (uint32_t)L.H * (uint32_t)L.B;
+    const uint32_t unit = (uint32_t)chunk + (uint32_t)d.n_chunks * ((uint32_t)h + (uint32_t)L.H * (uint32_t)b);
+    rot = nfull > 0 ? (int)(((uint64_t)unit * (uint64_t)nfull) / n_units) : 0;
+  }
 #endif
   // token start of full step number c (c >= nfull: past the chunk, every load reads zeros)
   auto step_ts = [&](int c) {
