@@ -124,21 +124,27 @@ struct Recs {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
+// CP: cache policy (kNT: non-temporal, for data read once)
+constexpr int kNT = 2;
+template <int CP = 0>
 __device__ __forceinline__ uint4 ld128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, CP));
 }
+template <int CP = 0>
 __device__ __forceinline__ uint2 ld64(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, CP));
 }
 __device__ __forceinline__ uint32_t ld32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
 }
 // with a uniform part of the offset in the scalar offset (the range check covers the sum)
+template <int CP = 0>
 __device__ __forceinline__ uint4 ld128s(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, CP));
 }
+template <int CP = 0>
 __device__ __forceinline__ uint2 ld64s(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0));
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, CP));
 }
 __device__ __forceinline__ uint32_t ld32s(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
@@ -444,15 +450,16 @@ __global__ void __launch_bounds__(Shape<PAGED>::kWaves * 64) KVQ_OCC decode_mfma
       const uint32_t ov = okv ? ev * CB + lcV : kOOB;
       const uint32_t mk = okk ? ek * MB + lmK : kOOB;
       const uint32_t mv = okv ? ev * MB + lmV : kOOB;
-      bf.kc = ld128(rcK, ok);
-      bf.vc = ld128(rcV, ov);
-      bf.km = ld64(rmK, mk);
-      bf.vm = ld64(rmV, mv);
+      bf.kc = ld128<kNT>(rcK, ok);
+      bf.vc = ld128<kNT>(rcV, ov);
+      bf.km = ld64<kNT>(rmK, mk);
+      bf.vm = ld64<kNT>(rmV, mv);
     } else if constexpr (FMT == FMT_C2) {
-      bf.kc = ld128s(rcK, coff, ts * CB);
-      bf.vc = ld128s(rcV, coffv, ts * CB);
-      bf.km = ld64s(rmK, moff, ts * MB);
-      bf.vm = ld64s(rmV, moffv, ts * MB);
+      // 2-bit rows are read once: non-temporal loads (measured faster; for FP4 rows, slower)
+      bf.kc = ld128s<kNT>(rcK, coff, ts * CB);
+      bf.vc = ld128s<kNT>(rcV, coffv, ts * CB);
+      bf.km = ld64s<kNT>(rmK, moff, ts * MB);
+      bf.vm = ld64s<kNT>(rmV, moffv, ts * MB);
     } else {
       bf.kc0 = ld128s(rcK, coff, ts * CB);
       bf.kc1 = ld128s(rcK, coff + 16, ts * CB);
