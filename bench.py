@@ -166,6 +166,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default="c2_b64_s32k")
     ap.add_argument("--split", type=int, default=-1, help="split-K chunk (default: workload's)")
+    ap.add_argument("--fmt", default=None,
+                    help="format variant stored like the workload's format (u2 for 2-bit "
+                         "workloads, int4s for INT4 ones): same shapes and data, other quantizer fit")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--flush", choices=("auto", "on", "off"), default="auto",
                     help="stream 1 GiB through the caches before every step (auto: when the "
@@ -185,6 +188,11 @@ def main():
     from workloads import generate as G
 
     w = CONFIGS[args.workload]
+    if args.fmt:
+        base = {"u2": "c2", "int4s": "int4"}.get(args.fmt)
+        if base != w.fmt:
+            sys.exit(f"--fmt {args.fmt}: not a variant of the workload's format {w.fmt}")
+        w = WD.variant(w, fmt=args.fmt)
     torch.cuda.set_device(0)
     ceiling = read_ceiling_gbs()
     log(f"measured read ceiling {ceiling:.0f} GB/s")
@@ -267,7 +275,7 @@ def main():
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f16" if w.fmt in ("c2", "fp4") else "f32", "data": "synthetic",
+        "dtype": "f16" if w.fmt in ("c2", "fp4", "u2") else "f32", "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "H": w.H, "D": w.D,
                    "S": int(lens_h.max()), "format": w.fmt, "group": w.group,
                    "outliers": w.outlier, "tau": w.sigma, "split_chunk": split if split else "default",

@@ -14,8 +14,23 @@ constexpr int kDefaultPagedChunk = 4096;
 
 bool is_quant_fmt(int f) { return f == FMT_INT4 || f == FMT_FP4 || f == FMT_C2; }
 
+// A format variant is checked, sized, stored and decoded as its base format; only the
+// quantizer's fit differs.  Entry points work on a copy whose format is the base format.
+struct Params {
+  kvq_params p;
+  int fit;
+  explicit Params(const kvq_params* in) : p(in ? *in : kvq_params{}), fit(in ? fit_of(in->format) : 0) {
+    p.format = storage_fmt(p.format);
+  }
+};
+
 int32_t check_params(const kvq_params* p) {
   if (!p) return KVQ_ERR_INVALID_ARG;
+  if (p->format == KVQ_FMT_UNIFORM2 || p->format == KVQ_FMT_INT4_SYM) {
+    if (p->page_size != 0) return KVQ_ERR_UNSUPPORTED;
+    const Params n(p);
+    return check_params(&n.p);
+  }
   if (p->batch < 1 || p->num_kv_heads < 1 || p->num_q_heads < 1 || p->max_seq_len < 1)
     return KVQ_ERR_INVALID_ARG;
   if (p->head_dim != kHeadDim) return KVQ_ERR_UNSUPPORTED;
@@ -102,8 +117,10 @@ int resolve_chunk(const kvq_params* p, int32_t split_chunk) {
 
 extern "C" {
 
-int32_t kvq_kv_bytes(const kvq_params* p, int32_t num_layers, int64_t num_tokens,
+int32_t kvq_kv_bytes(const kvq_params* pin, int32_t num_layers, int64_t num_tokens,
                      int64_t num_outliers, uint64_t* out_bytes) {
+  const Params n(pin);
+  const kvq_params* p = pin ? &n.p : nullptr;
   if (!p || !out_bytes || num_layers < 0 || num_tokens < 0 || num_outliers < 0 ||
       p->num_kv_heads < 1 || p->head_dim < 1)
     return KVQ_ERR_INVALID_ARG;
@@ -126,9 +143,11 @@ int32_t kvq_kv_bytes(const kvq_params* p, int32_t num_layers, int64_t num_tokens
   return KVQ_OK;
 }
 
-int32_t kvq_cache_sizes(const kvq_params* p, int64_t outl_capacity, kvq_cache_sizes_t* out) {
-  int32_t st = check_params(p);
+int32_t kvq_cache_sizes(const kvq_params* pin, int64_t outl_capacity, kvq_cache_sizes_t* out) {
+  int32_t st = check_params(pin);
   if (st) return st;
+  const Params n(pin);
+  const kvq_params* p = &n.p;
   if (!out || outl_capacity < 0) return KVQ_ERR_INVALID_ARG;
   memset(out, 0, sizeof(*out));
   out->code_bytes_per_row = code_bytes(p);
@@ -154,11 +173,13 @@ int32_t kvq_cache_sizes(const kvq_params* p, int64_t outl_capacity, kvq_cache_si
   return KVQ_OK;
 }
 
-int32_t kvq_quantize_append(const kvq_params* p, const kvq_cache* cache, const float* k_new,
+int32_t kvq_quantize_append(const kvq_params* pin, const kvq_cache* cache, const float* k_new,
                             const float* v_new, int32_t max_new, const int32_t* positions,
                             const int32_t* counts, const int32_t* block_table, void* stream) {
-  int32_t st = check_params(p);
+  int32_t st = check_params(pin);
   if (st) return st;
+  const Params n(pin);
+  const kvq_params* p = &n.p;
   st = check_cache(p, cache);
   if (st) return st;
   if (!k_new || !v_new || !positions || !counts || max_new < 1) return KVQ_ERR_INVALID_ARG;
@@ -177,13 +198,16 @@ int32_t kvq_quantize_append(const kvq_params* p, const kvq_cache* cache, const f
   q.lloyd = p->lloyd_iters;
   q.fmt = p->format;
   q.group = p->group_size;
+  q.fit = n.fit;
   if (launch_quantize_append(q, (hipStream_t)stream) != hipSuccess) return KVQ_ERR_HIP;
   return KVQ_OK;
 }
 
-int32_t kvq_workspace_bytes(const kvq_params* p, int32_t split_chunk, uint64_t* out_bytes) {
-  int32_t st = check_params(p);
+int32_t kvq_workspace_bytes(const kvq_params* pin, int32_t split_chunk, uint64_t* out_bytes) {
+  int32_t st = check_params(pin);
   if (st) return st;
+  const Params n(pin);
+  const kvq_params* p = &n.p;
   if (!out_bytes) return KVQ_ERR_INVALID_ARG;
   const int chunk = resolve_chunk(p, split_chunk);
   if (chunk < 0) return KVQ_ERR_INVALID_ARG;
@@ -192,12 +216,14 @@ int32_t kvq_workspace_bytes(const kvq_params* p, int32_t split_chunk, uint64_t* 
   return KVQ_OK;
 }
 
-int32_t kvq_decode_attention(const kvq_params* p, const kvq_cache* cache, const void* q_bf16,
+int32_t kvq_decode_attention(const kvq_params* pin, const kvq_cache* cache, const void* q_bf16,
                              const int32_t* seq_lens, const int32_t* block_table,
                              float sm_scale, int32_t split_chunk, float* out, void* workspace,
                              uint64_t ws_bytes, void* stream) {
-  int32_t st = check_params(p);
+  int32_t st = check_params(pin);
   if (st) return st;
+  const Params n(pin);
+  const kvq_params* p = &n.p;
   st = check_cache(p, cache);
   if (st) return st;
   if (!q_bf16 || !seq_lens || !out || !isfinite(sm_scale)) return KVQ_ERR_INVALID_ARG;

@@ -14,6 +14,16 @@ constexpr int kBlock = 16;      // tokens per outlier block and per page
 
 enum Fmt : int { FMT_FP8ROW = KVQ_FMT_FP8_E4M3_ROW, FMT_INT4 = KVQ_FMT_INT4_ASYM,
                  FMT_FP4 = KVQ_FMT_FP4_E2M1, FMT_C2 = KVQ_FMT_CENTROID2 };
+// Quantizer fits: a format variant is stored (and decoded) as its base format and differs only
+// in how the quantizer fits the group (uniform 2-bit codebook as FMT_C2, symmetric INT4 as
+// FMT_INT4).
+enum Fit : int { kFitDefault = 0, kFitUniform = 1, kFitSym = 2 };
+__host__ __device__ constexpr int storage_fmt(int fmt) {
+  return fmt == KVQ_FMT_UNIFORM2 ? FMT_C2 : (fmt == KVQ_FMT_INT4_SYM ? FMT_INT4 : fmt);
+}
+__host__ __device__ constexpr int fit_of(int fmt) {
+  return fmt == KVQ_FMT_UNIFORM2 ? kFitUniform : (fmt == KVQ_FMT_INT4_SYM ? kFitSym : kFitDefault);
+}
 
 __host__ __device__ constexpr int code_bits(int fmt) {
   return fmt == FMT_C2 ? 2 : (fmt == FMT_FP8ROW ? 8 : 4);

@@ -19,8 +19,9 @@ struct QuantizeLaunch {
   int outl;
   float tau2;
   int lloyd;
-  int fmt;
+  int fmt;            // storage format
   int group;
+  int fit;            // kFitDefault or the variant fit of a format stored as fmt
 };
 
 struct DecodeLaunch {

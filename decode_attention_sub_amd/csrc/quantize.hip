@@ -38,6 +38,7 @@ struct QArgs {
   int outl;          // kvq_outlier_dtype
   float tau2;        // fl32(tau * tau)
   int lloyd;
+  int fit;           // kFitDefault, or a variant fit of the storage format
 };
 
 // compile-time loop: f(std::integral_constant<int, I>) for I = 0 .. N-1
@@ -173,6 +174,57 @@ __device__ void fit_fp4(const float x[4], const bool keep[4], RowOut& o) {
   }
   o.meta[0] = s8;
   o.meta[1] = 0;
+}
+
+// Symmetric INT4 ("The Sub-10ms Barrier ...", section "2. FP4/INT4 KV-Cache Quantization", the
+// quantize_kv_cache_fp4 listing): scale absmax/7 over the non-outliers, at least 1e-5, stored as
+// fp16 S; code = clamp(round(x / S), -8, 7) + 8, stored as INT4 with zero -8 S.
+template <int G>
+__device__ void fit_int4sym(const float x[4], const bool keep[4], RowOut& o) {
+  constexpr int L = G / 4;
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (keep[i]) a = fmaxf(a, __builtin_fabsf(x[i]));
+  a = group_max<L>(a);
+  const uint32_t sh = f32_to_half_bits(fmaxf(a / 7.0f, 1e-5f));
+  const float S = half_bits_to_f32(sh);
+  const uint32_t zh = f32_to_half_bits(-8.0f * S);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float xx = keep[i] ? x[i] : 0.0f;
+    o.code[i] = (uint32_t)((int)fminf(fmaxf(__builtin_rintf(xx / S), -8.0f), 7.0f) + 8);
+  }
+  o.meta[0] = sh | (zh << 16);
+  o.meta[1] = 0;
+}
+
+// Uniform 2-bit codebook ("Hierarchical Token Routing and Sub-2-Bit Non-Linear KV Compression
+// ...", the compress_kv_head listing): the group's values with the outlier slots set to 0, 4
+// centroids linspace(min, max) formed as torch.linspace does (step fl32((max - min) / 3); min,
+// min + step, max - step, max), fp16 centroids, nearest centroid (first index on ties).
+template <int G>
+__device__ void fit_u2(const float x[4], const bool keep[4], RowOut& o) {
+  constexpr int L = G / 4;
+  float xx[4], mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    xx[i] = keep[i] ? x[i] : 0.0f;
+    mn = fminf(mn, xx[i]);
+    mx = fmaxf(mx, xx[i]);
+  }
+  mn = group_min<L>(mn) + 0.0f;  // a zero end is taken as +0
+  mx = group_max<L>(mx) + 0.0f;
+  const float step = (mx - mn) / 3.0f;
+  const float c[4] = {mn, mn + step, mx - step, mx};
+  uint32_t hb[4];
+  float ch[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) { hb[j] = f32_to_half_bits(c[j]); ch[j] = half_bits_to_f32(hb[j]); }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o.code[i] = nearest4(xx[i], ch);
+  o.meta[0] = hb[0] | (hb[1] << 16);
+  o.meta[1] = hb[2] | (hb[3] << 16);
 }
 
 // 2-bit centroids: seeds at ranks floor((2j+1) n / 8) of the sorted non-outliers, then
@@ -341,9 +393,15 @@ __global__ void __launch_bounds__(64 * NW) quantize_append_kernel(QArgs a) {
     } else {
       bool keep[4] = {true, true, true, true};
       if (a.outl != KVQ_OUTL_NONE) outlier_flags<G>(x, a.tau2, keep);
-      if constexpr (FMT == FMT_INT4) fit_int4<G>(x, keep, o);
-      else if constexpr (FMT == FMT_FP4) fit_fp4<G>(x, keep, o);
-      else fit_c2<G>(x, keep, jg, a.lloyd, o);
+      if constexpr (FMT == FMT_INT4) {
+        if (a.fit == kFitSym) fit_int4sym<G>(x, keep, o);
+        else fit_int4<G>(x, keep, o);
+      } else if constexpr (FMT == FMT_FP4) {
+        fit_fp4<G>(x, keep, o);
+      } else {
+        if (a.fit == kFitUniform) fit_u2<G>(x, keep, o);
+        else fit_c2<G>(x, keep, jg, a.lloyd, o);
+      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) o.flag[e] = keep[e] ? 0u : 1u;
     }
@@ -477,6 +535,7 @@ hipError_t launch_quantize_append(const QuantizeLaunch& q, hipStream_t st) {
   qa.outl = q.outl;
   qa.tau2 = q.tau2;
   qa.lloyd = q.lloyd;
+  qa.fit = q.fit;
   const int nlists = q.L.B * q.L.H * 2;
   switch (q.fmt) {
     case FMT_INT4: return q.group == 32 ? launch_quantize_t<FMT_INT4, 32>(qa, nlists, q.max_new, st)

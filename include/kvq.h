@@ -37,6 +37,16 @@
  *    ``lloyd_iters`` Lloyd iterations.  value = centroid[code].
  *  - FP8_E4M3_ROW: codes E4M3(x / s), one fp32 scale s = absmax / 448 per row (4 bytes), no
  *    outliers.  value = e4m3(code) * s.
+ *  - Format variants (contiguous caches only), laid out exactly like their base format and
+ *    decoded by the same kernels; only the quantizer's fit differs:
+ *    UNIFORM2 (as CENTROID2, g = 64): the uniform codebook of the compress_kv_head listing of
+ *    the "Hierarchical Token Routing ..." page: with the outlier slots set to 0, centroids
+ *    min, min + step, max - step, max of the group (step = fl32((max - min) / 3), torch's
+ *    linspace), fp16, nearest centroid with the first index on ties;
+ *    INT4_SYM (as INT4_ASYM, g = 32 or 64): the symmetric INT4 of the quantize_kv_cache_fp4
+ *    listing of "The Sub-10ms Barrier ..." page, section "2. FP4/INT4 KV-Cache Quantization":
+ *    S = fp16(max(absmax / 7, 1e-5)) over the non-outliers, code = clamp(rint(x / S), -8, 7) + 8,
+ *    z = fp16(-8 S).
  *  Codes are packed LSB-first along the channel axis (2-bit: channel 4k+r in bits 2r..2r+1 of
  *  byte k; 4-bit: channel 2k in bits 0-3, 2k+1 in bits 4-7 of byte k).
  *
@@ -71,7 +81,9 @@ typedef enum {
   KVQ_FMT_INT4_ASYM = 2,
   KVQ_FMT_FP4_E2M1 = 3,
   KVQ_FMT_CENTROID2 = 4,
-  KVQ_FMT_BF16 = 5           /* unquantized, for kvq_kv_bytes only */
+  KVQ_FMT_BF16 = 5,          /* unquantized, for kvq_kv_bytes only */
+  KVQ_FMT_UNIFORM2 = 6,      /* variant: stored and decoded as CENTROID2 */
+  KVQ_FMT_INT4_SYM = 7       /* variant: stored and decoded as INT4_ASYM */
 } kvq_format;
 
 typedef enum { KVQ_OUTL_NONE = 0, KVQ_OUTL_FP16 = 1, KVQ_OUTL_FP8_E4M3 = 2 } kvq_outlier_dtype;
@@ -79,9 +91,11 @@ typedef enum { KVQ_OUTL_NONE = 0, KVQ_OUTL_FP16 = 1, KVQ_OUTL_FP8_E4M3 = 2 } kvq
 /* Problem description (the pages' GQA heads H, head dim D, context S, batch B, group size,
  * bit width via the format, and outlier threshold tau).  Constraints checked on the host:
  * head_dim == 128; num_q_heads % num_kv_heads == 0 with 1 <= num_q_heads/num_kv_heads <= 16;
- * group_size in {32, 64} dividing head_dim (INT4 / FP4: 32 or 64; CENTROID2: 64);
+ * group_size in {32, 64} dividing head_dim (INT4 / FP4 / INT4_SYM: 32 or 64; CENTROID2 / UNIFORM2:
+ * 64);
  * max_seq_len >= 1; outlier_sigma > 0; lloyd_iters in [0, 64]; page_size 0 (contiguous) or 16
- * (paged, tiered: tier 2 = ``format``, tier 1 = FP8_E4M3_ROW; only CENTROID2 tier 2). */
+ * (paged, tiered: tier 2 = ``format``, tier 1 = FP8_E4M3_ROW; only CENTROID2 tier 2).
+ * Every entry point accepts the format variants and treats their buffers as the base format's. */
 typedef struct {
   int32_t batch;
   int32_t num_q_heads;

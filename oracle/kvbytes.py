@@ -17,6 +17,8 @@ BYTES_PER_ROW = {  # D = head dimension, g = group size
     "fp4": lambda D, g: D // 2 + (D // g) * 1,    # codes + E4M3 scale per group
     "c2": lambda D, g: D // 4 + (D // g) * 8,     # codes + 4 fp16 centroids per group
     "fp8row": lambda D, g: D + 4,                 # codes + fp32 scale per row
+    "u2": lambda D, g: D // 4 + (D // g) * 8,     # uniform 2-bit: stored like c2
+    "int4s": lambda D, g: D // 2 + (D // g) * 4,  # symmetric INT4: stored like int4
 }
 OUTLIER_VALUE_BYTES = {"none": 0, "fp16": 2, "e4m3": 1}
 

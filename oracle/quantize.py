@@ -13,7 +13,17 @@ Pages cited (titles abridged):
   [P4] "The Sub-10ms Barrier: Fusing Sparse MoE Routing with FP4 KV-Cache Quantization",
        section "2. FP4/INT4 KV-Cache Quantization" (the equations Q = Round(Clamp(X/Scale +
        ZeroPoint, Min, Max)) and S = (max - min)/(2^b - 1), groups of 32 or 64 along the head
-       dimension, E2M1).
+       dimension, E2M1) and the ``quantize_kv_cache_fp4`` listing of the same section
+       (symmetric INT4: absmax/7 scale clamped at 1e-5, round, clamp to [-8, 7]).
+
+Format variants (stored like their base formats, decoded by the same kernels):
+  * "u2": the [P1] listing's uniform codebook, linspace(min, max, 4) over the group's slots with
+    the outlier slots zero-filled (the listing's residuals), as torch.linspace forms it (the
+    first two points from min, the last two from max, step fl32((max - min) / 3)); stored and
+    decoded as "c2" (4 fp16 centroids per group of 64);
+  * "int4s": the [P4] listing's symmetric INT4, stored as "int4" with scale S = fp16(max(absmax
+    / 7, 1e-5)) over the non-outliers, zero -8 S, code = Clamp(Round(x / S), -8, 7) + 8 (the
+    fp16 scale is the one that divides, so that the stored scale reproduces the codes).
 
 Readings taken where the pages are silent (each is listed in the design doc):
   * every quantity that decides a code is computed in float32 with IEEE round-to-nearest-even,
@@ -48,9 +58,9 @@ from . import formats as F
 
 F32 = np.float32
 
-FORMATS = ("int4", "fp4", "c2", "fp8row")
+FORMATS = ("int4", "fp4", "c2", "fp8row", "u2", "int4s")
 OUTLIER_DTYPES = ("none", "fp16", "e4m3")
-CODE_BITS = {"int4": 4, "fp4": 4, "c2": 2, "fp8row": 8}
+CODE_BITS = {"int4": 4, "fp4": 4, "c2": 2, "fp8row": 8, "u2": 2, "int4s": 4}
 
 
 @dataclass(frozen=True)
@@ -71,7 +81,7 @@ def meta_bytes_per_row(spec: QuantSpec, D: int) -> int:
     if spec.fmt == "fp8row":
         return 4
     ng = D // spec.group
-    return ng * {"int4": 4, "fp4": 1, "c2": 8}[spec.fmt]
+    return ng * {"int4": 4, "fp4": 1, "c2": 8, "u2": 8, "int4s": 4}[spec.fmt]
 
 
 def code_bytes_per_row(spec: QuantSpec, D: int) -> int:
@@ -126,6 +136,38 @@ def _fit_int4(xg, keep):
     q = np.where(s_h[..., None] > 0, q, 0).astype(np.uint8)
     meta = np.stack([F.fp16_bits(s_h), F.fp16_bits(z_h)], axis=-1)  # [..., ng, 2] uint16
     return q, meta.view(np.uint8).reshape(*xg.shape[:-2], -1)
+
+
+def _fit_int4s(xg, keep):
+    """[P4] listing ``quantize_kv_cache_fp4``: symmetric scale absmax/7 clamped at 1e-5 (here
+    rounded to the fp16 that is stored), codes Clamp(Round(x / S), -8, 7) offset by 8; stored
+    as INT4 with zero -8 S, so that code * S + zero = (code - 8) * S."""
+    a = np.max(np.where(keep, np.abs(xg), F32(0.0)), axis=-1).astype(F32)
+    s = np.maximum((a / F32(7.0)).astype(F32), F32(1e-5)).astype(F32)
+    s_h = F.fp16_round(s)
+    z_h = F.fp16_round((F32(-8.0) * s_h).astype(F32))
+    xx = np.where(keep, xg, F32(0.0)).astype(F32)
+    y = (xx / s_h[..., None]).astype(F32)
+    q = np.clip(np.rint(y), F32(-8.0), F32(7.0)).astype(np.int32) + 8
+    meta = np.stack([F.fp16_bits(s_h), F.fp16_bits(z_h)], axis=-1)
+    return q.astype(np.uint8), meta.view(np.uint8).reshape(*xg.shape[:-2], -1)
+
+
+def _fit_u2(xg, keep):
+    """[P1] listing: residuals = the values with the outlier slots set to 0; centroids =
+    linspace(min, max, 4) of the residuals (here per group of g channels, the "block" of the
+    listing's comment); code = argmin |residual - centroid| (first index on ties).  linspace as
+    torch forms it: step = fl32((max - min) / 3), points min, min + step, max - step, max."""
+    xx = np.where(keep, xg, F32(0.0)).astype(F32)
+    mn = (np.min(xx, axis=-1).astype(F32) + F32(0.0)).astype(F32)   # a zero end is +0
+    mx = (np.max(xx, axis=-1).astype(F32) + F32(0.0)).astype(F32)
+    step = ((mx - mn).astype(F32) / F32(3.0)).astype(F32)
+    c = np.stack([mn, (mn + step).astype(F32), (mx - step).astype(F32), mx], axis=-1)
+    c_h = F.fp16_round(c)
+    g = xg.shape[-1]
+    codes = _nearest(xx.reshape(-1, g), c_h.reshape(-1, 4)).astype(np.uint8).reshape(xg.shape)
+    meta = F.fp16_bits(c_h)   # [..., ng, 4] uint16
+    return codes, meta.view(np.uint8).reshape(*xg.shape[:-2], -1)
 
 
 def _fit_fp4(xg, keep):
@@ -248,8 +290,12 @@ def quantize_rows(x: np.ndarray, spec: QuantSpec) -> QuantRows:
     keep = ~mask_g
     if spec.fmt == "int4":
         codes, meta = _fit_int4(xg, keep)
+    elif spec.fmt == "int4s":
+        codes, meta = _fit_int4s(xg, keep)
     elif spec.fmt == "fp4":
         codes, meta = _fit_fp4(xg, keep)
+    elif spec.fmt == "u2":
+        codes, meta = _fit_u2(xg, keep)
     else:
         codes, meta = _fit_c2(xg, keep, spec.lloyd_iters)
     codes = codes.reshape(R, D)
@@ -285,7 +331,7 @@ def dequantize_codes(codes: np.ndarray, meta: np.ndarray, spec: QuantSpec) -> np
     g = spec.group
     ng = D // g
     cg = codes.reshape(R, ng, g)
-    if spec.fmt == "int4":
+    if spec.fmt in ("int4", "int4s"):
         sz = F.fp16_from_bits(meta.view(np.uint16).reshape(R, ng, 2))
         out = cg * sz[..., 0:1] + sz[..., 1:2]
     elif spec.fmt == "fp4":

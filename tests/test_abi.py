@@ -114,3 +114,24 @@ def test_null_pointers_rejected_before_launch():
 def test_status_strings():
     for s in (0, -1, -2, -3, -4, -5):
         assert K.kvq_status_string(s) != "unknown status"
+
+
+def test_format_variants_size_and_check_like_their_base():
+    # uniform 2-bit is laid out as CENTROID2, symmetric INT4 as INT4_ASYM
+    for var, base, g, out in [("u2", "c2", 64, "e4m3"), ("int4s", "int4", 32, "fp16"),
+                              ("int4s", "int4", 64, "none")]:
+        pv = K.make_params(4, 32, 8, 1000, var, g, out)
+        pb = K.make_params(4, 32, 8, 1000, base, g, out)
+        sv, sb = K.kvq_cache_sizes(pv, 50), K.kvq_cache_sizes(pb, 50)
+        assert (sv.code_bytes_per_row, sv.meta_bytes_per_row, sv.codes, sv.meta, sv.outl_val) == \
+               (sb.code_bytes_per_row, sb.meta_bytes_per_row, sb.codes, sb.meta, sb.outl_val)
+        assert K.kvq_workspace_bytes(pv) == K.kvq_workspace_bytes(pb)
+        for L, T, n in [(1, 1, 0), (80, 12345, 678 if out != "none" else 0)]:
+            assert K.kvq_kv_bytes(pv, L, T, n) == KB.kv_bytes(var, L, 8, 128, T, g, n, out)
+    with pytest.raises(K.KvqError) as e:                       # uniform 2-bit: groups of 64 only
+        K.kvq_workspace_bytes(K.make_params(2, 8, 2, 100, "u2", 32, "e4m3"))
+    assert e.value.status == K.KVQ_ERR_UNSUPPORTED
+    with pytest.raises(K.KvqError) as e:                       # variants: contiguous caches only
+        K.kvq_workspace_bytes(K.make_params(2, 8, 2, 100, "u2", 64, "e4m3", page_size=16,
+                                            num_pages=9, num_pages_fp8=4, max_pages_per_seq=7))
+    assert e.value.status == K.KVQ_ERR_UNSUPPORTED

@@ -35,6 +35,13 @@ SMALL = {
     # tau = 1.5: crowded steps with more than 128 records per list (the kernel's slow path)
     "c2_dense_outliers": WD.variant(CONFIGS["c2_b16_s8k"], B=1, H=2, Hq=8, S=700, sigma=1.5),
     "fp4_dense_outliers": WD.variant(CONFIGS["fp4_b4_s128k"], B=1, H=1, Hq=8, S=650, sigma=1.5),
+    # format variants on the same kernels: uniform 2-bit codebook (stored as 2-bit centroids,
+    # MFMA decoder) and symmetric INT4 (stored as INT4, generic decoder), with and without
+    # outlier lists
+    "u2_small": WD.variant(CONFIGS["c2_b16_s8k"], B=2, H=2, Hq=8, S=900, fmt="u2"),
+    "int4s_small": WD.variant(CONFIGS["int4_b1_s1k"], B=2, S=650, fmt="int4s"),
+    "int4s_g64_noout": WD.variant(CONFIGS["int4_b1_s1k"], B=1, H=2, Hq=4, S=300, fmt="int4s",
+                                  group=64, outlier="none"),
     # tiered paged cache, variable lengths
     "tiered_small": WD.variant(CONFIGS["tiered_b32_paged"], B=3, H=2, Hq=8, S=3000,
                                S_range=(90, 3000), fp8_page_frac=0.3),

@@ -351,3 +351,99 @@ def test_int4_zero_minimum_is_positive_zero():
     q = Q.quantize_rows(x, Q.QuantSpec("int4", 32, "none"))
     z_bits = q.meta.view(np.uint16)[0, 1]
     assert z_bits == 0x0000
+
+
+# ----------------------------------------------------------------------------- format variants
+# Uniform 2-bit ([P1] listing: linspace(min, max, 4) of the residuals, argmin) and symmetric INT4
+# ([P4] listing quantize_kv_cache_fp4: absmax / 7 clamped at 1e-5, round, clamp to [-8, 7]).
+def test_u2_equally_spaced_values_are_exact():
+    # values 0, 1, 2, 3 in any order: the linspace is exactly the 4 values, every code is its value
+    rng = np.random.default_rng(21)
+    x = rng.permutation(np.repeat(np.arange(4, dtype=F32), 16))[None, :].astype(F32)
+    x = np.concatenate([x, x * F32(-0.5) + F32(10.0)], axis=1)   # second group: 10, 9.5, 9, 8.5
+    spec = Q.QuantSpec("u2", 64, "none")
+    q = Q.quantize_rows(x, spec)
+    assert np.array_equal(q.codes[0, :64], x[0, :64].astype(np.uint8))
+    assert np.array_equal(Q.dequantize_rows(q, spec)[0], x[0].astype(np.float64))
+    cent = F.fp16_from_bits(q.meta.view(np.uint16).reshape(2, 4))
+    assert cent[0].tolist() == [0.0, 1.0, 2.0, 3.0] and cent[1].tolist() == [8.5, 9.0, 9.5, 10.0]
+
+
+def test_u2_ends_are_min_and_max_of_the_zero_filled_residuals():
+    # the listing zero-fills outlier slots before taking min / max: with all non-outliers in
+    # [1, 2] and one outlier, the low end is 0, not 1
+    rng = np.random.default_rng(22)
+    x = rng.uniform(1.0, 2.0, 64).astype(F32)
+    x[17] = 500.0
+    spec = Q.QuantSpec("u2", 64, "fp16", sigma=3.0)
+    q = Q.quantize_rows(x[None, :], spec)
+    assert q.mask[0].tolist() == [i == 17 for i in range(64)]
+    cent = F.fp16_from_bits(q.meta.view(np.uint16).reshape(4))
+    kept = x[~q.mask[0]]
+    assert cent[0] == 0.0 and cent[3] == F.fp16_round(F32(kept.max()))
+    # without outlier isolation the ends are the plain min and max
+    q = Q.quantize_rows(x[None, :], Q.QuantSpec("u2", 64, "none"))
+    cent = F.fp16_from_bits(q.meta.view(np.uint16).reshape(4))
+    assert cent[0] == F.fp16_round(F32(x.min())) and cent[3] == F.fp16_round(F32(500.0))
+
+
+def test_u2_codes_are_nearest_centroids():
+    # invariant on random groups: each code's centroid is no farther than any other, and strictly
+    # nearer than every lower index (first index on ties); interior points within fp16 rounding
+    # of the exact thirds
+    rng = np.random.default_rng(23)
+    x = (rng.standard_normal((40, 128)) * rng.uniform(0.01, 50, (40, 1))).astype(F32)
+    spec = Q.QuantSpec("u2", 64, "none")
+    q = Q.quantize_rows(x, spec)
+    cent = F.fp16_from_bits(q.meta.view(np.uint16).reshape(40, 2, 4)).astype(np.float64)
+    for r in range(40):
+        for gi in range(2):
+            c = cent[r, gi]
+            lo, hi = float(x[r, 64 * gi:64 * gi + 64].min()), float(x[r, 64 * gi:64 * gi + 64].max())
+            for k, frac in enumerate((0.0, 1 / 3, 2 / 3, 1.0)):
+                assert abs(c[k] - (lo + frac * (hi - lo))) <= 2 ** -10 * max(abs(lo), abs(hi)) + 1e-30
+            for j in range(64):
+                v = float(x[r, 64 * gi + j])
+                code = int(q.codes[r, 64 * gi + j])
+                d = [abs(np.float32(v) - np.float32(ck)) for ck in c]
+                assert all(d[code] <= dk for dk in d)
+                assert all(d[code] < d[k] for k in range(code))
+
+
+def test_int4s_integer_grid_and_ties_to_even():
+    # absmax 7 gives S = 1: integers map to themselves (+8); halves round to even; -7.5 rounds
+    # to -8 (kept), 7.5 would round to 8 and clamp, but absmax 7 keeps it out of the group
+    g = np.array([-7, -6, -5, -4, -3, -2, -1, 0, 1, 2, 3, 4, 5, 6, 7, 0.5, 1.5, 2.5, -0.5, -1.5,
+                  -2.5, 6.5, -6.5, 3.25, -3.75, 0, 0, 0, 0, 0, 0, 0], dtype=F32)
+    x = np.tile(g, 4)[None, :]
+    spec = Q.QuantSpec("int4s", 32, "none")
+    q = Q.quantize_rows(x, spec)
+    want = np.array([-7, -6, -5, -4, -3, -2, -1, 0, 1, 2, 3, 4, 5, 6, 7, 0, 2, 2, 0, -2, -2, 6, -6,
+                     3, -4, 0, 0, 0, 0, 0, 0, 0]) + 8
+    assert np.array_equal(q.codes[0], np.tile(want, 4))
+    sz = F.fp16_from_bits(q.meta.view(np.uint16).reshape(4, 2))
+    assert sz[:, 0].tolist() == [1.0] * 4 and sz[:, 1].tolist() == [-8.0] * 4
+    assert np.array_equal(Q.dequantize_rows(q, spec)[0], np.tile(want - 8, 4).astype(np.float64))
+
+
+def test_int4s_clamp_and_bounds():
+    rng = np.random.default_rng(24)
+    spec = Q.QuantSpec("int4s", 64, "none")
+    # all-zero group: the scale clamps at 1e-5 (as fp16), every code is 8, the value 0
+    q = Q.quantize_rows(np.zeros((1, 128), F32), spec)
+    sz = F.fp16_from_bits(q.meta.view(np.uint16).reshape(2, 2))
+    assert sz[0, 0] == F.fp16_round(F32(1e-5)) and np.all(q.codes == 8)
+    assert not Q.dequantize_rows(q, spec).any()
+    # random groups: the absmax element maps to +-7, every value is within S/2 of its
+    # reconstruction, and the codes of -x are 16 - codes of x
+    x = (rng.standard_normal((30, 128)) * rng.uniform(0.1, 100, (30, 1))).astype(F32)
+    q, qn = Q.quantize_rows(x, spec), Q.quantize_rows(-x, spec)
+    S = F.fp16_from_bits(q.meta.view(np.uint16).reshape(30, 2, 2))[..., 0].astype(np.float64)
+    d = Q.dequantize_rows(q, spec)
+    for r in range(30):
+        for gi in range(2):
+            seg = slice(64 * gi, 64 * gi + 64)
+            a = np.argmax(np.abs(x[r, seg]))
+            assert abs(int(q.codes[r, seg][a]) - 8) == 7
+            assert np.all(np.abs(d[r, seg] - x[r, seg]) <= S[r, gi] / 2 * (1 + 2 ** -20))
+    assert np.array_equal(qn.codes.astype(int), 16 - q.codes.astype(int))
