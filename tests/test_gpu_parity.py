@@ -235,3 +235,80 @@ def test_decode_packed_chunks(name):
         for hq, o in ref.items():
             err = np.abs(got[b, hq] - o).max()
             assert err <= ATOL, f"{name} b={b} hq={hq} split={split}: max-abs {err}"
+
+
+PREFIX = {
+    # decode over a prefix of each list: lengths around the 16-token blocks and 32-token steps,
+    # with the lists' later tokens and outlier records present in the cache
+    "c2_g8": WD.variant(CONFIGS["c2_b64_s32k"], B=8, H=2, Hq=16, S=300),
+    "c2_g16": WD.variant(CONFIGS["c2_b64_s32k"], B=8, H=1, Hq=16, S=300),
+    "u2_g4": WD.variant(CONFIGS["c2_b16_s8k"], B=8, H=2, Hq=8, S=300, fmt="u2"),
+    "fp4_g8": WD.variant(CONFIGS["fp4_b4_s128k"], B=8, H=2, Hq=16, S=300),
+    "int4_g4": WD.variant(CONFIGS["int4_b1_s1k"], B=8, S=300),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PREFIX))
+def test_decode_prefix_lengths(name):
+    import dataclasses
+    from oracle import attention as OA
+    from gpu_util import dequant_from_device
+    w = PREFIX[name]
+    log(f"[gpu] prefix decode {name}")
+    dc = WD.build(w)
+    lens = np.array([1, 2, 15, 16, 17, 31, 33, 300], dtype=np.int32)[:w.B]
+    full = {(b, h): dequant_from_device(dc, b, h) for b in range(w.B) for h in range(w.H)}
+    dcp = dataclasses.replace(dc, seq_lens_host=lens, seq_lens=torch.from_numpy(lens).cuda())
+    sm = 1.0 / math.sqrt(w.D)
+    G_ = w.Hq // w.H
+    for split in (0, 64, 128):
+        got = run_decode(dcp, split_chunk=split, sm_scale=sm)
+        for b in range(w.B):
+            qf = OA.bf16_to_f64(dc.q_host[b])
+            for hq in range(w.Hq):
+                Kd, Vd = full[(b, hq // G_)]
+                ref = OA.attention_one(qf[hq], Kd[:lens[b]], Vd[:lens[b]], sm)
+                err = np.abs(got[b, hq] - ref).max()
+                assert err <= ATOL, f"{name} b={b} S={lens[b]} hq={hq} split={split}: max-abs {err}"
+
+
+def _special_rows(n_rep: int = 2):
+    """Rows that stress the fits: zeros, a constant, one spike, alternating signs, fp32
+    subnormals, large values, a value past the E4M3 range, fp16 rounding ties."""
+    rng = np.random.default_rng(99)
+    D = 128
+    rows = [np.zeros(D), np.full(D, 3.5), np.where(np.arange(D) == 7, 1000.0, 0.0),
+            np.where(np.arange(D) % 2 == 0, 1.0, -1.0), rng.standard_normal(D) * 1e-40,
+            rng.standard_normal(D) * 2e4, np.where(np.arange(D) == 100, 1e6, rng.standard_normal(D)),
+            (rng.integers(-64, 64, D) + 0.5) * 2.0 ** -10,
+            np.concatenate([np.full(64, -2.0), np.full(64, 5.0)])]
+    x = np.stack(rows * n_rep).astype(np.float32)
+    return x
+
+
+@pytest.mark.parametrize("fmt,group,outlier", [("c2", 64, "e4m3"), ("c2", 64, "none"),
+                                               ("u2", 64, "fp16"), ("int4", 32, "fp16"),
+                                               ("int4s", 64, "e4m3"), ("fp4", 32, "fp16")])
+def test_quantize_special_rows(fmt, group, outlier):
+    """Degenerate and extreme rows, appended in one call, are packed bit for bit like the
+    oracle's."""
+    import decode_attention_sub_amd as K
+    from oracle import cache as OC
+    from oracle import quantize as OQ
+    x = _special_rows()
+    n = x.shape[0]
+    w = WD.variant(CONFIGS["c2_b16_s8k"], B=1, H=1, Hq=4, S=n, fmt=fmt, group=group, outlier=outlier)
+    p = WD.make_params(w, 64)
+    cache = K.KVCache.allocate(p, 4096)
+    k = torch.from_numpy(x[None, None]).cuda()
+    v = torch.from_numpy(-x[None, None]).cuda()
+    zero = torch.zeros(1, dtype=torch.int32, device="cuda")
+    cnt = torch.full((1,), n, dtype=torch.int32, device="cuda")
+    K.kvq_quantize_append(p, cache, k, v, zero, cnt)
+    torch.cuda.synchronize()
+    assert cache.status() == 0
+    lens = np.array([n], dtype=np.int32)
+    dc = WD.DeviceCache(w, p, cache, lens, torch.from_numpy(lens).cuda(), None, None, None, None)
+    spec = OQ.QuantSpec(fmt, group, outlier, w.sigma, w.lloyd_iters)
+    for kv, rows in ((0, x), (1, -x)):
+        assert_list_equal(read_list(dc, 0, 0, kv), OC.build_list(rows, spec), f"{fmt} {outlier} kv={kv}")
