@@ -245,15 +245,20 @@ def main():
     for s in range(args.warmup):
         step(s)
     torch.cuda.synchronize()
-    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
+    # Two timed passes over the same K steps (new tokens of the later steps of the pass
+    # before).  The first has no event inside the loop and gives the step time; the second
+    # brackets every append and every decode with events and gives the decode kernel's time.
+    # With flushing, the step time is the sum of the per-step intervals of the second pass.
     g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     g0.record(stream)
     for i in range(args.steps):
-        step(args.warmup + i, evs[i])
+        step(args.warmup + i)
     g1.record(stream)
     torch.cuda.synchronize()
-    # with flushing, the steps are the event intervals (append + decode) without the flushes
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
     ms_step = (float(np.sum([e[2].elapsed_time(e[1]) for e in evs])) if flush
                else g0.elapsed_time(g1)) / args.steps
     dec_all = np.array([e[0].elapsed_time(e[1]) for e in evs])
