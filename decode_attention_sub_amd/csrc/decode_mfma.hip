@@ -11,11 +11,11 @@
 // the flash-attention reduction).
 //
 // Work unit: a workgroup of 12 waves (three per SIMD; 8 for paged caches) per (split-K chunk, KV
-// head, sequence).  Waves take 32-token steps of the chunk in turn.  Per step a lane owns (token,
-// 64-channel half row): it loads the packed codes and group metadata with 128-bit loads
-// (prefetched one or two steps ahead), expands them to fp16 in registers and writes the rows into
-// the wave's LDS tile; outlier
-// records of the step are written over their positions.  Scores are computed transposed,
+// head, sequence), or per several short chunks of one (KV head, sequence).  Waves take 32-token
+// steps of the chunk in turn.  Per step a lane owns (token, 64-channel half row): it loads the
+// packed codes and group metadata with 128-bit loads (prefetched one step ahead; 2-bit rows with
+// non-temporal loads, as they are read once), expands them to fp16 in registers and writes the
+// rows into the wave's LDS tile; outlier records of the step are written over their positions.  Scores are computed transposed,
 // S^T = K^ Q^T, with v_mfma_f32_16x16x32_f16 (16 tokens x 16 padded query rows), which leaves
 // every lane holding the probabilities of one query row for 4+4 tokens - exactly the B operand of
 // O^T = V^T P^T.  V^T operands come out of the LDS tile with ds_read_b64_tr_b16.  P is split into
