@@ -170,6 +170,9 @@ def main():
                     help="format variant stored like the workload's format (u2 for 2-bit "
                          "workloads, int4s for INT4 ones): same shapes and data, other quantizer fit")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--chan-mask", type=int, default=0,
+                    help="keep this many calibrated top channels per (KV head, K or V) as outlier "
+                         "records in every row (static channel mask) instead of the tau test")
     ap.add_argument("--flush", choices=("auto", "on", "off"), default="auto",
                     help="stream 1 GiB through the caches before every step (auto: when the "
                          "decode moves less than 768 MB)")
@@ -193,6 +196,8 @@ def main():
         if base != w.fmt:
             sys.exit(f"--fmt {args.fmt}: not a variant of the workload's format {w.fmt}")
         w = WD.variant(w, fmt=args.fmt)
+    if args.chan_mask:
+        w = WD.variant(w, chan_mask=args.chan_mask)
     torch.cuda.set_device(0)
     ceiling = read_ceiling_gbs()
     log(f"measured read ceiling {ceiling:.0f} GB/s")
@@ -284,7 +289,7 @@ def main():
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "H": w.H, "D": w.D,
                    "S": int(lens_h.max()), "format": w.fmt, "group": w.group,
                    "outliers": w.outlier, "tau": w.sigma, "split_chunk": split if split else "default",
-                   "layers": 1, "cache_flush_per_step": flush},
+                   "layers": 1, "cache_flush_per_step": flush, "channel_mask": w.chan_mask},
         "us_per_step_decode": round(dec_ms * 1e3, 2),
         "us_decode_p10_p50_p90": [round(float(np.percentile(dec_all, q)) * 1e3, 2) for q in (10, 50, 90)],
         "us_per_step": round(ms_step * 1e3, 2),

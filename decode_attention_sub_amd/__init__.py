@@ -41,7 +41,7 @@ class kvq_cache(C.Structure):
                 ("scale8", C.c_void_p * 2), ("outl_idx", C.c_void_p * 2),
                 ("outl_val", C.c_void_p * 2), ("outl_count", C.c_void_p),
                 ("outl_block_start", C.c_void_p), ("outl_capacity", C.c_int64),
-                ("status", C.c_void_p)]
+                ("status", C.c_void_p), ("chan_mask", C.c_void_p)]
 
 
 class kvq_cache_sizes_t(C.Structure):
@@ -140,7 +140,8 @@ class KVCache:
     struct: kvq_cache = None
 
     @classmethod
-    def allocate(cls, p: kvq_params, outl_capacity: int, device="cuda"):
+    def allocate(cls, p: kvq_params, outl_capacity: int, device="cuda", chan_mask=None):
+        """chan_mask: None, or a static channel mask as int32 [2, H, 4] (device) words."""
         import torch
         sz = kvq_cache_sizes(p, outl_capacity)
         u8 = dict(dtype=torch.uint8, device=device)
@@ -156,6 +157,10 @@ class KVCache:
         t["count"] = torch.zeros(sz.outl_count // 4, dtype=torch.int32, device=device)
         t["bstart"] = torch.zeros(sz.outl_block_start // 4, dtype=torch.int32, device=device)
         t["status"] = torch.zeros(1, dtype=torch.int32, device=device)
+        if chan_mask is not None:
+            assert chan_mask.dtype == torch.int32 and chan_mask.is_contiguous()
+            assert tuple(chan_mask.shape) == (2, p.num_kv_heads, 4)
+        t["chan_mask"] = chan_mask
         c = cls(p, outl_capacity, t)
         c.struct = kvq_cache(
             (C.c_void_p * 2)(_ptr(t["codes0"]), _ptr(t["codes1"])),
@@ -164,7 +169,8 @@ class KVCache:
             (C.c_void_p * 2)(_ptr(t["scale8_0"]), _ptr(t["scale8_1"])),
             (C.c_void_p * 2)(_ptr(t["idx0"]), _ptr(t["idx1"])),
             (C.c_void_p * 2)(_ptr(t["val0"]), _ptr(t["val1"])),
-            _ptr(t["count"]), _ptr(t["bstart"]), outl_capacity, _ptr(t["status"]))
+            _ptr(t["count"]), _ptr(t["bstart"]), outl_capacity, _ptr(t["status"]),
+            _ptr(chan_mask))
         return c
 
     def status(self) -> int:

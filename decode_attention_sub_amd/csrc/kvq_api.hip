@@ -87,6 +87,7 @@ int32_t check_cache(const kvq_params* p, const kvq_cache* c) {
   }
   if (!c->outl_count || !c->outl_block_start) return KVQ_ERR_INVALID_ARG;
   if (p->outlier_dtype != KVQ_OUTL_NONE && c->outl_capacity < 1) return KVQ_ERR_INVALID_ARG;
+  if (c->chan_mask && p->outlier_dtype == KVQ_OUTL_NONE) return KVQ_ERR_INVALID_ARG;
   if (c->outl_capacity > (int64_t(1) << 28)) return KVQ_ERR_INVALID_ARG;  // 32-bit record offsets
   return KVQ_OK;
 }

@@ -392,7 +392,18 @@ __global__ void __launch_bounds__(64 * NW) quantize_append_kernel(QArgs a) {
       fit_fp8row(x, o);
     } else {
       bool keep[4] = {true, true, true, true};
-      if (a.outl != KVQ_OUTL_NONE) outlier_flags<G>(x, a.tau2, keep);
+      if (a.outl != KVQ_OUTL_NONE) {
+        if (a.cache.chan_mask) {   // static channel mask: the masked channels are the outliers
+          const uint32_t* mw = a.cache.chan_mask + ((size_t)kv * Lo.H + h) * (kHeadDim / 32);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int c = gi * G + jg + L * e;
+            keep[e] = ((mw[c >> 5] >> (c & 31)) & 1u) == 0u;
+          }
+        } else {
+          outlier_flags<G>(x, a.tau2, keep);
+        }
+      }
       if constexpr (FMT == FMT_INT4) {
         if (a.fit == kFitSym) fit_int4sym<G>(x, keep, o);
         else fit_int4<G>(x, keep, o);

@@ -128,7 +128,14 @@ typedef struct {
  *              each value).
  * status: one int32 the kernels set (first error wins) to KVQ_ERR_CAPACITY or
  *         KVQ_ERR_INVALID_ARG when a device-side check fails; the library never clears it.
- * Buffers may be uninitialised except outl_count / status (zero before first use). */
+ * Buffers may be uninitialised except outl_count / status (zero before first use).
+ * chan_mask: NULL for the tau test, or a static channel mask ("The Sub-10ms Barrier ...", section
+ *         "Key Production Engineering Takeaways", item 2: the top channels by absolute magnitude
+ *         kept at high precision): bit c % 32 of word [kv][h][c / 32] set = channel c of that
+ *         list's rows is kept as an outlier record (at outlier_dtype, which must not be NONE) in
+ *         every appended row, in place of the tau test; the fit runs on the other channels.
+ *         Read by kvq_quantize_append only; decoding needs nothing more (the records are
+ *         ordinary records). */
 typedef struct {
   void* codes[2];
   void* meta[2];
@@ -140,6 +147,7 @@ typedef struct {
   int32_t* outl_block_start;
   int64_t outl_capacity;
   int32_t* status;
+  const uint32_t* chan_mask; /* device [2][H][4] or NULL: see below */
 } kvq_cache;
 
 /* Byte sizes of every buffer of kvq_cache for these params (host only). */

@@ -23,7 +23,12 @@ Format variants (stored like their base formats, decoded by the same kernels):
     decoded as "c2" (4 fp16 centroids per group of 64);
   * "int4s": the [P4] listing's symmetric INT4, stored as "int4" with scale S = fp16(max(absmax
     / 7, 1e-5)) over the non-outliers, zero -8 S, code = Clamp(Round(x / S), -8, 7) + 8 (the
-    fp16 scale is the one that divides, so that the stored scale reproduces the codes).
+    fp16 scale is the one that divides, so that the stored scale reproduces the codes);
+  * static channel mask ([P4] "Key Production Engineering Takeaways", item 2: a reserved
+    high-precision mask of the top channels by absolute magnitude, kept in FP16): with
+    ``channels`` set, the outliers of every row are exactly those channels (instead of the tau
+    test), stored as records like any outlier, and the fit runs on the other channels;
+    ``top_channels`` picks the mask from calibration rows.
 
 Readings taken where the pages are silent (each is listed in the design doc):
   * every quantity that decides a code is computed in float32 with IEEE round-to-nearest-even,
@@ -70,11 +75,14 @@ class QuantSpec:
     outlier: str        # one of OUTLIER_DTYPES
     sigma: float = 3.0  # outlier threshold tau, in standard deviations
     lloyd_iters: int = 8
+    channels: tuple = ()  # static channel mask: these channels are the outliers of every row
 
     def __post_init__(self):
         assert self.fmt in FORMATS and self.outlier in OUTLIER_DTYPES
         if self.fmt == "fp8row":
             assert self.outlier == "none", "the FP8 tier keeps no outliers"
+        if self.channels:
+            assert self.outlier != "none", "a channel mask keeps its channels as records"
 
 
 def meta_bytes_per_row(spec: QuantSpec, D: int) -> int:
@@ -117,6 +125,14 @@ def outlier_mask(xg: np.ndarray, sigma: float) -> np.ndarray:
     lhs = (e * F32(g - 1)).astype(F32)
     rhs = (tau2 * q2).astype(F32)
     return lhs > rhs[..., None]
+
+
+def top_channels(x: np.ndarray, k: int) -> tuple:
+    """[P4] "Key Production Engineering Takeaways" item 2: the k channels of largest mean absolute
+    value over calibration rows x [R, D] (float64 means; ties to the lower channel)."""
+    m = np.mean(np.abs(np.asarray(x, dtype=np.float64)), axis=0)
+    order = sorted(range(m.shape[0]), key=lambda c: (-m[c], c))
+    return tuple(sorted(order[:k]))
 
 
 # ----------------------------------------------------------------------------- fits
@@ -285,6 +301,10 @@ def quantize_rows(x: np.ndarray, spec: QuantSpec) -> QuantRows:
     xg = x.reshape(R, D // g, g)
     if spec.outlier == "none":
         mask_g = np.zeros(xg.shape, dtype=bool)
+    elif spec.channels:
+        chan = np.zeros(D, dtype=bool)
+        chan[list(spec.channels)] = True
+        mask_g = np.broadcast_to(chan.reshape(D // g, g), xg.shape).copy()
     else:
         mask_g = outlier_mask(xg, spec.sigma)
     keep = ~mask_g

@@ -9,6 +9,7 @@ Test infrastructure: it calls the oracle and the seeded generators only."""
 
 from __future__ import annotations
 
+import dataclasses
 import math
 import os
 import sys
@@ -23,7 +24,8 @@ from oracle import quantize as OQ           # noqa: E402
 from workloads import CONFIGS               # noqa: E402
 from workloads import generate as G         # noqa: E402
 
-# (label, format, group, outlier dtype): the workloads' formats and the variants stored like them
+# (label, format, group, outlier dtype[, static mask channels]): the workloads' formats and the
+# variants stored like them
 FORMATS = [
     ("2-bit centroids, Lloyd (c2)", "c2", 64, "e4m3"),
     ("2-bit uniform linspace (u2)", "u2", 64, "e4m3"),
@@ -33,6 +35,8 @@ FORMATS = [
     ("INT4 symmetric g32 (int4s)", "int4s", 32, "fp16"),
     ("INT4 symmetric g32, no outliers", "int4s", 32, "none"),
     ("FP4 E2M1 g32 (fp4)", "fp4", 32, "fp16"),
+    ("2-bit centroids, 2-channel fp16 mask", "c2", 64, "fp16", 2),
+    ("INT4 asymmetric g32, 4-channel fp16 mask", "int4", 32, "fp16", 4),
 ]
 
 
@@ -50,16 +54,20 @@ def measure(workload: str = "c2_b64_s32k", slices: int = 4, tokens: int = 2048, 
         ref = np.stack([OA.attention_one(q[i], x[0].astype(np.float64), x[1].astype(np.float64), sm)
                         for i in range(G_)])
         data.append((x, q, ref))
-    for label, fmt, g, out in formats:
-        spec = OQ.QuantSpec(fmt, g, out, w.sigma, w.lloyd_iters)
+    for label, fmt, g, out, *mask in formats:
+        wm = dataclasses.replace(w, chan_mask=mask[0]) if mask else w
+        spec_of = {(h, kv): OQ.QuantSpec(fmt, g, out, w.sigma, w.lloyd_iters,
+                                         channels=G.mask_channels(wm, h, kv) if mask else ())
+                   for _, h in picks for kv in (0, 1)}
         bits = 0
         se = [0.0, 0.0]
         ss = [0.0, 0.0]
         amax = 0.0
         rel = []
-        for x, q, ref in data:
+        for (b, h), (x, q, ref) in zip(picks, data):
             deq = []
             for kv in (0, 1):
+                spec = spec_of[(h, kv)]
                 ls = OC.build_list(x[kv], spec)
                 d = OC.dequantize_list(ls.codes, ls.meta, ls.idx, ls.vals, spec, D)
                 deq.append(d)
@@ -72,7 +80,8 @@ def measure(workload: str = "c2_b64_s32k", slices: int = 4, tokens: int = 2048, 
             amax = max(amax, float(np.max(np.abs(o - ref))))
             rel.append(float(np.sqrt(np.sum((o - ref) ** 2) / np.sum(ref ** 2))))
         n_el = 2 * len(data) * tokens * D
-        rows.append(dict(label=label, fmt=fmt, group=g, outlier=out, bits_per_element=bits / n_el,
+        rows.append(dict(label=label, fmt=fmt, group=g, outlier=out, mask=mask[0] if mask else 0,
+                         bits_per_element=bits / n_el,
                          k_rel_rmse=math.sqrt(se[0] / ss[0]), v_rel_rmse=math.sqrt(se[1] / ss[1]),
                          attn_max_abs=amax, attn_rel_rms=float(np.mean(rel))))
     return rows

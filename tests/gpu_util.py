@@ -24,15 +24,17 @@ def log(msg):
     sys.stdout.flush()
 
 
-def specs(w):
-    spec = OQ.QuantSpec(w.fmt, w.group, w.outlier, w.sigma, w.lloyd_iters)
+def specs(w, h: int = 0, kv: int = 0):
+    """Oracle specs of list (h, kv) of workload w (a static channel mask differs per list)."""
+    chans = G.mask_channels(w, h, kv) if w.chan_mask else ()
+    spec = OQ.QuantSpec(w.fmt, w.group, w.outlier, w.sigma, w.lloyd_iters, channels=chans)
     spec8 = OQ.QuantSpec("fp8row", 0, "none") if w.paged else None
     return spec, spec8
 
 
 def oracle_list(w, b: int, h: int, kv: int, S: int, tier1_pages=None):
     x = G.kv_rows(w, b, h, kv, 0, S)
-    spec, spec8 = specs(w)
+    spec, spec8 = specs(w, h, kv)
     return OC.build_list(x, spec, tier1_pages, spec8)
 
 
@@ -64,9 +66,9 @@ def page_tiers_of(dc, b):
 def dequant_from_device(dc, b: int, h: int):
     """float64 K, V [S, D] of (b, h) decoded by the oracle from the device cache bytes."""
     w = dc.w
-    spec, spec8 = specs(w)
     res = []
     for kv in (0, 1):
+        spec, spec8 = specs(w, h, kv)
         g = read_list(dc, b, h, kv)
         codes = OQ.unpack_codes(g["packed"], OQ.CODE_BITS[w.fmt], w.D)
         codes8 = g.get("packed8")

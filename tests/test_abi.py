@@ -135,3 +135,19 @@ def test_format_variants_size_and_check_like_their_base():
         K.kvq_workspace_bytes(K.make_params(2, 8, 2, 100, "u2", 64, "e4m3", page_size=16,
                                             num_pages=9, num_pages_fp8=4, max_pages_per_seq=7))
     assert e.value.status == K.KVQ_ERR_UNSUPPORTED
+
+
+def test_channel_mask_needs_an_outlier_dtype():
+    import ctypes as C
+    import numpy as np
+    p = K.make_params(1, 4, 1, 64, "int4", 32, "none")
+    c = K.kvq_cache()
+    buf = (C.c_uint8 * 64)()
+    for kv in range(2):
+        c.codes[kv] = c.meta[kv] = C.cast(buf, C.c_void_p)
+    c.outl_count = c.outl_block_start = C.cast(buf, C.c_void_p)
+    mask = np.zeros(8, np.uint32)
+    c.chan_mask = mask.ctypes.data
+    st = K._lib.kvq_quantize_append(C.byref(p), C.byref(c), C.cast(buf, C.c_void_p), C.cast(buf, C.c_void_p),
+                                    1, C.cast(buf, C.c_void_p), C.cast(buf, C.c_void_p), None, None)
+    assert st == K.KVQ_ERR_INVALID_ARG

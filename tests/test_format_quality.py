@@ -8,7 +8,8 @@ from format_quality import measure
 
 @pytest.mark.parametrize("workload", ["c2_b64_s32k", "c2_b16_s8k"])
 def test_format_error_orderings(workload):
-    r = {(x["fmt"], x["outlier"]): x for x in measure(workload, slices=2, tokens=512)}
+    r = {(x["fmt"], x["outlier"]) + ((x["mask"],) if x["mask"] else ()): x
+         for x in measure(workload, slices=2, tokens=512)}
     c2, u2 = r[("c2", "e4m3")], r[("u2", "e4m3")]
     # same storage, same bytes: the variants differ only in the fit
     assert c2["bits_per_element"] == u2["bits_per_element"]
@@ -28,3 +29,14 @@ def test_format_error_orderings(workload):
     # attention through 4-bit caches is closer to the unquantized result than through 2-bit ones
     for f in (("int4", "fp16"), ("int4s", "fp16"), ("fp4", "fp16")):
         assert r[f]["attn_rel_rms"] < c2["attn_rel_rms"] < u2["attn_rel_rms"]
+
+
+def test_channel_mask_on_scaled_channels():
+    # on data whose lists each have 4 channels scaled x20, keeping those 4 channels as fp16
+    # records costs 4 x 6 bytes per row and leaves every other channel on the unscaled grid:
+    # the INT4 error drops below that of the tau-sigma isolation
+    r = {(x["fmt"], x["outlier"], x["mask"]): x for x in measure("int4_b1_s1k", slices=2, tokens=512)}
+    masked, tau = r[("int4", "fp16", 4)], r[("int4", "fp16", 0)]
+    assert masked["bits_per_element"] > tau["bits_per_element"]
+    assert masked["k_rel_rmse"] < tau["k_rel_rmse"] and masked["v_rel_rmse"] < tau["v_rel_rmse"]
+    assert masked["attn_rel_rms"] < tau["attn_rel_rms"]

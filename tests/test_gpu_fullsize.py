@@ -27,7 +27,7 @@ EDGE = 160   # tokens checked bit for bit at each end of a sampled list (multipl
 def check_rows(dc, b, h, kv, ta, tb, dev):
     """Device rows [ta, tb) of list (b, h, kv) and their outlier records == the oracle's."""
     w = dc.w
-    spec, spec8 = specs(w)
+    spec, spec8 = specs(w, h, kv)
     x = G.kv_rows(w, b, h, kv, ta, tb)
     tiers = page_tiers_of(dc, b)
     tp = None if tiers is None else tiers[ta // 16:(tb + 15) // 16]

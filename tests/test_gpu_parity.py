@@ -42,6 +42,11 @@ SMALL = {
     "int4s_small": WD.variant(CONFIGS["int4_b1_s1k"], B=2, S=650, fmt="int4s"),
     "int4s_g64_noout": WD.variant(CONFIGS["int4_b1_s1k"], B=1, H=2, Hq=4, S=300, fmt="int4s",
                                   group=64, outlier="none"),
+    # static channel mask (top channels by magnitude kept as fp16 records in every row): INT4 on
+    # the data with 4 channels x20 per list, 2-bit on the LogNormal-channel keys
+    "int4_chanmask": WD.variant(CONFIGS["int4_b1_s1k"], B=2, S=600, chan_mask=4),
+    "c2_chanmask": WD.variant(CONFIGS["c2_b64_s32k"], B=2, H=2, Hq=16, S=700, chan_mask=2,
+                              outlier="fp16"),
     # tiered paged cache, variable lengths
     "tiered_small": WD.variant(CONFIGS["tiered_b32_paged"], B=3, H=2, Hq=8, S=3000,
                                S_range=(90, 3000), fp8_page_frac=0.3),

@@ -447,3 +447,52 @@ def test_int4s_clamp_and_bounds():
             assert abs(int(q.codes[r, seg][a]) - 8) == 7
             assert np.all(np.abs(d[r, seg] - x[r, seg]) <= S[r, gi] / 2 * (1 + 2 ** -20))
     assert np.array_equal(qn.codes.astype(int), 16 - q.codes.astype(int))
+
+
+# ----------------------------------------------------------------------------- channel mask
+# [P4] "Key Production Engineering Takeaways" item 2: a static mask of the top channels by
+# absolute magnitude kept at high precision.
+def test_channel_mask_records_exactly_the_masked_channels():
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal((20, 128)).astype(F32)
+    x[:, 77] *= 300.0
+    for fmt, g, out in [("int4", 32, "fp16"), ("c2", 64, "fp16"), ("fp4", 32, "e4m3")]:
+        spec = Q.QuantSpec(fmt, g, out, channels=(3, 77))
+        q = Q.quantize_rows(x, spec)
+        assert np.array_equal(np.nonzero(q.mask.any(axis=0))[0], [3, 77]) and q.mask[:, [3, 77]].all()
+        d = Q.dequantize_rows(q, spec)
+        want = F.fp16_round(x[:, [3, 77]]) if out == "fp16" else F.e4m3_decode(F.e4m3_encode(x[:, [3, 77]]))
+        assert np.array_equal(d[:, [3, 77]], want.astype(np.float64))
+        # the fit ignores the masked channels: other values there change no other code or metadata
+        y = x.copy()
+        y[:, [3, 77]] = rng.standard_normal((20, 2)).astype(F32) * 1e4
+        qy = Q.quantize_rows(y, spec)
+        keep = np.ones(128, bool)
+        keep[[3, 77]] = False
+        assert np.array_equal(qy.codes[:, keep], q.codes[:, keep]) and np.array_equal(qy.meta, q.meta)
+
+
+def test_top_channels_finds_the_scaled_channels():
+    from workloads import CONFIGS
+    from workloads import generate as G
+    w = CONFIGS["int4_b1_s1k"]   # 4 channels per (KV head, K or V) scaled x20
+    for h in range(w.H):
+        for kind in (G.K, G.V):
+            heavy = tuple(int(c) for c in np.nonzero(G._head_constants(w, h, kind) == 20.0)[0])
+            assert Q.top_channels(G.kv_rows(w, 0, h, kind, 0, 256), 4) == heavy
+    # ties go to the lower channels; k larger than the distinct maxima
+    z = np.ones((4, 128), F32)
+    z[:, 9] = 2.0
+    assert Q.top_channels(z, 3) == (0, 1, 9)
+
+
+def test_calibrated_mask_matches_top_channels():
+    # the workloads' calibration (what a caller does once) picks the oracle's top channels
+    from workloads import CONFIGS
+    from workloads import device as WD
+    from workloads import generate as G
+    for name, k in [("int4_b1_s1k", 4), ("c2_b64_s32k", 2)]:
+        w = WD.variant(CONFIGS[name], chan_mask=k)
+        for h in range(min(w.H, 3)):
+            for kind in (G.K, G.V):
+                assert G.mask_channels(w, h, kind) == Q.top_channels(G.kv_rows(w, 0, h, kind, 0, 256), k)

@@ -33,6 +33,8 @@ class Workload:
     fp8_page_frac: float = 0.0
     split_chunk: int = 0         # tokens per split-K chunk (0: library default)
     lloyd_iters: int = 8
+    chan_mask: int = 0           # >0: static mask of this many channels per (KV head, K or V)
+                                 # kept as outlier records in every row (see generate.py)
 
 
 CONFIGS = {

@@ -78,7 +78,16 @@ def build(w: Workload, S_cap: Optional[int] = None, device: str = "cuda",
         bt = torch.from_numpy(bt_host).to(device)
     p = make_params(w, S_cap, n2, n1, max_pages)
     cap = max_outliers_per_row(w.D, w.group, w.sigma) * S_cap
-    cache = K.KVCache.allocate(p, cap, device)
+    mask = None
+    if w.chan_mask:
+        assert w.chan_mask <= max_outliers_per_row(w.D, w.group, w.sigma)
+        words = np.zeros((2, w.H, w.D // 32), dtype=np.uint32)
+        for kv in (0, 1):
+            for h in range(w.H):
+                for c in G.mask_channels(w, h, kv):
+                    words[kv, h, c // 32] |= np.uint32(1) << np.uint32(c % 32)
+        mask = torch.from_numpy(words.view(np.int32)).to(device)
+    cache = K.KVCache.allocate(p, cap, device, chan_mask=mask)
     lens_t = torch.from_numpy(lens).to(device)
     with ThreadPoolExecutor(threads) as pool:
         for t0 in range(0, S_max, FILL_CHUNK):

@@ -69,6 +69,16 @@ def kv_rows(w: Workload, b: int, h: int, kind: int, t0: int, t1: int) -> np.ndar
     return out
 
 
+def mask_channels(w: Workload, h: int, kind: int, calib_tokens: int = 256) -> tuple:
+    """Static channel mask of a (KV head, K or V) list: the ``w.chan_mask`` channels of largest
+    mean |x| over the first ``calib_tokens`` rows of sequence 0 (float64 means, ties to the lower
+    channel), as a caller would calibrate it once."""
+    x = kv_rows(w, 0, h, K if kind in (K, NEW_K) else V, 0, calib_tokens).astype(np.float64)
+    m = np.abs(x).mean(axis=0)
+    order = np.lexsort((np.arange(w.D), -m))
+    return tuple(sorted(int(c) for c in order[:w.chan_mask]))
+
+
 def new_rows(w: Workload, b: int, h: int, kind: int, step: int, n: int = 1) -> np.ndarray:
     """Rows appended at decode step ``step`` (kind 3 = keys, 4 = values)."""
     return _chunk(w, b, h, kind, step, n)
