@@ -151,3 +151,56 @@ def test_channel_mask_needs_an_outlier_dtype():
     st = K._lib.kvq_quantize_append(C.byref(p), C.byref(c), C.cast(buf, C.c_void_p), C.cast(buf, C.c_void_p),
                                     1, C.cast(buf, C.c_void_p), C.cast(buf, C.c_void_p), None, None)
     assert st == K.KVQ_ERR_INVALID_ARG
+
+
+def _fake_cache(nbytes=256):
+    """A kvq_cache whose pointers are host memory: only for calls that the host checks reject
+    before any launch."""
+    import ctypes as C
+    buf = (C.c_uint8 * nbytes)()
+    c = K.kvq_cache()
+    ptr = C.cast(buf, C.c_void_p)
+    for kv in range(2):
+        c.codes[kv] = c.meta[kv] = c.outl_idx[kv] = c.outl_val[kv] = ptr
+    c.outl_count = c.outl_block_start = c.status = ptr
+    c.outl_capacity = 8
+    return c, buf, ptr
+
+
+def test_decode_host_checks_reject_before_launch():
+    import ctypes as C
+    c, buf, ptr = _fake_cache()
+    p = K.make_params(2, 8, 2, 1000, "c2", 64, "e4m3")
+    dec = K._lib.kvq_decode_attention
+    # split into chunks of 128 tokens needs a workspace: none, then one byte too small
+    need = K.kvq_workspace_bytes(p, 128)
+    assert need > 0
+    assert dec(C.byref(p), C.byref(c), ptr, ptr, None, C.c_float(0.1), 128, ptr, None, 0, None) \
+        == K.KVQ_ERR_WORKSPACE
+    assert dec(C.byref(p), C.byref(c), ptr, ptr, None, C.c_float(0.1), 128, ptr, ptr, need - 1, None) \
+        == K.KVQ_ERR_WORKSPACE
+    # split chunk not a multiple of 64, non-finite softmax scale, missing query / output
+    assert dec(C.byref(p), C.byref(c), ptr, ptr, None, C.c_float(0.1), 100, ptr, ptr, need, None) \
+        == K.KVQ_ERR_INVALID_ARG
+    assert dec(C.byref(p), C.byref(c), ptr, ptr, None, C.c_float(float("inf")), 0, ptr, ptr, need, None) \
+        == K.KVQ_ERR_INVALID_ARG
+    assert dec(C.byref(p), C.byref(c), None, ptr, None, C.c_float(0.1), 0, ptr, ptr, need, None) \
+        == K.KVQ_ERR_INVALID_ARG
+    assert dec(C.byref(p), C.byref(c), ptr, ptr, None, C.c_float(0.1), 0, None, ptr, need, None) \
+        == K.KVQ_ERR_INVALID_ARG
+    # a paged cache needs its block table
+    pp = K.make_params(2, 8, 2, 100, "c2", 64, "e4m3", page_size=16, num_pages=9,
+                       num_pages_fp8=0, max_pages_per_seq=7)
+    assert dec(C.byref(pp), C.byref(c), ptr, ptr, None, C.c_float(0.1), 0, ptr, ptr, 1 << 20, None) \
+        == K.KVQ_ERR_INVALID_ARG
+
+
+def test_append_host_checks_reject_before_launch():
+    import ctypes as C
+    c, buf, ptr = _fake_cache()
+    p = K.make_params(2, 8, 2, 1000, "int4", 32, "fp16")
+    app = K._lib.kvq_quantize_append
+    assert app(C.byref(p), C.byref(c), ptr, ptr, 0, ptr, ptr, None, None) == K.KVQ_ERR_INVALID_ARG
+    assert app(C.byref(p), C.byref(c), None, ptr, 1, ptr, ptr, None, None) == K.KVQ_ERR_INVALID_ARG
+    c.outl_capacity = (1 << 28) + 1                            # record offsets are 32-bit
+    assert app(C.byref(p), C.byref(c), ptr, ptr, 1, ptr, ptr, None, None) == K.KVQ_ERR_INVALID_ARG
