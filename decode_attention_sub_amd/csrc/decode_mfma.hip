@@ -746,12 +746,12 @@ __global__ void __launch_bounds__(Shape<PAGED>::kWaves * 64) KVQ_OCC decode_mfma
   };
   // ---- software pipeline: codes and records of the next kPF steps in flight, the record
   // bounds of the step after them too.  Wave wi of a chunk takes its full steps wi, wi + wpc, ...;
-  // whole groups
-  // of NB steps run without conditions, so every ring slot keeps its registers and the wait
-  // counters stay exact.  Loads for steps past the chunk return zeros without touching memory.
+  // whole groups of NB steps run without conditions, so every ring slot keeps its registers and
+  // the wait counters stay exact.  Loads for steps past the chunk return zeros without touching
+  // memory.
   //
-  // Two waves share each SIMD and the scheduler favours the older one; every group, a wave that
-  // is ahead of its SIMD partner lowers its priority, so both finish together.
+  // Two or three waves share each SIMD and the scheduler favours the oldest; every group, a wave
+  // that is ahead of the slower of its SIMD peers lowers its priority, so all finish together.
   constexpr int NB = kPF + 1;  // ring slots
   Buf<FMT> buf[NB];
   Recs rec[NB];
