@@ -19,6 +19,7 @@ BYTES_PER_ROW = {  # D = head dimension, g = group size
     "fp8row": lambda D, g: D + 4,                 # codes + fp32 scale per row
     "u2": lambda D, g: D // 4 + (D // g) * 8,     # uniform 2-bit: stored like c2
     "int4s": lambda D, g: D // 2 + (D // g) * 4,  # symmetric INT4: stored like int4
+    "int3": lambda D, g: 3 * D // 8 + (D // g) * 4,  # 3-bit codes + fp16 scale and zero per group
 }
 OUTLIER_VALUE_BYTES = {"none": 0, "fp16": 2, "e4m3": 1}
 

@@ -49,6 +49,9 @@ Readings taken where the pages are silent (each is listed in the design doc):
   * INT4: offset form of the equation: zero = fp16(min), code = Round(Clamp((x - zero)/S, 0,
     15)), which is the page's ZeroPoint = -zero/S written without a quantized-unit zero; a zero
     min or max is taken as +0;
+  * INT3 ([P3] "Sub-Byte KV-Cache Quantization": asymmetric 3-bit packed codes beside the
+    outliers): the INT4 fit with b = 3 (S = (max - min)/7, codes 0..7), codes packed LSB-first
+    as one bit stream along the channels;
   * FP4: E4M3 block scale = absmax/6 (6 is the largest E2M1 magnitude);
   * FP8 tier: per-row scale absmax/448 in fp32, no outliers.
 """
@@ -63,9 +66,9 @@ from . import formats as F
 
 F32 = np.float32
 
-FORMATS = ("int4", "fp4", "c2", "fp8row", "u2", "int4s")
+FORMATS = ("int4", "fp4", "c2", "fp8row", "u2", "int4s", "int3")
 OUTLIER_DTYPES = ("none", "fp16", "e4m3")
-CODE_BITS = {"int4": 4, "fp4": 4, "c2": 2, "fp8row": 8, "u2": 2, "int4s": 4}
+CODE_BITS = {"int4": 4, "fp4": 4, "c2": 2, "fp8row": 8, "u2": 2, "int4s": 4, "int3": 3}
 
 
 @dataclass(frozen=True)
@@ -89,7 +92,7 @@ def meta_bytes_per_row(spec: QuantSpec, D: int) -> int:
     if spec.fmt == "fp8row":
         return 4
     ng = D // spec.group
-    return ng * {"int4": 4, "fp4": 1, "c2": 8, "u2": 8, "int4s": 4}[spec.fmt]
+    return ng * {"int4": 4, "fp4": 1, "c2": 8, "u2": 8, "int4s": 4, "int3": 4}[spec.fmt]
 
 
 def code_bytes_per_row(spec: QuantSpec, D: int) -> int:
@@ -136,19 +139,20 @@ def top_channels(x: np.ndarray, k: int) -> tuple:
 
 
 # ----------------------------------------------------------------------------- fits
-def _fit_int4(xg, keep):
-    """[P4] S = (max - min)/(2^b - 1) with b = 4 over the non-outliers; fp16 scale and zero."""
+def _fit_int4(xg, keep, levels: int = 15):
+    """[P4] S = (max - min)/(2^b - 1) with b = 4 (levels = 15; b = 3 for INT3: 7) over the
+    non-outliers; fp16 scale and zero."""
     # min / max are order-free; a zero result is taken as +0 so the stored fp16 bits are
     # defined (x + 0.0 maps -0.0 to +0.0 and leaves every other value unchanged)
     mn = (np.min(np.where(keep, xg, np.inf), axis=-1).astype(F32) + F32(0.0)).astype(F32)
     mx = (np.max(np.where(keep, xg, -np.inf), axis=-1).astype(F32) + F32(0.0)).astype(F32)
-    s = ((mx - mn).astype(F32) / F32(15.0)).astype(F32)
+    s = ((mx - mn).astype(F32) / F32(levels)).astype(F32)
     s_h = F.fp16_round(s)
     z_h = F.fp16_round(mn)
     xx = np.where(keep, xg, F32(0.0)).astype(F32)
     with np.errstate(divide="ignore", invalid="ignore"):
         y = ((xx - z_h[..., None]).astype(F32) / s_h[..., None]).astype(F32)
-    q = np.rint(np.clip(y, F32(0.0), F32(15.0)))
+    q = np.rint(np.clip(y, F32(0.0), F32(levels)))
     q = np.where(s_h[..., None] > 0, q, 0).astype(np.uint8)
     meta = np.stack([F.fp16_bits(s_h), F.fp16_bits(z_h)], axis=-1)  # [..., ng, 2] uint16
     return q, meta.view(np.uint8).reshape(*xg.shape[:-2], -1)
@@ -248,11 +252,21 @@ def _fit_fp8row(x):
 def pack_codes(codes: np.ndarray, bits: int) -> np.ndarray:
     """Packing along the channel axis.  2-bit: every block of 16 channels fills 4 bytes; byte j
     of a block holds channels j, 4+j, 8+j, 12+j in bit pairs 0, 1, 2, 3 (channel 4s+j in bits
-    2s..2s+1).  4-bit: byte k holds channel 2k in bits 0-3 and 2k+1 in bits 4-7.  8-bit codes are
-    stored as they are."""
+    2s..2s+1).  4-bit: byte k holds channel 2k in bits 0-3 and 2k+1 in bits 4-7.  3-bit: one
+    little-endian bit stream, channel c in bits 3c..3c+2.  8-bit codes are stored as they are."""
     c = np.asarray(codes, dtype=np.uint8)
     if bits == 8:
         return c.copy()
+    if bits == 3:
+        D = c.shape[-1]
+        bitpos = 3 * np.arange(D)
+        out = np.zeros(c.shape[:-1] + (3 * D // 8,), dtype=np.uint8)
+        for b in range(3):   # bit b of channel ch goes to stream bit 3 ch + b
+            pos = bitpos + b
+            vals = ((c >> b) & 1).astype(np.uint8) << (pos % 8).astype(np.uint8)
+            for ch in range(D):
+                out[..., pos[ch] // 8] |= vals[..., ch]
+        return out
     if bits == 2:
         blk = c.reshape(*c.shape[:-1], -1, 4, 4).astype(np.uint16)   # [..., block, s, j]
         out = np.zeros(blk.shape[:-2] + (4,), dtype=np.uint16)       # [..., block, j]
@@ -268,6 +282,13 @@ def unpack_codes(packed: np.ndarray, bits: int, D: int) -> np.ndarray:
     p = np.asarray(packed, dtype=np.uint8)
     if bits == 8:
         return p.copy()
+    if bits == 3:
+        out = np.zeros(p.shape[:-1] + (D,), dtype=np.uint8)
+        for ch in range(D):
+            for b in range(3):
+                pos = 3 * ch + b
+                out[..., ch] |= ((p[..., pos // 8] >> (pos % 8)) & 1) << b
+        return out
     if bits == 2:
         blk = p.reshape(*p.shape[:-1], -1, 4)                         # [..., block, j]
         parts = [(blk >> (2 * sp)) & 3 for sp in range(4)]            # bit pair s
@@ -310,6 +331,8 @@ def quantize_rows(x: np.ndarray, spec: QuantSpec) -> QuantRows:
     keep = ~mask_g
     if spec.fmt == "int4":
         codes, meta = _fit_int4(xg, keep)
+    elif spec.fmt == "int3":
+        codes, meta = _fit_int4(xg, keep, 7)
     elif spec.fmt == "int4s":
         codes, meta = _fit_int4s(xg, keep)
     elif spec.fmt == "fp4":
@@ -351,7 +374,7 @@ def dequantize_codes(codes: np.ndarray, meta: np.ndarray, spec: QuantSpec) -> np
     g = spec.group
     ng = D // g
     cg = codes.reshape(R, ng, g)
-    if spec.fmt in ("int4", "int4s"):
+    if spec.fmt in ("int4", "int4s", "int3"):
         sz = F.fp16_from_bits(meta.view(np.uint16).reshape(R, ng, 2))
         out = cg * sz[..., 0:1] + sz[..., 1:2]
     elif spec.fmt == "fp4":

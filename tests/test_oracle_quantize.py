@@ -496,3 +496,37 @@ def test_calibrated_mask_matches_top_channels():
         for h in range(min(w.H, 3)):
             for kind in (G.K, G.V):
                 assert G.mask_channels(w, h, kind) == Q.top_channels(G.kv_rows(w, 0, h, kind, 0, 256), k)
+
+
+# ----------------------------------------------------------------------------- INT3
+# [P3] "Sub-Byte KV-Cache Quantization": asymmetric 3-bit packed codes.
+def test_int3_packing_is_one_little_endian_bit_stream():
+    codes = np.array([1, 2, 3, 4, 5, 6, 7, 0] * 16, dtype=np.uint8)
+    packed = Q.pack_codes(codes[None, :], 3)[0]
+    assert packed.shape == (48,)
+    stream = sum(int(c) << (3 * i) for i, c in enumerate(codes))       # channel i at bit 3 i
+    assert bytes(packed) == stream.to_bytes(48, "little")
+    assert list(packed[:3]) == [0xD1, 0x58, 0x1F]
+    rng = np.random.default_rng(41)
+    c = rng.integers(0, 8, (5, 128)).astype(np.uint8)
+    assert np.array_equal(Q.unpack_codes(Q.pack_codes(c, 3), 3, 128), c)
+
+
+def test_int3_grid_and_bound():
+    # min 0, max 7: S = 1, zero = 0, every integer is its own code
+    x = np.tile(np.arange(8, dtype=F32), 16)[None, :]
+    spec = Q.QuantSpec("int3", 32, "none")
+    q = Q.quantize_rows(x, spec)
+    assert np.array_equal(q.codes[0], x[0].astype(np.uint8))
+    sz = F.fp16_from_bits(q.meta.view(np.uint16).reshape(4, 2))
+    assert sz[:, 0].tolist() == [1.0] * 4 and sz[:, 1].tolist() == [0.0] * 4
+    # random groups: reconstruction within half a step (plus the fp16 rounding of S and zero)
+    rng = np.random.default_rng(42)
+    x = (rng.standard_normal((20, 128)) * rng.uniform(0.1, 10, (20, 1))).astype(F32)
+    for g in (32, 64):
+        spec = Q.QuantSpec("int3", g, "none")
+        q = Q.quantize_rows(x, spec)
+        d = Q.dequantize_rows(q, spec)
+        S = F.fp16_from_bits(q.meta.view(np.uint16).reshape(20, 128 // g, 2))[..., 0]
+        lim = np.repeat(S, g, axis=1) * 0.5 + np.abs(x) * 2.0 ** -10 + 1e-6
+        assert np.all(np.abs(d - x) <= lim) and q.codes.max() <= 7
