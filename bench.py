@@ -167,8 +167,9 @@ def main():
     ap.add_argument("--workload", default="c2_b64_s32k")
     ap.add_argument("--split", type=int, default=-1, help="split-K chunk (default: workload's)")
     ap.add_argument("--fmt", default=None,
-                    help="format variant stored like the workload's format (u2 for 2-bit "
-                         "workloads, int4s for INT4 ones): same shapes and data, other quantizer fit")
+                    help="other format on the workload's shapes and data: u2 for 2-bit workloads "
+                         "(uniform codebook, same storage), int4s (symmetric fit, same storage) or "
+                         "int3 (3-bit codes) for INT4 ones")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--chan-mask", type=int, default=0,
                     help="keep this many calibrated top channels per (KV head, K or V) as outlier "
@@ -192,9 +193,9 @@ def main():
 
     w = CONFIGS[args.workload]
     if args.fmt:
-        base = {"u2": "c2", "int4s": "int4"}.get(args.fmt)
+        base = {"u2": "c2", "int4s": "int4", "int3": "int4"}.get(args.fmt)
         if base != w.fmt:
-            sys.exit(f"--fmt {args.fmt}: not a variant of the workload's format {w.fmt}")
+            sys.exit(f"--fmt {args.fmt}: not an alternative to the workload's format {w.fmt}")
         w = WD.variant(w, fmt=args.fmt)
     if args.chan_mask:
         w = WD.variant(w, chan_mask=args.chan_mask)

@@ -20,7 +20,8 @@ LIB_PATH = os.path.join(_HERE, "libkvq.so")
 
 KVQ_OK, KVQ_ERR_INVALID_ARG, KVQ_ERR_UNSUPPORTED = 0, -1, -2
 KVQ_ERR_WORKSPACE, KVQ_ERR_HIP, KVQ_ERR_CAPACITY = -3, -4, -5
-FMT = {"fp16": 0, "fp8row": 1, "int4": 2, "fp4": 3, "c2": 4, "bf16": 5, "u2": 6, "int4s": 7}
+FMT = {"fp16": 0, "fp8row": 1, "int4": 2, "fp4": 3, "c2": 4, "bf16": 5, "u2": 6, "int4s": 7,
+       "int3": 8}
 OUTL = {"none": 0, "fp16": 1, "e4m3": 2}
 
 EXPORTED = ("kvq_kv_bytes", "kvq_cache_sizes", "kvq_quantize_append", "kvq_workspace_bytes",

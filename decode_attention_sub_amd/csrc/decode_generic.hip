@@ -60,6 +60,19 @@ __device__ __forceinline__ void dequant32(const RowRef& r, int part, float* dst)
     for (int k = 0; k < 16; ++k) dst[k] = c[(cw.x >> (8 * (k & 3) + 2 * (k >> 2))) & 3u];
 #pragma unroll
     for (int k = 0; k < 16; ++k) dst[16 + k] = c[(cw.y >> (8 * (k & 3) + 2 * (k >> 2))) & 3u];
+  } else if constexpr (FMT == FMT_INT3) {
+    // 32 channels = 96 stream bits = words 3 part .. 3 part + 2; channel c at stream bit 3c
+    const uint32_t* cp = (const uint32_t*)(r.codes + 12 * part);
+    const uint32_t w[4] = {cp[0], cp[1], cp[2], 0u};
+    const int gi = (32 * part) / GS;
+    const uint32_t m = *(const uint32_t*)(r.meta + 4 * gi);
+    const float S = half_bits_to_f32(m & 0xFFFFu), Z = half_bits_to_f32(m >> 16);
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      const int o = 3 * k, i = o >> 5, sh = o & 31;
+      const uint32_t v = sh > 29 ? (w[i] >> sh) | (w[i + 1] << (32 - sh)) : w[i] >> sh;
+      dst[k] = fmaf((float)(v & 7u), S, Z);
+    }
   } else {
     const uint4 cw = *(const uint4*)(r.codes + 16 * part);
     const uint32_t wv[4] = {cw.x, cw.y, cw.z, cw.w};
@@ -273,6 +286,10 @@ hipError_t launch_decode_generic(const DecodeLaunch& d, hipStream_t st) {
       else decode_generic_kernel<FMT_FP4, 64><<<grid, 256, 0, st>>>(d);
       break;
     case FMT_C2: decode_generic_kernel<FMT_C2, 64><<<grid, 256, 0, st>>>(d); break;
+    case FMT_INT3:
+      if (d.group == 32) decode_generic_kernel<FMT_INT3, 32><<<grid, 256, 0, st>>>(d);
+      else decode_generic_kernel<FMT_INT3, 64><<<grid, 256, 0, st>>>(d);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -12,7 +12,7 @@ namespace {
 
 constexpr int kDefaultPagedChunk = 4096;
 
-bool is_quant_fmt(int f) { return f == FMT_INT4 || f == FMT_FP4 || f == FMT_C2; }
+bool is_quant_fmt(int f) { return f == FMT_INT4 || f == FMT_FP4 || f == FMT_C2 || f == FMT_INT3; }
 
 // A format variant is checked, sized, stored and decoded as its base format; only the
 // quantizer's fit differs.  Entry points work on a copy whose format is the base format.

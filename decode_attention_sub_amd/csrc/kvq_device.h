@@ -13,7 +13,8 @@ constexpr int kHeadDim = 128;
 constexpr int kBlock = 16;      // tokens per outlier block and per page
 
 enum Fmt : int { FMT_FP8ROW = KVQ_FMT_FP8_E4M3_ROW, FMT_INT4 = KVQ_FMT_INT4_ASYM,
-                 FMT_FP4 = KVQ_FMT_FP4_E2M1, FMT_C2 = KVQ_FMT_CENTROID2 };
+                 FMT_FP4 = KVQ_FMT_FP4_E2M1, FMT_C2 = KVQ_FMT_CENTROID2,
+                 FMT_INT3 = KVQ_FMT_INT3_ASYM };
 // Quantizer fits: a format variant is stored (and decoded) as its base format and differs only
 // in how the quantizer fits the group (uniform 2-bit codebook as FMT_C2, symmetric INT4 as
 // FMT_INT4).
@@ -26,10 +27,10 @@ __host__ __device__ constexpr int fit_of(int fmt) {
 }
 
 __host__ __device__ constexpr int code_bits(int fmt) {
-  return fmt == FMT_C2 ? 2 : (fmt == FMT_FP8ROW ? 8 : 4);
+  return fmt == FMT_C2 ? 2 : (fmt == FMT_FP8ROW ? 8 : (fmt == FMT_INT3 ? 3 : 4));
 }
 __host__ __device__ constexpr int meta_bytes_per_group(int fmt) {
-  return fmt == FMT_INT4 ? 4 : (fmt == FMT_FP4 ? 1 : (fmt == FMT_C2 ? 8 : 0));
+  return fmt == FMT_INT4 || fmt == FMT_INT3 ? 4 : (fmt == FMT_FP4 ? 1 : (fmt == FMT_C2 ? 8 : 0));
 }
 
 // ------------------------------------------------------------------ scalar bit casts

@@ -131,7 +131,12 @@ __device__ __forceinline__ void outlier_flags(const float x[4], float tau2, bool
   for (int i = 0; i < 4; ++i) keep[i] = !(e[i] * (float)(G - 1) > rhs);
 }
 
-template <int G>
+// Asymmetric integer fit ("The Sub-10ms Barrier ...", section "2. FP4/INT4 KV-Cache
+// Quantization"): S = (max - min) / (2^b - 1) over the non-outliers, fp16 S and zero =
+// fp16(min), code = rint(clamp((x - z) / S)).  LEVELS = 2^b - 1: 15 for INT4, 7 for the
+// asymmetric 3-bit codes of "Sub-5ms MoE Inference ...", section "Sub-Byte KV-Cache
+// Quantization".
+template <int G, int LEVELS = 15>
 __device__ void fit_int4(const float x[4], const bool keep[4], RowOut& o) {
   constexpr int L = G / 4;
   float mn = INFINITY, mx = -INFINITY;
@@ -140,7 +145,7 @@ __device__ void fit_int4(const float x[4], const bool keep[4], RowOut& o) {
     if (keep[i]) { mn = fminf(mn, x[i]); mx = fmaxf(mx, x[i]); }
   mn = group_min<L>(mn) + 0.0f;  // a zero minimum is taken as +0
   mx = group_max<L>(mx) + 0.0f;
-  const float s = (mx - mn) / 15.0f;
+  const float s = (mx - mn) / (float)LEVELS;
   const uint32_t sh = f32_to_half_bits(s), zh = f32_to_half_bits(mn);
   const float S = half_bits_to_f32(sh), Z = half_bits_to_f32(zh);
 #pragma unroll
@@ -149,7 +154,7 @@ __device__ void fit_int4(const float x[4], const bool keep[4], RowOut& o) {
     uint32_t q = 0;
     if (S > 0.0f) {
       const float y = (xx - Z) / S;
-      q = (uint32_t)__builtin_rintf(fminf(fmaxf(y, 0.0f), 15.0f));
+      q = (uint32_t)__builtin_rintf(fminf(fmaxf(y, 0.0f), (float)LEVELS));
     }
     o.code[i] = q;
   }
@@ -407,6 +412,8 @@ __global__ void __launch_bounds__(64 * NW) quantize_append_kernel(QArgs a) {
       if constexpr (FMT == FMT_INT4) {
         if (a.fit == kFitSym) fit_int4sym<G>(x, keep, o);
         else fit_int4<G>(x, keep, o);
+      } else if constexpr (FMT == FMT_INT3) {
+        fit_int4<G, 7>(x, keep, o);
       } else if constexpr (FMT == FMT_FP4) {
         fit_fp4<G>(x, keep, o);
       } else {
@@ -460,7 +467,21 @@ __global__ void __launch_bounds__(64 * NW) quantize_append_kernel(QArgs a) {
       }
       const int bits = tr ? 8 : code_bits(FMT);
       const int per_word = 32 / bits;
-      if (lane < cb / 4) {
+      if (bits == 3) {
+        // one LSB-first bit stream: channel c in stream bits 3c..3c+2; word `lane` holds stream
+        // bits 32 lane .. 32 lane + 31, the channels that start in it and the head of one that
+        // starts in the word before
+        if (lane < cb / 4) {
+          uint32_t w = 0;
+          const int c0 = (32 * lane) / 3, c1 = (32 * lane + 31) / 3;
+          for (int c = c0; c <= c1; ++c) {
+            const int sh = 3 * c - 32 * lane;
+            const uint32_t v = s_code[slot][c];
+            w |= sh >= 0 ? v << sh : v >> -sh;
+          }
+          ((uint32_t*)codes_dst)[lane] = w;
+        }
+      } else if (lane < cb / 4) {
         // 2-bit: channel 4s + j of the word's 16 goes to byte j, bit pair s; otherwise LSB first
         uint32_t w = 0;
         for (int k = 0; k < per_word; ++k) {
@@ -554,6 +575,8 @@ hipError_t launch_quantize_append(const QuantizeLaunch& q, hipStream_t st) {
     case FMT_FP4: return q.group == 32 ? launch_quantize_t<FMT_FP4, 32>(qa, nlists, q.max_new, st)
                                        : launch_quantize_t<FMT_FP4, 64>(qa, nlists, q.max_new, st);
     case FMT_C2: return launch_quantize_t<FMT_C2, 64>(qa, nlists, q.max_new, st);
+    case FMT_INT3: return q.group == 32 ? launch_quantize_t<FMT_INT3, 32>(qa, nlists, q.max_new, st)
+                                        : launch_quantize_t<FMT_INT3, 64>(qa, nlists, q.max_new, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -47,8 +47,14 @@
  *    listing of "The Sub-10ms Barrier ..." page, section "2. FP4/INT4 KV-Cache Quantization":
  *    S = fp16(max(absmax / 7, 1e-5)) over the non-outliers, code = clamp(rint(x / S), -8, 7) + 8,
  *    z = fp16(-8 S).
+ *  - INT3_ASYM (contiguous caches, g = 32 or 64): the asymmetric 3-bit codes of the "Sub-5ms
+ *    MoE Inference ..." page, section "Sub-Byte KV-Cache Quantization", fitted as INT4_ASYM
+ *    with 2^b - 1 = 7: codes 0..7, S = fp16((max - min) / 7), z = fp16(min), value = code * S
+ *    + z; metadata per group [S, z] (4 bytes); 48 code bytes per 128-channel row.  A quotient
+ *    (x - z) / S with no value (S and z both beyond the fp16 range) gives code 0.
  *  Codes are packed LSB-first along the channel axis (2-bit: channel 4k+r in bits 2r..2r+1 of
- *  byte k; 4-bit: channel 2k in bits 0-3, 2k+1 in bits 4-7 of byte k).
+ *  byte k; 4-bit: channel 2k in bits 0-3, 2k+1 in bits 4-7 of byte k; 3-bit: one little-endian
+ *  bit stream per row, channel c in stream bits 3c..3c+2).
  *
  * Outlier side lists: one per (sequence b, KV head h, K=0 / V=1), records in ascending
  * (token, channel) order: uint32 index = token * D + channel and the ORIGINAL value rounded to
@@ -83,7 +89,8 @@ typedef enum {
   KVQ_FMT_CENTROID2 = 4,
   KVQ_FMT_BF16 = 5,          /* unquantized, for kvq_kv_bytes only */
   KVQ_FMT_UNIFORM2 = 6,      /* variant: stored and decoded as CENTROID2 */
-  KVQ_FMT_INT4_SYM = 7       /* variant: stored and decoded as INT4_ASYM */
+  KVQ_FMT_INT4_SYM = 7,      /* variant: stored and decoded as INT4_ASYM */
+  KVQ_FMT_INT3_ASYM = 8      /* contiguous caches only */
 } kvq_format;
 
 typedef enum { KVQ_OUTL_NONE = 0, KVQ_OUTL_FP16 = 1, KVQ_OUTL_FP8_E4M3 = 2 } kvq_outlier_dtype;
@@ -91,8 +98,8 @@ typedef enum { KVQ_OUTL_NONE = 0, KVQ_OUTL_FP16 = 1, KVQ_OUTL_FP8_E4M3 = 2 } kvq
 /* Problem description (the pages' GQA heads H, head dim D, context S, batch B, group size,
  * bit width via the format, and outlier threshold tau).  Constraints checked on the host:
  * head_dim == 128; num_q_heads % num_kv_heads == 0 with 1 <= num_q_heads/num_kv_heads <= 16;
- * group_size in {32, 64} dividing head_dim (INT4 / FP4 / INT4_SYM: 32 or 64; CENTROID2 / UNIFORM2:
- * 64);
+ * group_size in {32, 64} dividing head_dim (INT4 / FP4 / INT4_SYM / INT3: 32 or 64; CENTROID2 /
+ * UNIFORM2: 64);
  * max_seq_len >= 1; outlier_sigma > 0; lloyd_iters in [0, 64]; page_size 0 (contiguous) or 16
  * (paged, tiered: tier 2 = ``format``, tier 1 = FP8_E4M3_ROW; only CENTROID2 tier 2).
  * Every entry point accepts the format variants and treats their buffers as the base format's. */

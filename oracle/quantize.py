@@ -48,7 +48,8 @@ Readings taken where the pages are silent (each is listed in the design doc):
     cluster keeps its centroid; centroids stored as fp16;
   * INT4: offset form of the equation: zero = fp16(min), code = Round(Clamp((x - zero)/S, 0,
     15)), which is the page's ZeroPoint = -zero/S written without a quantized-unit zero; a zero
-    min or max is taken as +0;
+    min or max is taken as +0; a quotient with no value (scale and zero both beyond the fp16
+    range) gives code 0;
   * INT3 ([P3] "Sub-Byte KV-Cache Quantization": asymmetric 3-bit packed codes beside the
     outliers): the INT4 fit with b = 3 (S = (max - min)/7, codes 0..7), codes packed LSB-first
     as one bit stream along the channels;
@@ -152,6 +153,8 @@ def _fit_int4(xg, keep, levels: int = 15):
     xx = np.where(keep, xg, F32(0.0)).astype(F32)
     with np.errstate(divide="ignore", invalid="ignore"):
         y = ((xx - z_h[..., None]).astype(F32) / s_h[..., None]).astype(F32)
+    # a quotient with no value (scale and zero both overflowed fp16, inf / inf) gives code 0
+    y = np.where(np.isnan(y), F32(0.0), y)
     q = np.rint(np.clip(y, F32(0.0), F32(levels)))
     q = np.where(s_h[..., None] > 0, q, 0).astype(np.uint8)
     meta = np.stack([F.fp16_bits(s_h), F.fp16_bits(z_h)], axis=-1)  # [..., ng, 2] uint16

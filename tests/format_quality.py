@@ -24,8 +24,8 @@ from oracle import quantize as OQ           # noqa: E402
 from workloads import CONFIGS               # noqa: E402
 from workloads import generate as G         # noqa: E402
 
-# (label, format, group, outlier dtype[, static mask channels]): the workloads' formats and the
-# variants stored like them
+# (label, format, group, outlier dtype[, static mask channels]): the workloads' formats, the
+# variants stored like them and the 3-bit codes
 FORMATS = [
     ("2-bit centroids, Lloyd (c2)", "c2", 64, "e4m3"),
     ("2-bit uniform linspace (u2)", "u2", 64, "e4m3"),
@@ -35,6 +35,7 @@ FORMATS = [
     ("INT4 symmetric g32 (int4s)", "int4s", 32, "fp16"),
     ("INT4 symmetric g32, no outliers", "int4s", 32, "none"),
     ("FP4 E2M1 g32 (fp4)", "fp4", 32, "fp16"),
+    ("INT3 asymmetric g32 (int3)", "int3", 32, "fp16"),
     ("2-bit centroids, 2-channel fp16 mask", "c2", 64, "fp16", 2),
     ("INT4 asymmetric g32, 4-channel fp16 mask", "int4", 32, "fp16", 4),
 ]

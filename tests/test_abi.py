@@ -137,6 +137,25 @@ def test_format_variants_size_and_check_like_their_base():
     assert e.value.status == K.KVQ_ERR_UNSUPPORTED
 
 
+def test_int3_sizes_and_checks():
+    # 3-bit codes: 48 bytes per 128-channel row, fp16 scale and zero per group; contiguous only
+    for g, out in [(32, "e4m3"), (64, "fp16"), (32, "none")]:
+        p = K.make_params(4, 32, 8, 1000, "int3", g, out)
+        s = K.kvq_cache_sizes(p, 50)
+        assert (s.code_bytes_per_row, s.meta_bytes_per_row) == (48, (128 // g) * 4)
+        assert s.codes == 4 * 8 * 1000 * 48
+        for L, T, n in [(1, 1, 0), (80, 12345, 678 if out != "none" else 0)]:
+            assert K.kvq_kv_bytes(p, L, T, n) == KB.kv_bytes("int3", L, 8, 128, T, g, n, out)
+        assert K.kvq_workspace_bytes(p) == K.kvq_workspace_bytes(K.make_params(4, 32, 8, 1000, "int4", g, out))
+    with pytest.raises(K.KvqError) as e:
+        K.kvq_workspace_bytes(K.make_params(2, 8, 2, 100, "int3", 16, "e4m3"))
+    assert e.value.status == K.KVQ_ERR_UNSUPPORTED
+    with pytest.raises(K.KvqError) as e:
+        K.kvq_workspace_bytes(K.make_params(2, 8, 2, 100, "int3", 32, "e4m3", page_size=16,
+                                            num_pages=9, num_pages_fp8=4, max_pages_per_seq=7))
+    assert e.value.status == K.KVQ_ERR_UNSUPPORTED
+
+
 def test_channel_mask_needs_an_outlier_dtype():
     import ctypes as C
     import numpy as np

@@ -14,6 +14,7 @@ def test_format_error_orderings(workload):
     # same storage, same bytes: the variants differ only in the fit
     assert c2["bits_per_element"] == u2["bits_per_element"]
     assert r[("int4", "fp16")]["bits_per_element"] == r[("int4s", "fp16")]["bits_per_element"]
+    assert r[("int3", "fp16")]["bits_per_element"] < r[("int4", "fp16")]["bits_per_element"]
     # Lloyd iterations from quartile seeds reduce the squared error of the uniform codebook
     for k in ("k_rel_rmse", "v_rel_rmse"):
         assert c2[k] < u2[k]
@@ -22,6 +23,8 @@ def test_format_error_orderings(workload):
         # [-absmax, absmax] with one level unused on the short side
         assert r[("int4", "fp16")][k] < r[("int4s", "fp16")][k] < c2[k]
         assert r[("fp4", "fp16")][k] < c2[k]
+        # 8 levels of the same asymmetric grid: between INT4 and the 2-bit codebook
+        assert r[("int4", "fp16")][k] < r[("int3", "fp16")][k] < c2[k]
     # isolating outliers costs bytes and lowers the key error of both 2-bit codebooks
     assert c2["bits_per_element"] > r[("c2", "none")]["bits_per_element"] == 3.0
     assert c2["k_rel_rmse"] < r[("c2", "none")]["k_rel_rmse"]

@@ -42,6 +42,10 @@ SMALL = {
     "int4s_small": WD.variant(CONFIGS["int4_b1_s1k"], B=2, S=650, fmt="int4s"),
     "int4s_g64_noout": WD.variant(CONFIGS["int4_b1_s1k"], B=1, H=2, Hq=4, S=300, fmt="int4s",
                                   group=64, outlier="none"),
+    # asymmetric 3-bit codes packed as one bit stream (generic decoder), groups of 32 and 64
+    "int3_small": WD.variant(CONFIGS["int4_b1_s1k"], B=2, S=600, fmt="int3"),
+    "int3_g64_e4m3": WD.variant(CONFIGS["int4_b1_s1k"], B=1, H=2, Hq=8, S=333, fmt="int3",
+                                group=64, outlier="e4m3"),
     # static channel mask (top channels by magnitude kept as fp16 records in every row): INT4 on
     # the data with 4 channels x20 per list, 2-bit on the LogNormal-channel keys
     "int4_chanmask": WD.variant(CONFIGS["int4_b1_s1k"], B=2, S=600, chan_mask=4),
@@ -250,6 +254,7 @@ PREFIX = {
     "u2_g4": WD.variant(CONFIGS["c2_b16_s8k"], B=8, H=2, Hq=8, S=300, fmt="u2"),
     "fp4_g8": WD.variant(CONFIGS["fp4_b4_s128k"], B=8, H=2, Hq=16, S=300),
     "int4_g4": WD.variant(CONFIGS["int4_b1_s1k"], B=8, S=300),
+    "int3_g4": WD.variant(CONFIGS["int4_b1_s1k"], B=8, S=300, fmt="int3"),
 }
 
 
@@ -293,7 +298,9 @@ def _special_rows(n_rep: int = 2):
 
 @pytest.mark.parametrize("fmt,group,outlier", [("c2", 64, "e4m3"), ("c2", 64, "none"),
                                                ("u2", 64, "fp16"), ("int4", 32, "fp16"),
-                                               ("int4s", 64, "e4m3"), ("fp4", 32, "fp16")])
+                                               ("int4s", 64, "e4m3"), ("fp4", 32, "fp16"),
+                                               ("int3", 32, "fp16"), ("int3", 64, "none"),
+                                               ("int4", 64, "none")])
 def test_quantize_special_rows(fmt, group, outlier):
     """Degenerate and extreme rows, appended in one call, are packed bit for bit like the
     oracle's."""
@@ -301,6 +308,9 @@ def test_quantize_special_rows(fmt, group, outlier):
     from oracle import cache as OC
     from oracle import quantize as OQ
     x = _special_rows()
+    if fmt in ("int3", "int4") and outlier == "none":
+        # scale and zero both beyond the fp16 range: every quotient is inf / inf, code 0
+        x = np.concatenate([x, np.where(np.arange(128) % 2 == 0, 1e6, -1e6)[None].astype(np.float32)])
     n = x.shape[0]
     w = WD.variant(CONFIGS["c2_b16_s8k"], B=1, H=1, Hq=4, S=n, fmt=fmt, group=group, outlier=outlier)
     p = WD.make_params(w, 64)

@@ -530,3 +530,13 @@ def test_int3_grid_and_bound():
         S = F.fp16_from_bits(q.meta.view(np.uint16).reshape(20, 128 // g, 2))[..., 0]
         lim = np.repeat(S, g, axis=1) * 0.5 + np.abs(x) * 2.0 ** -10 + 1e-6
         assert np.all(np.abs(d - x) <= lim) and q.codes.max() <= 7
+
+
+def test_int_fits_beyond_the_fp16_range_give_code_zero():
+    # min -1e6, max 1e6: S and zero both round to +-inf in fp16, every quotient is inf / inf;
+    # the codes are 0 (no value is taken as the bottom of the clamp range), never an
+    # out-of-range integer
+    x = np.where(np.arange(128) % 2 == 0, 1e6, -1e6).astype(F32)[None, :]
+    for fmt in ("int4", "int3"):
+        q = Q.quantize_rows(x, Q.QuantSpec(fmt, 32, "none"))
+        assert not q.codes.any()
