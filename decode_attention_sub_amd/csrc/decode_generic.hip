@@ -230,46 +230,49 @@ __global__ void __launch_bounds__(256) decode_generic_kernel(DecodeLaunch d) {
   }
 }
 
-// out[b][hq] = sum_c 2^(m_c - M) o_c / sum_c 2^(m_c - M) l_c over the chunks holding tokens.
-// Latency-bound (one small workgroup per query head): the chunk maxima and weights are taken by
-// the 128 threads in parallel, 128 chunks at a time, and each channel thread then sums its
-// column with the weights from LDS, eight chunk rows in flight.  The order of every sum is fixed.
-__global__ void __launch_bounds__(128) lse_merge_kernel(DecodeLaunch d) {
-  __shared__ float s_w[128];
-  __shared__ float s_red[2];
-  const int hq = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, ch = tid;
+// out[b][hq] = sum_c 2^(m_c - M) o_c / sum_c 2^(m_c - M) l_c over the chunks holding tokens,
+// M = max_c m_c.  Latency-bound, so built for few dependent memory round trips: one workgroup per
+// query head, thread (g, ch) owns channel ch of the chunks c = g mod kMergeGroups and folds them
+// into a running (max, sum, output) state in chunk order (every load of a thread is independent
+// of its arithmetic, so an unrolled batch of chunks is in flight at once); the kMergeGroups
+// states of a channel are then combined through LDS in group order.  Deterministic.
+constexpr int kMergeGroups = 4;
+
+__global__ void __launch_bounds__(kMergeGroups * kHeadDim) lse_merge_kernel(DecodeLaunch d) {
+  __shared__ float s_st[kMergeGroups][3][kHeadDim];
+  const int hq = blockIdx.x, b = blockIdx.y;
+  const int ch = threadIdx.x % kHeadDim, g = threadIdx.x / kHeadDim;
   const int S = d.seq_lens[b];
   const int nc = min((S + d.chunk - 1) / d.chunk, d.n_chunks);
   const float* pp = d.partials + ((size_t)b * d.Hq + hq) * d.n_chunks * (kHeadDim + 2);
-  float m = -INFINITY;
-  for (int c = tid; c < nc; c += 128) m = fmaxf(m, pp[(size_t)c * (kHeadDim + 2)]);
-  m = wave_max(m);
-  if ((tid & 63) == 0) s_red[tid >> 6] = m;
-  __syncthreads();
-  const float M = fmaxf(s_red[0], s_red[1]);
-  float num = 0.0f, lsum = 0.0f;
-  for (int c0 = 0; c0 < nc; c0 += 128) {
-    const int c = c0 + tid;
-    float w = 0.0f;
-    if (c < nc) {
-      const float* q = pp + (size_t)c * (kHeadDim + 2);
-      w = exp2f(q[0] - M);
-      lsum = fmaf(w, q[1], lsum);
-    }
-    __syncthreads();   // the previous block's weights are consumed
-    s_w[tid] = w;
-    __syncthreads();
-    const int n = min(128, nc - c0);
-    const float* col = pp + (size_t)c0 * (kHeadDim + 2) + 2 + ch;
-#pragma unroll 8
-    for (int k = 0; k < n; ++k) num = fmaf(s_w[k], col[(size_t)k * (kHeadDim + 2)], num);
+  float M = -INFINITY, den = 0.0f, num = 0.0f;
+#pragma unroll 4
+  for (int c = g; c < nc; c += kMergeGroups) {
+    const float* q = pp + (size_t)c * (kHeadDim + 2);
+    const float m = q[0], l = q[1], o = q[2 + ch];      // a chunk holding tokens: m finite
+    const float Mn = fmaxf(M, m);
+    const float a = exp2f(M - Mn), w = exp2f(m - Mn);    // a = 0 while M is -inf
+    den = fmaf(w, l, den * a);
+    num = fmaf(w, o, num * a);
+    M = Mn;
   }
-  lsum = wave_sum(lsum);
+  s_st[g][0][ch] = M;
+  s_st[g][1][ch] = den;
+  s_st[g][2][ch] = num;
   __syncthreads();
-  if ((tid & 63) == 0) s_red[tid >> 6] = lsum;
-  __syncthreads();
-  const float den = s_red[0] + s_red[1];
-  d.out[((size_t)b * d.Hq + hq) * kHeadDim + ch] = num / den;
+  if (g != 0) return;
+  float Mt = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < kMergeGroups; ++i) Mt = fmaxf(Mt, s_st[i][0][ch]);
+  float D = 0.0f, N = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kMergeGroups; ++i) {
+    const float Mi = s_st[i][0][ch];
+    const float f = Mi == -INFINITY ? 0.0f : exp2f(Mi - Mt);   // a group with no chunk
+    D = fmaf(f, s_st[i][1][ch], D);
+    N = fmaf(f, s_st[i][2][ch], N);
+  }
+  d.out[((size_t)b * d.Hq + hq) * kHeadDim + ch] = N / D;
 }
 
 }  // namespace
@@ -296,7 +299,7 @@ hipError_t launch_decode_generic(const DecodeLaunch& d, hipStream_t st) {
 }
 
 hipError_t launch_lse_merge(const DecodeLaunch& d, hipStream_t st) {
-  lse_merge_kernel<<<dim3(d.Hq, d.L.B), 128, 0, st>>>(d);
+  lse_merge_kernel<<<dim3(d.Hq, d.L.B), kMergeGroups * kHeadDim, 0, st>>>(d);
   return hipGetLastError();
 }
 
