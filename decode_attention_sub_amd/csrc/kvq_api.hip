@@ -136,7 +136,7 @@ int32_t kvq_kv_bytes(const kvq_params* pin, int32_t num_layers, int64_t num_toke
   } else {
     if (!is_quant_fmt(p->format) || p->group_size < 1 || p->head_dim % p->group_size)
       return KVQ_ERR_INVALID_ARG;
-    row = (uint64_t)p->head_dim * code_bits(p->format) / 8 +
+    row = ((uint64_t)p->head_dim * code_bits(p->format) + 7) / 8 +   // whole bytes per row
           (uint64_t)(p->head_dim / p->group_size) * meta_bytes_per_group(p->format);
   }
   uint64_t vb = p->outlier_dtype == KVQ_OUTL_FP16 ? 2 : (p->outlier_dtype == KVQ_OUTL_FP8_E4M3 ? 1 : 0);

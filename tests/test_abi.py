@@ -156,6 +156,17 @@ def test_int3_sizes_and_checks():
     assert e.value.status == K.KVQ_ERR_UNSUPPORTED
 
 
+def test_kv_bytes_rounds_packed_codes_up_to_whole_bytes():
+    # 20 channels: 3-bit codes are 60 bits -> 8 bytes, 2-bit 40 bits -> 5, 4-bit 80 bits -> 10;
+    # plus the per-group metadata of 5 groups of 4 (4 B INT3 / INT4, 8 B 2-bit)
+    for fmt, row in (("int3", 8 + 5 * 4), ("c2", 5 + 5 * 8), ("int4", 10 + 5 * 4)):
+        p = K.make_params(1, 2, 2, 16, fmt, 4, "none", D=20)
+        assert K.kvq_kv_bytes(p, 1, 3) == 2 * 2 * 3 * row
+        assert KB.kv_bytes(fmt, 1, 2, 20, 3, 4) == 2 * 2 * 3 * row
+    p = K.make_params(1, 2, 2, 16, "int3", 7, "none", D=21)      # 63 bits -> 8 bytes
+    assert K.kvq_kv_bytes(p, 1, 1) == 2 * 2 * (8 + 3 * 4)
+
+
 def test_channel_mask_needs_an_outlier_dtype():
     import ctypes as C
     import numpy as np
