@@ -51,6 +51,7 @@ SMALL = {
     "int4_chanmask": WD.variant(CONFIGS["int4_b1_s1k"], B=2, S=600, chan_mask=4),
     "c2_chanmask": WD.variant(CONFIGS["c2_b64_s32k"], B=2, H=2, Hq=16, S=700, chan_mask=2,
                               outlier="fp16"),
+    "int3_chanmask": WD.variant(CONFIGS["int4_b1_s1k"], B=1, S=400, fmt="int3", chan_mask=4),
     # tiered paged cache, variable lengths
     "tiered_small": WD.variant(CONFIGS["tiered_b32_paged"], B=3, H=2, Hq=8, S=3000,
                                S_range=(90, 3000), fp8_page_frac=0.3),
