@@ -203,6 +203,60 @@ def test_out_of_range_position_reports_status():
     assert cache.status() == K.KVQ_ERR_INVALID_ARG
 
 
+@pytest.mark.parametrize("name", ["c2_g8_small", "int4_g64_small", "tiered_small"])
+def test_invalid_seq_len_reports_status(name):
+    """A sequence length of 0 or past the capacity is reported through the status word; that
+    sequence is skipped and every other sequence's output is the one of a valid call."""
+    import dataclasses
+    import decode_attention_sub_amd as K
+    w = SMALL[name]
+    dc = WD.build(w)
+    S_cap = dc.params.max_seq_len
+    for split in (0, 128):
+        good = run_decode(dc, split_chunk=split)
+        assert dc.cache.status() == 0
+        for bad in (0, S_cap + 1):
+            lens = dc.seq_lens_host.copy()
+            lens[0] = bad
+            dcb = dataclasses.replace(dc, seq_lens_host=lens, seq_lens=torch.from_numpy(lens).cuda())
+            log(f"[gpu] decode {name} with seq_len {bad} split={split}")
+            got = run_decode(dcb, split_chunk=split)
+            assert dc.cache.status() == K.KVQ_ERR_INVALID_ARG
+            dc.cache.tensors["status"].zero_()
+            assert np.array_equal(got[1:], good[1:])
+
+
+def test_zero_count_append_leaves_sequence_untouched():
+    """counts[b] = 0 appends nothing to sequence b (codes, metadata, lists, block starts)."""
+    import decode_attention_sub_amd as K
+    from workloads import generate as G
+    w = WD.variant(CONFIGS["c2_b16_s8k"], B=2, H=2, Hq=8, S=100)
+    dc = WD.build(w)
+    p = dc.params
+    before = {k: t.clone() for k, t in dc.cache.tensors.items() if t is not None}
+    n = 20
+    k = np.stack([[G.kv_rows(w, 1 - b, h, 0, 0, n) for h in range(w.H)] for b in range(w.B)])
+    v = np.stack([[G.kv_rows(w, 1 - b, h, 1, 0, n) for h in range(w.H)] for b in range(w.B)])
+    pos = torch.tensor([40, 40], dtype=torch.int32, device="cuda")
+    cnt = torch.tensor([n, 0], dtype=torch.int32, device="cuda")
+    K.kvq_quantize_append(p, dc.cache, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(), pos, cnt)
+    torch.cuda.synchronize()
+    assert dc.cache.status() == 0
+    from oracle import cache as OC
+    from gpu_util import specs
+
+    def share(t, b):   # sequence b's part of a buffer laid out [B, ...]
+        return t.reshape(w.B, -1)[b]
+    for key in ("codes0", "codes1", "meta0", "meta1", "count", "bstart"):
+        assert torch.equal(share(dc.cache.tensors[key], 1), share(before[key], 1)), key
+    assert not torch.equal(share(dc.cache.tensors["codes0"], 0), share(before["codes0"], 0))
+    for h in range(w.H):
+        for kv in (0, 1):
+            spec, _ = specs(w, h, kv)
+            ref = OC.build_list(G.kv_rows(w, 1, h, kv, 0, w.S), spec)
+            assert_list_equal(read_list(dc, 1, h, kv), ref, f"h={h} kv={kv}")
+
+
 def test_paged_bad_slot_reports_status():
     """A block-table entry naming a slot outside its pool is reported by the decoder (the rows
     of that page read as zeros; nothing is read outside the pools)."""
