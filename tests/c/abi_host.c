@@ -1,0 +1,61 @@
+/* Plain C client of include/kvq.h: the host-only entry points (byte counts, buffer sizes,
+ * workspace size, status text and argument checks), built with gcc and linked against libkvq.so
+ * with no C++ or Python in between.  Prints one line per check; exits non-zero on a mismatch. */
+#include <stdio.h>
+#include <string.h>
+
+#include "kvq.h"
+
+static int fails = 0;
+#define CHECK(cond, what)                                              \
+  do {                                                                 \
+    if (cond) printf("ok %s\n", what);                                 \
+    else { printf("FAIL %s\n", what); ++fails; }                       \
+  } while (0)
+
+int main(void) {
+  /* 2-bit centroids, g = 64, E4M3 outliers: 32 code bytes + 2 x 8 centroid bytes per row */
+  kvq_params p;
+  memset(&p, 0, sizeof p);
+  p.batch = 64; p.num_q_heads = 64; p.num_kv_heads = 8; p.head_dim = 128;
+  p.max_seq_len = 32768; p.format = KVQ_FMT_CENTROID2; p.group_size = 64;
+  p.outlier_dtype = KVQ_OUTL_FP8_E4M3; p.outlier_sigma = 3.0f; p.lloyd_iters = 8;
+
+  uint64_t bytes = 0;
+  CHECK(kvq_kv_bytes(&p, 1, 32768, 1000, &bytes) == KVQ_OK &&
+        bytes == 2ull * 8 * 32768 * 48 + 1000ull * 5, "kv_bytes 2-bit + E4M3 records");
+
+  kvq_params f = p;
+  f.format = KVQ_FMT_FP16;
+  CHECK(kvq_kv_bytes(&f, 80, 1, 0, &bytes) == KVQ_OK && bytes == 327680ull,
+        "kv_bytes FP16: 2 x 80 layers x 8 heads x 128 x 2 bytes per token");
+
+  kvq_cache_sizes_t s;
+  CHECK(kvq_cache_sizes(&p, 4096, &s) == KVQ_OK && s.code_bytes_per_row == 32 &&
+        s.meta_bytes_per_row == 16 && s.codes == 64ull * 8 * 32768 * 32,
+        "cache_sizes 2-bit rows");
+
+  kvq_params i3 = p;
+  i3.format = KVQ_FMT_INT3_ASYM; i3.group_size = 32;
+  CHECK(kvq_cache_sizes(&i3, 4096, &s) == KVQ_OK && s.code_bytes_per_row == 48 &&
+        s.meta_bytes_per_row == 16, "cache_sizes INT3 rows");
+
+  uint64_t ws = 1;
+  CHECK(kvq_workspace_bytes(&p, 0, &ws) == KVQ_OK && ws == 0,
+        "no workspace when one chunk covers the context");
+  CHECK(kvq_workspace_bytes(&p, 4096, &ws) == KVQ_OK &&
+        ws == 64ull * 64 * 8 * (128 + 2) * 4, "workspace of 8 chunks of 4096");
+
+  kvq_params bad = p;
+  bad.head_dim = 96;
+  CHECK(kvq_workspace_bytes(&bad, 0, &ws) == KVQ_ERR_UNSUPPORTED, "head_dim 96 unsupported");
+  bad = p;
+  bad.num_q_heads = 60;
+  CHECK(kvq_workspace_bytes(&bad, 0, &ws) == KVQ_ERR_INVALID_ARG, "Hq not a multiple of H");
+  CHECK(kvq_workspace_bytes(&p, 100, &ws) == KVQ_ERR_INVALID_ARG, "split not a multiple of 64");
+  CHECK(kvq_decode_attention(&p, NULL, NULL, NULL, NULL, 0.1f, 0, NULL, NULL, 0, NULL) ==
+        KVQ_ERR_INVALID_ARG, "decode with null cache rejected before any launch");
+  CHECK(strcmp(kvq_status_string(KVQ_ERR_CAPACITY), "unknown status") != 0,
+        "status text for capacity");
+  return fails ? 1 : 0;
+}
