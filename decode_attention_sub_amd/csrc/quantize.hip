@@ -362,16 +362,21 @@ __global__ void __launch_bounds__(64 * NW) quantize_append_kernel(QArgs a) {
   for (int e = 0; e < 4; ++e)
     x0[e] = slot < n ? src[(size_t)slot * kHeadDim + gi * G + jg + L * e] : 0.0f;
 
-  // truncate the list to the records of tokens < p
+  // truncate the list to the records of tokens < p: the records before the start of p's
+  // 16-token block, plus those of the block's rows before p.  A block holds at most 16 rows of D
+  // records, and the list is sorted, so each thread stops at its first record of a token >= p.
   if (tid == 0) s_trunc = 0;
   __syncthreads();
   int64_t running = 0;
   if (p > 0) {
     const int64_t start = max((int64_t)0, min((int64_t)bstart[(p - 1) >> 4], Lo.outl_cap));
     const int64_t old = max((int64_t)0, min((int64_t)a.cache.outl_count[lid], Lo.outl_cap));
+    const int64_t lim = min(old, start + (int64_t)kBlock * kHeadDim);
     int cnt = 0;
-    for (int64_t r = start + tid; r < old && r < start + 256; r += blockDim.x)
-      cnt += (oidx[r] < (uint32_t)p * kHeadDim) ? 1 : 0;
+    for (int64_t r = start + tid; r < lim; r += blockDim.x) {
+      if (oidx[r] >= (uint32_t)p * kHeadDim) break;
+      ++cnt;
+    }
     if (cnt) atomicAdd(&s_trunc, cnt);
     __syncthreads();
     running = start + s_trunc;
