@@ -387,6 +387,27 @@ def test_u2_ends_are_min_and_max_of_the_zero_filled_residuals():
     assert cent[0] == F.fp16_round(F32(x.min())) and cent[3] == F.fp16_round(F32(500.0))
 
 
+def test_u2_centroids_match_torch_linspace():
+    # library routine: the four uniform centroids are torch.linspace(min, max, 4) in float32 (the
+    # listing's call), rounded to fp16.  Random (min, max) pairs over many magnitudes, both signs,
+    # equal ends; each group holds its min and max and 62 values between them.
+    import torch
+    rng = np.random.default_rng(24)
+    n = 4000
+    a = (rng.standard_normal(n) * 10.0 ** rng.uniform(-4, 4, n)).astype(F32)
+    b = (rng.standard_normal(n) * 10.0 ** rng.uniform(-4, 4, n)).astype(F32)
+    mn, mx = np.minimum(a, b), np.maximum(a, b)
+    mx[:50] = mn[:50]
+    mid = (mn[:, None] + (mx - mn)[:, None] * rng.uniform(0, 1, (n, 62))).astype(F32)
+    mid = np.clip(mid, mn[:, None], mx[:, None]).astype(F32)
+    x = np.concatenate([mx[:, None], mid[:, :31], mn[:, None], mid[:, 31:]], axis=1).astype(F32)
+    q = Q.quantize_rows(np.concatenate([x, x], axis=1), Q.QuantSpec("u2", 64, "none"))
+    got = q.meta.view(np.uint16).reshape(n, 2, 4)[:, 0]
+    ref = np.stack([torch.linspace(float(lo), float(hi), 4, dtype=torch.float32).numpy()
+                    for lo, hi in zip(mn, mx)]).astype(F32)
+    assert np.array_equal(got, F.fp16_bits(F.fp16_round(ref)))
+
+
 def test_u2_codes_are_nearest_centroids():
     # invariant on random groups: each code's centroid is no farther than any other, and strictly
     # nearer than every lower index (first index on ties); interior points within fp16 rounding
