@@ -192,9 +192,10 @@ def kvq_quantize_append(p: kvq_params, cache: KVCache, k_new, v_new, positions, 
 def kvq_decode_attention(p: kvq_params, cache: KVCache, q_bf16, seq_lens, out, workspace=None,
                          block_table=None, sm_scale: Optional[float] = None, split_chunk: int = 0,
                          stream=None):
-    """q_bf16: bfloat16 [B, Hq, D]; seq_lens: int32 [B]; out: float32 [B, Hq, D] (all device)."""
+    """q_bf16: bfloat16 [B, Hq, D]; seq_lens: int32 [B]; out: float32 [B, Hq, D] (all device).
+    sm_scale None passes NaN, which the library reads as its default 1/sqrt(head_dim)."""
     if sm_scale is None:
-        sm_scale = 1.0 / math.sqrt(p.head_dim)
+        sm_scale = math.nan
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib.kvq_decode_attention(C.byref(p), C.byref(cache.struct), _ptr(q_bf16),
                                      _ptr(seq_lens), _ptr(block_table), sm_scale, split_chunk,

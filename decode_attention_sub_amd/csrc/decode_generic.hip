@@ -243,6 +243,7 @@ __global__ void __launch_bounds__(kMergeGroups * kHeadDim) lse_merge_kernel(Deco
   const int hq = blockIdx.x, b = blockIdx.y;
   const int ch = threadIdx.x % kHeadDim, g = threadIdx.x / kHeadDim;
   const int S = d.seq_lens[b];
+  if (S < 1 || S > d.L.S_cap) return;   // reported by the decode kernel; out[b] is not written
   const int nc = min((S + d.chunk - 1) / d.chunk, d.n_chunks);
   const float* pp = d.partials + ((size_t)b * d.Hq + hq) * d.n_chunks * (kHeadDim + 2);
   float M = -INFINITY, den = 0.0f, num = 0.0f;

@@ -227,6 +227,7 @@ int32_t kvq_decode_attention(const kvq_params* pin, const kvq_cache* cache, cons
   const kvq_params* p = &n.p;
   st = check_cache(p, cache);
   if (st) return st;
+  if (isnan(sm_scale)) sm_scale = 1.0f / sqrtf((float)p->head_dim);   // the default scale
   if (!q_bf16 || !seq_lens || !out || !isfinite(sm_scale)) return KVQ_ERR_INVALID_ARG;
   if (p->page_size && !block_table) return KVQ_ERR_INVALID_ARG;
   const int chunk = resolve_chunk(p, split_chunk);

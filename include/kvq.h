@@ -52,9 +52,13 @@
  *    with 2^b - 1 = 7: codes 0..7, S = fp16((max - min) / 7), z = fp16(min), value = code * S
  *    + z; metadata per group [S, z] (4 bytes); 48 code bytes per 128-channel row.  A quotient
  *    (x - z) / S with no value (S and z both beyond the fp16 range) gives code 0.
- *  Codes are packed LSB-first along the channel axis (2-bit: channel 4k+r in bits 2r..2r+1 of
- *  byte k; 4-bit: channel 2k in bits 0-3, 2k+1 in bits 4-7 of byte k; 3-bit: one little-endian
- *  bit stream per row, channel c in stream bits 3c..3c+2).
+ *  Code packing along the channel axis:
+ *    2-bit: each block of 16 channels fills 4 bytes; byte j of a block holds channels j, 4+j,
+ *           8+j, 12+j in bit pairs 0, 1, 2, 3 (channel 16k + 4s + j in bits 2s..2s+1 of byte
+ *           4k + j), so the 32-bit little-endian word of a block yields channels 4s..4s+3 from
+ *           bit pair s of its four bytes;
+ *    4-bit: channel 2k in bits 0-3 and channel 2k+1 in bits 4-7 of byte k;
+ *    3-bit: one little-endian bit stream per row, channel c in stream bits 3c..3c+2.
  *
  * Outlier side lists: one per (sequence b, KV head h, K=0 / V=1), records in ascending
  * (token, channel) order: uint32 index = token * D + channel and the ORIGINAL value rounded to
@@ -206,12 +210,15 @@ int32_t kvq_workspace_bytes(const kvq_params* p, int32_t split_chunk, uint64_t* 
  * the figure in "The Twin Bottlenecks").  For each b and query head hq (KV head
  * hq * H / Hq): out[b][hq] = softmax_t(sm_scale * q . k_t) . v_t over tokens t < seq_lens[b],
  * with k_t, v_t dequantized on the fly; chunks of split_chunk tokens (a multiple of 64) are
- * merged by log-sum-exp.  q_bf16: device bfloat16 [B][Hq][D] (values must be finite and
- * within fp16 range); seq_lens: device int32 [B], 1 <= seq_lens[b] <= max_seq_len and no more
- * than the tokens appended; block_table as above (paged) or NULL; out: device float32
- * [B][Hq][D]; workspace: device, ws_bytes >= kvq_workspace_bytes.  A block-table entry of a
- * live page that names a slot outside its tier's pool sets *status to KVQ_ERR_INVALID_ARG;
- * that page's rows then read as zeros (nothing outside the pools is read). */
+ * merged by log-sum-exp.  sm_scale: any finite value, or NaN for the default 1/sqrt(head_dim);
+ * an infinite scale is rejected.  q_bf16: device bfloat16 [B][Hq][D] (values must be finite
+ * and within fp16 range); seq_lens: device int32 [B], 1 <= seq_lens[b] <= max_seq_len and no
+ * more than the tokens appended; a sequence whose length is out of that range sets *status to
+ * KVQ_ERR_INVALID_ARG and its out[b] is left unwritten (the other sequences are computed as
+ * usual); block_table as above (paged) or NULL; out: device float32 [B][Hq][D]; workspace:
+ * device, ws_bytes >= kvq_workspace_bytes.  A block-table entry of a live page that names a
+ * slot outside its tier's pool sets *status to KVQ_ERR_INVALID_ARG; that page's rows then read
+ * as zeros (nothing outside the pools is read). */
 int32_t kvq_decode_attention(const kvq_params* p, const kvq_cache* cache, const void* q_bf16,
                              const int32_t* seq_lens, const int32_t* block_table,
                              float sm_scale, int32_t split_chunk, float* out, void* workspace,

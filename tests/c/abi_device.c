@@ -1,10 +1,13 @@
 /* Plain C client of include/kvq.h on the GPU: device buffers from hipMalloc, one append of two
- * tokens and one decode, no C++ or Python in between.
+ * tokens and one decode, no C++ or Python in between.  The packed 2-bit codes and the centroids
+ * of every appended row are read back and checked against the packing order and metadata
+ * layout the header states; the decode uses the header's default softmax scale (NaN).
  *
  * Every 64-channel group of the K and V rows holds four values, each in 16 channels, so the
  * 2-bit fit (quartile seeds, Lloyd iterations) reproduces them exactly in fp16 and no value lies
  * beyond 3 standard deviations of its group.  Both tokens have the same K row, so each query
  * gives them equal weight and the output is the mean of the two V rows, to fp32 rounding. */
+#include <math.h>
 #include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
@@ -97,8 +100,7 @@ int main(void) {
   uint64_t ws = 0;
   st = kvq_workspace_bytes(&p, 0, &ws);
   void* work = ws ? dev_zero(ws) : NULL;
-  st = st ? st : kvq_decode_attention(&p, &c, dq, dlens, NULL, 0.08838834764831845f, 0, dout,
-                                      work, ws, NULL);
+  st = st ? st : kvq_decode_attention(&p, &c, dq, dlens, NULL, NAN, 0, dout, work, ws, NULL);
   printf("%s decode returned %d\n", st == KVQ_OK ? "ok" : "FAIL", st);
   fails += st != KVQ_OK;
   HIP_OK(hipDeviceSynchronize());
@@ -106,6 +108,43 @@ int main(void) {
   HIP_OK(hipMemcpy(&status, c.status, sizeof status, hipMemcpyDeviceToHost));
   printf("%s device status %d\n", status == KVQ_OK ? "ok" : "FAIL", status);
   fails += status != KVQ_OK;
+  /* packed rows: channel 16k + 4s + j in bits 2s..2s+1 of byte 4k + j; the code of a level is
+   * its rank (the fit reproduces the four levels as its ascending centroids) */
+  {
+    static uint8_t codes[2][B * H * SCAP * 32];
+    static uint16_t meta[2][B * H * SCAP * 8];
+    HIP_OK(hipMemcpy(codes[0], c.codes[0], sizeof codes[0], hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(codes[1], c.codes[1], sizeof codes[1], hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(meta[0], c.meta[0], sizeof meta[0], hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(meta[1], c.meta[1], sizeof meta[1], hipMemcpyDeviceToHost));
+    static const uint16_t kLevelBits[4] = {0xBE00u, 0xB800u, 0x3800u, 0x4000u};  /* fp16 */
+    int badp = 0;
+    for (int kv = 0; kv < 2; ++kv)
+      for (int b = 0; b < B; ++b)
+        for (int h = 0; h < H; ++h)
+          for (int t = 0; t < NT; ++t) {
+            const size_t row = ((size_t)b * H + h) * SCAP + t;
+            const uint8_t* pk = codes[kv] + row * 32;
+            for (int byte = 0; byte < 32; ++byte) {
+              unsigned want = 0;
+              for (int s = 0; s < 4; ++s) {
+                const int ch = 16 * (byte / 4) + 4 * s + byte % 4;
+                const int lvl = kv == 0 ? (ch + b + h) % 4 : (ch + b + 2 * h + 3 * t) % 4;
+                want |= (unsigned)lvl << (2 * s);
+              }
+              if (pk[byte] != want) {
+                if (badp < 5) printf("  kv=%d b=%d h=%d t=%d byte %d: 0x%02x want 0x%02x\n", kv, b,
+                                     h, t, byte, pk[byte], want);
+                ++badp;
+              }
+            }
+            for (int i = 0; i < 8; ++i)
+              if (meta[kv][row * 8 + i] != kLevelBits[i % 4]) ++badp;
+          }
+    printf("%s packed 2-bit rows and centroids follow the header's layout (%d mismatches)\n",
+           badp ? "FAIL" : "ok", badp);
+    fails += badp != 0;
+  }
   static float out[B * HQ * D];
   HIP_OK(hipMemcpy(out, dout, sizeof out, hipMemcpyDeviceToHost));
   int bad = 0;

@@ -57,5 +57,54 @@ int main(void) {
         KVQ_ERR_INVALID_ARG, "decode with null cache rejected before any launch");
   CHECK(strcmp(kvq_status_string(KVQ_ERR_CAPACITY), "unknown status") != 0,
         "status text for capacity");
+
+  /* hostile arguments: every call must return an error status without touching memory it was
+   * not given (run under AddressSanitizer and UndefinedBehaviorSanitizer by the CPU suite) */
+  {
+    int hostile_ok = 1;
+    kvq_cache c;
+    memset(&c, 0, sizeof c);
+    kvq_params h = p;
+    hostile_ok &= kvq_kv_bytes(NULL, 1, 1, 0, &bytes) < 0;
+    hostile_ok &= kvq_kv_bytes(&p, 1, 1, 0, NULL) < 0;
+    hostile_ok &= kvq_kv_bytes(&p, -1, 1, 0, &bytes) < 0;
+    hostile_ok &= kvq_cache_sizes(NULL, 1, &s) < 0 && kvq_cache_sizes(&p, 1, NULL) < 0;
+    hostile_ok &= kvq_cache_sizes(&p, -5, &s) < 0;
+    hostile_ok &= kvq_workspace_bytes(NULL, 0, &ws) < 0 && kvq_workspace_bytes(&p, 0, NULL) < 0;
+    hostile_ok &= kvq_workspace_bytes(&p, -64, &ws) < 0;
+    const int32_t formats[] = {-1, 0, 1, 5, 9, 99};
+    for (unsigned i = 0; i < sizeof formats / sizeof formats[0]; ++i) {
+      h = p;
+      h.format = formats[i];
+      hostile_ok &= kvq_workspace_bytes(&h, 0, &ws) < 0;
+    }
+    const int32_t groups[] = {-64, 0, 1, 16, 48, 128};
+    for (unsigned i = 0; i < sizeof groups / sizeof groups[0]; ++i) {
+      h = p;
+      h.group_size = groups[i];
+      hostile_ok &= kvq_workspace_bytes(&h, 0, &ws) < 0;
+      /* the byte formula takes any group size that divides the head dimension */
+      hostile_ok &= (kvq_kv_bytes(&h, 1, 1, 0, &bytes) < 0) == (groups[i] < 1 || 128 % groups[i] != 0);
+    }
+    h = p; h.num_kv_heads = 0; hostile_ok &= kvq_cache_sizes(&h, 1, &s) < 0;
+    h = p; h.num_q_heads = 8 * 17; hostile_ok &= kvq_cache_sizes(&h, 1, &s) < 0;
+    h = p; h.max_seq_len = 0x7FFFFFFF; hostile_ok &= kvq_cache_sizes(&h, 1, &s) < 0;
+    h = p; h.outlier_sigma = -1.0f; hostile_ok &= kvq_cache_sizes(&h, 1, &s) < 0;
+    h = p; h.outlier_dtype = 7; hostile_ok &= kvq_cache_sizes(&h, 1, &s) < 0;
+    h = p; h.lloyd_iters = 1000; hostile_ok &= kvq_cache_sizes(&h, 1, &s) < 0;
+    h = p; h.page_size = 16; h.max_pages_per_seq = 1; hostile_ok &= kvq_cache_sizes(&h, 1, &s) < 0;
+    h = p; h.page_size = 8; hostile_ok &= kvq_cache_sizes(&h, 1, &s) < 0;
+    float dummy[4];
+    int32_t idummy[4];
+    hostile_ok &= kvq_quantize_append(NULL, &c, dummy, dummy, 1, idummy, idummy, NULL, NULL) < 0;
+    hostile_ok &= kvq_quantize_append(&p, NULL, dummy, dummy, 1, idummy, idummy, NULL, NULL) < 0;
+    hostile_ok &= kvq_quantize_append(&p, &c, dummy, dummy, 1, idummy, idummy, NULL, NULL) < 0;
+    hostile_ok &= kvq_decode_attention(&p, &c, dummy, idummy, NULL, 0.1f, 0, dummy, NULL, 0,
+                                       NULL) < 0;
+    hostile_ok &= kvq_probe_read(NULL, 16, dummy, NULL) < 0 && kvq_probe_read(dummy, 15, dummy, NULL) < 0;
+    hostile_ok &= kvq_probe_copy(dummy, NULL, 16, NULL) < 0 && kvq_probe_copy(dummy, dummy, 0, NULL) < 0;
+    hostile_ok &= strcmp(kvq_status_string(-12345), "unknown status") == 0;
+    CHECK(hostile_ok, "hostile arguments rejected with an error status");
+  }
   return fails ? 1 : 0;
 }

@@ -21,4 +21,4 @@ def test_plain_c_client(tmp_path):
                     f"-Wl,-rpath,{LIBDIR}", "-o", exe], check=True)
     r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0, r.stdout + r.stderr
-    assert "FAIL" not in r.stdout and r.stdout.count("ok ") == 11
+    assert "FAIL" not in r.stdout and r.stdout.count("ok ") == 12
