@@ -53,21 +53,7 @@ __device__ __forceinline__ half4v read_tr16(const lds_half* p) {
 }
 
 constexpr int kStep = 32;                  // tokens per wave step
-#ifndef KVQ_TILE_ROW
-#define KVQ_TILE_ROW 136
-#endif
-constexpr int kRow = KVQ_TILE_ROW;         // LDS row stride in halfs (272 bytes by default)
-#ifdef KVQ_WAVES_PER_EU
-#define KVQ_OCC __attribute__((amdgpu_waves_per_eu(KVQ_WAVES_PER_EU)))
-#else
-#define KVQ_OCC
-#endif
-#ifndef KVQ_ROTATE
-#define KVQ_ROTATE 1
-#endif
-#ifndef KVQ_PRIO
-#define KVQ_PRIO 1
-#endif
+constexpr int kRow = 136;                  // LDS row stride in halfs (272 bytes)
 constexpr int kTile = kStep * kRow;        // halfs per tile
 
 // Workgroup shape.  Contiguous caches: 12 waves (three per SIMD), one LDS tile per wave for both
@@ -292,7 +278,7 @@ constexpr int kRowRor8 = 0x128;   // lane i <- lane (i + 8) mod 16 of its row
 // r < 8; the softmax runs on 4 scores per lane after moving tile 1's rows into lanes r >= 8.
 // PAGED: 2-bit pages behind a block table, some of them (tier 1) FP8 rows with a per-row scale.
 template <int FMT, int OUTL, bool CMP, bool PAGED>
-__global__ void __launch_bounds__(Shape<PAGED>::kWaves * 64) KVQ_OCC decode_mfma_kernel(DecodeLaunch d) {
+__global__ void __launch_bounds__(Shape<PAGED>::kWaves * 64) decode_mfma_kernel(DecodeLaunch d) {
   constexpr int kWaves = Shape<PAGED>::kWaves;
   constexpr int kWaveLds = Shape<PAGED>::kWaveLds;
   constexpr int kPF = Shape<PAGED>::kPF;
@@ -399,13 +385,11 @@ __global__ void __launch_bounds__(Shape<PAGED>::kWaves * 64) KVQ_OCC decode_mfma
   // (Paged caches scatter their pages anyway, and the scalar registers the rotation takes are
   // worth more there.)
   int rot = 0;
-#if KVQ_ROTATE
   if constexpr (!PAGED) {
     const uint32_t n_units = (uint32_t)d.n_chunks * (uint32_t)L.H * (uint32_t)L.B;
     const uint32_t unit = (uint32_t)chunk + (uint32_t)d.n_chunks * ((uint32_t)h + (uint32_t)L.H * (uint32_t)b);
     rot = nfull > 0 ? (int)(((uint64_t)unit * (uint64_t)nfull) / n_units) : 0;
   }
-#endif
   // token start of full step number c (c >= nfull: past the chunk, every load reads zeros)
   auto step_ts = [&](int c) {
     if (c >= nfull) return t1 + 2 * kStep;
@@ -758,7 +742,6 @@ __global__ void __launch_bounds__(Shape<PAGED>::kWaves * 64) KVQ_OCC decode_mfma
   Bnd bnd[NB];
   const int nmine = wi < nfull ? (nfull - wi + wpc - 1) / wpc : 0;
   auto wts = [&](int j) { return step_ts(j < nmine ? wi + wpc * j : nfull); };
-#if KVQ_PRIO
   const int mysimd = (int)((__builtin_amdgcn_s_getreg((31 << 11) | 4) >> 4) & 3);   // HW_ID.simd
   if (lane == 0) { s_simd[wave] = mysimd; s_prog[wave] = 0; }
   __syncthreads();
@@ -775,7 +758,6 @@ __global__ void __launch_bounds__(Shape<PAGED>::kWaves * 64) KVQ_OCC decode_mfma
   const int* const prog_p1 = &s_prog[peer1];
   const int* const prog_p2 = &s_prog[peer2];
   int partner_seen = 0;
-#endif
 #pragma unroll
   for (int k = 0; k < NB; ++k) bnd[k] = issue_bounds(wts(k));
 #pragma unroll
@@ -785,11 +767,9 @@ __global__ void __launch_bounds__(Shape<PAGED>::kWaves * 64) KVQ_OCC decode_mfma
   }
   const int ngroups = nmine / NB;
   for (int g = 0; g < ngroups; ++g) {
-#if KVQ_PRIO
     if (g > partner_seen) __builtin_amdgcn_s_setprio(0);
     else __builtin_amdgcn_s_setprio(1);
     if (lane == 0) *prog_mine = g;
-#endif
 #pragma unroll
     for (int u = 0; u < NB; ++u) {
       const int jj = g * NB + u;
@@ -798,13 +778,9 @@ __global__ void __launch_bounds__(Shape<PAGED>::kWaves * 64) KVQ_OCC decode_mfma
       issue_codes(buf[(u + kPF) % NB], bnd[(u + kPF) % NB], wts(jj + kPF), std::false_type{});
       consume(buf[u], rec[u], wts(jj), std::true_type{});
     }
-#if KVQ_PRIO
     partner_seen = min(__builtin_amdgcn_readfirstlane(*prog_p1), __builtin_amdgcn_readfirstlane(*prog_p2));
-#endif
   }
-#if KVQ_PRIO
   __builtin_amdgcn_s_setprio(0);
-#endif
 #pragma unroll
   for (int u = 0; u < NB; ++u) {
     const int jj = ngroups * NB + u;
