@@ -108,13 +108,44 @@ def read_ceiling_gbs(device="cuda") -> float:
     return gbs
 
 
-def cpu_baseline(dc, budget_s: float = 12.0):
-    """The oracle (float64 dequantization + attention, float32 quantization of the new token),
-    as it stands, on a sample of (sequence, KV head) groups of the same step; extrapolated to
-    the full step and expressed in the metric's unit (GB/s of algorithmic bytes)."""
-    from threadpoolctl import threadpool_info
+def _oracle_worker_init():
+    from threadpoolctl import threadpool_limits
+    threadpool_limits(1)   # one thread per worker process: cores = worker processes
+
+
+def _oracle_slice(task):
+    """The oracle's work for one (sequence, KV head) group of one step: float32 quantization of
+    the new token's K and V rows, float64 dequantization of both lists, float64 attention of the
+    group's query heads.  Returns (seconds, algorithmic bytes)."""
     from oracle import attention as OA
     from oracle import cache as OC
+    from oracle import quantize as OQ
+    spec, spec8, D, lists, x_new, qf, sm, vb = task
+    t0 = time.perf_counter()
+    for x in x_new:
+        OQ.quantize_rows(x, spec)
+    KV = []
+    for g in lists:
+        codes = OQ.unpack_codes(g["packed"], OQ.CODE_BITS[spec.fmt], D)
+        KV.append(OC.dequantize_list(codes, g["meta"], g["idx"], g["vals"], spec, D,
+                                     g["tier1"], g.get("packed8"), g.get("meta8"), spec8))
+    for q in qf:
+        OA.attention_one(q, KV[0], KV[1], sm)
+    dt = time.perf_counter() - t0
+    S = lists[0]["packed"].shape[0]
+    n_out = len(lists[0]["idx"]) + len(lists[1]["idx"])
+    row = lists[0]["packed"].shape[1] + lists[0]["meta"].shape[1]
+    return dt, 2 * S * row + n_out * (vb + 4) + len(qf) * D * 6
+
+
+def cpu_baseline(dc, single_budget_s: float = 8.0, max_groups: int = 256):
+    """The oracle (float32 quantization of the new token, float64 dequantization and attention),
+    as it stands, on a sample of (sequence, KV head) groups of the same step, in the metric's
+    unit (GB/s of algorithmic bytes).  The groups run in parallel worker processes, one per
+    host core available to this process (at most 16), each single-threaded; a second figure
+    runs groups one after another on a single core."""
+    import multiprocessing as mp
+    from oracle import attention as OA
     from oracle import quantize as OQ
     from workloads import generate as G
     from workloads.device import read_list
@@ -122,41 +153,50 @@ def cpu_baseline(dc, budget_s: float = 12.0):
     w = dc.w
     spec = OQ.QuantSpec(w.fmt, w.group, w.outlier, w.sigma, w.lloyd_iters)
     spec8 = OQ.QuantSpec("fp8row", 0, "none") if w.paged else None
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     pairs = [(b, h) for b in range(w.B) for h in range(w.H)]
     rng = np.random.default_rng(0)
     rng.shuffle(pairs)
-    done, t_total, bytes_done = 0, 0.0, 0
+    pairs = pairs[:max_groups]
+    G_ = w.Hq // w.H
     sm = 1.0 / math.sqrt(w.D)
-    for b, h in pairs:
-        lists = [read_list(dc, b, h, kv) for kv in (0, 1)]   # device bytes, read outside timing
-        S = int(dc.seq_lens_host[b])
+    vb = 2 if w.outlier == "fp16" else 1
+    tasks = []
+    for b, h in pairs:   # device bytes are read back before any timing
+        lists = [read_list(dc, b, h, kv) for kv in (0, 1)]
         x_new = [G.new_rows(w, b, h, G.NEW_K + kv, 0) for kv in (0, 1)]
+        qf = OA.bf16_to_f64(dc.q_host[b])[h * G_:(h + 1) * G_]
+        tasks.append((spec, spec8, w.D, lists, x_new, qf, sm, vb))
+    host_cpus = os.cpu_count() or 1
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = host_cpus
+    workers = max(1, min(avail, 16))
+    ctx = mp.get_context("spawn")
+    with ctx.Pool(workers, initializer=_oracle_worker_init) as pool:
+        pool.map(_oracle_slice, tasks[:workers], chunksize=1)   # warm the workers
         t0 = time.perf_counter()
-        for kv in (0, 1):
-            OQ.quantize_rows(x_new[kv], spec)                # append of the new token
-        KV = []
-        for g in lists:
-            codes = OQ.unpack_codes(g["packed"], OQ.CODE_BITS[w.fmt], w.D)
-            KV.append(OC.dequantize_list(codes, g["meta"], g["idx"], g["vals"], spec, w.D,
-                                         g["tier1"], g.get("packed8"), g.get("meta8"), spec8))
-        qf = OA.bf16_to_f64(dc.q_host[b])
-        G_ = w.Hq // w.H
-        for hq in range(h * G_, (h + 1) * G_):
-            OA.attention_one(qf[hq], KV[0], KV[1], sm)
-        t_total += time.perf_counter() - t0
-        n_out = len(lists[0]["idx"]) + len(lists[1]["idx"])
-        sz_row = lists[0]["packed"].shape[1] + lists[0]["meta"].shape[1]
-        bytes_done += 2 * S * sz_row + n_out * ((2 if w.outlier == "fp16" else 1) + 4) \
-            + G_ * w.D * 6
-        done += 1
-        if t_total >= budget_s:
-            break
-    gbs = bytes_done / t_total / 1e9
-    return {"value": round(gbs, 6), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} of {len(pairs)} (sequence, KV head) groups of one step "
-                      f"({done * (w.Hq // w.H)} query heads over their full context), "
-                      f"{t_total:.1f} s of oracle time, extrapolated by bytes"}
+        res = pool.map(_oracle_slice, tasks, chunksize=1)
+        wall = time.perf_counter() - t0
+    par_bytes = sum(r[1] for r in res)
+    with ctx.Pool(1, initializer=_oracle_worker_init) as pool:
+        pool.map(_oracle_slice, tasks[:1])
+        one_t, one_b, n_one = 0.0, 0, 0
+        for dt, nb in pool.imap(_oracle_slice, tasks, chunksize=1):
+            one_t += dt
+            one_b += nb
+            n_one += 1
+            if one_t >= single_budget_s:
+                break
+    return {"value": round(par_bytes / wall / 1e9, 6), "unit": "GB/s", "cores": workers,
+            "kind": "oracle",
+            "sample": f"{len(tasks)} of {w.B * w.H} (sequence, KV head) groups of one step "
+                      f"({len(tasks) * G_} query heads over their full context) in {workers} "
+                      f"single-threaded worker processes, {wall:.1f} s wall, "
+                      f"{sum(r[0] for r in res):.1f} s of oracle time; host has {host_cpus} CPUs, "
+                      f"{avail} available to the process",
+            "single_core": {"value": round(one_b / one_t / 1e9, 6), "unit": "GB/s", "cores": 1,
+                            "sample": f"{n_one} groups one after another, {one_t:.1f} s"}}
 
 
 def main():
