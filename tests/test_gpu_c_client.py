@@ -19,4 +19,4 @@ def test_plain_c_client_on_gpu():
     r = subprocess.run([EXE], capture_output=True, text=True, timeout=120)
     print(r.stdout, flush=True)
     assert r.returncode == 0, r.stdout + r.stderr
-    assert "FAIL" not in r.stdout and r.stdout.count("ok ") == 4
+    assert "FAIL" not in r.stdout and r.stdout.count("ok ") == 5
