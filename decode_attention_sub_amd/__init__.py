@@ -25,7 +25,9 @@ FMT = {"fp16": 0, "fp8row": 1, "int4": 2, "fp4": 3, "c2": 4, "bf16": 5, "u2": 6,
 OUTL = {"none": 0, "fp16": 1, "e4m3": 2}
 
 EXPORTED = ("kvq_kv_bytes", "kvq_cache_sizes", "kvq_quantize_append", "kvq_workspace_bytes",
-            "kvq_decode_attention", "kvq_probe_read", "kvq_probe_copy", "kvq_status_string")
+            "kvq_decode_attention", "kvq_decode_attention_noalloc", "kvq_probe_read",
+            "kvq_probe_copy", "kvq_status_string")
+NOALLOC_SCRATCH_BYTES = 32 << 20   # KVQ_NOALLOC_SCRATCH_BYTES
 
 
 class kvq_params(C.Structure):
@@ -68,6 +70,8 @@ def _load():
         "kvq_workspace_bytes": (C.c_int32, [P, C.c_int32, C.POINTER(C.c_uint64)]),
         "kvq_decode_attention": (C.c_int32, [P, Pc, vp, vp, vp, C.c_float, C.c_int32, vp, vp,
                                              C.c_uint64, vp]),
+        "kvq_decode_attention_noalloc": (C.c_int32, [P, Pc, vp, vp, vp, C.c_float, C.c_int32,
+                                                     vp, vp]),
         "kvq_probe_read": (C.c_int32, [vp, C.c_uint64, vp, vp]),
         "kvq_probe_copy": (C.c_int32, [vp, vp, C.c_uint64, vp]),
         "kvq_status_string": (C.c_char_p, [C.c_int32]),
@@ -201,6 +205,19 @@ def kvq_decode_attention(p: kvq_params, cache: KVCache, q_bf16, seq_lens, out, w
                                      _ptr(seq_lens), _ptr(block_table), sm_scale, split_chunk,
                                      _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)),
            "kvq_decode_attention")
+
+
+def kvq_decode_attention_noalloc(p: kvq_params, cache: KVCache, q_bf16, seq_lens, out,
+                                 block_table=None, sm_scale: Optional[float] = None,
+                                 split_chunk: int = 0, stream=None):
+    """kvq_decode_attention without a workspace: the split-K partials live in the library's
+    per-GPU scratch array (at most NOALLOC_SCRATCH_BYTES); nothing is allocated."""
+    if sm_scale is None:
+        sm_scale = math.nan
+    _check(_lib.kvq_decode_attention_noalloc(C.byref(p), C.byref(cache.struct), _ptr(q_bf16),
+                                             _ptr(seq_lens), _ptr(block_table), sm_scale,
+                                             split_chunk, _ptr(out), _stream(stream)),
+           "kvq_decode_attention_noalloc")
 
 
 def kvq_probe_read(src, sink, stream=None):

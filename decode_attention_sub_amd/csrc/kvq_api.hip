@@ -3,6 +3,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "kvq_device.h"
 #include "kvq_launch.h"
 
@@ -114,6 +116,82 @@ int resolve_chunk(const kvq_params* p, int32_t split_chunk) {
   return split_chunk;
 }
 
+
+// Scratch memory of kvq_decode_attention_noalloc: the split-K partials of callers that cannot
+// allocate.  Each GPU the library runs on holds its own copy until the process ends; host code
+// never uses the array's name as an address (it is a host-side stand-in): the device address is
+// looked up once per device with hipGetSymbolAddress, with that device current, and kept here.
+__device__ __align__(256) uint8_t scratch[KVQ_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// Device address of the current device's scratch array.
+int32_t scratch_ptr(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return KVQ_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return KVQ_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return KVQ_ERR_HIP;
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return KVQ_OK;
+}
+
+// Validation and launches of a decode.  workspace == nullptr with use_scratch: the split-K
+// partials go to this device's scratch array (kvq_decode_attention_noalloc).
+int32_t decode_impl(const kvq_params* pin, const kvq_cache* cache, const void* q_bf16,
+                    const int32_t* seq_lens, const int32_t* block_table, float sm_scale,
+                    int32_t split_chunk, float* out, void* workspace, uint64_t ws_bytes,
+                    bool use_scratch, void* stream) {
+  int32_t st = check_params(pin);
+  if (st) return st;
+  const Params n(pin);
+  const kvq_params* p = &n.p;
+  st = check_cache(p, cache);
+  if (st) return st;
+  if (isnan(sm_scale)) sm_scale = 1.0f / sqrtf((float)p->head_dim);   // the default scale
+  if (!q_bf16 || !seq_lens || !out || !isfinite(sm_scale)) return KVQ_ERR_INVALID_ARG;
+  if (p->page_size && !block_table) return KVQ_ERR_INVALID_ARG;
+  const int chunk = resolve_chunk(p, split_chunk);
+  if (chunk < 0) return KVQ_ERR_INVALID_ARG;
+  uint64_t need = 0;
+  kvq_workspace_bytes(p, chunk, &need);
+  if (use_scratch && need) {
+    if (need > KVQ_NOALLOC_SCRATCH_BYTES) return KVQ_ERR_WORKSPACE;
+    st = scratch_ptr(&workspace);
+    if (st) return st;
+    ws_bytes = KVQ_NOALLOC_SCRATCH_BYTES;
+  }
+  if (need && (!workspace || ws_bytes < need)) return KVQ_ERR_WORKSPACE;
+  DecodeLaunch d;
+  d.L = make_layout(p, cache->outl_capacity);
+  d.cache = *cache;
+  d.q = (const uint16_t*)q_bf16;
+  d.seq_lens = seq_lens;
+  d.block_table = p->page_size ? block_table : nullptr;
+  d.out = out;
+  d.Hq = p->num_q_heads;
+  d.fmt = p->format;
+  d.group = p->group_size;
+  d.outl = p->outlier_dtype;
+  d.chunk = chunk;
+  d.n_chunks = (p->max_seq_len + chunk - 1) / chunk;
+  d.partials = d.n_chunks > 1 ? (float*)workspace : nullptr;
+  d.scale_log2 = sm_scale * 1.4426950408889634f;
+  d.cpw = 1;
+  hipStream_t s = (hipStream_t)stream;
+  bool handled = false;
+  if (launch_decode_mfma(d, s, &handled) != hipSuccess) return KVQ_ERR_HIP;
+  if (!handled && launch_decode_generic(d, s) != hipSuccess) return KVQ_ERR_HIP;
+  if (d.n_chunks > 1 && launch_lse_merge(d, s) != hipSuccess) return KVQ_ERR_HIP;
+  return KVQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -221,42 +299,16 @@ int32_t kvq_decode_attention(const kvq_params* pin, const kvq_cache* cache, cons
                              const int32_t* seq_lens, const int32_t* block_table,
                              float sm_scale, int32_t split_chunk, float* out, void* workspace,
                              uint64_t ws_bytes, void* stream) {
-  int32_t st = check_params(pin);
-  if (st) return st;
-  const Params n(pin);
-  const kvq_params* p = &n.p;
-  st = check_cache(p, cache);
-  if (st) return st;
-  if (isnan(sm_scale)) sm_scale = 1.0f / sqrtf((float)p->head_dim);   // the default scale
-  if (!q_bf16 || !seq_lens || !out || !isfinite(sm_scale)) return KVQ_ERR_INVALID_ARG;
-  if (p->page_size && !block_table) return KVQ_ERR_INVALID_ARG;
-  const int chunk = resolve_chunk(p, split_chunk);
-  if (chunk < 0) return KVQ_ERR_INVALID_ARG;
-  uint64_t need = 0;
-  kvq_workspace_bytes(p, chunk, &need);
-  if (need && (!workspace || ws_bytes < need)) return KVQ_ERR_WORKSPACE;
-  DecodeLaunch d;
-  d.L = make_layout(p, cache->outl_capacity);
-  d.cache = *cache;
-  d.q = (const uint16_t*)q_bf16;
-  d.seq_lens = seq_lens;
-  d.block_table = p->page_size ? block_table : nullptr;
-  d.out = out;
-  d.Hq = p->num_q_heads;
-  d.fmt = p->format;
-  d.group = p->group_size;
-  d.outl = p->outlier_dtype;
-  d.chunk = chunk;
-  d.n_chunks = (p->max_seq_len + chunk - 1) / chunk;
-  d.partials = d.n_chunks > 1 ? (float*)workspace : nullptr;
-  d.scale_log2 = sm_scale * 1.4426950408889634f;
-  d.cpw = 1;
-  hipStream_t s = (hipStream_t)stream;
-  bool handled = false;
-  if (launch_decode_mfma(d, s, &handled) != hipSuccess) return KVQ_ERR_HIP;
-  if (!handled && launch_decode_generic(d, s) != hipSuccess) return KVQ_ERR_HIP;
-  if (d.n_chunks > 1 && launch_lse_merge(d, s) != hipSuccess) return KVQ_ERR_HIP;
-  return KVQ_OK;
+  return decode_impl(pin, cache, q_bf16, seq_lens, block_table, sm_scale, split_chunk, out,
+                     workspace, ws_bytes, false, stream);
+}
+
+int32_t kvq_decode_attention_noalloc(const kvq_params* pin, const kvq_cache* cache,
+                                     const void* q_bf16, const int32_t* seq_lens,
+                                     const int32_t* block_table, float sm_scale,
+                                     int32_t split_chunk, float* out, void* stream) {
+  return decode_impl(pin, cache, q_bf16, seq_lens, block_table, sm_scale, split_chunk, out,
+                     nullptr, 0, true, stream);
 }
 
 int32_t kvq_probe_read(const void* src, uint64_t bytes, void* sink, void* stream) {

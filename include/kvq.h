@@ -3,7 +3,8 @@
  *
  * C ABI of libkvq.so.  Every pointer argument named "device" is a HIP device pointer; every
  * other pointer is host memory.  The caller owns and frees every buffer; the library keeps no
- * global state and allocates no device memory.  Work is enqueued on the caller's stream
+ * global state and allocates no device memory (kvq_decode_attention_noalloc keeps one static
+ * scratch array per GPU, see there).  Work is enqueued on the caller's stream
  * (``stream`` is a hipStream_t, passed as void*; NULL is the default stream) and the call
  * returns before the work completes.  Functions return KVQ_OK (0) or a negative kvq_status.
  *
@@ -223,6 +224,22 @@ int32_t kvq_decode_attention(const kvq_params* p, const kvq_cache* cache, const 
                              const int32_t* seq_lens, const int32_t* block_table,
                              float sm_scale, int32_t split_chunk, float* out, void* workspace,
                              uint64_t ws_bytes, void* stream);
+
+/* kvq_decode_attention for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same computation and the
+ * same kernels, with the split-K partials in a scratch array the library holds in each GPU's
+ * memory (a static device array of KVQ_NOALLOC_SCRATCH_BYTES, kept until the process ends);
+ * nothing is allocated by the call.  The caller still passes the inputs and the output; the
+ * current device must be the device of `stream`.  Returns KVQ_ERR_WORKSPACE when the partials
+ * of this call (kvq_workspace_bytes for the same params and split_chunk) exceed
+ * KVQ_NOALLOC_SCRATCH_BYTES; choose a longer split_chunk then.  All calls on one GPU share its
+ * scratch array: calls that may overlap on one GPU (different streams without ordering) race
+ * and must not be issued.  Otherwise as kvq_decode_attention. */
+#define KVQ_NOALLOC_SCRATCH_BYTES (32ull << 20)
+int32_t kvq_decode_attention_noalloc(const kvq_params* p, const kvq_cache* cache,
+                                     const void* q_bf16, const int32_t* seq_lens,
+                                     const int32_t* block_table, float sm_scale,
+                                     int32_t split_chunk, float* out, void* stream);
 
 /* Streaming read of `bytes` (multiple of 16) from device buffer src, XOR-reduced into sink
  * (device, >= 4 * 1024 * 256 bytes): measures the practical HBM read ceiling. */
