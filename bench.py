@@ -204,6 +204,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--ramp-s", type=float, default=0.3,
+                    help="seconds of back-to-back steps before the warmup steps, so the shader "
+                         "clock has ramped up whatever --warmup is (not timed, not counted)")
     ap.add_argument("--workload", default="c2_b64_s32k")
     ap.add_argument("--split", type=int, default=-1, help="split-K chunk (default: workload's)")
     ap.add_argument("--fmt", default=None,
@@ -288,6 +291,14 @@ def main():
         if ev is not None:
             ev[1].record(stream)
 
+    # clock ramp: the shader clock climbs over the first few dozen back-to-back decodes
+    t_ramp = time.perf_counter()
+    n_ramp = 0
+    while time.perf_counter() - t_ramp < args.ramp_s:
+        for _ in range(5):
+            step(n_ramp % n_total)
+            n_ramp += 1
+        torch.cuda.synchronize()
     for s in range(args.warmup):
         step(s)
     torch.cuda.synchronize()
@@ -330,7 +341,8 @@ def main():
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "H": w.H, "D": w.D,
                    "S": int(lens_h.max()), "format": w.fmt, "group": w.group,
                    "outliers": w.outlier, "tau": w.sigma, "split_chunk": split if split else "default",
-                   "layers": 1, "cache_flush_per_step": flush, "channel_mask": w.chan_mask},
+                   "layers": 1, "cache_flush_per_step": flush, "channel_mask": w.chan_mask,
+                   "clock_ramp_steps": n_ramp},
         "us_per_step_decode": round(dec_ms * 1e3, 2),
         "us_decode_p10_p50_p90": [round(float(np.percentile(dec_all, q)) * 1e3, 2) for q in (10, 50, 90)],
         "us_per_step": round(ms_step * 1e3, 2),

@@ -56,30 +56,27 @@ constexpr int kStep = 32;                  // tokens per wave step
 constexpr int kRow = 136;                  // LDS row stride in halfs (272 bytes)
 constexpr int kTile = kStep * kRow;        // halfs per tile
 
-// Workgroup shape.  Contiguous caches: 12 waves (three per SIMD), one LDS tile per wave for both
-// K and V rows, one step of loads in flight, score MFMAs issued before the V rows are expanded
-// (their operands then die early): the registers fit three waves per SIMD.  Paged caches keep
-// 8 waves with separate K and V tiles and one step in flight; their extra addressing state
-// does not fit three waves per SIMD.
-template <bool PAGED> struct Shape {
-  static constexpr int kWaves = PAGED ? 8 : 12;
-  static constexpr int kTiles = PAGED ? 2 : 1;
-  static constexpr int kPF = 1;                   // steps of codes / records in flight per wave
-  static constexpr bool kEarlyS = !PAGED;
-  static constexpr int kWaveLds = kTiles * kTile; // halfs of LDS per wave
-};
-
+// Workgroup shape: 12 waves (three per SIMD), one LDS tile per wave that holds the K rows and
+// then the V rows of a step, one step of codes and records in flight, score MFMAs issued before
+// the V rows are expanded (their operands then die early): the registers fit three waves per
+// SIMD.
+constexpr int kWaves = 12;
+constexpr int kPF = 1;                     // steps of codes / records in flight per wave
+// Paged caches: a workgroup lists the pages of its chunk by tier, this many pages at a time.
+constexpr int kSegPages = 256;
+constexpr uint32_t kDead = 0xFFFFFFFFu;    // no page: its rows read as zeros
 
 template <int FMT> struct Buf;
-// ek, ev: pool-row bases of the pages of the lane's K and V tokens (paged caches)
-template <> struct Buf<FMT_C2> { uint4 kc, vc; uint2 km, vm; uint32_t ek, ev; };
-template <> struct Buf<FMT_FP4> { uint4 kc0, kc1, vc0, vc1; uint32_t km, vm, ek, ev; };
-// record bounds of a step (lanes 0..3) and, for paged caches, the block-table entries of the
-// pages of the lane's K and V tokens (per lane: the page state stays out of scalar registers)
-struct Bnd { uint32_t rec, pk, pv; };
-// FP8-tier rows of a step (paged caches): a lane's K and V half rows and their rows' scales;
-// fk / fv tell whether the lane's K / V token sits on an FP8 page, slow whether any token does
-struct F8 { uint4 k[4], v[4]; uint32_t ks, vs; bool fk, fv, slow; };
+template <> struct Buf<FMT_C2> { uint4 kc, vc; uint2 km, vm; };
+template <> struct Buf<FMT_FP4> { uint4 kc0, kc1, vc0, vc1; uint32_t km, vm; };
+
+// A step of a paged cache: two pages of one tier (uniform): their pool rows of this KV head
+// (kDead: no page) and logical page numbers.
+struct PStep { uint32_t rowA, rowB; int pA, pB; };
+
+// FP8-tier rows of a step (paged caches): a lane's K and V half rows, and the row scales of the
+// tokens of its scores (K) and probabilities (V)
+struct Buf8 { uint4 k[4], v[4]; floatx4 ks0, ks1, vs0, vs1; };
 
 // FP8 row codes -> fp16 in channel order (E4M3 values are exact in fp16)
 __device__ __forceinline__ void expand_fp8(const uint4 (&c)[4], _Float16* dst) {
@@ -98,12 +95,17 @@ __device__ __forceinline__ void expand_fp8(const uint4 (&c)[4], _Float16* dst) {
   }
 }
 
-// Outlier records of one step: lane slots K and V hold records kr0 + lane and vr0 + lane.
-// Values are kept as the aligned 32-bit words that hold them.
+// The outlier records of one step of one list: records a0 .. a0 + na - 1, then (paged caches:
+// those of the step's second page) b0 .. b0 + nb - 1.  baseA / baseB: the record index (token *
+// 128 + channel) of tile row 0 for the records of each range.
+struct RecList { int a0, na, b0, nb; uint32_t baseA, baseB; };
+// Lane slot i of a list holds record i of the step.  Values are kept as the aligned 32-bit words
+// that hold them; kb, vb (paged caches): the lane's record's base and its value's bit offset.
 struct Recs {
   uint32_t ik, vk;         // K: index word, value word
   uint32_t iv, vv;         // V: index word, value word
-  int kr0, nk, vr0, nv;    // first record and record count of each list (uniform)
+  uint32_t kbase, kbit, vbase, vbit;
+  RecList k, v;
 };
 
 // raw buffer resource (gfx9 family): loads at byte offsets >= num_records return zero
@@ -230,11 +232,12 @@ __device__ __forceinline__ uint32_t tile_pos_v(uint32_t dd) {
   return (uint32_t)vrow_of((int)t) * (uint32_t)kRow + (dd & 127u);
 }
 
-// Overwrite one outlier position of a tile straight from the record (crowded or ragged steps).
-// A record outside the step goes to a pad slot (row 0, column 128) that no operand read touches.
+// Overwrite one outlier position of a tile straight from the record (crowded steps); base is the
+// record index of tile row 0.  A record outside the step's valid tokens goes to a pad slot (row
+// 0, column 128) that no operand read touches.
 template <int FMT, int OUTL, bool VT>
-__device__ __forceinline__ void patch_at(_Float16* tile, uint32_t idx, uint32_t val, int ts, int nval) {
-  const uint32_t dd = idx - (uint32_t)ts * 128u;
+__device__ __forceinline__ void patch_at(_Float16* tile, uint32_t idx, uint32_t val, uint32_t base, int nval) {
+  const uint32_t dd = idx - base;
   const uint32_t at = dd < (uint32_t)nval * 128u ? (VT ? tile_pos_v(dd) : tile_pos(dd)) : (uint32_t)kHeadDim;
   tile[at] = outl_half<OUTL>(val);
 }
@@ -277,15 +280,19 @@ constexpr int kRowRor8 = 0x128;   // lane i <- lane (i + 8) mod 16 of its row
 // CMP: at most 8 query heads per KV head.  Score tiles then hold real query rows only in lanes
 // r < 8; the softmax runs on 4 scores per lane after moving tile 1's rows into lanes r >= 8.
 // PAGED: 2-bit pages behind a block table, some of them (tier 1) FP8 rows with a per-row scale.
+// The workgroup lists the pages of its chunk by tier (kSegPages at a time, in logical order) and
+// takes the 2-bit pages two at a time as 32-token steps shaped like a contiguous cache's, then
+// the FP8 pages two at a time (attention does not depend on the order of the tokens).  Only the
+// last step of each tier's list can hold fewer than 32 tokens (a single page, or the sequence's
+// partial last page).
 template <int FMT, int OUTL, bool CMP, bool PAGED>
-__global__ void __launch_bounds__(Shape<PAGED>::kWaves * 64) decode_mfma_kernel(DecodeLaunch d) {
-  constexpr int kWaves = Shape<PAGED>::kWaves;
-  constexpr int kWaveLds = Shape<PAGED>::kWaveLds;
-  constexpr int kPF = Shape<PAGED>::kPF;
-  __shared__ __attribute__((aligned(16))) _Float16 s_lds[kWaves * kWaveLds];
+__global__ void __launch_bounds__(kWaves * 64) decode_mfma_kernel(DecodeLaunch d) {
+  __shared__ __attribute__((aligned(16))) _Float16 s_lds[kWaves * kTile];
   __shared__ float s_ml[kWaves][16][2];
   __shared__ int s_simd[kWaves], s_prog[kWaves];   // SIMD of each wave, groups done
-  __shared__ __attribute__((aligned(16))) float s_rs[PAGED ? kWaves : 1][2][kStep];   // FP8-tier row scales (K, V)
+  // paged: the listed pages of each tier: {pool row of this KV head or kDead, logical page}
+  __shared__ __attribute__((aligned(16))) uint32_t s_pl[PAGED ? 2 : 1][PAGED ? kSegPages : 1][2];
+  __shared__ int s_wn[PAGED ? kSegPages / 64 : 1][2];   // pages per tier of each listing wave
 
   const Layout& L = d.L;
   // KV head fastest: consecutive workgroups (dealt round-robin to the XCDs) then carry the same
@@ -296,7 +303,7 @@ __global__ void __launch_bounds__(Shape<PAGED>::kWaves * 64) decode_mfma_kernel(
     if (threadIdx.x == 0 && grp == 0 && h == 0) report(d.cache.status, KVQ_ERR_INVALID_ARG);
     return;
   }
-  // The workgroup covers chunks cpw * grp .. + cpw - 1, wpc waves each.
+  // The workgroup covers chunks cpw * grp .. + cpw - 1, wpc waves each (paged caches: cpw = 1).
   const int cpw = d.cpw, wpc = kWaves / cpw;
   if (grp * cpw * d.chunk >= S) return;
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
@@ -313,10 +320,10 @@ __global__ void __launch_bounds__(Shape<PAGED>::kWaves * 64) decode_mfma_kernel(
   constexpr int VB = OUTL == KVQ_OUTL_FP16 ? 2 : 1;
   constexpr bool HAS_OUTL = OUTL != KVQ_OUTL_NONE;
 
-  // With one tile, K rows are expanded and read back as operands before V rows overwrite them
-  // (a wave's LDS operations complete in issue order).
-  _Float16* ktile = s_lds + wave * kWaveLds;
-  _Float16* vtile = ktile + (Shape<PAGED>::kTiles - 1) * kTile;
+  // One tile per wave: K rows are expanded and read back as operands before V rows overwrite
+  // them (a wave's LDS operations complete in issue order).
+  _Float16* const ktile = s_lds + wave * kTile;
+  _Float16* const vtile = ktile;
 
   // query operand (B of S^T = K^ Q^T): lane (row r, k-group kg), positions 32*ks + 8*kg + e
   half8 qop[4];
@@ -337,16 +344,13 @@ __global__ void __launch_bounds__(Shape<PAGED>::kWaves * 64) decode_mfma_kernel(
   }
 
   // buffer resources.  Contiguous: rows [0, t1) of this (sequence, KV head); rows past t1 read as
-  // zero.  Paged: the whole page pools (rows past t1 get out-of-range offsets).
+  // zero.  Paged: the whole page pools (rows of absent pages get out-of-range offsets).
   const size_t rowbase = PAGED ? 0 : ((size_t)b * L.H + h) * (size_t)L.S_cap;
   const uint32_t nrows = PAGED ? (uint32_t)L.num_pages * (uint32_t)L.H * kBlock : (uint32_t)t1;
   const __amdgpu_buffer_rsrc_t rcK = make_rsrc((const uint8_t*)d.cache.codes[0] + rowbase * CB, nrows * CB);
   const __amdgpu_buffer_rsrc_t rcV = make_rsrc((const uint8_t*)d.cache.codes[1] + rowbase * CB, nrows * CB);
   const __amdgpu_buffer_rsrc_t rmK = make_rsrc((const uint8_t*)d.cache.meta[0] + rowbase * MB, nrows * MB);
   const __amdgpu_buffer_rsrc_t rmV = make_rsrc((const uint8_t*)d.cache.meta[1] + rowbase * MB, nrows * MB);
-  // paged: this sequence's block-table row (FP8-tier rows are read through plain pointers on the
-  // rare steps that have them, keeping their descriptors out of the scalar registers)
-  const int32_t* __restrict__ btrow = PAGED ? d.block_table + (size_t)b * L.max_pages : nullptr;
   const uint32_t coff = (uint32_t)(trow * CB + half * (CB / 2));
   const uint32_t coffv = (uint32_t)(vtok(trow) * CB + half * (CB / 2));
   const uint32_t lane4 = (uint32_t)lane * 4u, laneVB = (uint32_t)lane * VB, laneVB8 = laneVB * 8u;
@@ -374,154 +378,7 @@ __global__ void __launch_bounds__(Shape<PAGED>::kWaves * 64) decode_mfma_kernel(
     cntV = max(0, min(d.cache.outl_count[lidK + 1], cap));
   }
 
-  // The chunk's full 32-token steps are spread over its waves; its ragged last step (if any) is
-  // left to the chunk's first wave after the others.
-  const int nsteps = (t1 - t0 + kStep - 1) / kStep;
-  const bool ragged = (t1 - t0) % kStep != 0;
-  const int nfull = nsteps - (ragged ? 1 : 0);
-  // Workgroups walk their full steps in rotated order, starting at evenly spread points.  Every
-  // (sequence, head) slice starts at the same power-of-two-aligned offset; walking them in
-  // lockstep would send every workgroup to the same HBM channels at the same time.
-  // (Paged caches scatter their pages anyway, and the scalar registers the rotation takes are
-  // worth more there.)
-  int rot = 0;
-  if constexpr (!PAGED) {
-    const uint32_t n_units = (uint32_t)d.n_chunks * (uint32_t)L.H * (uint32_t)L.B;
-    const uint32_t unit = (uint32_t)chunk + (uint32_t)d.n_chunks * ((uint32_t)h + (uint32_t)L.H * (uint32_t)b);
-    rot = nfull > 0 ? (int)(((uint64_t)unit * (uint64_t)nfull) / n_units) : 0;
-  }
-  // token start of full step number c (c >= nfull: past the chunk, every load reads zeros)
-  auto step_ts = [&](int c) {
-    if (c >= nfull) return t1 + 2 * kStep;
-    int a = c + rot;
-    if (a >= nfull) a -= nfull;
-    return t0 + kStep * a;
-  };
-
   constexpr uint32_t kOOB = 0xFFFFFFF0u;   // an offset past every buffer range
-  // Paged caches: a page entry is turned into the pool row of the page's first row for this KV
-  // head, (slot * H + h) * 16, or'ed with 2^31 for an FP8 page, or kDead when the page holds no
-  // token < t1 or its slot lies outside its pool (flagged in bad_page, reported at the end).
-  // Rows of 2-bit pages lie below 2^27 (pools below 4 GiB), FP8 rows below 2^25.
-  constexpr uint32_t kDead = 0xFFFFFFFFu;
-  bool bad_page = false;
-  auto enc_page = [&](uint32_t e, bool live) -> uint32_t {
-    const uint32_t slot = e & 0x7FFFFFFFu;
-    const bool in_pool = slot < (uint32_t)((e >> 31) ? L.num_pages_fp8 : L.num_pages);
-    bad_page = bad_page || __builtin_amdgcn_ballot_w64(live && !in_pool) != 0;
-    return live && in_pool ? ((slot * (uint32_t)L.H + (uint32_t)h) * kBlock) | (e & 0x80000000u) : kDead;
-  };
-  // lane constants: a lane's K token is trow (second page from 16 on), its V token vtok(trow)
-  const bool kpageB = trow >= 16, vpageB = (trow & 1) != 0;
-  const uint32_t lcK = (uint32_t)(trow & 15) * CB + half * (CB / 2);
-  const uint32_t lcV = (uint32_t)(trow >> 1) * CB + half * (CB / 2);
-  const uint32_t lmK = (uint32_t)(trow & 15) * MB + half * (MB / 2);
-  const uint32_t lmV = (uint32_t)(trow >> 1) * MB + half * (MB / 2);
-  // RAGGED: the step may hold tokens >= t1 (only the chunk's last step)
-  auto issue_codes = [&](Buf<FMT>& bf, const Bnd& bd, int tsi, auto ragged_tag) {
-    const uint32_t ts = (uint32_t)tsi;
-    if constexpr (PAGED) {
-      constexpr bool RAGGED = decltype(ragged_tag)::value;
-      bf.ek = enc_page(bd.pk, tsi + (kpageB ? 16 : 0) < t1);
-      bf.ev = enc_page(bd.pv, tsi + (vpageB ? 16 : 0) < t1);
-      const uint32_t ek = bf.ek, ev = bf.ev;
-      bool okk = ek < (1u << 27), okv = ev < (1u << 27);
-      if constexpr (RAGGED) {
-        okk = okk && tsi + trow < t1;
-        okv = okv && tsi + vtok(trow) < t1;
-      }
-      const uint32_t ok = okk ? ek * CB + lcK : kOOB;
-      const uint32_t ov = okv ? ev * CB + lcV : kOOB;
-      const uint32_t mk = okk ? ek * MB + lmK : kOOB;
-      const uint32_t mv = okv ? ev * MB + lmV : kOOB;
-      bf.kc = ld128<kNT>(rcK, ok);
-      bf.vc = ld128<kNT>(rcV, ov);
-      bf.km = ld64<kNT>(rmK, mk);
-      bf.vm = ld64<kNT>(rmV, mv);
-    } else if constexpr (FMT == FMT_C2) {
-      // 2-bit rows are read once: non-temporal loads (measured faster; for FP4 rows, slower)
-      bf.kc = ld128s<kNT>(rcK, coff, ts * CB);
-      bf.vc = ld128s<kNT>(rcV, coffv, ts * CB);
-      bf.km = ld64s<kNT>(rmK, moff, ts * MB);
-      bf.vm = ld64s<kNT>(rmV, moffv, ts * MB);
-    } else {
-      bf.kc0 = ld128s(rcK, coff, ts * CB);
-      bf.kc1 = ld128s(rcK, coff + 16, ts * CB);
-      bf.vc0 = ld128s(rcV, coffv, ts * CB);
-      bf.vc1 = ld128s(rcV, coffv + 16, ts * CB);
-      bf.km = ld16s(rmK, moff, ts * MB);
-      bf.vm = ld16s(rmV, moffv, ts * MB);
-    }
-  };
-  // lanes 0..3 load {K start, K end, V start, V end} of the step's records (block starts); for
-  // paged caches lanes 0, 1 also load the block-table entries of its two pages
-  auto issue_bounds = [&](int ts) -> Bnd {
-    Bnd bd{0u, 0u, 0u};
-    const int blk = ts >> 4;
-    if constexpr (HAS_OUTL) {
-      const int which = lane & 3;  // 0: K blk, 1: K blk+2, 2: V blk, 3: V blk+2
-      const uint32_t off = (uint32_t)(((which >> 1) * L.nblk + blk + 2 * (which & 1)) * 4);
-      bd.rec = ld32(rbs, off);
-    }
-    if constexpr (PAGED) {   // entries past the row are clamped to its last (their pages are dead)
-      const int last = L.max_pages - 1;
-      bd.pk = (uint32_t)btrow[min(blk + (kpageB ? 1 : 0), last)];
-      bd.pv = (uint32_t)btrow[min(blk + (vpageB ? 1 : 0), last)];
-    }
-    return bd;
-  };
-  auto issue_recs = [&](Recs& rc, const Bnd& bd, int ts) {
-    if constexpr (HAS_OUTL) {
-      const uint32_t bnd = bd.rec;
-      const bool last = ts + kStep >= S;
-      const int k0 = max(0, min(__builtin_amdgcn_readlane((int)bnd, 0), cap));
-      const int k1 = last ? cntK : max(0, min(__builtin_amdgcn_readlane((int)bnd, 1), cap));
-      const int v0 = max(0, min(__builtin_amdgcn_readlane((int)bnd, 2), cap));
-      const int v1 = last ? cntV : max(0, min(__builtin_amdgcn_readlane((int)bnd, 3), cap));
-      rc.kr0 = k0; rc.nk = max(k1 - k0, 0);
-      rc.vr0 = v0; rc.nv = max(v1 - v0, 0);
-      // Slots past a list's records read past its range (zeros) or unused records.  Values are
-      // read as the aligned 32-bit word that holds them and extracted where they are used: a byte
-      // or short load would leave the compiler a narrow value that it re-extends at the loop
-      // back-edge, waiting for the load there.
-      rc.ik = ld32s(riK, lane4, (uint32_t)k0 * 4u);
-      rc.iv = ld32s(riV, lane4, (uint32_t)v0 * 4u);
-      // value word of a lane's record: the list's byte offset k0 * VB + lv3 (uniform) split into
-      // its word-aligned part (scalar offset) and its remainder, which joins the lane's bytes
-      const uint32_t bk = (uint32_t)k0 * VB + lv3, bv = (uint32_t)v0 * VB + lv3;
-      rc.vk = ld32s(rvK, ((bk & 3u) + laneVB) & ~3u, bk & ~3u);
-      rc.vv = ld32s(rvV, ((bv & 3u) + laneVB) & ~3u, bv & ~3u);
-    }
-  };
-  // paged: FP8-tier rows of a step, loaded when the step is consumed (only when one of its pages
-  // is FP8, one step in five; holding them a step ahead cost more in registers than their
-  // latency costs here)
-  auto load_fp8 = [&](F8& f, const Buf<FMT>& bf, int ts) {
-    if constexpr (PAGED) {
-      const auto is8 = [](uint32_t e) { return (e >> 31) != 0 && e != kDead; };
-      f.slow = __builtin_amdgcn_ballot_w64(is8(bf.ek) || is8(bf.ev)) != 0;
-      if (f.slow) {
-        const uint32_t ek = bf.ek, ev = bf.ev;
-        f.fk = is8(ek) && ts + trow < t1;
-        f.fv = is8(ev) && ts + vtok(trow) < t1;
-        const uint32_t rk = (ek & 0x7FFFFFFFu) + (uint32_t)(trow & 15);
-        const uint32_t rv = (ev & 0x7FFFFFFFu) + (uint32_t)(trow >> 1);
-        // only lanes whose row lies on a live FP8 page (inside its pool) load
-        if (f.fk) {
-          const uint4* src = (const uint4*)((const uint8_t*)d.cache.codes8[0] + (size_t)rk * kHeadDim + 64u * half);
-#pragma unroll
-          for (int k = 0; k < 4; ++k) f.k[k] = src[k];
-          f.ks = as_u32(d.cache.scale8[0][rk]);
-        }
-        if (f.fv) {
-          const uint4* src = (const uint4*)((const uint8_t*)d.cache.codes8[1] + (size_t)rv * kHeadDim + 64u * half);
-#pragma unroll
-          for (int k = 0; k < 4; ++k) f.v[k] = src[k];
-          f.vs = as_u32(d.cache.scale8[1][rv]);
-        }
-      }
-    }
-  };
 
   floatx4 oacc[8];
 #pragma unroll
@@ -532,17 +389,16 @@ __global__ void __launch_bounds__(Shape<PAGED>::kWaves * 64) decode_mfma_kernel(
   float m_thr = -INFINITY;
   const float sl2 = fabsf(d.scale_log2);
 
-  // One 32-token step.  FULL: every token of the step is valid.  Records past the first 64 of a
-  // step (per list) are written by rarely taken loops.  Otherwise the body is one
-  // branch-free block: K rows are expanded and written, the K^ operand reads are issued, V rows
-  // are expanded while those reads are in flight, the score MFMAs run, the V^T operand reads are
-  // issued before the softmax needs them.
-  auto consume = [&](const Buf<FMT>& bf, const Recs& rc, int ts, auto full_tag) {
+  // One 32-token step.  FULL: every token of the step is valid; otherwise tokens < nval are.
+  // IS8: FP8-tier rows (b8) with per-row scales, no outliers; otherwise codes (bf) and outlier
+  // records (rc; records of tile row 0 at rc's bases).  Records past the first 64 of a step (per
+  // list) are written by rarely taken loops.  Otherwise the body is one branch-free block: K rows
+  // are expanded and written, the K^ operand reads are issued, the score MFMAs run, V rows are
+  // expanded while those finish, the V^T operand reads are issued before the softmax needs them.
+  auto consume = [&](const Buf<FMT>& bf, const Buf8& b8, const Recs& rc, uint32_t kb0, uint32_t vb0,
+                     int nval, auto full_tag, auto is8_tag) {
     constexpr bool FULL = decltype(full_tag)::value;
-    F8 f8;
-    f8.slow = false;
-    load_fp8(f8, bf, ts);
-    const int nval = FULL ? kStep : min(kStep, t1 - ts);
+    constexpr bool IS8 = decltype(is8_tag)::value;
     _Float16* krow = ktile + trow * kRow + 64 * half;
     _Float16* vrow = vtile + trow * kRow + 64 * half;
     // tile positions of this lane's record slots; an unused slot writes the lane's own pad slot
@@ -551,40 +407,31 @@ __global__ void __launch_bounds__(Shape<PAGED>::kWaves * 64) decode_mfma_kernel(
     const uint32_t pad = (uint32_t)(trow * kRow + kHeadDim + 4 * half);
     uint32_t posK = pad, posV = pad;
     _Float16 ovK, ovV;
-    if constexpr (HAS_OUTL) {
+    const int nk = rc.k.na + rc.k.nb, nv = rc.v.na + rc.v.nb;
+    if constexpr (HAS_OUTL && !IS8) {
       // bit offsets of the values inside their words (bit-field extraction takes them modulo 32)
-      const uint32_t bitK = laneVB8 + ((uint32_t)rc.kr0 * VB + lv3) * 8u;
-      const uint32_t bitV = laneVB8 + ((uint32_t)rc.vr0 * VB + lv3) * 8u;
+      const uint32_t bitK = PAGED ? rc.kbit : laneVB8 + ((uint32_t)rc.k.a0 * VB + lv3) * 8u;
+      const uint32_t bitV = PAGED ? rc.vbit : laneVB8 + ((uint32_t)rc.v.a0 * VB + lv3) * 8u;
       const uint32_t lim = (uint32_t)nval * 128u;
-      const uint32_t ddk = rc.ik - (uint32_t)ts * 128u;
-      posK = lane < rc.nk && ddk < lim ? tile_pos(ddk) : pad;
+      const uint32_t ddk = rc.ik - (PAGED ? rc.kbase : kb0);
+      posK = lane < nk && ddk < lim ? tile_pos(ddk) : pad;
       ovK = outl_from_word<OUTL>(rc.vk, bitK);
-      const uint32_t ddv = rc.iv - (uint32_t)ts * 128u;
-      posV = lane < rc.nv && ddv < lim ? tile_pos_v(ddv) : pad;
+      const uint32_t ddv = rc.iv - (PAGED ? rc.vbase : vb0);
+      posV = lane < nv && ddv < lim ? tile_pos_v(ddv) : pad;
       ovV = outl_from_word<OUTL>(rc.vv, bitV);
     }
-    if constexpr (FMT == FMT_C2) expand_c2(bf.kc, bf.km, krow);
+    if constexpr (IS8) expand_fp8(b8.k, krow);
+    else if constexpr (FMT == FMT_C2) expand_c2(bf.kc, bf.km, krow);
     else expand_fp4(bf.kc0, bf.kc1, bf.km, krow);
-    float* const rsk = PAGED ? s_rs[wave][0] : nullptr;
-    float* const rsv = PAGED ? s_rs[wave][1] : nullptr;
-    if constexpr (PAGED) {
-      // FP8 rows replace the (zero) 2-bit rows of their tokens; the row scales multiply the
-      // scores (K) and the probabilities (V); tier-2 rows have scale 1
-      if (f8.slow) {
-        if (f8.fk) expand_fp8(f8.k, krow);
-        if (half == 0) {
-          rsk[trow] = f8.fk ? as_f32(f8.ks) : 1.0f;
-          rsv[vtok(trow)] = f8.fv ? as_f32(f8.vs) : 1.0f;
-        }
-      }
-    }
-    if constexpr (HAS_OUTL) {
+    if constexpr (HAS_OUTL && !IS8) {
       ktile[posK] = ovK;
-      if (rc.nk > 64) {
-        for (int a = 64 + lane; a < rc.nk; a += 64) {  // the rest of a crowded step
-          const uint32_t at = (uint32_t)(rc.kr0 + a), byte = at * VB + lv3;
+      if (nk > 64) {
+        for (int a = 64 + lane; a < nk; a += 64) {  // the rest of a crowded step
+          const bool inA = a < rc.k.na;
+          const uint32_t at = (uint32_t)(inA ? rc.k.a0 + a : rc.k.b0 + (a - rc.k.na));
+          const uint32_t byte = at * VB + lv3;
           const uint32_t v = __builtin_amdgcn_ubfe(ld32(rvK, byte & ~3u), (byte & 3u) * 8u, VB * 8);
-          patch_at<FMT, OUTL, false>(ktile, ld32(riK, at * 4u), v, ts, nval);
+          patch_at<FMT, OUTL, false>(ktile, ld32(riK, at * 4u), v, inA ? rc.k.baseA : rc.k.baseB, nval);
         }
       }
     }
@@ -595,33 +442,24 @@ __global__ void __launch_bounds__(Shape<PAGED>::kWaves * 64) decode_mfma_kernel(
       ak[4 + ks] = *(const half8*)(ktile + (16 + r) * kRow + 32 * ks + 8 * kg);
     }
     floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (Shape<PAGED>::kEarlyS) {
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak[ks], qop[ks], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak[4 + ks], qop[ks], s1, 0, 0, 0);
-      }
+    for (int ks = 0; ks < 4; ++ks) {
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak[ks], qop[ks], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak[4 + ks], qop[ks], s1, 0, 0, 0);
     }
-    if constexpr (FMT == FMT_C2) expand_c2(bf.vc, bf.vm, vrow);
+    if constexpr (IS8) expand_fp8(b8.v, vrow);
+    else if constexpr (FMT == FMT_C2) expand_c2(bf.vc, bf.vm, vrow);
     else expand_fp4(bf.vc0, bf.vc1, bf.vm, vrow);
-    if constexpr (PAGED) {
-      if (f8.slow && f8.fv) expand_fp8(f8.v, vrow);
-    }
-    if constexpr (HAS_OUTL) {
+    if constexpr (HAS_OUTL && !IS8) {
       vtile[posV] = ovV;
-      if (rc.nv > 64) {
-        for (int i = 64 + lane; i < rc.nv; i += 64) {
-          const uint32_t at = (uint32_t)(rc.vr0 + i), byte = at * VB + lv3;
+      if (nv > 64) {
+        for (int a = 64 + lane; a < nv; a += 64) {
+          const bool inA = a < rc.v.na;
+          const uint32_t at = (uint32_t)(inA ? rc.v.a0 + a : rc.v.b0 + (a - rc.v.na));
+          const uint32_t byte = at * VB + lv3;
           const uint32_t v = __builtin_amdgcn_ubfe(ld32(rvV, byte & ~3u), (byte & 3u) * 8u, VB * 8);
-          patch_at<FMT, OUTL, true>(vtile, ld32(riV, at * 4u), v, ts, nval);
+          patch_at<FMT, OUTL, true>(vtile, ld32(riV, at * 4u), v, inA ? rc.v.baseA : rc.v.baseB, nval);
         }
-      }
-    }
-    if constexpr (!Shape<PAGED>::kEarlyS) {
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak[ks], qop[ks], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak[4 + ks], qop[ks], s1, 0, 0, 0);
       }
     }
     // V^T operands (16 channels x 32 tokens per M-tile) through transposing LDS reads
@@ -651,19 +489,9 @@ __global__ void __launch_bounds__(Shape<PAGED>::kWaves * 64) decode_mfma_kernel(
 #pragma unroll
       for (int v = 0; v < 4; ++v) { sc[v] = s0[v]; sc[4 + v] = s1[v]; }
     }
-    // tokens of the lane's scores: 4 kg + v (+16 for tile 1)
-    const int tb0 = CMP ? (r >= 8 ? 16 : 0) + 4 * kg : 4 * kg;
-    floatx4 vsc[NS / 4];
-    if constexpr (PAGED) {
-      if (f8.slow) {
+    if constexpr (IS8) {   // FP8 rows: the K row scales multiply the scores
 #pragma unroll
-        for (int i = 0; i < NS / 4; ++i) {
-          const floatx4 ksc = *(const floatx4*)(rsk + tb0 + 16 * i);
-          vsc[i] = *(const floatx4*)(rsv + tb0 + 16 * i);
-#pragma unroll
-          for (int v = 0; v < 4; ++v) sc[4 * i + v] *= ksc[v];
-        }
-      }
+      for (int v = 0; v < NS; ++v) sc[v] *= (v < 4 ? b8.ks0 : b8.ks1)[v % 4];
     }
     bool valid[NS];
 #pragma unroll
@@ -699,8 +527,10 @@ __global__ void __launch_bounds__(Shape<PAGED>::kWaves * 64) decode_mfma_kernel(
       float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[v + 1], sl2, -m_run));
       if constexpr (!FULL) { p0 = valid[v] ? p0 : 0.0f; p1 = valid[v + 1] ? p1 : 0.0f; }
       psum = v == 0 ? p0 + p1 : psum + (p0 + p1);
-      if constexpr (PAGED) {
-        if (f8.slow) { p0 *= vsc[v / 4][v % 4]; p1 *= vsc[v / 4][v % 4 + 1]; }
+      if constexpr (IS8) {   // FP8 rows: the V row scales multiply the probabilities
+        const floatx4 vs = v < 4 ? b8.vs0 : b8.vs1;
+        p0 = FULL || valid[v] ? p0 * vs[v % 4] : 0.0f;
+        p1 = FULL || valid[v + 1] ? p1 * vs[v % 4 + 1] : 0.0f;
       }
       const half2v hi = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(p0, p1));
       hw[v / 2] = __builtin_bit_cast(uint32_t, hi);
@@ -728,20 +558,10 @@ __global__ void __launch_bounds__(Shape<PAGED>::kWaves * 64) decode_mfma_kernel(
       }
     }
   };
-  // ---- software pipeline: codes and records of the next kPF steps in flight, the record
-  // bounds of the step after them too.  Wave wi of a chunk takes its full steps wi, wi + wpc, ...;
-  // whole groups of NB steps run without conditions, so every ring slot keeps its registers and
-  // the wait counters stay exact.  Loads for steps past the chunk return zeros without touching
-  // memory.
-  //
-  // Two or three waves share each SIMD and the scheduler favours the oldest; every group, a wave
-  // that is ahead of the slower of its SIMD peers lowers its priority, so all finish together.
-  constexpr int NB = kPF + 1;  // ring slots
-  Buf<FMT> buf[NB];
-  Recs rec[NB];
-  Bnd bnd[NB];
-  const int nmine = wi < nfull ? (nfull - wi + wpc - 1) / wpc : 0;
-  auto wts = [&](int j) { return step_ts(j < nmine ? wi + wpc * j : nfull); };
+
+  // Two or three waves share each SIMD and the scheduler favours the oldest; every group of
+  // steps, a wave that is ahead of the slower of its SIMD peers lowers its priority, so all
+  // finish together.
   const int mysimd = (int)((__builtin_amdgcn_s_getreg((31 << 11) | 4) >> 4) & 3);   // HW_ID.simd
   if (lane == 0) { s_simd[wave] = mysimd; s_prog[wave] = 0; }
   __syncthreads();
@@ -757,50 +577,360 @@ __global__ void __launch_bounds__(Shape<PAGED>::kWaves * 64) decode_mfma_kernel(
   int* const prog_mine = &s_prog[wave];
   const int* const prog_p1 = &s_prog[peer1];
   const int* const prog_p2 = &s_prog[peer2];
-  int partner_seen = 0;
+
+  const Buf8 no8{};
+  constexpr int NB = kPF + 1;  // ring slots
+
+  if constexpr (!PAGED) {
+    // The chunk's full 32-token steps are spread over its waves; its ragged last step (if any) is
+    // left to the chunk's first wave after the others.
+    const int nsteps = (t1 - t0 + kStep - 1) / kStep;
+    const bool ragged = (t1 - t0) % kStep != 0;
+    const int nfull = nsteps - (ragged ? 1 : 0);
+    // Workgroups walk their full steps in rotated order, starting at evenly spread points.  Every
+    // (sequence, head) slice starts at the same power-of-two-aligned offset; walking them in
+    // lockstep would send every workgroup to the same HBM channels at the same time.
+    const uint32_t n_units = (uint32_t)d.n_chunks * (uint32_t)L.H * (uint32_t)L.B;
+    const uint32_t unit = (uint32_t)chunk + (uint32_t)d.n_chunks * ((uint32_t)h + (uint32_t)L.H * (uint32_t)b);
+    const int rot = nfull > 0 ? (int)(((uint64_t)unit * (uint64_t)nfull) / n_units) : 0;
+    // token start of full step number c (c >= nfull: past the chunk, every load reads zeros)
+    auto step_ts = [&](int c) {
+      if (c >= nfull) return t1 + 2 * kStep;
+      int a = c + rot;
+      if (a >= nfull) a -= nfull;
+      return t0 + kStep * a;
+    };
+    // RAGGED: the step may hold tokens >= t1 (only the chunk's last step); the buffer ranges end
+    // at row t1, so those rows read as zeros
+    auto issue_codes = [&](Buf<FMT>& bf, int tsi) {
+      const uint32_t ts = (uint32_t)tsi;
+      if constexpr (FMT == FMT_C2) {
+        // 2-bit rows are read once: non-temporal loads (measured faster; for FP4 rows, slower)
+        bf.kc = ld128s<kNT>(rcK, coff, ts * CB);
+        bf.vc = ld128s<kNT>(rcV, coffv, ts * CB);
+        bf.km = ld64s<kNT>(rmK, moff, ts * MB);
+        bf.vm = ld64s<kNT>(rmV, moffv, ts * MB);
+      } else {
+        bf.kc0 = ld128s(rcK, coff, ts * CB);
+        bf.kc1 = ld128s(rcK, coff + 16, ts * CB);
+        bf.vc0 = ld128s(rcV, coffv, ts * CB);
+        bf.vc1 = ld128s(rcV, coffv + 16, ts * CB);
+        bf.km = ld16s(rmK, moff, ts * MB);
+        bf.vm = ld16s(rmV, moffv, ts * MB);
+      }
+    };
+    // lanes 0..3 load {K start, K end, V start, V end} of the step's records (block starts)
+    auto issue_bounds = [&](int ts) -> uint32_t {
+      if constexpr (HAS_OUTL) {
+        const int which = lane & 3;  // 0: K blk, 1: K blk+2, 2: V blk, 3: V blk+2
+        const uint32_t off = (uint32_t)(((which >> 1) * L.nblk + (ts >> 4) + 2 * (which & 1)) * 4);
+        return ld32(rbs, off);
+      }
+      return 0u;
+    };
+    auto issue_recs = [&](Recs& rc, uint32_t bnd, int ts) {
+      if constexpr (HAS_OUTL) {
+        const bool last = ts + kStep >= S;
+        const int k0 = max(0, min(__builtin_amdgcn_readlane((int)bnd, 0), cap));
+        const int k1 = last ? cntK : max(0, min(__builtin_amdgcn_readlane((int)bnd, 1), cap));
+        const int v0 = max(0, min(__builtin_amdgcn_readlane((int)bnd, 2), cap));
+        const int v1 = last ? cntV : max(0, min(__builtin_amdgcn_readlane((int)bnd, 3), cap));
+        const uint32_t base = (uint32_t)ts * 128u;   // record index of the step's first row
+        rc.k = RecList{k0, max(k1 - k0, 0), 0, 0, base, base};
+        rc.v = RecList{v0, max(v1 - v0, 0), 0, 0, base, base};
+        // Slots past a list's records read past its range (zeros) or unused records.  Values are
+        // read as the aligned 32-bit word that holds them and extracted where they are used: a
+        // byte or short load would leave the compiler a narrow value that it re-extends at the
+        // loop back-edge, waiting for the load there.
+        rc.ik = ld32s(riK, lane4, (uint32_t)k0 * 4u);
+        rc.iv = ld32s(riV, lane4, (uint32_t)v0 * 4u);
+        // value word of a lane's record: the list's byte offset k0 * VB + lv3 (uniform) split
+        // into its word-aligned part (scalar offset) and its remainder, which joins the lane's bytes
+        const uint32_t bk = (uint32_t)k0 * VB + lv3, bv = (uint32_t)v0 * VB + lv3;
+        rc.vk = ld32s(rvK, ((bk & 3u) + laneVB) & ~3u, bk & ~3u);
+        rc.vv = ld32s(rvV, ((bv & 3u) + laneVB) & ~3u, bv & ~3u);
+      } else {
+        rc.k = RecList{0, 0, 0, 0, 0u, 0u};
+        rc.v = rc.k;
+      }
+    };
+    // ---- software pipeline: codes and records of the next kPF steps in flight, the record
+    // bounds of the step after them too.  Wave wi of a chunk takes its full steps wi, wi + wpc,
+    // ...; whole groups of NB steps run without conditions, so every ring slot keeps its
+    // registers and the wait counters stay exact.  Loads for steps past the chunk return zeros
+    // without touching memory.
+    Buf<FMT> buf[NB];
+    Recs rec[NB];
+    uint32_t bnd[NB];
+    const int nmine = wi < nfull ? (nfull - wi + wpc - 1) / wpc : 0;
+    auto wts = [&](int j) { return step_ts(j < nmine ? wi + wpc * j : nfull); };
+    int partner_seen = 0;
 #pragma unroll
-  for (int k = 0; k < NB; ++k) bnd[k] = issue_bounds(wts(k));
+    for (int k = 0; k < NB; ++k) bnd[k] = issue_bounds(wts(k));
 #pragma unroll
-  for (int k = 0; k < kPF; ++k) {
-    issue_recs(rec[k], bnd[k], wts(k));
-    issue_codes(buf[k], bnd[k], wts(k), std::false_type{});
-  }
-  const int ngroups = nmine / NB;
-  for (int g = 0; g < ngroups; ++g) {
-    if (g > partner_seen) __builtin_amdgcn_s_setprio(0);
-    else __builtin_amdgcn_s_setprio(1);
-    if (lane == 0) *prog_mine = g;
+    for (int k = 0; k < kPF; ++k) {
+      issue_recs(rec[k], bnd[k], wts(k));
+      issue_codes(buf[k], wts(k));
+    }
+    const int ngroups = nmine / NB;
+    for (int g = 0; g < ngroups; ++g) {
+      if (g > partner_seen) __builtin_amdgcn_s_setprio(0);
+      else __builtin_amdgcn_s_setprio(1);
+      if (lane == 0) *prog_mine = g;
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+        const int jj = g * NB + u;
+        bnd[u] = issue_bounds(wts(jj + NB));
+        issue_recs(rec[(u + kPF) % NB], bnd[(u + kPF) % NB], wts(jj + kPF));
+        issue_codes(buf[(u + kPF) % NB], wts(jj + kPF));
+        const uint32_t base = (uint32_t)wts(jj) * 128u;
+        consume(buf[u], no8, rec[u], base, base, kStep, std::true_type{}, std::false_type{});
+      }
+      partner_seen = min(__builtin_amdgcn_readfirstlane(*prog_p1), __builtin_amdgcn_readfirstlane(*prog_p2));
+    }
+    __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int u = 0; u < NB; ++u) {
-      const int jj = g * NB + u;
-      bnd[u] = issue_bounds(wts(jj + NB));
-      issue_recs(rec[(u + kPF) % NB], bnd[(u + kPF) % NB], wts(jj + kPF));
-      issue_codes(buf[(u + kPF) % NB], bnd[(u + kPF) % NB], wts(jj + kPF), std::false_type{});
-      consume(buf[u], rec[u], wts(jj), std::true_type{});
+      const int jj = ngroups * NB + u;
+      if (jj < nmine) {
+        bnd[u] = issue_bounds(wts(jj + NB));
+        issue_recs(rec[(u + kPF) % NB], bnd[(u + kPF) % NB], wts(jj + kPF));
+        issue_codes(buf[(u + kPF) % NB], wts(jj + kPF));
+        const uint32_t base = (uint32_t)wts(jj) * 128u;
+        consume(buf[u], no8, rec[u], base, base, kStep, std::true_type{}, std::false_type{});
+      }
     }
-    partner_seen = min(__builtin_amdgcn_readfirstlane(*prog_p1), __builtin_amdgcn_readfirstlane(*prog_p2));
-  }
-  __builtin_amdgcn_s_setprio(0);
+    if (ragged && wi == 0) {
+      const int ts = t0 + kStep * (nsteps - 1);
+      const uint32_t b0 = issue_bounds(ts);
+      issue_recs(rec[0], b0, ts);
+      issue_codes(buf[0], ts);
+      consume(buf[0], no8, rec[0], (uint32_t)ts * 128u, (uint32_t)ts * 128u, t1 - ts,
+              std::false_type{}, std::false_type{});
+    }
+  } else {
+    // ---------------------------------------------------------------- paged caches
+    const int pend = (t1 + kBlock - 1) / kBlock;   // pages [t0 / 16, pend) of the chunk
+    const int32_t* btrow = d.block_table + (size_t)b * L.max_pages;
+    const uint32_t rows8 = (uint32_t)L.num_pages_fp8 * (uint32_t)L.H * kBlock;
+    const __amdgpu_buffer_rsrc_t r8K = make_rsrc(d.cache.codes8[0], rows8 * kHeadDim);
+    const __amdgpu_buffer_rsrc_t r8V = make_rsrc(d.cache.codes8[1], rows8 * kHeadDim);
+    const __amdgpu_buffer_rsrc_t rsK = make_rsrc(d.cache.scale8[0], rows8 * 4u);
+    const __amdgpu_buffer_rsrc_t rsV = make_rsrc(d.cache.scale8[1], rows8 * 4u);
+    // tokens of page p present in the sequence
+    auto page_tokens = [&](int p) { return min(kBlock, S - kBlock * p); };
+    // the pool row of the lane's K token (row trow of the tile) and V token (vtok(trow)) in a step
+    // (fields are copied before any select: a select between two fields of one struct keeps the
+    // struct in memory)
+    auto krow_of = [&](const PStep& st) {
+      const uint32_t ra = st.rowA, rb = st.rowB;
+      const uint32_t base = trow < 16 ? ra : rb;
+      return base == kDead ? kDead : base + (uint32_t)(trow & 15);
+    };
+    auto vrow_of_step = [&](const PStep& st) {
+      const uint32_t ra = st.rowA, rb = st.rowB;
+      const uint32_t base = (trow & 1) ? rb : ra;
+      return base == kDead ? kDead : base + (uint32_t)(trow >> 1);
+    };
+    // step j of a tier's list of n pages (entries 2j, 2j + 1); an absent page has page number
+    // -1 and no rows
+    auto pstep = [&](int tier, int j, int n) -> PStep {
+      if (2 * j >= n) return PStep{kDead, kDead, -1, -1};
+      const uint4 e = *(const uint4*)&s_pl[tier][2 * j][0];   // a pair of entries
+      const bool hasB = 2 * j + 1 < n;
+      return PStep{(uint32_t)__builtin_amdgcn_readfirstlane((int)e.x),
+                   hasB ? (uint32_t)__builtin_amdgcn_readfirstlane((int)e.z) : kDead,
+                   __builtin_amdgcn_readfirstlane((int)e.y),
+                   hasB ? __builtin_amdgcn_readfirstlane((int)e.w) : -1};
+    };
+    // tokens of a step (a prefix of its 32: only the last entry of a list can be partial)
+    auto step_tokens = [&](const PStep& st) {
+      return (st.pA < 0 ? 0 : page_tokens(st.pA)) + (st.pB < 0 ? 0 : page_tokens(st.pB));
+    };
+    // RAGGED: rows of tokens >= nval get out-of-range offsets (they read as zeros)
+    auto issue_codes = [&](Buf<FMT>& bf, const PStep& st, int nval, auto ragged_tag) {
+      constexpr bool RAGGED = decltype(ragged_tag)::value;
+      const uint32_t rk = krow_of(st), rv = vrow_of_step(st);
+      const bool okk = rk != kDead && (!RAGGED || trow < nval);
+      const bool okv = rv != kDead && (!RAGGED || vtok(trow) < nval);
+      bf.kc = ld128<kNT>(rcK, okk ? rk * CB + half * (CB / 2) : kOOB);
+      bf.vc = ld128<kNT>(rcV, okv ? rv * CB + half * (CB / 2) : kOOB);
+      bf.km = ld64<kNT>(rmK, okk ? rk * MB + half * (MB / 2) : kOOB);
+      bf.vm = ld64<kNT>(rmV, okv ? rv * MB + half * (MB / 2) : kOOB);
+    };
+    // lanes 0..7 load the block starts {K: pA, pA + 1, pB, pB + 1; V: the same}
+    auto issue_bounds = [&](const PStep& st) -> uint32_t {
+      if constexpr (HAS_OUTL) {
+        const int which = lane & 7;
+        const int pa = st.pA, pb = st.pB;
+        const int p = max((which & 2) ? pb : pa, 0) + (which & 1);
+        return ld32(rbs, (uint32_t)(((which >> 2) * L.nblk + p) * 4));
+      }
+      return 0u;
+    };
+    auto issue_recs = [&](Recs& rc, uint32_t bnd, const PStep& st) {
+      if constexpr (HAS_OUTL) {
+        auto range = [&](int l0, int l1, int pg, uint32_t row, int cnt) {
+          const int a = max(0, min(__builtin_amdgcn_readlane((int)bnd, l0), cap));
+          const int e = kBlock * (pg + 1) >= S ? cnt : max(0, min(__builtin_amdgcn_readlane((int)bnd, l1), cap));
+          return int2{a, pg < 0 || row == kDead ? 0 : max(e - a, 0)};   // none for absent pages
+        };
+        const int2 kA = range(0, 1, st.pA, st.rowA, cntK), kB = range(2, 3, st.pB, st.rowB, cntK);
+        const int2 vA = range(4, 5, st.pA, st.rowA, cntV), vB = range(6, 7, st.pB, st.rowB, cntV);
+        const uint32_t baseA = (uint32_t)st.pA * (kBlock * 128u);
+        const uint32_t baseB = (uint32_t)st.pB * (kBlock * 128u) - kBlock * 128u;
+        rc.k = RecList{kA.x, kA.y, kB.x, kB.y, baseA, baseB};
+        rc.v = RecList{vA.x, vA.y, vB.x, vB.y, baseA, baseB};
+        const bool ka = lane < kA.y, va = lane < vA.y;
+        const uint32_t rk = (uint32_t)(ka ? kA.x + lane : kB.x + lane - kA.y);
+        const uint32_t rv = (uint32_t)(va ? vA.x + lane : vB.x + lane - vA.y);
+        rc.kbase = ka ? baseA : baseB;
+        rc.vbase = va ? baseA : baseB;
+        rc.ik = ld32(riK, rk * 4u);
+        rc.iv = ld32(riV, rv * 4u);
+        const uint32_t bk = rk * VB + lv3, bv = rv * VB + lv3;
+        rc.vk = ld32(rvK, bk & ~3u);
+        rc.vv = ld32(rvV, bv & ~3u);
+        rc.kbit = (bk & 3u) * 8u;
+        rc.vbit = (bv & 3u) * 8u;
+      } else {
+        rc.k = RecList{0, 0, 0, 0, 0u, 0u};
+        rc.v = rc.k;
+      }
+    };
+    auto load8 = [&](Buf8& f, const PStep& st, int nval) {
+      const uint32_t rk = krow_of(st), rv = vrow_of_step(st);
+      const uint32_t ok = rk != kDead && trow < nval ? rk * kHeadDim + 64u * half : kOOB;
+      const uint32_t ov = rv != kDead && vtok(trow) < nval ? rv * kHeadDim + 64u * half : kOOB;
 #pragma unroll
-  for (int u = 0; u < NB; ++u) {
-    const int jj = ngroups * NB + u;
-    if (jj < nmine) {
-      bnd[u] = issue_bounds(wts(jj + NB));
-      issue_recs(rec[(u + kPF) % NB], bnd[(u + kPF) % NB], wts(jj + kPF));
-      issue_codes(buf[(u + kPF) % NB], bnd[(u + kPF) % NB], wts(jj + kPF), std::false_type{});
-      consume(buf[u], rec[u], wts(jj), std::true_type{});
-    }
-  }
-  if (ragged && wi == 0) {
-    const int ts = t0 + kStep * (nsteps - 1);
-    const Bnd b0 = issue_bounds(ts);
-    issue_recs(rec[0], b0, ts);
-    issue_codes(buf[0], b0, ts, std::true_type{});
-    consume(buf[0], rec[0], ts, std::false_type{});
-  }
+      for (int k = 0; k < 4; ++k) {
+        f.k[k] = ld128(r8K, ok == kOOB ? kOOB : ok + 16u * k);
+        f.v[k] = ld128(r8V, ov == kOOB ? kOOB : ov + 16u * k);
+      }
+      // scales of the lane's score tokens: CMP 4 kg + v of tile (r >= 8), else of both tiles
+#pragma unroll
+      for (int i = 0; i < (CMP ? 1 : 2); ++i) {
+        const int tb = (CMP ? (r >= 8 ? 16 : 0) : 16 * i) + 4 * kg;
+        const uint32_t ra = st.rowA, rb = st.rowB;
+        const uint32_t base = tb < 16 ? ra : rb;
+        const uint32_t off = base != kDead && tb < nval ? (base + (uint32_t)(tb & 15)) * 4u : kOOB;
+        const floatx4 ks = __builtin_bit_cast(floatx4, ld128(rsK, off));
+        const floatx4 vs = __builtin_bit_cast(floatx4, ld128(rsV, off));
+        if (i == 0) { f.ks0 = ks; f.vs0 = vs; } else { f.ks1 = ks; f.vs1 = vs; }
+      }
+    };
+    const Buf<FMT> no2{};
+    Recs norec;
+    norec.k = RecList{0, 0, 0, 0, 0u, 0u};
+    norec.v = norec.k;
 
-  if constexpr (PAGED) {
-    if (bad_page && lane == 0) report(d.cache.status, KVQ_ERR_INVALID_ARG);
+    for (int sp0 = t0 / kBlock; sp0 < pend; sp0 += kSegPages) {
+      const int np = min(kSegPages, pend - sp0);
+      // ---- list the segment's pages by tier, in logical order (threads 0 .. kSegPages - 1)
+      const int tid = threadIdx.x;
+      int tier = -1;
+      uint32_t prow = kDead;
+      if (tid < np) {
+        const uint32_t e = (uint32_t)btrow[sp0 + tid];
+        const uint32_t slot = e & 0x7FFFFFFFu;
+        const bool is8 = (e >> 31) != 0;
+        const bool in_pool = slot < (uint32_t)(is8 ? L.num_pages_fp8 : L.num_pages);
+        if (!in_pool) report(d.cache.status, KVQ_ERR_INVALID_ARG);
+        tier = in_pool && is8 ? 1 : 0;   // a slot outside its pool: listed as a page of no rows
+        prow = in_pool ? (slot * (uint32_t)L.H + (uint32_t)h) * kBlock : kDead;
+      }
+      const uint64_t m0 = __builtin_amdgcn_ballot_w64(tier == 0);
+      const uint64_t m1 = __builtin_amdgcn_ballot_w64(tier == 1);
+      if (tid < kSegPages && lane == 0) {
+        s_wn[tid >> 6][0] = __builtin_popcountll(m0);
+        s_wn[tid >> 6][1] = __builtin_popcountll(m1);
+      }
+      if (lane == 0) *prog_mine = 0;
+      __syncthreads();
+      if (tier >= 0) {
+        int pos = 0;
+        for (int w2 = 0; w2 < (tid >> 6); ++w2) pos += s_wn[w2][tier];
+        const uint64_t m = tier ? m1 : m0;
+        pos += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        s_pl[tier][pos][0] = prow;
+        s_pl[tier][pos][1] = (uint32_t)(sp0 + tid);
+      }
+      int n2 = 0, n8 = 0;
+#pragma unroll
+      for (int w2 = 0; w2 < kSegPages / 64; ++w2) { n2 += s_wn[w2][0]; n8 += s_wn[w2][1]; }
+      n2 = __builtin_amdgcn_readfirstlane(n2);
+      n8 = __builtin_amdgcn_readfirstlane(n8);
+      __syncthreads();
+
+      // ---- 2-bit pages, two per step: full steps pipelined as for contiguous caches
+      const int ns2 = (n2 + 1) / 2;
+      const bool rag2 = n2 > 0 && ((n2 & 1) || page_tokens((int)s_pl[0][n2 - 1][1]) < kBlock);
+      const int nfull = ns2 - (rag2 ? 1 : 0);
+      {
+        Buf<FMT> buf[NB];
+        Recs rec[NB];
+        uint32_t bnd[NB];
+        PStep st[NB];
+        const int nmine = wi < nfull ? (nfull - wi + wpc - 1) / wpc : 0;
+        auto wst = [&](int j) { return pstep(0, j < nmine ? wi + wpc * j : nfull, 2 * nfull); };
+        int partner_seen = 0;
+#pragma unroll
+        for (int k = 0; k < NB; ++k) { st[k] = wst(k); bnd[k] = issue_bounds(st[k]); }
+#pragma unroll
+        for (int k = 0; k < kPF; ++k) {
+          issue_recs(rec[k], bnd[k], st[k]);
+          issue_codes(buf[k], st[k], kStep, std::false_type{});
+        }
+        const int ngroups = nmine / NB;
+        for (int g = 0; g < ngroups; ++g) {
+          if (g > partner_seen) __builtin_amdgcn_s_setprio(0);
+          else __builtin_amdgcn_s_setprio(1);
+          if (lane == 0) *prog_mine = g;
+#pragma unroll
+          for (int u = 0; u < NB; ++u) {
+            const int jj = g * NB + u;
+            st[u] = wst(jj + NB);
+            bnd[u] = issue_bounds(st[u]);
+            issue_recs(rec[(u + kPF) % NB], bnd[(u + kPF) % NB], st[(u + kPF) % NB]);
+            issue_codes(buf[(u + kPF) % NB], st[(u + kPF) % NB], kStep, std::false_type{});
+            consume(buf[u], no8, rec[u], 0u, 0u, kStep, std::true_type{}, std::false_type{});
+          }
+          partner_seen = min(__builtin_amdgcn_readfirstlane(*prog_p1), __builtin_amdgcn_readfirstlane(*prog_p2));
+        }
+        __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+          const int jj = ngroups * NB + u;
+          if (jj < nmine) {
+            st[u] = wst(jj + NB);
+            bnd[u] = issue_bounds(st[u]);
+            issue_recs(rec[(u + kPF) % NB], bnd[(u + kPF) % NB], st[(u + kPF) % NB]);
+            issue_codes(buf[(u + kPF) % NB], st[(u + kPF) % NB], kStep, std::false_type{});
+            consume(buf[u], no8, rec[u], 0u, 0u, kStep, std::true_type{}, std::false_type{});
+          }
+        }
+        if (rag2 && wi == nfull % wpc) {   // the list's last, partly filled step
+          const PStep sr = pstep(0, ns2 - 1, n2);
+          const int nval = step_tokens(sr);
+          const uint32_t b0 = issue_bounds(sr);
+          issue_recs(rec[0], b0, sr);
+          issue_codes(buf[0], sr, nval, std::true_type{});
+          consume(buf[0], no8, rec[0], 0u, 0u, nval, std::false_type{}, std::false_type{});
+        }
+      }
+      // ---- FP8 pages, two per step, continuing the round-robin over the waves
+      {
+        const int ns8 = (n8 + 1) / 2;
+        for (int j = (wi - ns2 % wpc + wpc) % wpc; j < ns8; j += wpc) {
+          const PStep s8 = pstep(1, j, n8);
+          const int nval = step_tokens(s8);
+          Buf8 f;
+          load8(f, s8, nval);
+          consume(no2, f, norec, 0u, 0u, nval, std::false_type{}, std::true_type{});
+        }
+      }
+      __syncthreads();   // the lists are rebuilt for the next segment
+    }
   }
 
   // ---- merge the waves of the workgroup
@@ -814,7 +944,7 @@ __global__ void __launch_bounds__(Shape<PAGED>::kWaves * 64) decode_mfma_kernel(
   if constexpr (CMP) l_row += dpp_f32<kRowRor8>(l_row);
   l_row += __shfl_xor(l_row, 16, 64);
   l_row += __shfl_xor(l_row, 32, 64);
-  float* s_o = (float*)(s_lds + wave * kWaveLds);   // [16 rows][128 channels] of this wave
+  float* s_o = (float*)(s_lds + wave * kTile);   // [16 rows][128 channels] of this wave
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
@@ -833,7 +963,7 @@ __global__ void __launch_bounds__(Shape<PAGED>::kWaves * 64) decode_mfma_kernel(
       const float mw = s_ml[w][row][0];
       const float f = mw == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
       den += f * s_ml[w][row][1];
-      num += f * ((const float*)(s_lds + w * kWaveLds))[row * kHeadDim + ch];
+      num += f * ((const float*)(s_lds + w * kTile))[row * kHeadDim + ch];
     }
     const size_t hq = (size_t)h * G + row;
     if (d.n_chunks == 1) {
@@ -849,9 +979,9 @@ __global__ void __launch_bounds__(Shape<PAGED>::kWaves * 64) decode_mfma_kernel(
 template <int FMT, bool CMP, bool PAGED>
 void launch_cmp(const DecodeLaunch& d, dim3 grid, hipStream_t st) {
   switch (d.outl) {
-    case KVQ_OUTL_NONE: decode_mfma_kernel<FMT, KVQ_OUTL_NONE, CMP, PAGED><<<grid, Shape<PAGED>::kWaves * 64, 0, st>>>(d); break;
-    case KVQ_OUTL_FP16: decode_mfma_kernel<FMT, KVQ_OUTL_FP16, CMP, PAGED><<<grid, Shape<PAGED>::kWaves * 64, 0, st>>>(d); break;
-    default: decode_mfma_kernel<FMT, KVQ_OUTL_FP8_E4M3, CMP, PAGED><<<grid, Shape<PAGED>::kWaves * 64, 0, st>>>(d); break;
+    case KVQ_OUTL_NONE: decode_mfma_kernel<FMT, KVQ_OUTL_NONE, CMP, PAGED><<<grid, kWaves * 64, 0, st>>>(d); break;
+    case KVQ_OUTL_FP16: decode_mfma_kernel<FMT, KVQ_OUTL_FP16, CMP, PAGED><<<grid, kWaves * 64, 0, st>>>(d); break;
+    default: decode_mfma_kernel<FMT, KVQ_OUTL_FP8_E4M3, CMP, PAGED><<<grid, kWaves * 64, 0, st>>>(d); break;
   }
 }
 
@@ -875,16 +1005,14 @@ hipError_t launch_decode_mfma(const DecodeLaunch& d, hipStream_t st, bool* handl
     if (d.fmt != FMT_C2 || rows2 * 32 > 0xFFFFF000ull || rows8 * kHeadDim > 0xFFFFF000ull)
       return hipSuccess;
   }
-  // Short chunks are packed several to a workgroup (a divisor of its wave count) so that every
-  // wave keeps a run of steps: up to 32 for contiguous caches (FP4 at 2048-token chunks: 206 ->
-  // 180 us), 16 for paged ones, whose variable sequence lengths leave larger workgroups unevenly
-  // loaded; never below one workgroup per CU (256).
-  const int waves = d.L.paged ? Shape<true>::kWaves : Shape<false>::kWaves;
-  const int run = d.L.paged ? 16 : 32;
+  // Short chunks of contiguous caches are packed several to a workgroup (a divisor of its wave
+  // count) so that every wave keeps a run of up to 32 steps (FP4 at 2048-token chunks: 206 ->
+  // 180 us), never below one workgroup per CU (256).  A paged cache's workgroup lists the pages
+  // of one chunk.
   const int64_t units = (int64_t)d.L.H * d.L.B;
   DecodeLaunch dd = d;
   dd.cpw = 1;
-  while (waves % (dd.cpw * 2) == 0 && d.chunk * dd.cpw * 2 <= run * kStep * waves &&
+  while (!d.L.paged && kWaves % (dd.cpw * 2) == 0 && d.chunk * dd.cpw * 2 <= 32 * kStep * kWaves &&
          units * ((d.n_chunks + dd.cpw * 2 - 1) / (dd.cpw * 2)) >= 256)
     dd.cpw *= 2;
   dim3 grid(d.L.H, (d.n_chunks + dd.cpw - 1) / dd.cpw, d.L.B);
