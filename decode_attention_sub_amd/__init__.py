@@ -25,8 +25,9 @@ FMT = {"fp16": 0, "fp8row": 1, "int4": 2, "fp4": 3, "c2": 4, "bf16": 5, "u2": 6,
 OUTL = {"none": 0, "fp16": 1, "e4m3": 2}
 
 EXPORTED = ("kvq_kv_bytes", "kvq_cache_sizes", "kvq_quantize_append", "kvq_workspace_bytes",
-            "kvq_decode_attention", "kvq_decode_attention_noalloc", "kvq_probe_read",
-            "kvq_probe_copy", "kvq_status_string")
+            "kvq_decode_attention", "kvq_decode_attention_noalloc", "kvq_mass_workspace_bytes",
+            "kvq_decode_attention_mass", "kvq_retier_workspace_bytes", "kvq_retier",
+            "kvq_probe_read", "kvq_probe_copy", "kvq_status_string")
 NOALLOC_SCRATCH_BYTES = 32 << 20   # KVQ_NOALLOC_SCRATCH_BYTES
 
 
@@ -72,6 +73,12 @@ def _load():
                                              C.c_uint64, vp]),
         "kvq_decode_attention_noalloc": (C.c_int32, [P, Pc, vp, vp, vp, C.c_float, C.c_int32,
                                                      vp, vp]),
+        "kvq_mass_workspace_bytes": (C.c_int32, [P, C.c_int32, C.POINTER(C.c_uint64)]),
+        "kvq_decode_attention_mass": (C.c_int32, [P, Pc, vp, vp, vp, C.c_float, C.c_int32, vp, vp,
+                                                  vp, C.c_uint64, vp]),
+        "kvq_retier_workspace_bytes": (C.c_int32, [P, C.c_int32, C.POINTER(C.c_uint64)]),
+        "kvq_retier": (C.c_int32, [P, Pc, vp, vp, vp, C.c_float, vp, C.c_int32, vp, vp, vp,
+                                   C.c_uint64, vp]),
         "kvq_probe_read": (C.c_int32, [vp, C.c_uint64, vp, vp]),
         "kvq_probe_copy": (C.c_int32, [vp, vp, C.c_uint64, vp]),
         "kvq_status_string": (C.c_char_p, [C.c_int32]),
@@ -218,6 +225,48 @@ def kvq_decode_attention_noalloc(p: kvq_params, cache: KVCache, q_bf16, seq_lens
                                              _ptr(seq_lens), _ptr(block_table), sm_scale,
                                              split_chunk, _ptr(out), _stream(stream)),
            "kvq_decode_attention_noalloc")
+
+
+def kvq_mass_workspace_bytes(p: kvq_params, split_chunk: int = 0) -> int:
+    out = C.c_uint64()
+    _check(_lib.kvq_mass_workspace_bytes(C.byref(p), split_chunk, C.byref(out)),
+           "kvq_mass_workspace_bytes")
+    return out.value
+
+
+def kvq_decode_attention_mass(p: kvq_params, cache: KVCache, q_bf16, seq_lens, out, page_mass,
+                              workspace, block_table, sm_scale: Optional[float] = None,
+                              split_chunk: int = 0, stream=None):
+    """kvq_decode_attention of a paged cache that also writes page_mass: float32 [B,
+    max_pages_per_seq] (device), the attention mass of every page."""
+    if sm_scale is None:
+        sm_scale = math.nan
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(_lib.kvq_decode_attention_mass(C.byref(p), C.byref(cache.struct), _ptr(q_bf16),
+                                          _ptr(seq_lens), _ptr(block_table), sm_scale,
+                                          split_chunk, _ptr(out), _ptr(page_mass),
+                                          _ptr(workspace), ws_bytes, _stream(stream)),
+           "kvq_decode_attention_mass")
+
+
+def kvq_retier_workspace_bytes(p: kvq_params, n_free: int) -> int:
+    out = C.c_uint64()
+    _check(_lib.kvq_retier_workspace_bytes(C.byref(p), n_free, C.byref(out)),
+           "kvq_retier_workspace_bytes")
+    return out.value
+
+
+def kvq_retier(p: kvq_params, cache: KVCache, block_table, seq_lens, page_mass, keep_frac: float,
+               free_slots, freed_slots, n_moved, workspace, stream=None):
+    """Move the cold FP8 pages to the 2-bit tier.  block_table int32 [B, max_pages] (device,
+    rewritten); free_slots int32 [n_free] (device); freed_slots int32 (device, capacity
+    min(n_free, num_pages_fp8)); n_moved int32 [1] (device)."""
+    n_free = 0 if free_slots is None else free_slots.numel()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.kvq_retier(C.byref(p), C.byref(cache.struct), _ptr(block_table), _ptr(seq_lens),
+                           _ptr(page_mass), keep_frac, _ptr(free_slots), n_free,
+                           _ptr(freed_slots), _ptr(n_moved), _ptr(workspace), ws_bytes,
+                           _stream(stream)), "kvq_retier")
 
 
 def kvq_probe_read(src, sink, stream=None):

@@ -274,6 +274,7 @@ __global__ void __launch_bounds__(kMergeGroups * kHeadDim) lse_merge_kernel(Deco
     N = fmaf(f, s_st[i][2][ch], N);
   }
   d.out[((size_t)b * d.Hq + hq) * kHeadDim + ch] = N / D;
+  if (d.total_lse && ch == 0) d.total_lse[(size_t)b * d.Hq + hq] = Mt + __builtin_log2f(D);
 }
 
 }  // namespace

@@ -285,7 +285,10 @@ constexpr int kRowRor8 = 0x128;   // lane i <- lane (i + 8) mod 16 of its row
 // the FP8 pages two at a time (attention does not depend on the order of the tokens).  Only the
 // last step of each tier's list can hold fewer than 32 tokens (a single page, or the sequence's
 // partial last page).
-template <int FMT, int OUTL, bool CMP, bool PAGED>
+// MASS (paged caches): every step also writes, per query head and page, log2 of the sum of the
+// page's exp2-domain probabilities (the page's log-sum-exp), and the epilogue writes each query
+// head's total; a later pass turns them into page attention masses.
+template <int FMT, int OUTL, bool CMP, bool PAGED, bool MASS>
 __global__ void __launch_bounds__(kWaves * 64) decode_mfma_kernel(DecodeLaunch d) {
   __shared__ __attribute__((aligned(16))) _Float16 s_lds[kWaves * kTile];
   __shared__ float s_ml[kWaves][16][2];
@@ -396,7 +399,7 @@ __global__ void __launch_bounds__(kWaves * 64) decode_mfma_kernel(DecodeLaunch d
   // are expanded and written, the K^ operand reads are issued, the score MFMAs run, V rows are
   // expanded while those finish, the V^T operand reads are issued before the softmax needs them.
   auto consume = [&](const Buf<FMT>& bf, const Buf8& b8, const Recs& rc, uint32_t kb0, uint32_t vb0,
-                     int nval, auto full_tag, auto is8_tag) {
+                     int nval, int pA, int pB, auto full_tag, auto is8_tag) {
     constexpr bool FULL = decltype(full_tag)::value;
     constexpr bool IS8 = decltype(is8_tag)::value;
     _Float16* krow = ktile + trow * kRow + 64 * half;
@@ -520,13 +523,15 @@ __global__ void __launch_bounds__(kWaves * 64) decode_mfma_kernel(DecodeLaunch d
       m_thr = sl2 > 0.0f ? (m_run + 8.0f) / sl2 : (m_run == -INFINITY ? -INFINITY : INFINITY);
     }
     uint32_t hw[NS / 2], lw[NS / 2];
-    float psum;
+    float psum, psumA = 0.0f, psumB = 0.0f;   // without CMP: the tile-0 and tile-1 parts
 #pragma unroll
     for (int v = 0; v < NS; v += 2) {
       float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[v], sl2, -m_run));
       float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[v + 1], sl2, -m_run));
       if constexpr (!FULL) { p0 = valid[v] ? p0 : 0.0f; p1 = valid[v + 1] ? p1 : 0.0f; }
       psum = v == 0 ? p0 + p1 : psum + (p0 + p1);
+      if (v < 4) psumA += p0 + p1;
+      else psumB += p0 + p1;
       if constexpr (IS8) {   // FP8 rows: the V row scales multiply the probabilities
         const floatx4 vs = v < 4 ? b8.vs0 : b8.vs1;
         p0 = FULL || valid[v] ? p0 * vs[v % 4] : 0.0f;
@@ -537,6 +542,30 @@ __global__ void __launch_bounds__(kWaves * 64) decode_mfma_kernel(DecodeLaunch d
       lw[v / 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(rem_lo(hw[v / 2], p0), rem_hi(hw[v / 2], p1)));
     }
     l_run += psum;
+    if constexpr (MASS) {
+      // page sums: over the 4 lanes (k-groups) holding a query row's tokens of a tile; tile 0 is
+      // page pA, tile 1 page pB
+      auto kg_sum = [](float x) {
+        const auto x16 = __builtin_amdgcn_permlane16_swap(as_u32(x), as_u32(x), false, false);
+        x = as_f32(x16[0]) + as_f32(x16[1]);
+        const auto x32 = __builtin_amdgcn_permlane32_swap(as_u32(x), as_u32(x), false, false);
+        return as_f32(x32[0]) + as_f32(x32[1]);
+      };
+      const float sA = kg_sum(CMP ? psum : psumA);
+      const float sB = CMP ? 0.0f : kg_sum(psumB);
+      const int row = CMP ? (r & 7) : r;
+      if (kg == 0 && row < G) {
+        float* dst = d.page_lse + ((size_t)b * d.Hq + (size_t)h * G + row) * L.max_pages;
+        auto lse = [&](float x) { return x > 0.0f ? m_run + __builtin_log2f(x) : -INFINITY; };
+        if constexpr (CMP) {
+          const int pg = r < 8 ? pA : pB;
+          if (pg >= 0) dst[pg] = lse(sA);
+        } else {
+          if (pA >= 0) dst[pA] = lse(sA);
+          if (pB >= 0) dst[pB] = lse(sB);
+        }
+      }
+    }
     if constexpr (CMP) {
       // One B operand carries both parts: column r < 8 the hi parts of query r (tile-0 tokens of
       // its own lane, tile-1 tokens from lane r + 8), column r + 8 the lo parts of query r
@@ -684,7 +713,7 @@ __global__ void __launch_bounds__(kWaves * 64) decode_mfma_kernel(DecodeLaunch d
         issue_recs(rec[(u + kPF) % NB], bnd[(u + kPF) % NB], wts(jj + kPF));
         issue_codes(buf[(u + kPF) % NB], wts(jj + kPF));
         const uint32_t base = (uint32_t)wts(jj) * 128u;
-        consume(buf[u], no8, rec[u], base, base, kStep, std::true_type{}, std::false_type{});
+        consume(buf[u], no8, rec[u], base, base, kStep, 0, 0, std::true_type{}, std::false_type{});
       }
       partner_seen = min(__builtin_amdgcn_readfirstlane(*prog_p1), __builtin_amdgcn_readfirstlane(*prog_p2));
     }
@@ -697,7 +726,7 @@ __global__ void __launch_bounds__(kWaves * 64) decode_mfma_kernel(DecodeLaunch d
         issue_recs(rec[(u + kPF) % NB], bnd[(u + kPF) % NB], wts(jj + kPF));
         issue_codes(buf[(u + kPF) % NB], wts(jj + kPF));
         const uint32_t base = (uint32_t)wts(jj) * 128u;
-        consume(buf[u], no8, rec[u], base, base, kStep, std::true_type{}, std::false_type{});
+        consume(buf[u], no8, rec[u], base, base, kStep, 0, 0, std::true_type{}, std::false_type{});
       }
     }
     if (ragged && wi == 0) {
@@ -705,7 +734,7 @@ __global__ void __launch_bounds__(kWaves * 64) decode_mfma_kernel(DecodeLaunch d
       const uint32_t b0 = issue_bounds(ts);
       issue_recs(rec[0], b0, ts);
       issue_codes(buf[0], ts);
-      consume(buf[0], no8, rec[0], (uint32_t)ts * 128u, (uint32_t)ts * 128u, t1 - ts,
+      consume(buf[0], no8, rec[0], (uint32_t)ts * 128u, (uint32_t)ts * 128u, t1 - ts, 0, 0,
               std::false_type{}, std::false_type{});
     }
   } else {
@@ -889,11 +918,12 @@ __global__ void __launch_bounds__(kWaves * 64) decode_mfma_kernel(DecodeLaunch d
 #pragma unroll
           for (int u = 0; u < NB; ++u) {
             const int jj = g * NB + u;
+            const int cA = st[u].pA, cB = st[u].pB;
             st[u] = wst(jj + NB);
             bnd[u] = issue_bounds(st[u]);
             issue_recs(rec[(u + kPF) % NB], bnd[(u + kPF) % NB], st[(u + kPF) % NB]);
             issue_codes(buf[(u + kPF) % NB], st[(u + kPF) % NB], kStep, std::false_type{});
-            consume(buf[u], no8, rec[u], 0u, 0u, kStep, std::true_type{}, std::false_type{});
+            consume(buf[u], no8, rec[u], 0u, 0u, kStep, cA, cB, std::true_type{}, std::false_type{});
           }
           partner_seen = min(__builtin_amdgcn_readfirstlane(*prog_p1), __builtin_amdgcn_readfirstlane(*prog_p2));
         }
@@ -902,11 +932,12 @@ __global__ void __launch_bounds__(kWaves * 64) decode_mfma_kernel(DecodeLaunch d
         for (int u = 0; u < NB; ++u) {
           const int jj = ngroups * NB + u;
           if (jj < nmine) {
+            const int cA = st[u].pA, cB = st[u].pB;
             st[u] = wst(jj + NB);
             bnd[u] = issue_bounds(st[u]);
             issue_recs(rec[(u + kPF) % NB], bnd[(u + kPF) % NB], st[(u + kPF) % NB]);
             issue_codes(buf[(u + kPF) % NB], st[(u + kPF) % NB], kStep, std::false_type{});
-            consume(buf[u], no8, rec[u], 0u, 0u, kStep, std::true_type{}, std::false_type{});
+            consume(buf[u], no8, rec[u], 0u, 0u, kStep, cA, cB, std::true_type{}, std::false_type{});
           }
         }
         if (rag2 && wi == nfull % wpc) {   // the list's last, partly filled step
@@ -915,7 +946,7 @@ __global__ void __launch_bounds__(kWaves * 64) decode_mfma_kernel(DecodeLaunch d
           const uint32_t b0 = issue_bounds(sr);
           issue_recs(rec[0], b0, sr);
           issue_codes(buf[0], sr, nval, std::true_type{});
-          consume(buf[0], no8, rec[0], 0u, 0u, nval, std::false_type{}, std::false_type{});
+          consume(buf[0], no8, rec[0], 0u, 0u, nval, sr.pA, sr.pB, std::false_type{}, std::false_type{});
         }
       }
       // ---- FP8 pages, two per step, continuing the round-robin over the waves
@@ -926,7 +957,7 @@ __global__ void __launch_bounds__(kWaves * 64) decode_mfma_kernel(DecodeLaunch d
           const int nval = step_tokens(s8);
           Buf8 f;
           load8(f, s8, nval);
-          consume(no2, f, norec, 0u, 0u, nval, std::false_type{}, std::true_type{});
+          consume(no2, f, norec, 0u, 0u, nval, s8.pA, s8.pB, std::false_type{}, std::true_type{});
         }
       }
       __syncthreads();   // the lists are rebuilt for the next segment
@@ -968,6 +999,7 @@ __global__ void __launch_bounds__(kWaves * 64) decode_mfma_kernel(DecodeLaunch d
     const size_t hq = (size_t)h * G + row;
     if (d.n_chunks == 1) {
       d.out[((size_t)b * d.Hq + hq) * kHeadDim + ch] = num / den;
+      if (MASS && ch == 0) d.total_lse[(size_t)b * d.Hq + hq] = M + __builtin_log2f(den);
     } else {
       float* pp = d.partials + (((size_t)b * d.Hq + hq) * d.n_chunks + chunk2) * (kHeadDim + 2);
       if (ch == 0) { pp[0] = M; pp[1] = den; }
@@ -976,19 +1008,19 @@ __global__ void __launch_bounds__(kWaves * 64) decode_mfma_kernel(DecodeLaunch d
   }
 }
 
-template <int FMT, bool CMP, bool PAGED>
+template <int FMT, bool CMP, bool PAGED, bool MASS>
 void launch_cmp(const DecodeLaunch& d, dim3 grid, hipStream_t st) {
   switch (d.outl) {
-    case KVQ_OUTL_NONE: decode_mfma_kernel<FMT, KVQ_OUTL_NONE, CMP, PAGED><<<grid, kWaves * 64, 0, st>>>(d); break;
-    case KVQ_OUTL_FP16: decode_mfma_kernel<FMT, KVQ_OUTL_FP16, CMP, PAGED><<<grid, kWaves * 64, 0, st>>>(d); break;
-    default: decode_mfma_kernel<FMT, KVQ_OUTL_FP8_E4M3, CMP, PAGED><<<grid, kWaves * 64, 0, st>>>(d); break;
+    case KVQ_OUTL_NONE: decode_mfma_kernel<FMT, KVQ_OUTL_NONE, CMP, PAGED, MASS><<<grid, kWaves * 64, 0, st>>>(d); break;
+    case KVQ_OUTL_FP16: decode_mfma_kernel<FMT, KVQ_OUTL_FP16, CMP, PAGED, MASS><<<grid, kWaves * 64, 0, st>>>(d); break;
+    default: decode_mfma_kernel<FMT, KVQ_OUTL_FP8_E4M3, CMP, PAGED, MASS><<<grid, kWaves * 64, 0, st>>>(d); break;
   }
 }
 
-template <int FMT, bool PAGED>
+template <int FMT, bool PAGED, bool MASS = false>
 void launch_fmt(const DecodeLaunch& d, dim3 grid, hipStream_t st) {
-  if (d.Hq / d.L.H <= 8) launch_cmp<FMT, true, PAGED>(d, grid, st);
-  else launch_cmp<FMT, false, PAGED>(d, grid, st);
+  if (d.Hq / d.L.H <= 8) launch_cmp<FMT, true, PAGED, MASS>(d, grid, st);
+  else launch_cmp<FMT, false, PAGED, MASS>(d, grid, st);
 }
 
 }  // namespace
@@ -1017,7 +1049,8 @@ hipError_t launch_decode_mfma(const DecodeLaunch& d, hipStream_t st, bool* handl
     dd.cpw *= 2;
   dim3 grid(d.L.H, (d.n_chunks + dd.cpw - 1) / dd.cpw, d.L.B);
   if (grid.y > 65535u) return hipSuccess;
-  if (d.L.paged) launch_fmt<FMT_C2, true>(dd, grid, st);
+  if (d.L.paged && d.page_lse) launch_fmt<FMT_C2, true, true>(dd, grid, st);
+  else if (d.L.paged) launch_fmt<FMT_C2, true>(dd, grid, st);
   else if (d.fmt == FMT_C2) launch_fmt<FMT_C2, false>(dd, grid, st);
   else launch_fmt<FMT_FP4, false>(dd, grid, st);
   *handled = true;

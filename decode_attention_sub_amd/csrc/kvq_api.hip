@@ -117,6 +117,13 @@ int resolve_chunk(const kvq_params* p, int32_t split_chunk) {
 }
 
 
+uint64_t align256(uint64_t x) { return (x + 255) & ~255ull; }
+// workspace of a decode with page masses: the decode's own, then page and total log-sum-exps
+uint64_t mass_ws_bytes(const kvq_params* p, uint64_t decode_bytes) {
+  return align256(decode_bytes) +
+         ((uint64_t)p->batch * p->num_q_heads * (uint64_t)(p->max_pages_per_seq + 1)) * 4ull;
+}
+
 // Scratch memory of kvq_decode_attention_noalloc: the split-K partials of callers that cannot
 // allocate.  Each GPU the library runs on holds its own copy until the process ends; host code
 // never uses the array's name as an address (it is a host-side stand-in): the device address is
@@ -147,7 +154,7 @@ int32_t scratch_ptr(void** out) {
 int32_t decode_impl(const kvq_params* pin, const kvq_cache* cache, const void* q_bf16,
                     const int32_t* seq_lens, const int32_t* block_table, float sm_scale,
                     int32_t split_chunk, float* out, void* workspace, uint64_t ws_bytes,
-                    bool use_scratch, void* stream) {
+                    bool use_scratch, void* stream, float* page_mass = nullptr) {
   int32_t st = check_params(pin);
   if (st) return st;
   const Params n(pin);
@@ -161,6 +168,12 @@ int32_t decode_impl(const kvq_params* pin, const kvq_cache* cache, const void* q
   if (chunk < 0) return KVQ_ERR_INVALID_ARG;
   uint64_t need = 0;
   kvq_workspace_bytes(p, chunk, &need);
+  uint64_t need_mass = need;
+  if (page_mass) {   // per-page and per-head log-sum-exps after the partials
+    if (!p->page_size) return KVQ_ERR_UNSUPPORTED;
+    need_mass = mass_ws_bytes(p, need);
+    if (!workspace || ws_bytes < need_mass) return KVQ_ERR_WORKSPACE;
+  }
   if (use_scratch && need) {
     if (need > KVQ_NOALLOC_SCRATCH_BYTES) return KVQ_ERR_WORKSPACE;
     st = scratch_ptr(&workspace);
@@ -182,13 +195,32 @@ int32_t decode_impl(const kvq_params* pin, const kvq_cache* cache, const void* q
   d.chunk = chunk;
   d.n_chunks = (p->max_seq_len + chunk - 1) / chunk;
   d.partials = d.n_chunks > 1 ? (float*)workspace : nullptr;
+  d.page_lse = nullptr;
+  d.total_lse = nullptr;
+  if (page_mass) {
+    d.page_lse = (float*)((uint8_t*)workspace + align256(need));
+    d.total_lse = d.page_lse + (size_t)p->batch * p->num_q_heads * p->max_pages_per_seq;
+  }
   d.scale_log2 = sm_scale * 1.4426950408889634f;
   d.cpw = 1;
   hipStream_t s = (hipStream_t)stream;
   bool handled = false;
   if (launch_decode_mfma(d, s, &handled) != hipSuccess) return KVQ_ERR_HIP;
+  if (!handled && page_mass) return KVQ_ERR_UNSUPPORTED;   // nothing launched
   if (!handled && launch_decode_generic(d, s) != hipSuccess) return KVQ_ERR_HIP;
   if (d.n_chunks > 1 && launch_lse_merge(d, s) != hipSuccess) return KVQ_ERR_HIP;
+  if (page_mass) {
+    MassLaunch m;
+    m.page_lse = d.page_lse;
+    m.total_lse = d.total_lse;
+    m.seq_lens = seq_lens;
+    m.mass = page_mass;
+    m.B = p->batch;
+    m.Hq = p->num_q_heads;
+    m.max_pages = p->max_pages_per_seq;
+    m.S_cap = p->max_seq_len;
+    if (launch_mass_normalize(m, s) != hipSuccess) return KVQ_ERR_HIP;
+  }
   return KVQ_OK;
 }
 
@@ -309,6 +341,92 @@ int32_t kvq_decode_attention_noalloc(const kvq_params* pin, const kvq_cache* cac
                                      int32_t split_chunk, float* out, void* stream) {
   return decode_impl(pin, cache, q_bf16, seq_lens, block_table, sm_scale, split_chunk, out,
                      nullptr, 0, true, stream);
+}
+
+int32_t kvq_mass_workspace_bytes(const kvq_params* pin, int32_t split_chunk, uint64_t* out_bytes) {
+  int32_t st = check_params(pin);
+  if (st) return st;
+  if (!out_bytes) return KVQ_ERR_INVALID_ARG;
+  if (!pin->page_size) return KVQ_ERR_UNSUPPORTED;
+  const Params n(pin);
+  uint64_t need = 0;
+  st = kvq_workspace_bytes(&n.p, split_chunk, &need);
+  if (st) return st;
+  *out_bytes = mass_ws_bytes(&n.p, need);
+  return KVQ_OK;
+}
+
+int32_t kvq_decode_attention_mass(const kvq_params* pin, const kvq_cache* cache, const void* q_bf16,
+                                  const int32_t* seq_lens, const int32_t* block_table,
+                                  float sm_scale, int32_t split_chunk, float* out,
+                                  float* page_mass, void* workspace, uint64_t ws_bytes,
+                                  void* stream) {
+  if (!page_mass) return KVQ_ERR_INVALID_ARG;
+  return decode_impl(pin, cache, q_bf16, seq_lens, block_table, sm_scale, split_chunk, out,
+                     workspace, ws_bytes, false, stream, page_mass);
+}
+
+namespace {
+uint64_t retier_n_cand(const kvq_params* p, int32_t n_free) {
+  return (uint64_t)(n_free < p->num_pages_fp8 ? n_free : p->num_pages_fp8);
+}
+}  // namespace
+
+int32_t kvq_retier_workspace_bytes(const kvq_params* pin, int32_t n_free, uint64_t* out_bytes) {
+  int32_t st = check_params(pin);
+  if (st) return st;
+  if (!out_bytes || n_free < 0) return KVQ_ERR_INVALID_ARG;
+  if (!pin->page_size) return KVQ_ERR_UNSUPPORTED;
+  if (pin->max_pages_per_seq > kRetierMaxPages) return KVQ_ERR_UNSUPPORTED;
+  const uint64_t cells = (uint64_t)pin->batch * pin->max_pages_per_seq;
+  const uint64_t nc = retier_n_cand(pin, n_free);
+  *out_bytes = 3 * cells * 4 + nc * 4 + nc * (uint64_t)pin->num_kv_heads * 2 * kBlock * 4 * 4;
+  return KVQ_OK;
+}
+
+int32_t kvq_retier(const kvq_params* pin, const kvq_cache* cache, int32_t* block_table,
+                   const int32_t* seq_lens, const float* page_mass, float keep_frac,
+                   const int32_t* free_slots, int32_t n_free, int32_t* freed_slots,
+                   int32_t* n_moved, void* workspace, uint64_t ws_bytes, void* stream) {
+  uint64_t need = 0;
+  int32_t st = kvq_retier_workspace_bytes(pin, n_free, &need);
+  if (st) return st;
+  const Params n(pin);
+  const kvq_params* p = &n.p;
+  st = check_cache(p, cache);
+  if (st) return st;
+  if (!block_table || !seq_lens || !page_mass || !n_moved || !(keep_frac >= 0.0f && keep_frac <= 1.0f))
+    return KVQ_ERR_INVALID_ARG;
+  const uint64_t nc = retier_n_cand(p, n_free);
+  if (nc > 0 && (!free_slots || !freed_slots || !cache->codes8[0] || !cache->scale8[0]))
+    return KVQ_ERR_INVALID_ARG;
+  if (need && (!workspace || ws_bytes < need)) return KVQ_ERR_WORKSPACE;
+  RetierLaunch r;
+  r.L = make_layout(p, cache->outl_capacity);
+  r.cache = *cache;
+  r.block_table = block_table;
+  r.seq_lens = seq_lens;
+  r.mass = page_mass;
+  r.keep_frac = keep_frac;
+  r.free_slots = free_slots;
+  r.n_free = n_free;
+  r.n_cand = (int)nc;
+  r.freed = freed_slots;
+  r.n_moved = n_moved;
+  const uint64_t cells = (uint64_t)p->batch * p->max_pages_per_seq;
+  r.cand = (int32_t*)workspace;
+  r.moves = r.cand + cells;
+  r.rank = r.moves + cells;
+  r.moved = r.rank + cells;
+  r.bitmaps = (uint32_t*)(r.moved + nc);
+  r.outl = p->outlier_dtype;
+  r.tau2 = p->outlier_sigma * p->outlier_sigma;
+  r.lloyd = p->lloyd_iters;
+  hipStream_t s = (hipStream_t)stream;
+  if (launch_retier_select(r, s) != hipSuccess) return KVQ_ERR_HIP;
+  if (launch_retier_demote(r, s) != hipSuccess) return KVQ_ERR_HIP;
+  if (launch_retier_commit(r, s) != hipSuccess) return KVQ_ERR_HIP;
+  return KVQ_OK;
 }
 
 int32_t kvq_probe_read(const void* src, uint64_t bytes, void* sink, void* stream) {

@@ -547,6 +547,191 @@ __global__ void __launch_bounds__(64 * NW) quantize_append_kernel(QArgs a) {
   if (tid == 0) a.cache.outl_count[lid] = (int32_t)min(running, Lo.outl_cap);
 }
 
+// ---------------------------------------------------------------- tiering: FP8 pages to 2-bit
+// The rows of a moved page (one workgroup per (moved page, KV head, K or V); 16 rows of 32
+// lanes): x' = fl32(e4m3(code) * row scale) from the page's FP8 slot, the outlier predicate (or
+// the static channel mask) and the 2-bit fit as in an append, codes and centroids written to the
+// page's new 2-bit slot, the outlier flags kept as a bitmap (16 rows x 4 words) for the list pass.
+__global__ void __launch_bounds__(16 * kRowLanes) retier_quantize_kernel(RetierLaunch r) {
+  constexpr int G = 64, L = G / 4;
+  __shared__ uint8_t s_code[kBlock][kHeadDim];
+  __shared__ uint8_t s_flag[kBlock][kHeadDim];
+  const Layout& Lo = r.L;
+  const int item = blockIdx.x;
+  const int kv = item & 1, h = (item >> 1) % Lo.H, rank = (item >> 1) / Lo.H;
+  if (rank >= *r.n_moved) return;
+  const int32_t e = r.moved[rank];
+  if (e < 0) return;
+  const int b = e / Lo.max_pages, p = e % Lo.max_pages;
+  const int S = r.seq_lens[b];
+  const int tid = threadIdx.x, row = tid / kRowLanes, lane = tid % kRowLanes;
+  const int gi = lane / L, jg = lane % L;
+  const bool valid = kBlock * p + row < S;
+  const uint32_t slot8 = (uint32_t)r.block_table[e] & 0x7FFFFFFFu;   // not yet rewritten
+  const uint32_t slot2 = (uint32_t)r.moves[e];
+  const size_t r8 = ((size_t)slot8 * Lo.H + h) * kBlock + row;
+  const uint8_t* c8 = (const uint8_t*)r.cache.codes8[kv] + r8 * kHeadDim;
+  const float s8 = valid ? r.cache.scale8[kv][r8] : 0.0f;
+  float x[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) x[k] = valid ? e4m3_to_f32(c8[gi * G + jg + L * k]) * s8 : 0.0f;
+  bool keep[4] = {true, true, true, true};
+  if (r.outl != KVQ_OUTL_NONE) {
+    if (r.cache.chan_mask) {
+      const uint32_t* mw = r.cache.chan_mask + ((size_t)kv * Lo.H + h) * (kHeadDim / 32);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int c = gi * G + jg + L * k;
+        keep[k] = ((mw[c >> 5] >> (c & 31)) & 1u) == 0u;
+      }
+    } else {
+      outlier_flags<G>(x, r.tau2, keep);
+    }
+  }
+  RowOut o;
+  fit_c2<G>(x, keep, jg, r.lloyd, o);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int c = gi * G + jg + L * k;
+    s_code[row][c] = (uint8_t)o.code[k];
+    s_flag[row][c] = valid && !keep[k] ? 1 : 0;
+  }
+  __syncthreads();
+  uint32_t* bm = r.bitmaps + ((size_t)rank * Lo.H * 2 + (size_t)h * 2 + kv) * (kBlock * 4);
+  if (lane < 4) {
+    uint32_t w = 0;
+    for (int k = 0; k < 32; ++k) w |= (uint32_t)s_flag[row][32 * lane + k] << k;
+    bm[row * 4 + lane] = w;
+  }
+  if (!valid) return;
+  const size_t r2 = ((size_t)slot2 * Lo.H + h) * kBlock + row;
+  if (lane < 8) {   // 2-bit: channel 4s + j of the word's 16 goes to byte j, bit pair s
+    uint32_t w = 0;
+    for (int k = 0; k < 16; ++k) w |= (uint32_t)s_code[row][lane * 16 + k] << (8 * (k & 3) + 2 * (k >> 2));
+    ((uint32_t*)((uint8_t*)r.cache.codes[kv] + r2 * 32))[lane] = w;
+  }
+  if (jg == 0) {
+    uint32_t* md = (uint32_t*)((uint8_t*)r.cache.meta[kv] + r2 * 16);
+    md[2 * gi] = o.meta[0];
+    md[2 * gi + 1] = o.meta[1];
+  }
+}
+
+// One list (sequence, KV head, K or V): the record counts of its pages (a moved page: its bitmap;
+// any other: its old range), new block starts by a prefix sum, the old records moved to their
+// new places (back to front, a block of 256 at a time: records only move up), the moved pages'
+// records written in token and channel order, then the block starts and the count.  Records
+// past the list's capacity are dropped and reported, as in an append.
+__global__ void __launch_bounds__(256) retier_lists_kernel(RetierLaunch r) {
+  __shared__ int s_new[kRetierMaxPages + 1];
+  __shared__ int s_part[256];
+  const Layout& Lo = r.L;
+  const int list = blockIdx.x;
+  const int kv = list & 1, h = (list >> 1) % Lo.H, b = (list >> 1) / Lo.H;
+  const int S = r.seq_lens[b];
+  if (S < 1 || S > Lo.S_cap) return;
+  const int np = (S + kBlock - 1) / kBlock;
+  const int tid = threadIdx.x;
+  const size_t lid = list_id(Lo, b, h, kv);
+  int32_t* bstart = r.cache.outl_block_start + lid * (size_t)Lo.nblk;
+  uint32_t* oidx = r.cache.outl_idx[kv] + ((size_t)b * Lo.H + h) * (size_t)Lo.outl_cap;
+  const int VB = r.outl == KVQ_OUTL_FP16 ? 2 : 1;
+  uint8_t* oval = (uint8_t*)r.cache.outl_val[kv] + ((size_t)b * Lo.H + h) * (size_t)Lo.outl_cap * VB;
+  const int64_t cap = Lo.outl_cap;
+  const int old = (int)max((int64_t)0, min((int64_t)r.cache.outl_count[lid], cap));
+  const int32_t* mv = r.moves + (size_t)b * Lo.max_pages;
+  const int32_t* rk = r.rank + (size_t)b * Lo.max_pages;
+  // a sequence with no moved page keeps its lists as they are
+  int any = 0;
+  for (int p = tid; p < np; p += 256) any |= mv[p] >= 0;
+  if (!__syncthreads_or(any)) return;
+  auto bitmap = [&](int p) {
+    return r.bitmaps + ((size_t)rk[p] * Lo.H * 2 + (size_t)h * 2 + kv) * (kBlock * 4);
+  };
+  auto old_start = [&](int p) { return p < np ? max(0, min(bstart[p], old)) : old; };
+  // counts per page, then an exclusive scan in place (chunks of pages per thread)
+  for (int p = tid; p < np; p += 256) {
+    int c;
+    if (mv[p] >= 0) {
+      const uint32_t* bm = bitmap(p);
+      c = 0;
+      for (int i = 0; i < kBlock * 4; ++i) c += __builtin_popcount(bm[i]);
+    } else {
+      c = max(0, old_start(p + 1) - old_start(p));
+    }
+    s_new[p] = c;
+  }
+  __syncthreads();
+  const int per = (np + 255) / 256;
+  const int q0 = min(np, per * tid), q1 = min(np, q0 + per);
+  int sum = 0;
+  for (int q = q0; q < q1; ++q) sum += s_new[q];
+  s_part[tid] = sum;
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {
+    const int v = tid >= o ? s_part[tid - o] : 0;
+    __syncthreads();
+    s_part[tid] += v;
+    __syncthreads();
+  }
+  int run = s_part[tid] - sum;
+  for (int q = q0; q < q1; ++q) { const int c = s_new[q]; s_new[q] = run; run += c; }
+  if (tid == 255) s_new[np] = s_part[255];
+  __syncthreads();
+  const int total = s_new[np];
+  // old records move up by the records inserted before their page
+  for (int j = old; j > 0; j -= 256) {
+    const int i = j - 256 + tid;
+    uint32_t ix = 0, vl = 0;
+    int dst = -1;
+    if (i >= 0) {
+      ix = oidx[i];
+      vl = VB == 2 ? ((const uint16_t*)oval)[i] : oval[i];
+      const int pg = min((int)(ix / kHeadDim) / kBlock, np);
+      dst = i + (pg < np ? s_new[pg] - old_start(pg) : total - old);
+    }
+    __syncthreads();
+    if (i >= 0 && dst < cap) {
+      oidx[dst] = ix;
+      if (VB == 2) ((uint16_t*)oval)[dst] = (uint16_t)vl;
+      else oval[dst] = (uint8_t)vl;
+    }
+  }
+  __syncthreads();
+  // records of the moved pages: one thread per (page, row)
+  for (int q = tid; q < np * kBlock; q += 256) {
+    const int p = q / kBlock, row = q % kBlock;
+    if (mv[p] < 0) continue;
+    const uint32_t* bm = bitmap(p);
+    int pos = s_new[p];
+    for (int i = 0; i < row * 4; ++i) pos += __builtin_popcount(bm[i]);
+    const uint32_t slot8 = (uint32_t)r.block_table[(size_t)b * Lo.max_pages + p] & 0x7FFFFFFFu;
+    const size_t r8 = ((size_t)slot8 * Lo.H + h) * kBlock + row;
+    const uint8_t* c8 = (const uint8_t*)r.cache.codes8[kv] + r8 * kHeadDim;
+    const float s8 = r.cache.scale8[kv][r8];
+    const uint32_t t = (uint32_t)(kBlock * p + row);
+    for (int w = 0; w < 4; ++w) {
+      uint32_t bits = bm[row * 4 + w];
+      while (bits) {
+        const int c = 32 * w + __builtin_ctz(bits);
+        bits &= bits - 1;
+        if (pos < cap) {
+          const float xv = e4m3_to_f32(c8[c]) * s8;
+          oidx[pos] = t * kHeadDim + (uint32_t)c;
+          if (VB == 2) ((uint16_t*)oval)[pos] = (uint16_t)f32_to_half_bits(xv);
+          else oval[pos] = (uint8_t)f32_to_e4m3(xv);
+        }
+        ++pos;
+      }
+    }
+  }
+  for (int p = tid; p < np; p += 256) bstart[p] = s_new[p];
+  if (tid == 0) {
+    if (total > cap) report(r.cache.status, KVQ_ERR_CAPACITY);
+    r.cache.outl_count[lid] = (int32_t)min((int64_t)total, cap);
+  }
+}
+
 template <int FMT, int G>
 hipError_t launch_quantize_t(const QArgs& qa, int nlists, int max_new, hipStream_t st) {
   if (max_new <= 2) {
@@ -558,6 +743,15 @@ hipError_t launch_quantize_t(const QArgs& qa, int nlists, int max_new, hipStream
 }
 
 }  // namespace
+
+hipError_t launch_retier_demote(const RetierLaunch& r, hipStream_t st) {
+  if (r.n_cand > 0) {
+    retier_quantize_kernel<<<(unsigned)((int64_t)r.n_cand * r.L.H * 2), 16 * kRowLanes, 0, st>>>(r);
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  }
+  retier_lists_kernel<<<(unsigned)(r.L.B * r.L.H * 2), 256, 0, st>>>(r);
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize_append(const QuantizeLaunch& q, hipStream_t st) {
   QArgs qa;

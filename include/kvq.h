@@ -241,6 +241,50 @@ int32_t kvq_decode_attention_noalloc(const kvq_params* p, const kvq_cache* cache
                                      const int32_t* block_table, float sm_scale,
                                      int32_t split_chunk, float* out, void* stream);
 
+/* Entropy-guided tiering of paged caches ("Hierarchical Token Gating and Tiered KV-Cache Paging
+ * ...", section "2. Entropy-Guided Tiered KV-Cache Quantization": the pages holding most of the
+ * attention weight stay FP8, the rest is 2-bit; "Operational Blueprint for AI Systems Engineers",
+ * item 2: the ranking is refreshed every N decode steps).  A decode with page masses feeds the
+ * re-tiering call; the caller runs the pair every N steps and appends new tokens into FP8 pages.
+ *
+ * kvq_decode_attention_mass: kvq_decode_attention of a paged cache (2-bit tier, pools below
+ * 4 GiB; otherwise KVQ_ERR_UNSUPPORTED, nothing launched) that also writes page_mass (device
+ * float32 [B][max_pages_per_seq]): the attention mass of page p of sequence b, the mean over the
+ * Hq query heads of the sum of the softmax weights of its tokens (each sequence's masses sum to
+ * 1; entries of pages past seq_lens[b], and of sequences whose length is rejected, are 0).  The
+ * workspace (ws_bytes >= kvq_mass_workspace_bytes) holds the split-K partials and per-page and
+ * per-head log-sum-exps. */
+int32_t kvq_mass_workspace_bytes(const kvq_params* p, int32_t split_chunk, uint64_t* out_bytes);
+int32_t kvq_decode_attention_mass(const kvq_params* p, const kvq_cache* cache, const void* q_bf16,
+                                  const int32_t* seq_lens, const int32_t* block_table,
+                                  float sm_scale, int32_t split_chunk, float* out,
+                                  float* page_mass, void* workspace, uint64_t ws_bytes,
+                                  void* stream);
+
+/* kvq_retier: moves the cold FP8 pages of a paged cache to the 2-bit tier.  Per sequence b
+ * (tokens < seq_lens[b], all appended), the hot pages are its ceil(keep_frac * n) pages of
+ * largest page_mass (device float32 [B][max_pages_per_seq], e.g. from
+ * kvq_decode_attention_mass), ties to the lower page; every FP8 page that is not hot is a
+ * candidate.  Candidates in (sequence, page) order take the slots free_slots[0], [1], ... (device
+ * int32 slots of the 2-bit pool, n_free of them); those past n_free or past num_pages_fp8 stay
+ * FP8.  A moved page's rows (every KV head, K and V) are dequantized from FP8 in float32,
+ * x = fl32(e4m3(code) * row scale), and quantized again exactly as kvq_quantize_append quantizes
+ * a 2-bit row (outlier predicate or channel mask, Lloyd fit, records of the original x at the
+ * outlier dtype); its records enter each sorted outlier list at its tokens' place (later records
+ * move up; block starts and counts are rewritten; records past a list's capacity are dropped
+ * and set *status to KVQ_ERR_CAPACITY).  Then block_table (device, in/out) names the new slots.
+ * 2-bit pages never move up.  On return of the device work: *n_moved (device int32) = k, the
+ * number of slots handed out; freed_slots[0 .. k-1] (device int32, capacity min(n_free,
+ * num_pages_fp8)) = the FP8 slots released, in the same order as the free slots taken (-1 where
+ * a free slot named a slot outside the 2-bit pool: that page stayed, *status is set to
+ * KVQ_ERR_INVALID_ARG).  workspace: ws_bytes >= kvq_retier_workspace_bytes(p, n_free).  Paged
+ * caches with max_pages_per_seq <= 8192 only (else KVQ_ERR_UNSUPPORTED). */
+int32_t kvq_retier_workspace_bytes(const kvq_params* p, int32_t n_free, uint64_t* out_bytes);
+int32_t kvq_retier(const kvq_params* p, const kvq_cache* cache, int32_t* block_table,
+                   const int32_t* seq_lens, const float* page_mass, float keep_frac,
+                   const int32_t* free_slots, int32_t n_free, int32_t* freed_slots,
+                   int32_t* n_moved, void* workspace, uint64_t ws_bytes, void* stream);
+
 /* Streaming read of `bytes` (multiple of 16) from device buffer src, XOR-reduced into sink
  * (device, >= 4 * 1024 * 256 bytes): measures the practical HBM read ceiling. */
 int32_t kvq_probe_read(const void* src, uint64_t bytes, void* sink, void* stream);

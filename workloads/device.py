@@ -60,8 +60,11 @@ def _rows_for(w: Workload, kind: int, t0: int, n: int, lens: np.ndarray, pool) -
 
 
 def build(w: Workload, S_cap: Optional[int] = None, device: str = "cuda",
-          threads: int = 16, extra_capacity_tokens: int = 0, log=None) -> DeviceCache:
-    """Allocate and fill the cache of workload ``w`` (all B sequences, every token)."""
+          threads: int = 16, extra_capacity_tokens: int = 0, log=None,
+          spare_pages: int = 0) -> DeviceCache:
+    """Allocate and fill the cache of workload ``w`` (all B sequences, every token).
+    spare_pages (paged): free slots left at the end of the 2-bit pool (slots n2 .. n2 +
+    spare_pages - 1), e.g. for pages moved there from the FP8 tier."""
     import torch
     import decode_attention_sub_amd as K
 
@@ -76,7 +79,7 @@ def build(w: Workload, S_cap: Optional[int] = None, device: str = "cuda",
         tiers = G.page_tiers(w, np.minimum(lens + extra_capacity_tokens, S_cap))
         bt_host, n2, n1 = G.block_tables(w, tiers, max_pages)
         bt = torch.from_numpy(bt_host).to(device)
-    p = make_params(w, S_cap, n2, n1, max_pages)
+    p = make_params(w, S_cap, n2 + spare_pages, n1, max_pages)
     cap = max_outliers_per_row(w.D, w.group, w.sigma) * S_cap
     mask = None
     if w.chan_mask:
