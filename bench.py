@@ -39,6 +39,12 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def fp8_pages(dc, seq_lens: np.ndarray) -> int:
+    """Pages of the sequences' live token ranges that the block table puts in the FP8 tier."""
+    tiers = (dc.block_table_host.view(np.uint32) >> 31) == 1
+    return sum(int(tiers[b, :(int(s) + 15) // 16].sum()) for b, s in enumerate(seq_lens))
+
+
 def algorithmic_bytes(dc, n_outliers: int, seq_lens: np.ndarray) -> int:
     """Bytes the decode must move: codes + per-group metadata of every row, outlier records
     (value + 4-byte index) actually present, the bf16 query read and the fp32 output written,
@@ -49,9 +55,7 @@ def algorithmic_bytes(dc, n_outliers: int, seq_lens: np.ndarray) -> int:
     tokens = int(seq_lens.sum())
     vb = 2 if w.outlier == "fp16" else 1
     if w.paged:
-        tiers = (dc.block_table_host.view(np.uint32) >> 31) == 1
-        pages_fp8 = sum(int(tiers[b, :(int(s) + 15) // 16].sum()) for b, s in enumerate(seq_lens))
-        tok8 = pages_fp8 * 16  # whole pages (the last page of a sequence may be partial)
+        tok8 = fp8_pages(dc, seq_lens) * 16  # whole pages (the last page of a sequence may be partial)
         tok8 = min(tok8, tokens)
         kv = 2 * w.H * ((tokens - tok8) * (sz.code_bytes_per_row + sz.meta_bytes_per_row)
                         + tok8 * (w.D + 4))
@@ -220,12 +224,18 @@ def main():
     ap.add_argument("--flush", choices=("auto", "on", "off"), default="auto",
                     help="stream 1 GiB through the caches before every step (auto: when the "
                          "decode moves less than 768 MB)")
+    ap.add_argument("--retier-every", type=int, default=0,
+                    help="paged workloads: every N-th timed step decodes with page masses and "
+                         "moves the cold FP8 pages to the 2-bit tier (after one initial conversion, "
+                         "timed on its own)")
+    ap.add_argument("--retier-keep", type=float, default=0.15,
+                    help="fraction of each sequence's pages (by attention mass) kept in FP8")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 1 GiB device copy (reference for byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the decode path is "
-              "sharded by (sequence, KV head) with no exchange, see DESIGN.md", file=sys.stderr)
+              "sharded by (sequence, KV head) and needs no exchange between GPUs", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -252,7 +262,12 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     t0 = time.time()
-    dc = WD.build(w, log=log if w.S >= 32768 else None)
+    spare = 0
+    if args.retier_every:
+        if not w.paged:
+            sys.exit("--retier-every needs a paged workload")
+        spare = int(sum(int(t.sum()) for t in G.page_tiers(w, G.seq_lens(w))))   # FP8 pages
+    dc = WD.build(w, log=log if w.S >= 32768 else None, spare_pages=spare)
     log(f"cache built in {time.time() - t0:.1f} s")
     p, cache = dc.params, dc.cache
     split = w.split_chunk if args.split < 0 else args.split
@@ -279,7 +294,52 @@ def main():
         fsink = torch.empty(1024 * 256, dtype=torch.int32, device="cuda")
         log("streaming 1 GiB through the caches before every step")
 
-    def step(s, ev=None):
+    retier = None
+    if args.retier_every:
+        # The FP8 pages of the built cache are a Bernoulli draw; one initial conversion moves the
+        # cold ones to spare 2-bit slots (timed on its own).  Later calls, every N-th timed step,
+        # refresh the ranking; each takes its own slice of the remaining free slots.
+        mws = K.kvq_mass_workspace_bytes(p, split)
+        mwork = torch.zeros(mws // 4 + 1, dtype=torch.float32, device="cuda")
+        mass = torch.zeros((w.B, p.max_pages_per_seq), dtype=torch.float32, device="cuda")
+        free_all = list(range(p.num_pages - spare, p.num_pages))
+        n_moved = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+        def retier_call(free_list):
+            n_free = len(free_list)
+            rws = K.kvq_retier_workspace_bytes(p, n_free)
+            rwork = torch.empty(rws // 4 + 1, dtype=torch.int32, device="cuda")
+            free_t = torch.tensor(free_list, dtype=torch.int32, device="cuda") if n_free else None
+            freed = torch.empty(max(1, min(n_free, p.num_pages_fp8)), dtype=torch.int32, device="cuda")
+            return rwork, free_t, freed
+
+        fp8_before = fp8_pages(dc, dc.seq_lens_host)
+        ini = retier_call(free_all)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        K.kvq_decode_attention_mass(p, cache, dc.q, lens, out, mass, mwork, dc.block_table,
+                                    split_chunk=split)
+        K.kvq_retier(p, cache, dc.block_table, lens, mass, args.retier_keep, ini[1], ini[2],
+                     n_moved, ini[0])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        moved0 = int(n_moved.item())
+        dc.block_table_host[:] = dc.block_table.cpu().numpy()
+        remaining = free_all[moved0:]
+        n_calls = 2 * ((args.steps + args.retier_every - 1) // args.retier_every) + 1
+        per = max(1, len(remaining) // n_calls) if remaining else 0
+        calls = [retier_call(remaining[i * per:(i + 1) * per]) for i in range(n_calls)]
+        retier = {"every": args.retier_every, "keep_frac": args.retier_keep,
+                  "fp8_pages_before": fp8_before, "initial_pages_moved": moved0,
+                  "initial_us": round(e0.elapsed_time(e1) * 1e3, 1),
+                  "fp8_pages_after": fp8_pages(dc, dc.seq_lens_host),
+                  "free_slots_per_call": per}
+        log(f"initial re-tier: {moved0} of {fp8_before} FP8 pages moved in "
+            f"{retier['initial_us']} us")
+        call_i = [0]
+        rt_ev = []
+
+    def step(s, ev=None, do_retier=False):
         if flush:
             K.kvq_probe_read(fbuf, fsink)
         if ev is not None:
@@ -287,9 +347,26 @@ def main():
         K.kvq_quantize_append(p, cache, new_k[s], new_v[s], pos, ones, dc.block_table)
         if ev is not None:
             ev[0].record(stream)
+        if do_retier:
+            K.kvq_decode_attention_mass(p, cache, dc.q, lens, out, mass, mwork, dc.block_table,
+                                        split_chunk=split)
+            if ev is not None:
+                ev[1].record(stream)
+            c = calls[min(call_i[0], len(calls) - 1)]
+            call_i[0] += 1
+            K.kvq_retier(p, cache, dc.block_table, lens, mass, args.retier_keep, c[1], c[2],
+                         n_moved, c[0])
+            if ev is not None:
+                r_ev = torch.cuda.Event(enable_timing=True)
+                r_ev.record(stream)
+                rt_ev.append((ev[1], r_ev))
+            return
         K.kvq_decode_attention(p, cache, dc.q, lens, out, work, dc.block_table, split_chunk=split)
         if ev is not None:
             ev[1].record(stream)
+
+    def retier_now(i):
+        return retier is not None and (i + 1) % args.retier_every == 0
 
     # clock ramp: the shader clock climbs over the first few dozen back-to-back decodes
     t_ramp = time.perf_counter()
@@ -309,17 +386,24 @@ def main():
     g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     g0.record(stream)
     for i in range(args.steps):
-        step(args.warmup + i)
+        step(args.warmup + i, None, retier_now(i))
     g1.record(stream)
     torch.cuda.synchronize()
     evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
     for i in range(args.steps):
-        step(args.warmup + i, evs[i])
+        step(args.warmup + i, evs[i], retier_now(i))
     torch.cuda.synchronize()
     ms_step = (float(np.sum([e[2].elapsed_time(e[1]) for e in evs])) if flush
                else g0.elapsed_time(g1)) / args.steps
-    dec_all = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    plain = [i for i in range(args.steps) if not retier_now(i)]   # steps without re-tiering
+    dec_all = np.array([evs[i][0].elapsed_time(evs[i][1]) for i in plain])
     dec_ms = float(np.mean(dec_all))
+    if retier is not None:
+        mass_ms = [evs[i][0].elapsed_time(evs[i][1]) for i in range(args.steps) if retier_now(i)]
+        retier["us_mass_decode"] = round(float(np.mean(mass_ms)) * 1e3, 2) if mass_ms else None
+        retier["us_per_retier"] = (round(float(np.mean([a.elapsed_time(b) for a, b in rt_ev])) * 1e3, 2)
+                                   if rt_ev else None)
+        dc.block_table_host[:] = dc.block_table.cpu().numpy()   # the byte count uses the tiers now
     status = cache.status()
     if status != 0:
         raise RuntimeError(f"device status {status}: {K.kvq_status_string(status)}")
@@ -356,6 +440,8 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(w.name)},
     }
+    if retier is not None:
+        res["retier"] = retier
     if not args.no_cpu_baseline:
         log("timing the oracle on a sample of the step")
         res["cpu_baseline"] = cpu_baseline(dc)
