@@ -3,7 +3,8 @@
     rows of (sequence b, KV head h, kind) for tokens [2048*c, 2048*(c+1))
         <- numpy Generator(PCG64(SeedSequence([seed, b, h, kind, c])))
 
-kind: 0 = keys, 1 = values, 2 = queries, 3/4 = keys/values appended at decode step ``c``.
+kind: 0 = keys, 1 = values, 2 = queries, 3/4 = keys/values appended at decode step ``c``,
+5 = hidden states (decode step ``c``), 6 = RMSNorm gain, 7 = projection rows [1024 c, 1024 (c+1)).
 Per-head constants (the x20 channels, the LogNormal channel scales) come from
 SeedSequence([seed, 9999, h, kind]); sequence lengths, page tiers and block tables from
 SeedSequence([seed, 7777, ...]).
@@ -16,6 +17,10 @@ Distributions ("dist" of a workload):
   lognormal_key_channels  keys: sigma_c * N(0, 1) with sigma_c ~ LogNormal(0, 0.5) per
                           (KV head, channel); values: N(0, 1)
 Queries are N(0, 1) rounded to bfloat16 (round to nearest even).
+
+Attention-prologue inputs (bfloat16, round to nearest even), for a model width d (Hq * D unless
+given): hidden states N(0, 1) [B, d]; RMSNorm gain 1 + 0.1 N(0, 1) [d]; projection
+N(0, 1 / d) [(Hq + 2 H) D, d], so the projected rows have unit variance.
 """
 
 from __future__ import annotations
@@ -26,6 +31,8 @@ from .configs import Workload
 
 GEN_CHUNK = 2048
 K, V, Q, NEW_K, NEW_V = 0, 1, 2, 3, 4
+HIDDEN, GAIN, WEIGHT = 5, 6, 7
+W_CHUNK = 1024
 
 
 def _rng(*key) -> np.random.Generator:
@@ -132,3 +139,34 @@ def block_tables(w: Workload, tiers: list, max_pages: int):
                 table[b, p] = int(perm2[i2])
                 i2 += 1
     return table.astype(np.uint32).view(np.int32), n2, n1
+
+
+def model_width(w: Workload) -> int:
+    return w.Hq * w.D
+
+
+def hidden_states(w: Workload, step: int = 0, d: int = 0) -> np.ndarray:
+    """bfloat16 bit patterns [B, d] of the hidden states entering the attention at ``step``."""
+    d = d or model_width(w)
+    return np.stack([f32_to_bf16_bits(_rng(w.seed, b, 0, HIDDEN, step).standard_normal(d, dtype=np.float32))
+                     for b in range(w.B)])
+
+
+def norm_gain(w: Workload, d: int = 0) -> np.ndarray:
+    """bfloat16 bit patterns [d] of the RMSNorm gain."""
+    d = d or model_width(w)
+    g = 1.0 + 0.1 * _rng(w.seed, 0, 0, GAIN, 0).standard_normal(d, dtype=np.float32)
+    return f32_to_bf16_bits(g.astype(np.float32))
+
+
+def projection(w: Workload, d: int = 0) -> np.ndarray:
+    """bfloat16 bit patterns [(Hq + 2 H) D, d] of the joint Q/K/V projection."""
+    d = d or model_width(w)
+    n = (w.Hq + 2 * w.H) * w.D
+    out = np.empty((n, d), dtype=np.uint16)
+    sd = np.float32(1.0 / np.sqrt(d))
+    for c in range((n + W_CHUNK - 1) // W_CHUNK):
+        r0, r1 = c * W_CHUNK, min(n, (c + 1) * W_CHUNK)
+        x = _rng(w.seed, 0, 0, WEIGHT, c).standard_normal((r1 - r0, d), dtype=np.float32) * sd
+        out[r0:r1] = f32_to_bf16_bits(x)
+    return out
