@@ -71,13 +71,21 @@ KERNEL_SOURCES = ["decode_attention_sub_amd/csrc/decode_mfma.hip",
                   "decode_attention_sub_amd/csrc/kvq_launch.h"]
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per decode launch from the committed counter record of this workload, or None
-    when there is none or the decode kernel's sources have changed since it was taken."""
+def measured_counters(workload: str) -> dict:
+    """HBM bytes and busy fractions per decode launch from the committed counter record of this
+    workload: {"traffic": bytes, "mfma_busy": fraction, "valu_busy": fraction}, each None when the
+    record lacks it, and all None when there is no record or the decode kernel's sources have
+    changed since it was taken.
+
+    mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE * 1024 SIMDs): the share of SIMD
+    cycles with a matrix instruction in flight.  valu_busy = 4 * SQ_ACTIVE_INST_VALU /
+    (GRBM_GUI_ACTIVE * 1024): the share of SIMD cycles issuing vector ALU instructions
+    (SQ_ACTIVE_INST_VALU counts in units of four cycles)."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"decode_mfma_{workload}_traffic.txt")
+    none = {"traffic": None, "mfma_busy": None, "valu_busy": None}
+    path = os.path.join(ROOT, "profiles", f"decode_mfma_{workload}_counters.txt")
     if not os.path.exists(path):
-        return None
+        return none
     rec = {}
     for ln in open(path):
         if ln.startswith("#") or ":" not in ln:
@@ -89,8 +97,14 @@ def measured_traffic(workload: str):
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     if rec.get("workload") != workload or rec.get("kernel_sources_sha256") != h.hexdigest():
-        return None
-    return int(rec["traffic_bytes_per_launch"])
+        return none
+    out = dict(none)
+    if "traffic_bytes_per_launch" in rec:
+        out["traffic"] = int(rec["traffic_bytes_per_launch"])
+    for k in ("mfma_busy", "valu_busy"):
+        if k in rec:
+            out[k] = float(rec[k])
+    return out
 
 
 def read_ceiling_gbs(device="cuda") -> float:
@@ -438,7 +452,7 @@ def main():
         "decode_bytes": dec_bytes,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(w.name)},
+                     **measured_counters(w.name)},
     }
     if retier is not None:
         res["retier"] = retier

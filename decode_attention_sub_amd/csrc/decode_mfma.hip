@@ -100,11 +100,12 @@ __device__ __forceinline__ void expand_fp8(const uint4 (&c)[4], _Float16* dst) {
 // 128 + channel) of tile row 0 for the records of each range.
 struct RecList { int a0, na, b0, nb; uint32_t baseA, baseB; };
 // Lane slot i of a list holds record i of the step.  Values are kept as the aligned 32-bit words
-// that hold them; kb, vb (paged caches): the lane's record's base and its value's bit offset.
+// that hold them; kb, vb (paged caches): the lane's record's base (a multiple of 2048) plus its
+// value's bit offset inside the word (0, 8, 16 or 24).
 struct Recs {
   uint32_t ik, vk;         // K: index word, value word
   uint32_t iv, vv;         // V: index word, value word
-  uint32_t kbase, kbit, vbase, vbit;
+  uint32_t kb, vb;
   RecList k, v;
 };
 
@@ -413,13 +414,13 @@ __global__ void __launch_bounds__(kWaves * 64) decode_mfma_kernel(DecodeLaunch d
     const int nk = rc.k.na + rc.k.nb, nv = rc.v.na + rc.v.nb;
     if constexpr (HAS_OUTL && !IS8) {
       // bit offsets of the values inside their words (bit-field extraction takes them modulo 32)
-      const uint32_t bitK = PAGED ? rc.kbit : laneVB8 + ((uint32_t)rc.k.a0 * VB + lv3) * 8u;
-      const uint32_t bitV = PAGED ? rc.vbit : laneVB8 + ((uint32_t)rc.v.a0 * VB + lv3) * 8u;
+      const uint32_t bitK = PAGED ? rc.kb : laneVB8 + ((uint32_t)rc.k.a0 * VB + lv3) * 8u;
+      const uint32_t bitV = PAGED ? rc.vb : laneVB8 + ((uint32_t)rc.v.a0 * VB + lv3) * 8u;
       const uint32_t lim = (uint32_t)nval * 128u;
-      const uint32_t ddk = rc.ik - (PAGED ? rc.kbase : kb0);
+      const uint32_t ddk = rc.ik - (PAGED ? rc.kb & ~31u : kb0);
       posK = lane < nk && ddk < lim ? tile_pos(ddk) : pad;
       ovK = outl_from_word<OUTL>(rc.vk, bitK);
-      const uint32_t ddv = rc.iv - (PAGED ? rc.vbase : vb0);
+      const uint32_t ddv = rc.iv - (PAGED ? rc.vb & ~31u : vb0);
       posV = lane < nv && ddv < lim ? tile_pos_v(ddv) : pad;
       ovV = outl_from_word<OUTL>(rc.vv, bitV);
     }
@@ -813,15 +814,14 @@ __global__ void __launch_bounds__(kWaves * 64) decode_mfma_kernel(DecodeLaunch d
         const bool ka = lane < kA.y, va = lane < vA.y;
         const uint32_t rk = (uint32_t)(ka ? kA.x + lane : kB.x + lane - kA.y);
         const uint32_t rv = (uint32_t)(va ? vA.x + lane : vB.x + lane - vA.y);
-        rc.kbase = ka ? baseA : baseB;
-        rc.vbase = va ? baseA : baseB;
+
         rc.ik = ld32(riK, rk * 4u);
         rc.iv = ld32(riV, rv * 4u);
         const uint32_t bk = rk * VB + lv3, bv = rv * VB + lv3;
         rc.vk = ld32(rvK, bk & ~3u);
         rc.vv = ld32(rvV, bv & ~3u);
-        rc.kbit = (bk & 3u) * 8u;
-        rc.vbit = (bv & 3u) * 8u;
+        rc.kb = (ka ? baseA : baseB) | (bk & 3u) * 8u;
+        rc.vb = (va ? baseA : baseB) | (bv & 3u) * 8u;
       } else {
         rc.k = RecList{0, 0, 0, 0, 0u, 0u};
         rc.v = rc.k;
