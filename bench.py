@@ -244,6 +244,10 @@ def main():
                          "timed on its own)")
     ap.add_argument("--retier-keep", type=float, default=0.15,
                     help="fraction of each sequence's pages (by attention mass) kept in FP8")
+    ap.add_argument("--prologue", action="store_true",
+                    help="each step runs the fused attention prologue (RMSNorm, Q/K/V projection of "
+                         "width Hq*D with seeded bf16 weights, KV-cache write of the new token) in "
+                         "place of the append, and decodes with the queries it produced")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 1 GiB device copy (reference for byte counters)")
     args = ap.parse_args()
@@ -298,6 +302,17 @@ def main():
         v = np.stack([[G.new_rows(w, b, h, G.NEW_V, s)[0] for h in range(w.H)] for b in range(w.B)])
         new_k.append(torch.from_numpy(k[:, :, None, :]).cuda())
         new_v.append(torch.from_numpy(v[:, :, None, :]).cuda())
+    q_dec = dc.q
+    if args.prologue:
+        d_model = G.model_width(w)
+        log(f"prologue: generating the {(w.Hq + 2 * w.H) * w.D} x {d_model} projection")
+        W_dev = torch.from_numpy(G.projection(w, d_model).view(np.int16)).cuda()
+        gain_dev = torch.from_numpy(G.norm_gain(w, d_model).view(np.int16)).cuda()
+        n_hid = min(n_total, 8)
+        hid = [torch.from_numpy(G.hidden_states(w, s, d_model).view(np.int16)).cuda() for s in range(n_hid)]
+        pws = torch.zeros(K.kvq_prologue_workspace_bytes(p, d_model) // 4 + 1, dtype=torch.int32,
+                          device="cuda")
+        q_dec = torch.empty((w.B, w.Hq, w.D), dtype=torch.int16, device="cuda")
     stream = torch.cuda.current_stream()
     n_est = int(cache.tensors["count"].sum().item())
     flush = args.flush == "on" or (args.flush == "auto" and
@@ -358,7 +373,11 @@ def main():
             K.kvq_probe_read(fbuf, fsink)
         if ev is not None:
             ev[2].record(stream)
-        K.kvq_quantize_append(p, cache, new_k[s], new_v[s], pos, ones, dc.block_table)
+        if args.prologue:
+            K.kvq_attention_prologue(p, cache, hid[s % n_hid], gain_dev, W_dev, 1e-5, pos, q_dec, pws,
+                                     block_table=dc.block_table)
+        else:
+            K.kvq_quantize_append(p, cache, new_k[s], new_v[s], pos, ones, dc.block_table)
         if ev is not None:
             ev[0].record(stream)
         if do_retier:
@@ -375,7 +394,7 @@ def main():
                 r_ev.record(stream)
                 rt_ev.append((ev[1], r_ev))
             return
-        K.kvq_decode_attention(p, cache, dc.q, lens, out, work, dc.block_table, split_chunk=split)
+        K.kvq_decode_attention(p, cache, q_dec, lens, out, work, dc.block_table, split_chunk=split)
         if ev is not None:
             ev[1].record(stream)
 
@@ -427,6 +446,16 @@ def main():
     dec_bytes = algorithmic_bytes(dc, n_out, lens_h)
     app_bytes = w.B * w.H * 2 * (w.D * 4 + K.kvq_cache_sizes(p, 1).code_bytes_per_row
                                  + K.kvq_cache_sizes(p, 1).meta_bytes_per_row)
+    if args.prologue:
+        # the projection's weights, the hidden states, the gain and q written, and the new rows'
+        # codes and metadata (as for the append, without its float32 inputs)
+        sz = K.kvq_cache_sizes(p, 1)
+        pro_bytes = ((w.Hq + 2 * w.H) * w.D * d_model * 2 + w.B * d_model * 2 + d_model * 2
+                     + w.B * w.Hq * w.D * 2 + w.B * w.H * 2 * (sz.code_bytes_per_row + sz.meta_bytes_per_row))
+        pro_all = np.array([evs[i][2].elapsed_time(evs[i][0]) for i in plain])
+        pro_ms = float(np.mean(pro_all))
+        pro_flop = 2.0 * w.B * d_model * (w.Hq + 2 * w.H) * w.D
+        app_bytes = pro_bytes
     step_bytes = dec_bytes + app_bytes
     value = step_bytes / (ms_step * 1e-3) / 1e9
     achieved = dec_bytes / (dec_ms * 1e-3) / 1e9
@@ -456,6 +485,14 @@ def main():
     }
     if retier is not None:
         res["retier"] = retier
+    if args.prologue:
+        res["prologue"] = {
+            "d_model": d_model, "us": round(pro_ms * 1e3, 2),
+            "us_p10_p50_p90": [round(float(np.percentile(pro_all, q)) * 1e3, 2) for q in (10, 50, 90)],
+            "bytes": pro_bytes, "GBs": round(pro_bytes / (pro_ms * 1e-3) / 1e9, 1),
+            "frac_hbm": round(pro_bytes / (pro_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "tflops_bf16": round(pro_flop / (pro_ms * 1e-3) / 1e12, 2),
+            "frac_mfma_bf16": round(pro_flop / (pro_ms * 1e-3) / 1e12 / 2500.0, 4)}
     if not args.no_cpu_baseline:
         log("timing the oracle on a sample of the step")
         res["cpu_baseline"] = cpu_baseline(dc)

@@ -27,6 +27,7 @@ OUTL = {"none": 0, "fp16": 1, "e4m3": 2}
 EXPORTED = ("kvq_kv_bytes", "kvq_cache_sizes", "kvq_quantize_append", "kvq_workspace_bytes",
             "kvq_decode_attention", "kvq_decode_attention_noalloc", "kvq_mass_workspace_bytes",
             "kvq_decode_attention_mass", "kvq_retier_workspace_bytes", "kvq_retier",
+            "kvq_prologue_workspace_bytes", "kvq_attention_prologue",
             "kvq_probe_read", "kvq_probe_copy", "kvq_status_string")
 NOALLOC_SCRATCH_BYTES = 32 << 20   # KVQ_NOALLOC_SCRATCH_BYTES
 
@@ -79,6 +80,9 @@ def _load():
         "kvq_retier_workspace_bytes": (C.c_int32, [P, C.c_int32, C.POINTER(C.c_uint64)]),
         "kvq_retier": (C.c_int32, [P, Pc, vp, vp, vp, C.c_float, vp, C.c_int32, vp, vp, vp,
                                    C.c_uint64, vp]),
+        "kvq_prologue_workspace_bytes": (C.c_int32, [P, C.c_int32, C.POINTER(C.c_uint64)]),
+        "kvq_attention_prologue": (C.c_int32, [P, Pc, vp, vp, vp, C.c_int32, C.c_float, vp, vp, vp,
+                                               vp, vp, C.c_uint64, vp]),
         "kvq_probe_read": (C.c_int32, [vp, C.c_uint64, vp, vp]),
         "kvq_probe_copy": (C.c_int32, [vp, vp, C.c_uint64, vp]),
         "kvq_status_string": (C.c_char_p, [C.c_int32]),
@@ -267,6 +271,28 @@ def kvq_retier(p: kvq_params, cache: KVCache, block_table, seq_lens, page_mass, 
                            _ptr(page_mass), keep_frac, _ptr(free_slots), n_free,
                            _ptr(freed_slots), _ptr(n_moved), _ptr(workspace), ws_bytes,
                            _stream(stream)), "kvq_retier")
+
+
+def kvq_prologue_workspace_bytes(p: kvq_params, d_model: int) -> int:
+    n = C.c_uint64(0)
+    _check(_lib.kvq_prologue_workspace_bytes(C.byref(p), d_model, C.byref(n)),
+           "kvq_prologue_workspace_bytes")
+    return n.value
+
+
+def kvq_attention_prologue(p: kvq_params, cache: KVCache, hidden_bf16, gain_bf16, weight_bf16,
+                           eps: float, positions, q_out, workspace, block_table=None,
+                           proj_out=None, stream=None):
+    """hidden_bf16: bfloat16 [B, d]; gain_bf16: [d]; weight_bf16: [(Hq + 2H) * D, d]; positions:
+    int32 [B]; q_out: bfloat16 [B, Hq, D]; proj_out: optional float32 [B, (Hq + 2H) * D];
+    workspace: zero-filled before its first use (all device)."""
+    d_model = hidden_bf16.shape[-1]
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(_lib.kvq_attention_prologue(C.byref(p), C.byref(cache.struct), _ptr(hidden_bf16),
+                                       _ptr(gain_bf16), _ptr(weight_bf16), d_model, float(eps),
+                                       _ptr(positions), _ptr(block_table), _ptr(q_out),
+                                       _ptr(proj_out), _ptr(workspace), ws_bytes, _stream(stream)),
+           "kvq_attention_prologue")
 
 
 def kvq_probe_read(src, sink, stream=None):

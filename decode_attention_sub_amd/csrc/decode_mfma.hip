@@ -10,9 +10,11 @@
 // section "2. FP4/INT4 KV-Cache Quantization", item 3 (dequantize into fp16 operand space inside
 // the flash-attention reduction).
 //
-// Work unit: a workgroup of 12 waves (three per SIMD; 8 for paged caches) per (split-K chunk, KV
-// head, sequence), or per several short chunks of one (KV head, sequence).  Waves take 32-token
-// steps of the chunk in turn.  Per step a lane owns (token, 64-channel half row): it loads the
+// Work split: the (sequence, KV head) lists are cut into 32-token steps and laid end to end; each
+// workgroup of 12 waves (three per SIMD) takes an equal contiguous range of steps (one
+// workgroup per CU by default), so sequences of any mix of lengths keep every CU equally busy.
+// A workgroup's range is a run of pieces, each the part of one list inside the range; the waves
+// take the 32-token steps of a piece in turn.  Per step a lane owns (token, 64-channel half row): it loads the
 // packed codes and group metadata with 128-bit loads (prefetched one step ahead; 2-bit rows with
 // non-temporal loads, as they are read once), expands them to fp16 in registers and writes the
 // rows into the wave's LDS tile; outlier records of the step are written over their positions.  Scores are computed transposed,
@@ -21,9 +23,10 @@
 // O^T = V^T P^T.  V^T operands come out of the LDS tile with ds_read_b64_tr_b16.  P is split into
 // fp16 hi + lo parts so that large outlier values in V see fp32-grade probabilities; with at most
 // 8 query rows both parts ride in one B operand (hi parts in columns 0-7, lo parts in the padding
-// columns 8-15), otherwise they take two MFMAs.  The waves'
-// states are merged in LDS; a chunk writes either the final output or a (max, sum, output)
-// partial.  The waves of a SIMD keep pace with each other through their issue priority.
+// columns 8-15), otherwise they take two MFMAs.  The waves' states are merged in LDS; a piece
+// that is a whole list writes the final output, a part of a list (only the first and the last
+// piece of a range can be one) a (max, sum, output) partial that streamk_merge_kernel combines.
+// The waves of a SIMD keep pace with each other through their issue priority.
 //
 // 2-bit expansion: per 64-bit centroid word, two byte tables (low bytes and high bytes of the 4
 // fp16 centroids) are built once; the four codes of one bit pair of a 32-bit code word (one per
@@ -62,8 +65,8 @@ constexpr int kTile = kStep * kRow;        // halfs per tile
 // SIMD.
 constexpr int kWaves = 12;
 constexpr int kPF = 1;                     // steps of codes / records in flight per wave
-// Paged caches: a workgroup lists the pages of its chunk by tier, this many pages at a time.
-constexpr int kSegPages = 256;
+// Paged caches: a workgroup lists the pages of its piece by tier, this many pages at a time.
+constexpr int kSegPages = 1024;
 constexpr uint32_t kDead = 0xFFFFFFFFu;    // no page: its rows read as zeros
 
 template <int FMT> struct Buf;
@@ -281,7 +284,7 @@ constexpr int kRowRor8 = 0x128;   // lane i <- lane (i + 8) mod 16 of its row
 // CMP: at most 8 query heads per KV head.  Score tiles then hold real query rows only in lanes
 // r < 8; the softmax runs on 4 scores per lane after moving tile 1's rows into lanes r >= 8.
 // PAGED: 2-bit pages behind a block table, some of them (tier 1) FP8 rows with a per-row scale.
-// The workgroup lists the pages of its chunk by tier (kSegPages at a time, in logical order) and
+// The workgroup lists the pages of its piece by tier (kSegPages at a time, in logical order) and
 // takes the 2-bit pages two at a time as 32-token steps shaped like a contiguous cache's, then
 // the FP8 pages two at a time (attention does not depend on the order of the tokens).  Only the
 // last step of each tier's list can hold fewer than 32 tokens (a single page, or the sequence's
@@ -297,24 +300,13 @@ __global__ void __launch_bounds__(kWaves * 64) decode_mfma_kernel(DecodeLaunch d
   // paged: the listed pages of each tier: {pool row of this KV head or kDead, logical page}
   __shared__ __attribute__((aligned(16))) uint32_t s_pl[PAGED ? 2 : 1][PAGED ? kSegPages : 1][2];
   __shared__ int s_wn[PAGED ? kSegPages / 64 : 1][2];   // pages per tier of each listing wave
+  __shared__ uint64_t s_sc[kWaves];   // per-wave sums of the work split
+  __shared__ int s_loc[3];            // the list and step where the workgroup's range starts
 
   const Layout& L = d.L;
-  // KV head fastest: consecutive workgroups (dealt round-robin to the XCDs) then carry the same
-  // amount of work, whatever the mix of sequence lengths
-  const int h = blockIdx.x, grp = blockIdx.y, b = blockIdx.z;
-  const int S = d.seq_lens[b];
-  if (S < 1 || S > L.S_cap) {
-    if (threadIdx.x == 0 && grp == 0 && h == 0) report(d.cache.status, KVQ_ERR_INVALID_ARG);
-    return;
-  }
-  // The workgroup covers chunks cpw * grp .. + cpw - 1, wpc waves each (paged caches: cpw = 1).
-  const int cpw = d.cpw, wpc = kWaves / cpw;
-  if (grp * cpw * d.chunk >= S) return;
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-  const int ci = wave / wpc, wi = wave - ci * wpc;   // chunk of this wave, its place in the chunk
-  const int chunk = grp * cpw + ci;
-  const int t0 = chunk * d.chunk;
-  const int t1 = chunk < d.n_chunks && t0 < S ? min(t0 + d.chunk, S) : t0;   // empty: past S
+  constexpr int wpc = kWaves;                        // every wave works on every piece
+  const int wi = wave;                               // the wave's place among them
   const int G = d.Hq / L.H;
   const int lane = threadIdx.x & 63;
   const int r = lane & 15, kg = lane >> 4;           // MFMA lane coordinates
@@ -328,6 +320,140 @@ __global__ void __launch_bounds__(kWaves * 64) decode_mfma_kernel(DecodeLaunch d
   // them (a wave's LDS operations complete in issue order).
   _Float16* const ktile = s_lds + wave * kTile;
   _Float16* const vtile = ktile;
+
+  // Two or three waves share each SIMD and the scheduler favours the oldest; every group of
+  // steps, a wave that is ahead of the slower of its SIMD peers lowers its priority, so all
+  // finish together.
+  const int mysimd = (int)((__builtin_amdgcn_s_getreg((31 << 11) | 4) >> 4) & 3);   // HW_ID.simd
+  if (lane == 0) { s_simd[wave] = mysimd; s_prog[wave] = 0; }
+  __syncthreads();
+  // the (up to two) other waves of this SIMD; a wave ahead of the slower of them yields
+  int peer1 = wave, peer2 = wave;
+  for (int w2 = 0; w2 < kWaves; ++w2) {
+    if (w2 != wave && __builtin_amdgcn_readfirstlane(s_simd[w2]) == mysimd) {
+      if (peer1 == wave) peer1 = w2;
+      else peer2 = w2;
+    }
+  }
+  if (peer2 == wave) peer2 = peer1;
+  int* const prog_mine = &s_prog[wave];
+  const int* const prog_p1 = &s_prog[peer1];
+  const int* const prog_p2 = &s_prog[peer2];
+
+
+  // ---- this workgroup's share of the work.  Every list (sequence b, KV head h) of a valid
+  // sequence is cut into n_b = ceil(S_b / 32) steps; the lists are laid end to end in (sequence,
+  // head) order, U steps in all, and workgroup i of N takes steps [floor(i U / N),
+  // floor((i + 1) U / N)).  A piece is the part of one list inside that range: only the first
+  // and the last piece of a workgroup can be parts of a list, every other piece is a whole list.
+  // Steps per head of every sequence, summed, then scanned to find the sequence that holds the
+  // range's first step: all threads of the workgroup, 768 sequences at a time.
+  constexpr int kT = kWaves * 64;
+  const int tid = threadIdx.x;
+  auto seq_steps = [&](int bb) -> uint64_t {
+    if (bb >= L.B) return 0u;
+    const int Sb = d.seq_lens[bb];
+    return Sb >= 1 && Sb <= L.S_cap ? (uint64_t)((Sb + kStep - 1) / kStep) : 0u;
+  };
+  auto wave_sum = [&](uint64_t v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+  };
+  auto wave_scan = [&](uint64_t v) {   // inclusive scan over the wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint64_t y = __shfl_up(v, o, 64);
+      if (lane >= o) v += y;
+    }
+    return v;
+  };
+  const uint64_t nwg = gridDim.x;
+  uint64_t U = 0, ub = 0, ue = 0;
+  int b = 0, h = 0, s0 = 0;   // the list and step of the first piece
+  if (L.B <= kT) {
+    // one sequence per thread: one scan gives the total and every sequence's first step
+    uint64_t n = 0;
+    if (tid < L.B) {
+      const int Sb = d.seq_lens[tid];
+      const bool ok = Sb >= 1 && Sb <= L.S_cap;
+      if (!ok && blockIdx.x == 0) report(d.cache.status, KVQ_ERR_INVALID_ARG);
+      n = ok ? (uint64_t)((Sb + kStep - 1) / kStep) : 0u;
+    }
+    const uint64_t incl = wave_scan(n);
+    if (lane == 63) s_sc[wave] = incl;
+    __syncthreads();
+    uint64_t woff = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      woff += w < wave ? s_sc[w] : 0u;
+      U += s_sc[w];
+    }
+    U *= (uint64_t)L.H;
+    ub = (uint64_t)blockIdx.x * U / nwg;
+    ue = ((uint64_t)blockIdx.x + 1) * U / nwg;
+    if (ub >= ue) return;
+    const uint64_t lo = (woff + incl - n) * (uint64_t)L.H;   // the sequence's first step
+    if (n > 0 && lo <= ub && ub < lo + n * (uint64_t)L.H) {
+      s_loc[0] = tid;
+      s_loc[1] = (int)((ub - lo) / n);
+      s_loc[2] = (int)((ub - lo) % n);
+    }
+    __syncthreads();
+  } else {
+    // blocks of 768 sequences: the total first, then the scan until the range's start
+    uint64_t mine = 0;
+    for (int bb = tid; bb < L.B; bb += kT) {
+      const int Sb = d.seq_lens[bb];
+      const bool ok = Sb >= 1 && Sb <= L.S_cap;
+      if (!ok && blockIdx.x == 0) report(d.cache.status, KVQ_ERR_INVALID_ARG);
+      mine += ok ? (uint64_t)((Sb + kStep - 1) / kStep) : 0u;
+    }
+    mine = wave_sum(mine);
+    if (lane == 0) s_sc[wave] = mine;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) U += s_sc[w];
+    U *= (uint64_t)L.H;
+    __syncthreads();
+    ub = (uint64_t)blockIdx.x * U / nwg;
+    ue = ((uint64_t)blockIdx.x + 1) * U / nwg;
+    if (ub >= ue) return;
+    uint64_t carry = 0;   // steps per head of the sequences before this block of sequences
+    for (int c0 = 0;; c0 += kT) {
+      const int bb = c0 + tid;
+      const uint64_t n = seq_steps(bb);
+      const uint64_t incl = wave_scan(n);
+      if (lane == 63) s_sc[wave] = incl;
+      __syncthreads();
+      uint64_t woff = 0, tot = 0;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        woff += w < wave ? s_sc[w] : 0u;
+        tot += s_sc[w];
+      }
+      const uint64_t lo = (carry + woff + incl - n) * (uint64_t)L.H;
+      if (n > 0 && lo <= ub && ub < lo + n * (uint64_t)L.H) {
+        s_loc[0] = bb;
+        s_loc[1] = (int)((ub - lo) / n);
+        s_loc[2] = (int)((ub - lo) % n);
+      }
+      __syncthreads();
+      if ((carry + tot) * (uint64_t)L.H > ub) break;   // found in this block
+      carry += tot;
+    }
+  }
+  b = s_loc[0];
+  h = s_loc[1];
+  s0 = s_loc[2];
+
+  uint32_t left = (uint32_t)(ue - ub);   // steps of the range not yet taken
+  for (bool first = true;; first = false) {
+  const int S = d.seq_lens[b];
+  const int nb = (S + kStep - 1) / kStep;
+  const int s1 = (int)min((uint32_t)nb, (uint32_t)s0 + left);
+  const int t0 = kStep * s0, t1 = min(kStep * s1, S);   // the piece's tokens
+  const bool whole = s0 == 0 && s1 == nb;
 
   // query operand (B of S^T = K^ Q^T): lane (row r, k-group kg), positions 32*ks + 8*kg + e
   half8 qop[4];
@@ -589,48 +715,27 @@ __global__ void __launch_bounds__(kWaves * 64) decode_mfma_kernel(DecodeLaunch d
     }
   };
 
-  // Two or three waves share each SIMD and the scheduler favours the oldest; every group of
-  // steps, a wave that is ahead of the slower of its SIMD peers lowers its priority, so all
-  // finish together.
-  const int mysimd = (int)((__builtin_amdgcn_s_getreg((31 << 11) | 4) >> 4) & 3);   // HW_ID.simd
-  if (lane == 0) { s_simd[wave] = mysimd; s_prog[wave] = 0; }
-  __syncthreads();
-  // the (up to two) other waves of this SIMD; a wave ahead of the slower of them yields
-  int peer1 = wave, peer2 = wave;
-  for (int w2 = 0; w2 < kWaves; ++w2) {
-    if (w2 != wave && __builtin_amdgcn_readfirstlane(s_simd[w2]) == mysimd) {
-      if (peer1 == wave) peer1 = w2;
-      else peer2 = w2;
-    }
-  }
-  if (peer2 == wave) peer2 = peer1;
-  int* const prog_mine = &s_prog[wave];
-  const int* const prog_p1 = &s_prog[peer1];
-  const int* const prog_p2 = &s_prog[peer2];
-
   const Buf8 no8{};
   constexpr int NB = kPF + 1;  // ring slots
 
   if constexpr (!PAGED) {
-    // The chunk's full 32-token steps are spread over its waves; its ragged last step (if any) is
-    // left to the chunk's first wave after the others.
+    // The piece's full 32-token steps are spread over the waves; the list's ragged last step (if
+    // it is in the piece) is left to the first wave after the others.
     const int nsteps = (t1 - t0 + kStep - 1) / kStep;
     const bool ragged = (t1 - t0) % kStep != 0;
     const int nfull = nsteps - (ragged ? 1 : 0);
-    // Workgroups walk their full steps in rotated order, starting at evenly spread points.  Every
-    // (sequence, head) slice starts at the same power-of-two-aligned offset; walking them in
-    // lockstep would send every workgroup to the same HBM channels at the same time.
-    const uint32_t n_units = (uint32_t)d.n_chunks * (uint32_t)L.H * (uint32_t)L.B;
-    const uint32_t unit = (uint32_t)chunk + (uint32_t)d.n_chunks * ((uint32_t)h + (uint32_t)L.H * (uint32_t)b);
-    const int rot = nfull > 0 ? (int)(((uint64_t)unit * (uint64_t)nfull) / n_units) : 0;
-    // token start of full step number c (c >= nfull: past the chunk, every load reads zeros)
+    // Workgroups walk their full steps in rotated order, starting at evenly spread points: lists
+    // start at power-of-two-aligned offsets, and walking them in lockstep would send every
+    // workgroup to the same HBM channels at the same time.
+    const int rot = nfull > 0 ? (int)(((uint64_t)blockIdx.x * (uint64_t)nfull) / nwg) : 0;
+    // token start of full step number c (c >= nfull: past the piece, every load reads zeros)
     auto step_ts = [&](int c) {
       if (c >= nfull) return t1 + 2 * kStep;
       int a = c + rot;
       if (a >= nfull) a -= nfull;
       return t0 + kStep * a;
     };
-    // RAGGED: the step may hold tokens >= t1 (only the chunk's last step); the buffer ranges end
+    // RAGGED: the step may hold tokens >= t1 (only the list's last step); the buffer ranges end
     // at row t1, so those rows read as zeros
     auto issue_codes = [&](Buf<FMT>& bf, int tsi) {
       const uint32_t ts = (uint32_t)tsi;
@@ -685,9 +790,9 @@ __global__ void __launch_bounds__(kWaves * 64) decode_mfma_kernel(DecodeLaunch d
       }
     };
     // ---- software pipeline: codes and records of the next kPF steps in flight, the record
-    // bounds of the step after them too.  Wave wi of a chunk takes its full steps wi, wi + wpc,
+    // bounds of the step after them too.  Wave wi takes its full steps wi, wi + wpc,
     // ...; whole groups of NB steps run without conditions, so every ring slot keeps its
-    // registers and the wait counters stay exact.  Loads for steps past the chunk return zeros
+    // registers and the wait counters stay exact.  Loads for steps past the piece return zeros
     // without touching memory.
     Buf<FMT> buf[NB];
     Recs rec[NB];
@@ -740,7 +845,7 @@ __global__ void __launch_bounds__(kWaves * 64) decode_mfma_kernel(DecodeLaunch d
     }
   } else {
     // ---------------------------------------------------------------- paged caches
-    const int pend = (t1 + kBlock - 1) / kBlock;   // pages [t0 / 16, pend) of the chunk
+    const int pend = (t1 + kBlock - 1) / kBlock;   // pages [t0 / 16, pend) of the piece
     const int32_t* btrow = d.block_table + (size_t)b * L.max_pages;
     const uint32_t rows8 = (uint32_t)L.num_pages_fp8 * (uint32_t)L.H * kBlock;
     const __amdgpu_buffer_rsrc_t r8K = make_rsrc(d.cache.codes8[0], rows8 * kHeadDim);
@@ -855,34 +960,47 @@ __global__ void __launch_bounds__(kWaves * 64) decode_mfma_kernel(DecodeLaunch d
 
     for (int sp0 = t0 / kBlock; sp0 < pend; sp0 += kSegPages) {
       const int np = min(kSegPages, pend - sp0);
-      // ---- list the segment's pages by tier, in logical order (threads 0 .. kSegPages - 1)
-      const int tid = threadIdx.x;
-      int tier = -1;
-      uint32_t prow = kDead;
-      if (tid < np) {
-        const uint32_t e = (uint32_t)btrow[sp0 + tid];
-        const uint32_t slot = e & 0x7FFFFFFFu;
-        const bool is8 = (e >> 31) != 0;
-        const bool in_pool = slot < (uint32_t)(is8 ? L.num_pages_fp8 : L.num_pages);
-        if (!in_pool) report(d.cache.status, KVQ_ERR_INVALID_ARG);
-        tier = in_pool && is8 ? 1 : 0;   // a slot outside its pool: listed as a page of no rows
-        prow = in_pool ? (slot * (uint32_t)L.H + (uint32_t)h) * kBlock : kDead;
-      }
-      const uint64_t m0 = __builtin_amdgcn_ballot_w64(tier == 0);
-      const uint64_t m1 = __builtin_amdgcn_ballot_w64(tier == 1);
-      if (tid < kSegPages && lane == 0) {
-        s_wn[tid >> 6][0] = __builtin_popcountll(m0);
-        s_wn[tid >> 6][1] = __builtin_popcountll(m1);
+      // ---- list the segment's pages by tier, in logical order: page k of the segment is taken by
+      // thread k mod 768 (pass k / 768); its 64-page group k / 64 is one wave's ballot
+      constexpr int kListers = kWaves * 64;
+      constexpr int kPasses = (kSegPages + kListers - 1) / kListers;
+      int tier[kPasses];
+      uint32_t prow[kPasses];
+      uint64_t m0[kPasses], m1[kPasses];
+#pragma unroll
+      for (int k = 0; k < kPasses; ++k) {
+        const int pi = tid + kListers * k;
+        tier[k] = -1;
+        prow[k] = kDead;
+        if (pi < np) {
+          const uint32_t e = (uint32_t)btrow[sp0 + pi];
+          const uint32_t slot = e & 0x7FFFFFFFu;
+          const bool is8 = (e >> 31) != 0;
+          const bool in_pool = slot < (uint32_t)(is8 ? L.num_pages_fp8 : L.num_pages);
+          if (!in_pool) report(d.cache.status, KVQ_ERR_INVALID_ARG);
+          tier[k] = in_pool && is8 ? 1 : 0;   // a slot outside its pool: listed as a page of no rows
+          prow[k] = in_pool ? (slot * (uint32_t)L.H + (uint32_t)h) * kBlock : kDead;
+        }
+        m0[k] = __builtin_amdgcn_ballot_w64(tier[k] == 0);
+        m1[k] = __builtin_amdgcn_ballot_w64(tier[k] == 1);
+        if (pi < kSegPages && lane == 0) {
+          s_wn[pi >> 6][0] = __builtin_popcountll(m0[k]);
+          s_wn[pi >> 6][1] = __builtin_popcountll(m1[k]);
+        }
       }
       if (lane == 0) *prog_mine = 0;
       __syncthreads();
-      if (tier >= 0) {
-        int pos = 0;
-        for (int w2 = 0; w2 < (tid >> 6); ++w2) pos += s_wn[w2][tier];
-        const uint64_t m = tier ? m1 : m0;
-        pos += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-        s_pl[tier][pos][0] = prow;
-        s_pl[tier][pos][1] = (uint32_t)(sp0 + tid);
+#pragma unroll
+      for (int k = 0; k < kPasses; ++k) {
+        if (tier[k] >= 0) {
+          const int pi = tid + kListers * k;
+          int pos = 0;
+          for (int w2 = 0; w2 < (pi >> 6); ++w2) pos += s_wn[w2][tier[k]];
+          const uint64_t m = tier[k] ? m1[k] : m0[k];
+          pos += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+          s_pl[tier[k]][pos][0] = prow[k];
+          s_pl[tier[k]][pos][1] = (uint32_t)(sp0 + pi);
+        }
       }
       int n2 = 0, n8 = 0;
 #pragma unroll
@@ -964,7 +1082,7 @@ __global__ void __launch_bounds__(kWaves * 64) decode_mfma_kernel(DecodeLaunch d
     }
   }
 
-  // ---- merge the waves of the workgroup
+  // ---- merge the waves of the workgroup for the piece
   if constexpr (CMP) {   // column r of query r < 8 += its lo column r + 8
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt)
@@ -982,30 +1100,123 @@ __global__ void __launch_bounds__(kWaves * 64) decode_mfma_kernel(DecodeLaunch d
     for (int v = 0; v < 4; ++v) s_o[r * kHeadDim + (16 * mt + 4 * kg + v)] = oacc[mt][v];
   if (kg == 0) { s_ml[wave][r][0] = m_run; s_ml[wave][r][1] = l_row; }
   __syncthreads();
-  for (int i = threadIdx.x; i < cpw * G * kHeadDim; i += kWaves * 64) {
-    const int c2 = i / (G * kHeadDim), row = (i / kHeadDim) % G, ch = i % kHeadDim;
-    const int chunk2 = grp * cpw + c2;
-    if (chunk2 >= d.n_chunks || chunk2 * d.chunk >= S) continue;
-    const int w0 = c2 * wpc;
+  for (int i = threadIdx.x; i < G * kHeadDim; i += kWaves * 64) {
+    const int row = i / kHeadDim, ch = i % kHeadDim;
     float M = -INFINITY;
-    for (int w = w0; w < w0 + wpc; ++w) M = fmaxf(M, s_ml[w][row][0]);
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_ml[w][row][0]);
     float num = 0.0f, den = 0.0f;
-    for (int w = w0; w < w0 + wpc; ++w) {
+    for (int w = 0; w < kWaves; ++w) {
       const float mw = s_ml[w][row][0];
       const float f = mw == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
       den += f * s_ml[w][row][1];
       num += f * ((const float*)(s_lds + w * kTile))[row * kHeadDim + ch];
     }
     const size_t hq = (size_t)h * G + row;
-    if (d.n_chunks == 1) {
+    if (whole) {
       d.out[((size_t)b * d.Hq + hq) * kHeadDim + ch] = num / den;
       if (MASS && ch == 0) d.total_lse[(size_t)b * d.Hq + hq] = M + __builtin_log2f(den);
     } else {
-      float* pp = d.partials + (((size_t)b * d.Hq + hq) * d.n_chunks + chunk2) * (kHeadDim + 2);
+      // a part of a list leaves a (max, sum, output) partial per query head in slot 0 (the
+      // workgroup's first piece) or 1 (its last)
+      float* pp = d.partials + (((size_t)blockIdx.x * 2 + (first ? 0 : 1)) * G + row) * (kHeadDim + 2);
       if (ch == 0) { pp[0] = M; pp[1] = den; }
       pp[2 + ch] = num;
     }
   }
+  if (lane == 0) *prog_mine = 0;
+  left -= (uint32_t)(s1 - s0);
+  if (left == 0) break;
+  __syncthreads();   // the tiles and the wave states are reused by the next piece
+  s0 = 0;
+  if (++h == L.H) {   // the next list with steps (a sequence of invalid length has none)
+    h = 0;
+    do { ++b; } while (!(d.seq_lens[b] >= 1 && d.seq_lens[b] <= L.S_cap));
+  }
+  }
+}
+
+// Lists cut between workgroups: the block of (sequence b, query head hq) merges the partials of
+// the workgroups that worked on its list (b, hq's KV head), in workgroup order, into out[b][hq]
+// (and the total log2-sum-exp of a decode with page masses), out = sum_i 2^(m_i - M) o_i /
+// sum_i 2^(m_i - M) l_i with M = max_i m_i.  The owner of step u (the workgroup whose range
+// holds it) is floor(((u + 1) N - 1) / U), the inverse of the ranges [floor(i U / N),
+// floor((i + 1) U / N)).  A list that one workgroup finished whole was written by the decode;
+// workgroups with empty ranges (more workgroups than steps) hold nothing.  Thread (group g,
+// channel) folds every kMergeGroups-th partial from the g-th, in workgroup order (its loads do not
+// wait on its arithmetic, so an unrolled batch of them is in flight at once); the groups' states
+// are combined in group order: deterministic.
+constexpr int kMergeGroups = 4;
+constexpr int kMergeThreads = kMergeGroups * kHeadDim;
+__global__ void __launch_bounds__(kMergeThreads) streamk_merge_kernel(DecodeLaunch d) {
+  __shared__ uint64_t s_red[kMergeThreads / 64][2];
+  __shared__ float s_st[kMergeGroups][3][kHeadDim];
+  const Layout& L = d.L;
+  const int hq = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x, ch = tid % kHeadDim, g = tid / kHeadDim;
+  const int S = d.seq_lens[b];
+  if (S < 1 || S > L.S_cap) return;   // reported by the decode; out[b] is not written
+  // steps per head of the sequences before b and of all sequences (each thread sums a strided
+  // share of the sequences; the waves' sums are added in order)
+  uint64_t before = 0, total = 0;
+  for (int bb = tid; bb < L.B; bb += kMergeThreads) {
+    const int Sb = d.seq_lens[bb];
+    const uint64_t n = Sb >= 1 && Sb <= L.S_cap ? (uint64_t)((Sb + kStep - 1) / kStep) : 0u;
+    before += bb < b ? n : 0u;
+    total += n;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    before += __shfl_xor(before, o, 64);
+    total += __shfl_xor(total, o, 64);
+  }
+  if ((tid & 63) == 0) { s_red[tid >> 6][0] = before; s_red[tid >> 6][1] = total; }
+  __syncthreads();
+  before = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < kMergeThreads / 64; ++w) { before += s_red[w][0]; total += s_red[w][1]; }
+  const int G = d.Hq / L.H, h = hq / G, row = hq % G;
+  const uint64_t nb = (uint64_t)((S + kStep - 1) / kStep);
+  const uint64_t U = total * (uint64_t)L.H, N = (uint64_t)d.nwg;
+  const uint64_t u0 = before * (uint64_t)L.H + (uint64_t)h * nb, u1 = u0 + nb - 1;
+  const int i0 = (int)(((u0 + 1) * N - 1) / U), i1 = (int)(((u1 + 1) * N - 1) / U);
+  if (i0 == i1) return;
+  // workgroup i0 holds the list's start in its first piece (slot 0) if its range starts there,
+  // else in its last piece (slot 1); every later workgroup holds a part in its first piece
+  const int slot0 = (uint64_t)i0 * U / N == u0 ? 0 : 1;
+  const int np = i1 - i0 + 1;
+  float M = -INFINITY, den = 0.0f, num = 0.0f;
+#pragma unroll 4
+  for (int k = g; k < np; k += kMergeGroups) {
+    const uint64_t i = (uint64_t)(i0 + k);
+    if (k > 0 && i * U / N == (i + 1) * U / N) continue;   // a workgroup without steps
+    const size_t slot = (size_t)i * 2 + (k == 0 ? slot0 : 0);
+    const float* q = d.partials + (slot * G + row) * (kHeadDim + 2);
+    const float m = q[0], l = q[1], o = q[2 + ch];      // a part holding tokens: m finite
+    const float Mn = fmaxf(M, m);
+    const float al = exp2f(M - Mn), w = exp2f(m - Mn);   // al = 0 while M is -inf
+    den = fmaf(w, l, den * al);
+    num = fmaf(w, o, num * al);
+    M = Mn;
+  }
+  s_st[g][0][ch] = M;
+  s_st[g][1][ch] = den;
+  s_st[g][2][ch] = num;
+  __syncthreads();
+  if (g != 0) return;
+  float Mt = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < kMergeGroups; ++k) Mt = fmaxf(Mt, s_st[k][0][ch]);
+  float Dn = 0.0f, Nm = 0.0f;
+#pragma unroll
+  for (int k = 0; k < kMergeGroups; ++k) {
+    const float Mk = s_st[k][0][ch];
+    const float f = Mk == -INFINITY ? 0.0f : exp2f(Mk - Mt);   // a group with no part
+    Dn = fmaf(f, s_st[k][1][ch], Dn);
+    Nm = fmaf(f, s_st[k][2][ch], Nm);
+  }
+  d.out[((size_t)b * d.Hq + hq) * kHeadDim + ch] = Nm / Dn;
+  if (d.total_lse && ch == 0) d.total_lse[(size_t)b * d.Hq + hq] = Mt + __builtin_log2f(Dn);
 }
 
 template <int FMT, bool CMP, bool PAGED, bool MASS>
@@ -1027,33 +1238,17 @@ void launch_fmt(const DecodeLaunch& d, dim3 grid, hipStream_t st) {
 
 hipError_t launch_decode_mfma(const DecodeLaunch& d, hipStream_t st, bool* handled) {
   *handled = false;
-  if (d.fmt != FMT_C2 && !(d.fmt == FMT_FP4 && d.group == 32)) return hipSuccess;
-  if (d.chunk % kStep) return hipSuccess;
-  if (d.L.paged) {
-    // pools are addressed with 32-bit byte offsets (the largest must stay below the offset that
-    // marks a skipped row); FP4 pages take the generic kernel
-    const uint64_t rows2 = (uint64_t)d.L.num_pages * d.L.H * kBlock;
-    const uint64_t rows8 = (uint64_t)d.L.num_pages_fp8 * d.L.H * kBlock;
-    if (d.fmt != FMT_C2 || rows2 * 32 > 0xFFFFF000ull || rows8 * kHeadDim > 0xFFFFF000ull)
-      return hipSuccess;
-  }
-  // Short chunks of contiguous caches are packed several to a workgroup (a divisor of its wave
-  // count) so that every wave keeps a run of up to 32 steps (FP4 at 2048-token chunks: 206 ->
-  // 180 us), never below one workgroup per CU (256).  A paged cache's workgroup lists the pages
-  // of one chunk.
-  const int64_t units = (int64_t)d.L.H * d.L.B;
-  DecodeLaunch dd = d;
-  dd.cpw = 1;
-  while (!d.L.paged && kWaves % (dd.cpw * 2) == 0 && d.chunk * dd.cpw * 2 <= 32 * kStep * kWaves &&
-         units * ((d.n_chunks + dd.cpw * 2 - 1) / (dd.cpw * 2)) >= 256)
-    dd.cpw *= 2;
-  dim3 grid(d.L.H, (d.n_chunks + dd.cpw - 1) / dd.cpw, d.L.B);
-  if (grid.y > 65535u) return hipSuccess;
-  if (d.L.paged && d.page_lse) launch_fmt<FMT_C2, true, true>(dd, grid, st);
-  else if (d.L.paged) launch_fmt<FMT_C2, true>(dd, grid, st);
-  else if (d.fmt == FMT_C2) launch_fmt<FMT_C2, false>(dd, grid, st);
-  else launch_fmt<FMT_FP4, false>(dd, grid, st);
+  if (!mfma_decodes(d.fmt, d.group, d.L.paged, d.L.num_pages, d.L.num_pages_fp8, d.L.H)) return hipSuccess;
+  if (d.nwg < 1 || !d.partials) return hipSuccess;
+  const dim3 grid(d.nwg);
+  if (d.L.paged && d.page_lse) launch_fmt<FMT_C2, true, true>(d, grid, st);
+  else if (d.L.paged) launch_fmt<FMT_C2, true>(d, grid, st);
+  else if (d.fmt == FMT_C2) launch_fmt<FMT_C2, false>(d, grid, st);
+  else launch_fmt<FMT_FP4, false>(d, grid, st);
   *handled = true;
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  streamk_merge_kernel<<<dim3(d.Hq, d.L.B), kMergeThreads, 0, st>>>(d);
   return hipGetLastError();
 }
 

@@ -3,6 +3,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "kvq_device.h"
@@ -117,7 +118,55 @@ int resolve_chunk(const kvq_params* p, int32_t split_chunk) {
 }
 
 
+// Workgroups of the MFMA decoder, which share the 32-token steps of all lists evenly: one per CU
+// of an MI355X (256, one resident workgroup each) by default, never fewer than 12 steps (one per
+// wave) each at max_seq_len; with a split, about one per split_chunk tokens of all lists at
+// max_seq_len (at most kMaxDecodeWGs).
+constexpr int64_t kDecodeWGs = 256;
+constexpr int64_t kMaxDecodeWGs = 16384;
+bool mfma_format(const kvq_params* p) {
+  return mfma_decodes(p->format, p->group_size, p->page_size != 0, p->num_pages, p->num_pages_fp8,
+                      p->num_kv_heads);
+}
+int64_t decode_wgs(const kvq_params* p, int32_t split_chunk) {
+  const int64_t lists = (int64_t)p->batch * p->num_kv_heads;
+  const int64_t steps = lists * ((p->max_seq_len + 31) / 32);
+  int64_t n = split_chunk > 0 ? (lists * p->max_seq_len + split_chunk - 1) / split_chunk
+                              : std::min(kDecodeWGs, (steps + 11) / 12);
+  return std::max<int64_t>(1, std::min({n, steps, kMaxDecodeWGs}));
+}
+// partials of the MFMA decoder: two (max, sum, output) slots of Hq / H query heads per workgroup
+uint64_t mfma_partial_bytes(const kvq_params* p, int32_t split_chunk) {
+  if (!mfma_format(p)) return 0;
+  return (uint64_t)decode_wgs(p, split_chunk) * 2ull * (uint64_t)(p->num_q_heads / p->num_kv_heads) *
+         (kHeadDim + 2) * 4ull;
+}
+
 uint64_t align256(uint64_t x) { return (x + 255) & ~255ull; }
+
+// Attention prologue: workgroups per K / V tile and per Q tile (a tile is one head's 128 output
+// columns for up to 64 batch rows): about 256 Q workgroups in all, four times finer slices of
+// d_model for the K / V tiles (they finish first; the Q workgroups then quantize their rows).
+// Workspace: control words (zero between calls), the finished K / V rows, the partial tiles.
+struct PrologueShape {
+  int splits_kv, splits_q, row_blocks, nwg;
+  uint64_t control_bytes, rows_bytes, partial_bytes;
+};
+PrologueShape prologue_shape(const kvq_params* p, int32_t d_model) {
+  PrologueShape s;
+  const int nch = d_model / 128;
+  s.row_blocks = (p->batch + kPrologueRows - 1) / kPrologueRows;
+  const int64_t q_tiles = (int64_t)p->num_q_heads * s.row_blocks;
+  s.splits_q = (int)std::max<int64_t>(1, std::min<int64_t>(nch, (256 + q_tiles - 1) / q_tiles));
+  s.splits_kv = std::min(nch, 4 * s.splits_q);
+  s.nwg = 2 * p->num_kv_heads * s.splits_kv + p->num_q_heads * s.splits_q;
+  const uint64_t words = (uint64_t)s.row_blocks * (2 * p->num_kv_heads + p->num_q_heads) +
+                         (uint64_t)s.row_blocks * 2 * p->num_kv_heads + s.row_blocks + 2;
+  s.control_bytes = align256(words * 4ull);
+  s.rows_bytes = align256((uint64_t)s.row_blocks * 2 * p->num_kv_heads * kPrologueRows * kHeadDim * 4ull);
+  s.partial_bytes = (uint64_t)s.row_blocks * s.nwg * (kPrologueRows * kHeadDim + kPrologueRows) * 4ull;
+  return s;
+}
 // workspace of a decode with page masses: the decode's own, then page and total log-sum-exps
 uint64_t mass_ws_bytes(const kvq_params* p, uint64_t decode_bytes) {
   return align256(decode_bytes) +
@@ -167,7 +216,7 @@ int32_t decode_impl(const kvq_params* pin, const kvq_cache* cache, const void* q
   const int chunk = resolve_chunk(p, split_chunk);
   if (chunk < 0) return KVQ_ERR_INVALID_ARG;
   uint64_t need = 0;
-  kvq_workspace_bytes(p, chunk, &need);
+  kvq_workspace_bytes(p, split_chunk, &need);
   uint64_t need_mass = need;
   if (page_mass) {   // per-page and per-head log-sum-exps after the partials
     if (!p->page_size) return KVQ_ERR_UNSUPPORTED;
@@ -194,7 +243,8 @@ int32_t decode_impl(const kvq_params* pin, const kvq_cache* cache, const void* q
   d.outl = p->outlier_dtype;
   d.chunk = chunk;
   d.n_chunks = (p->max_seq_len + chunk - 1) / chunk;
-  d.partials = d.n_chunks > 1 ? (float*)workspace : nullptr;
+  d.partials = need ? (float*)workspace : nullptr;
+  d.nwg = (int)decode_wgs(p, split_chunk);
   d.page_lse = nullptr;
   d.total_lse = nullptr;
   if (page_mass) {
@@ -202,13 +252,12 @@ int32_t decode_impl(const kvq_params* pin, const kvq_cache* cache, const void* q
     d.total_lse = d.page_lse + (size_t)p->batch * p->num_q_heads * p->max_pages_per_seq;
   }
   d.scale_log2 = sm_scale * 1.4426950408889634f;
-  d.cpw = 1;
   hipStream_t s = (hipStream_t)stream;
   bool handled = false;
   if (launch_decode_mfma(d, s, &handled) != hipSuccess) return KVQ_ERR_HIP;
   if (!handled && page_mass) return KVQ_ERR_UNSUPPORTED;   // nothing launched
   if (!handled && launch_decode_generic(d, s) != hipSuccess) return KVQ_ERR_HIP;
-  if (d.n_chunks > 1 && launch_lse_merge(d, s) != hipSuccess) return KVQ_ERR_HIP;
+  if (!handled && d.n_chunks > 1 && launch_lse_merge(d, s) != hipSuccess) return KVQ_ERR_HIP;
   if (page_mass) {
     MassLaunch m;
     m.page_lse = d.page_lse;
@@ -323,7 +372,8 @@ int32_t kvq_workspace_bytes(const kvq_params* pin, int32_t split_chunk, uint64_t
   const int chunk = resolve_chunk(p, split_chunk);
   if (chunk < 0) return KVQ_ERR_INVALID_ARG;
   const uint64_t nc = (uint64_t)((p->max_seq_len + chunk - 1) / chunk);
-  *out_bytes = nc <= 1 ? 0 : (uint64_t)p->batch * p->num_q_heads * nc * (kHeadDim + 2) * 4ull;
+  const uint64_t chunked = nc <= 1 ? 0 : (uint64_t)p->batch * p->num_q_heads * nc * (kHeadDim + 2) * 4ull;
+  *out_bytes = mfma_format(p) ? mfma_partial_bytes(p, split_chunk) : chunked;
   return KVQ_OK;
 }
 
@@ -426,6 +476,68 @@ int32_t kvq_retier(const kvq_params* pin, const kvq_cache* cache, int32_t* block
   if (launch_retier_select(r, s) != hipSuccess) return KVQ_ERR_HIP;
   if (launch_retier_demote(r, s) != hipSuccess) return KVQ_ERR_HIP;
   if (launch_retier_commit(r, s) != hipSuccess) return KVQ_ERR_HIP;
+  return KVQ_OK;
+}
+
+int32_t kvq_prologue_workspace_bytes(const kvq_params* pin, int32_t d_model, uint64_t* out_bytes) {
+  int32_t st = check_params(pin);
+  if (st) return st;
+  const Params n(pin);
+  if (!out_bytes || d_model < 128 || d_model % 128) return KVQ_ERR_INVALID_ARG;
+  const PrologueShape sh = prologue_shape(&n.p, d_model);
+  *out_bytes = sh.control_bytes + sh.rows_bytes + sh.partial_bytes;
+  return KVQ_OK;
+}
+
+int32_t kvq_attention_prologue(const kvq_params* pin, const kvq_cache* cache, const void* hidden_bf16,
+                               const void* gain_bf16, const void* weight_bf16, int32_t d_model,
+                               float eps, const int32_t* positions, const int32_t* block_table,
+                               void* q_bf16_out, float* proj_out, void* workspace, uint64_t ws_bytes,
+                               void* stream) {
+  uint64_t need = 0;
+  int32_t st = kvq_prologue_workspace_bytes(pin, d_model, &need);
+  if (st) return st;
+  const Params n(pin);
+  const kvq_params* p = &n.p;
+  st = check_cache(p, cache);
+  if (st) return st;
+  if (!hidden_bf16 || !gain_bf16 || !weight_bf16 || !positions || !q_bf16_out) return KVQ_ERR_INVALID_ARG;
+  if (!(eps >= 0.0f) || !isfinite(eps)) return KVQ_ERR_INVALID_ARG;
+  if (((uintptr_t)hidden_bf16 | (uintptr_t)gain_bf16 | (uintptr_t)weight_bf16) & 15) return KVQ_ERR_INVALID_ARG;
+  if (p->page_size && !block_table) return KVQ_ERR_INVALID_ARG;
+  if (!workspace || ws_bytes < need) return KVQ_ERR_WORKSPACE;
+  const PrologueShape sh = prologue_shape(p, d_model);
+  PrologueLaunch a;
+  a.L = make_layout(p, cache->outl_capacity);
+  a.cache = *cache;
+  a.hidden = (const uint16_t*)hidden_bf16;
+  a.gain = (const uint16_t*)gain_bf16;
+  a.weight = (const uint16_t*)weight_bf16;
+  a.positions = positions;
+  a.block_table = p->page_size ? block_table : nullptr;
+  a.q_out = (uint16_t*)q_bf16_out;
+  a.proj_out = proj_out;
+  int32_t* ctl = (int32_t*)workspace;
+  a.arrive = ctl;
+  a.ready = a.arrive + (size_t)sh.row_blocks * (2 * p->num_kv_heads + p->num_q_heads);
+  a.claim = a.ready + (size_t)sh.row_blocks * 2 * p->num_kv_heads;
+  a.ticket = a.claim + sh.row_blocks;
+  a.done = a.ticket + 1;
+  a.kvrows = (float*)((uint8_t*)workspace + sh.control_bytes);
+  a.partials = (float*)((uint8_t*)workspace + sh.control_bytes + sh.rows_bytes);
+  a.row_blocks = sh.row_blocks;
+  a.Hq = p->num_q_heads;
+  a.d = d_model;
+  a.splits_kv = sh.splits_kv;
+  a.splits_q = sh.splits_q;
+  a.eps = eps;
+  a.fmt = p->format;
+  a.group = p->group_size;
+  a.outl = p->outlier_dtype;
+  a.fit = n.fit;
+  a.lloyd = p->lloyd_iters;
+  a.tau2 = p->outlier_sigma * p->outlier_sigma;
+  if (launch_prologue(a, (hipStream_t)stream) != hipSuccess) return KVQ_ERR_HIP;
   return KVQ_OK;
 }
 

@@ -31,7 +31,8 @@ struct DecodeLaunch {
   const int32_t* seq_lens;
   const int32_t* block_table;
   float* out;                 // [B][Hq][D]
-  float* partials;            // [B][Hq][n_chunks][D + 2] or null when n_chunks == 1
+  float* partials;            // generic decoder: [B][Hq][n_chunks][D + 2] or null when n_chunks
+                              // == 1; MFMA decoder: [nwg][2 slots][Hq / H][D + 2]
   float* page_lse;            // paged, or null: [B][Hq][max_pages] log2-sum-exp of each page
   float* total_lse;           // with page_lse: [B][Hq] log2-sum-exp of every token
   int Hq;
@@ -41,8 +42,20 @@ struct DecodeLaunch {
   int chunk;                  // tokens per split-K chunk (multiple of 64)
   int n_chunks;               // ceil(S_cap / chunk)
   float scale_log2;           // sm_scale * log2(e)
-  int cpw;                    // MFMA decoder: chunks per workgroup (set by its launcher)
+  int nwg;                    // MFMA decoder: workgroups sharing the steps of all lists
 };
+
+// The MFMA decoder takes 2-bit caches and FP4 caches with groups of 32 (contiguous), and paged
+// 2-bit caches whose pools it addresses with 32-bit byte offsets (the largest must stay below
+// the offset that marks a skipped row); everything else takes the generic decoder.
+inline bool mfma_decodes(int fmt, int group, bool paged, int64_t num_pages, int64_t num_pages_fp8,
+                         int H) {
+  if (fmt != FMT_C2 && !(fmt == FMT_FP4 && group == 32)) return false;
+  if (!paged) return true;
+  const uint64_t rows2 = (uint64_t)num_pages * (uint64_t)H * kBlock;
+  const uint64_t rows8 = (uint64_t)num_pages_fp8 * (uint64_t)H * kBlock;
+  return fmt == FMT_C2 && rows2 * 32 <= 0xFFFFF000ull && rows8 * kHeadDim <= 0xFFFFF000ull;
+}
 
 // Page attention masses of a paged decode (tiering.hip)
 struct MassLaunch {
@@ -77,6 +90,37 @@ struct RetierLaunch {
   int lloyd;
 };
 
+// Attention prologue of a decode step (prologue.hip): RMSNorm, joint Q/K/V projection and the
+// KV-cache write of the new token
+constexpr int kPrologueRows = 64;     // batch rows per row block of the projection
+struct PrologueLaunch {
+  Layout L;
+  kvq_cache cache;
+  const uint16_t* hidden;     // bf16 [B][d]
+  const uint16_t* gain;       // bf16 [d]
+  const uint16_t* weight;     // bf16 [(Hq + 2H) * 128][d]: Q heads, K heads, V heads
+  const int32_t* positions;   // [B]: token of the new K / V rows, < 0: no write
+  const int32_t* block_table;
+  uint16_t* q_out;            // bf16 [B][Hq][128]
+  float* proj_out;            // optional fp32 [B][(Hq + 2H) * 128]
+  float* partials;            // [row blocks][workgroups][64 * 128 + 64]
+  float* kvrows;              // [row blocks][2H][64][128] finished K / V rows
+  // control words, zero between calls: arrival counters [row blocks][2H + Hq], K / V tile ready
+  // flags [row blocks][2H], row-batch claims [row blocks], the role ticket, finished workgroups
+  int32_t* arrive;
+  int32_t* ready;
+  int32_t* claim;
+  int32_t* ticket;
+  int32_t* done;
+  int Hq, d;
+  int splits_kv, splits_q;    // workgroups per K / V tile and per Q tile
+  int row_blocks;
+  float eps;
+  int fmt, group, outl, fit, lloyd;
+  float tau2;
+};
+
+hipError_t launch_prologue(const PrologueLaunch& a, hipStream_t st);
 hipError_t launch_mass_normalize(const MassLaunch& m, hipStream_t st);
 hipError_t launch_retier_select(const RetierLaunch& r, hipStream_t st);
 hipError_t launch_retier_demote(const RetierLaunch& r, hipStream_t st);

@@ -1,0 +1,534 @@
+// Attention prologue of a decode step in one kernel: RMSNorm of every sequence's hidden state,
+// the joint Q / K / V projection on the MFMA matrix cores, and the KV-cache write of the new
+// token's K and V rows (quantized exactly as an append of those rows).
+//
+// "Sub-5ms MoE Inference: Sub-Byte KV Quantization and Expert Pipelining at Scale", section
+// "Engineering Real-Time Autonomous Workflows", item 1: RMSNorm, the self-attention projection
+// and the KV-cache write fused into a single kernel.
+//
+// Arithmetic.  y = W (g * h) / rms(h), rms(h) = sqrt(mean(h^2) + eps), is formed as r * (W a)
+// with a = bf16(h * g) (a bf16 x bf16 product is exact in fp32; it is rounded once to bf16) and
+// r = 1 / sqrt(sum(h^2) / d + eps) applied to each row after the product (r is one number per
+// row).  W a runs on v_mfma_f32_16x16x32_bf16 with fp32 accumulation; sum(h^2) is an fp32 sum of
+// exact squares.  A row's value is the fp32 sum of its K-slice partials in slice order, times r:
+// the result does not depend on which workgroup finishes last.
+//
+// Work split.  A tile is one head's 128 output columns (K heads, then V heads, then Q heads, so
+// that the K / V tiles are dispatched first) for up to 64 batch rows; the d_model reduction of a
+// tile is split over several workgroups (K / V tiles more finely, so that their epilogues, which
+// quantize the rows, start early and overlap the Q tiles' weight streaming).  A workgroup streams
+// its weight slice from HBM straight into MFMA operand registers (every weight is read once),
+// stages bf16(h * g) of its slice in LDS 128 columns at a time, and writes a partial tile; the
+// last workgroup of a tile to arrive sums the partials and finishes the tile: q rows in bf16, or
+// the K / V rows quantized into the cache.  Partials cross workgroups on different XCDs, whose L2
+// caches are not coherent with each other: they are stored and loaded with agent-scope atomics
+// (which carry the coherence cache policy), the arrival counter is an agent-scope atomic, and the
+// last workgroup returns the counter to zero.
+#include "kvq_device.h"
+#include "kvq_launch.h"
+#include "quant_row.h"
+
+namespace kvq {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kPThreads = 256;            // 4 waves, 32 output columns each
+constexpr int kPRows = kPrologueRows;     // batch rows of a row block
+constexpr int kPKc = 128;                 // d_model columns per LDS stage
+constexpr int kPStride = kPKc + 8;        // bf16 per staged row: 272 bytes, conflict-free reads
+constexpr int kPSlots = kPThreads / kRowLanes;   // rows quantized at once in a K / V epilogue
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return as_f32(b << 16); }
+// nearest-even bfloat16 of a finite float
+__device__ __forceinline__ uint32_t f32_to_bf16(float x) {
+  const uint32_t u = as_u32(x);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Partials: 16-byte buffer loads and stores carrying the cache policy bit sc1 of gfx940-family
+// memory instructions, which agent-scope atomic loads and stores carry: they reach the device's
+// coherence point, past the XCD's own L2.
+constexpr int kSc1 = 16;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void store_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off, floatx4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)off, 0, kSc1);
+}
+__device__ __forceinline__ floatx4 load_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kSc1));
+}
+
+// LDS staging of the rows quantized in one round of a K / V epilogue
+struct RowStage {
+  uint8_t code[kPSlots][kHeadDim];
+  uint8_t flag[kPSlots][kHeadDim];
+  float x[kPSlots][kHeadDim];
+  uint32_t meta[kPSlots][8];
+};
+
+// The records of list (b, h, kv) of tokens < t: those before t's 16-token block plus those of
+// the block's rows before t (a block holds at most 16 rows of D records, and the list is sorted,
+// so each of the n lanes stops at its first record of a token >= t); the lanes' counts are
+// summed over the n-lane group (n a power of two, aligned in the wave).
+template <int N>
+__device__ int64_t records_before(const PrologueLaunch& a, int b, int h, int kv, int t, int lane) {
+  const Layout& Lo = a.L;
+  int64_t start = 0;
+  int cnt = 0;
+  if (t > 0) {
+    const size_t lid = list_id(Lo, b, h, kv);
+    const uint32_t* oidx = a.cache.outl_idx[kv] + ((size_t)b * Lo.H + h) * (size_t)Lo.outl_cap;
+    start = max((int64_t)0, min((int64_t)a.cache.outl_block_start[lid * (size_t)Lo.nblk + ((t - 1) >> 4)],
+                                Lo.outl_cap));
+    const int64_t old = max((int64_t)0, min((int64_t)a.cache.outl_count[lid], Lo.outl_cap));
+    const int64_t lim = min(old, start + (int64_t)kBlock * kHeadDim);
+    for (int64_t r = start + lane; r < lim; r += N) {
+      if (oidx[r] >= (uint32_t)t * kHeadDim) break;
+      ++cnt;
+    }
+  }
+#pragma unroll
+  for (int o = N / 2; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o, N);
+  return start + cnt;
+}
+
+// Appends one token's row (32 lanes of one slot; lane = gi * (G / 4) + jg holds channels
+// gi * G + jg + (G / 4) e) to list (b, h, kv) at token t, after the `running` records of tokens
+// < t (the list is cut back to them): the row is quantized (FP8 tier or outlier isolation + fit),
+// its codes and metadata are written to its row slot and its outlier records appended in channel
+// order.  Every thread of the workgroup calls this once per round (it holds workgroup barriers);
+// `valid` false: the slot has no row this round.
+template <int FMT, int G>
+__device__ void append_row(const PrologueLaunch& a, bool valid, int b, int h, int kv, int t,
+                           int64_t running, const float x[4], int lane, int slot, RowStage& st) {
+  constexpr int L = G / 4;
+  constexpr int CB = kHeadDim * code_bits(FMT) / 8;
+  const Layout& Lo = a.L;
+  const int gi = lane / L, jg = lane % L;
+  if (valid && t >= Lo.S_cap) {
+    if (lane == 0) report(a.cache.status, KVQ_ERR_INVALID_ARG);
+    valid = false;
+  }
+  const size_t lid = list_id(Lo, b, h, kv);
+  int32_t* bstart = a.cache.outl_block_start + lid * (size_t)Lo.nblk;
+  uint32_t* oidx = a.cache.outl_idx[kv] + ((size_t)b * Lo.H + h) * (size_t)Lo.outl_cap;
+  uint8_t* oval = (uint8_t*)a.cache.outl_val[kv] +
+                  ((size_t)b * Lo.H + h) * (size_t)Lo.outl_cap * (a.outl == KVQ_OUTL_FP16 ? 2 : 1);
+
+  int tier1 = 0;
+  size_t pslot = 0;
+  bool row_ok = valid;
+  if (Lo.paged && valid) {
+    row_ok = page_slot(Lo, a.block_table, b, t, &tier1, &pslot);
+    if (!row_ok && lane == 0) report(a.cache.status, KVQ_ERR_INVALID_ARG);
+  }
+  RowOut o;
+  quantize_row<FMT, G>(x, tier1, a.cache.chan_mask, a.outl, a.tau2, a.fit, a.lloyd, kv, h, Lo.H, gi,
+                       jg, o);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int c = gi * G + jg + L * e;
+    st.code[slot][c] = (uint8_t)o.code[e];
+    st.flag[slot][c] = valid ? (uint8_t)o.flag[e] : 0;
+    st.x[slot][c] = x[e];
+  }
+  if (tier1) {
+    if (lane == 0) st.meta[slot][0] = o.meta[0];
+  } else if (jg == 0) {
+    constexpr int MB = meta_bytes_per_group(FMT);
+    if constexpr (MB == 8) { st.meta[slot][2 * gi] = o.meta[0]; st.meta[slot][2 * gi + 1] = o.meta[1]; }
+    else if constexpr (MB == 4) { st.meta[slot][gi] = o.meta[0]; }
+    else { ((uint8_t*)st.meta[slot])[gi] = (uint8_t)o.meta[0]; }
+  }
+  __syncthreads();
+
+  if (row_ok) {
+    uint8_t* codes_dst;
+    uint8_t* meta_dst;
+    int cb, mb;
+    if (!Lo.paged) {
+      const size_t row = ((size_t)b * Lo.H + h) * (size_t)Lo.S_cap + (size_t)t;
+      codes_dst = (uint8_t*)a.cache.codes[kv] + row * CB;
+      meta_dst = (uint8_t*)a.cache.meta[kv] + row * Lo.meta_bytes;
+      cb = CB; mb = Lo.meta_bytes;
+    } else {
+      const size_t prow = (pslot * Lo.H + h) * kBlock + (t & 15);
+      if (tier1) {
+        codes_dst = (uint8_t*)a.cache.codes8[kv] + prow * kHeadDim;
+        meta_dst = (uint8_t*)(a.cache.scale8[kv] + prow);
+        cb = kHeadDim; mb = 4;
+      } else {
+        codes_dst = (uint8_t*)a.cache.codes[kv] + prow * CB;
+        meta_dst = (uint8_t*)a.cache.meta[kv] + prow * Lo.meta_bytes;
+        cb = CB; mb = Lo.meta_bytes;
+      }
+    }
+    const int bits = tier1 ? 8 : code_bits(FMT);
+    if (lane < cb / 4) ((uint32_t*)codes_dst)[lane] = pack_word(st.code[slot], lane, bits);
+    if (lane < mb / 4) ((uint32_t*)meta_dst)[lane] = st.meta[slot][lane];
+    else if (mb < 4 && lane == 0) {
+      for (int k = 0; k < mb; ++k) meta_dst[k] = ((uint8_t*)st.meta[slot])[k];
+    }
+  }
+
+  // the row's outlier records in channel order: channels 4 lane .. 4 lane + 3
+  uint32_t fl = 0;
+  int cnt = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t f = st.flag[slot][4 * lane + k];
+    fl |= f << k;
+    cnt += (int)f;
+  }
+  int incl = cnt;
+#pragma unroll
+  for (int dd = 1; dd < kRowLanes; dd <<= 1) {
+    const int y = __shfl_up(incl, dd, kRowLanes);
+    if (lane >= dd) incl += y;
+  }
+  const int total = __shfl(incl, kRowLanes - 1, kRowLanes);
+  if (valid) {
+    if ((t & 15) == 0 && lane == 0) bstart[t >> 4] = (int32_t)min(running, (int64_t)INT32_MAX);
+    int64_t k = running + (incl - cnt);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if ((fl >> q) & 1u) {
+        const int c = 4 * lane + q;
+        if (k < Lo.outl_cap) {
+          oidx[k] = (uint32_t)t * kHeadDim + (uint32_t)c;
+          const float xv = st.x[slot][c];
+          if (a.outl == KVQ_OUTL_FP16) ((uint16_t*)oval)[k] = (uint16_t)f32_to_half_bits(xv);
+          else oval[k] = (uint8_t)f32_to_e4m3(xv);
+        } else {
+          report(a.cache.status, KVQ_ERR_CAPACITY);
+        }
+        ++k;
+      }
+    }
+    if (lane == 0) a.cache.outl_count[lid] = (int32_t)min(running + total, Lo.outl_cap);
+  }
+  __syncthreads();   // the staging is reused by the next round
+}
+
+template <int FMT, int G>
+__global__ void __launch_bounds__(kPThreads) prologue_kernel(PrologueLaunch a) {
+  // the staged activations of two 128-column stages; the last workgroup of a tile reuses them
+  // for the tile's summed rows
+  __shared__ __attribute__((aligned(16))) uint16_t s_a[2][kPRows * kPStride];
+  __shared__ float s_r[kPRows];
+  __shared__ RowStage s_st;
+  __shared__ int s_word;
+  static_assert(sizeof(s_a) >= kPRows * (kHeadDim + 1) * sizeof(float), "row tile fits the staging");
+
+  const Layout& L = a.L;
+  const int H = L.H, Hq = a.Hq, d = a.d;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int nkv = 2 * H * a.splits_kv, nx = nkv + Hq * a.splits_q;
+  const int nall = nx * a.row_blocks;
+  // Roles are handed out in the order the workgroups start (an arrival ticket), K / V slices of
+  // a row block before its Q slices: a Q workgroup that waits for K / V rows below only waits for
+  // workgroups that have started before it, which never wait themselves.
+  if (tid == 0) s_word = __hip_atomic_fetch_add(a.ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const int ticket = s_word;
+  __syncthreads();   // s_word is written again below
+  if (ticket >= nall) {   // the control words were not zero before the call
+    if (tid == 0) report(a.cache.status, KVQ_ERR_WORKSPACE);
+    return;
+  }
+  const int rb = ticket / nx, wg = ticket % nx, row0 = rb * kPRows;
+  const int nrows = min(kPRows, L.B - row0);
+  // tile and K-slice of this role; the tile's slices are consecutive
+  int tile, split, splits, first;
+  if (wg < nkv) {
+    tile = wg / a.splits_kv; split = wg % a.splits_kv; splits = a.splits_kv; first = tile * a.splits_kv;
+  } else {
+    tile = 2 * H + (wg - nkv) / a.splits_q; split = (wg - nkv) % a.splits_q; splits = a.splits_q;
+    first = nkv + (tile - 2 * H) * a.splits_q;
+  }
+  // output rows of the projection: K head j at Hq + j, V head j at Hq + H + j, Q head j at j
+  const int head_row = tile < 2 * H ? Hq + tile : tile - 2 * H;
+  const int col0 = head_row * kHeadDim;
+  const int nch = d / kPKc;
+  const int per = (nch + splits - 1) / splits;
+  const int c0 = min(nch, split * per), c1 = min(nch, c0 + per);
+
+  // staging map: thread -> 8 columns (kseg) of rows srow + 16 i
+  const int kseg = tid & 15, srow = tid >> 4;
+  // MFMA map: lane (r16, kg); wave -> columns 32 wave .. 32 wave + 31
+  const int r16 = lane & 15, kg = lane >> 4;
+  const uint16_t* wrow0 = a.weight + (size_t)(col0 + 32 * wave + r16) * d + 8 * kg;
+  const uint16_t* wrow1 = wrow0 + (size_t)16 * d;
+
+  float ss[4] = {0.f, 0.f, 0.f, 0.f};
+  floatx4 acc[4][2];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) acc[mt][0] = acc[mt][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  uint4 hv[4], gv;
+  auto load_h = [&](int c) {
+    const int k0 = c * kPKc + 8 * kseg;
+    gv = *(const uint4*)(a.gain + k0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = srow + 16 * i;
+      hv[i] = r < nrows ? *(const uint4*)(a.hidden + (size_t)(row0 + r) * d + k0) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  // weights are read once: non-temporal loads, two stages ahead of their use
+  u32x4 w0[2][4], w1[2][4], w2[2][4];
+  auto load_w = [&](u32x4 (&w)[2][4], int c) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      w[0][ks] = __builtin_nontemporal_load((const u32x4*)(wrow0 + c * kPKc + 32 * ks));
+      w[1][ks] = __builtin_nontemporal_load((const u32x4*)(wrow1 + c * kPKc + 32 * ks));
+    }
+  };
+  // bf16(h * g) of the staged columns into LDS, h^2 into the row sums
+  auto stage = [&](int buf) {
+    const uint32_t g[4] = {gv.x, gv.y, gv.z, gv.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t hw[4] = {hv[i].x, hv[i].y, hv[i].z, hv[i].w};
+      uint32_t o[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float h0 = bf16_to_f32(hw[j] & 0xFFFFu), h1 = bf16_to_f32(hw[j] >> 16);
+        const float g0 = bf16_to_f32(g[j] & 0xFFFFu), g1 = bf16_to_f32(g[j] >> 16);
+        ss[i] += h0 * h0;
+        ss[i] += h1 * h1;
+        o[j] = f32_to_bf16(h0 * g0) | (f32_to_bf16(h1 * g1) << 16);
+      }
+      *(uint4*)&s_a[buf][(srow + 16 * i) * kPStride + 8 * kseg] = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+  };
+  auto mfma = [&](int buf, const u32x4 (&w)[2][4]) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8 b0 = __builtin_bit_cast(bf16x8, w[0][ks]);
+      const bf16x8 b1 = __builtin_bit_cast(bf16x8, w[1][ks]);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const bf16x8 av = __builtin_bit_cast(
+            bf16x8, *(const uint4*)&s_a[buf][(16 * mt + r16) * kPStride + 32 * ks + 8 * kg]);
+        acc[mt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b0, acc[mt][0], 0, 0, 0);
+        acc[mt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b1, acc[mt][1], 0, 0, 0);
+      }
+    }
+  };
+
+  // ---- the K-slice: stage c (activations one stage ahead), multiply c (weights two ahead)
+  if (c0 < c1) {
+    load_h(c0);
+    load_w(w0, c0);
+    if (c0 + 1 < c1) load_w(w1, c0 + 1);
+    int buf = 0;
+    for (int c = c0; c < c1; c += 3) {
+      stage(buf);
+      if (c + 1 < c1) load_h(c + 1);
+      if (c + 2 < c1) load_w(w2, c + 2);
+      __syncthreads();
+      mfma(buf, w0);
+      buf ^= 1;
+      if (c + 1 >= c1) break;
+      stage(buf);
+      if (c + 2 < c1) load_h(c + 2);
+      if (c + 3 < c1) load_w(w0, c + 3);
+      __syncthreads();
+      mfma(buf, w1);
+      buf ^= 1;
+      if (c + 2 >= c1) break;
+      stage(buf);
+      if (c + 3 < c1) load_h(c + 3);
+      if (c + 4 < c1) load_w(w1, c + 4);
+      __syncthreads();
+      mfma(buf, w2);
+      buf ^= 1;
+    }
+  }
+  // row sums of h^2 over the slice: the 16 threads of a row are one 16-lane DPP row
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    ss[i] += xor_f32<8>(ss[i]);
+    ss[i] += xor_f32<4>(ss[i]);
+    ss[i] += xor_f32<2>(ss[i]);
+    ss[i] += xor_f32<1>(ss[i]);
+  }
+
+  // ---- partial tile: [128 columns][64 rows] (a lane's four rows of a column are contiguous),
+  // then the [64] row sums of h^2
+  constexpr int kPart = kPRows * kHeadDim + kPRows;
+  const __amdgpu_buffer_rsrc_t rpart = make_rsrc(a.partials + ((size_t)rb * nx + wg) * kPart, kPart * 4);
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+      store_coherent(rpart, ((32 * wave + 16 * nt + r16) * kPRows + 16 * mt + 4 * kg) * 4, acc[mt][nt]);
+  if (kseg == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s_r[srow + 16 * i] = ss[i];
+  }
+  __syncthreads();
+  if (tid < kPRows / 4)
+    store_coherent(rpart, (kPRows * kHeadDim + 4 * tid) * 4,
+                   floatx4{s_r[4 * tid], s_r[4 * tid + 1], s_r[4 * tid + 2], s_r[4 * tid + 3]});
+  // every store of the workgroup has completed before it arrives
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  int* ctr = a.arrive + (size_t)rb * (2 * H + Hq) + tile;
+  if (tid == 0) s_word = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == splits - 1;
+  __syncthreads();
+  const bool last = s_word != 0;
+  __syncthreads();   // s_word is written again below
+
+  if (last) {
+    // ---- the last workgroup of the tile: rows y = r * (sum of the partials in slice order)
+    float* s_y = (float*)&s_a[0][0];   // [64][129]
+    const __amdgpu_buffer_rsrc_t rall = make_rsrc(a.partials + ((size_t)rb * nx + first) * kPart,
+                                                  (uint32_t)splits * kPart * 4);
+    // every thread's vectors of 4 consecutive rows of a column (or of the row sums), summed over
+    // the slices in slice order; the loads of two slices are in flight at once
+    constexpr int kVec = kPart / 4, kPer = (kVec + kPThreads - 1) / kPThreads;
+    floatx4 v[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) v[u] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+    for (int sl = 0; sl < splits; ++sl) {
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) {
+        const int i = tid + kPThreads * u;
+        if (i < kVec) v[u] += load_coherent(rall, ((uint32_t)sl * kPart + 4 * i) * 4);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int i = tid + kPThreads * u;
+      if (i >= kVec) continue;
+      if (4 * i < kPRows * kHeadDim) {
+        const int c = (4 * i) / kPRows, r = (4 * i) % kPRows;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) s_y[(r + j) * (kHeadDim + 1) + c] = v[u][j];
+      } else {
+        const int r = 4 * i - kPRows * kHeadDim;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) s_r[r + j] = 1.0f / sqrtf(v[u][j] / (float)d + a.eps);
+      }
+    }
+    __syncthreads();
+    if (tid == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int ncols = (Hq + 2 * H) * kHeadDim;
+    if (a.proj_out) {
+      for (int i = tid; i < nrows * kHeadDim; i += kPThreads) {
+        const int r = i >> 7, c = i & 127;
+        a.proj_out[(size_t)(row0 + r) * ncols + col0 + c] = s_y[r * (kHeadDim + 1) + c] * s_r[r];
+      }
+    }
+    if (tile >= 2 * H) {   // query head: bf16 q
+      for (int i = tid; i < nrows * kHeadDim; i += kPThreads) {
+        const int r = i >> 7, c = i & 127;
+        const float y = s_y[r * (kHeadDim + 1) + c] * s_r[r];
+        a.q_out[((size_t)(row0 + r) * Hq + head_row) * kHeadDim + c] = (uint16_t)f32_to_bf16(y);
+      }
+    } else {
+      // key or value head: the rows for the quantizing workgroups, then the tile's ready flag
+      const __amdgpu_buffer_rsrc_t rrows =
+          make_rsrc(a.kvrows + ((size_t)rb * 2 * H + tile) * kPRows * kHeadDim, kPRows * kHeadDim * 4);
+      for (int i = tid; i < kPRows * kHeadDim / 4; i += kPThreads) {
+        const int r = (4 * i) >> 7, c = (4 * i) & 127;
+        const float* y = &s_y[r * (kHeadDim + 1) + c];
+        store_coherent(rrows, 4 * i * 4, floatx4{y[0] * s_r[r], y[1] * s_r[r], y[2] * s_r[r], y[3] * s_r[r]});
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (tid == 0)
+        __hip_atomic_store(a.ready + (size_t)rb * 2 * H + tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+  }
+
+  // ---- Q slices, once their own part is done, quantize the K / V rows of their row block into
+  // the cache, kPSlots rows of one tile at a time (claimed in order from a counter)
+  if (wg >= nkv) {
+    constexpr int Lg = G / 4;
+    const int slot = tid / kRowLanes, l32 = tid % kRowLanes;
+    const int gi = l32 / Lg, jg = l32 % Lg;
+    const int nbt = (nrows + kPSlots - 1) / kPSlots;   // batches per tile
+    for (;;) {
+      if (tid == 0) s_word = __hip_atomic_fetch_add(a.claim + rb, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      const int batch = s_word;
+      __syncthreads();
+      if (batch >= 2 * H * nbt) break;
+      const int kvtile = batch / nbt, r = (batch % nbt) * kPSlots + slot;
+      const int kv = kvtile < H ? 0 : 1, hk = kvtile < H ? kvtile : kvtile - H;
+      // the tile's rows are ready once its last slice has written them (bounded wait: the slices
+      // started before this workgroup and wait for nothing)
+      if (tid == 0) {
+        const int* flag = a.ready + (size_t)rb * 2 * H + kvtile;
+        int ok = 0;
+        for (int it = 0; it < (1 << 22); ++it) {
+          if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) { ok = 1; break; }
+          __builtin_amdgcn_s_sleep(2);
+        }
+        if (!ok) report(a.cache.status, KVQ_ERR_HIP);
+        s_word = ok;
+      }
+      __syncthreads();
+      const bool ready = s_word != 0;
+      __syncthreads();
+      if (!ready) continue;
+      const int b = row0 + min(r, nrows - 1);
+      const int t = a.positions[b];
+      const bool valid = r < nrows && t >= 0;
+      const float* yrow = a.kvrows + (((size_t)rb * 2 * H + kvtile) * kPRows + min(r, nrows - 1)) * kHeadDim;
+      float x[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        x[e] = valid ? __hip_atomic_load(const_cast<float*>(yrow + gi * G + jg + Lg * e), __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT)
+                     : 0.0f;
+      const int64_t run = records_before<kRowLanes>(a, b, hk, kv, valid && t < L.S_cap ? t : 0, l32);
+      append_row<FMT, G>(a, valid, b, hk, kv, t, run, x, l32, slot, s_st);
+    }
+  }
+
+  // ---- the last workgroup to finish returns the control words to zero
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __syncthreads();
+  if (tid == 0 && __hip_atomic_fetch_add(a.done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nall - 1) {
+    for (int i = 0; i < a.row_blocks * 2 * H; ++i)
+      __hip_atomic_store(a.ready + i, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int i = 0; i < a.row_blocks; ++i)
+      __hip_atomic_store(a.claim + i, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(a.ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(a.done, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+template <int FMT, int G>
+hipError_t launch_fmt(const PrologueLaunch& a, dim3 grid, hipStream_t st) {
+  prologue_kernel<FMT, G><<<grid, kPThreads, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prologue(const PrologueLaunch& a, hipStream_t st) {
+  const dim3 grid((2 * a.L.H * a.splits_kv + a.Hq * a.splits_q) * a.row_blocks);
+  const bool g32 = a.group == 32;
+  switch (a.fmt) {
+    case FMT_C2: return g32 ? hipErrorInvalidValue : launch_fmt<FMT_C2, 64>(a, grid, st);
+    case FMT_INT4: return g32 ? launch_fmt<FMT_INT4, 32>(a, grid, st) : launch_fmt<FMT_INT4, 64>(a, grid, st);
+    case FMT_FP4: return g32 ? launch_fmt<FMT_FP4, 32>(a, grid, st) : launch_fmt<FMT_FP4, 64>(a, grid, st);
+    case FMT_INT3: return g32 ? launch_fmt<FMT_INT3, 32>(a, grid, st) : launch_fmt<FMT_INT3, 64>(a, grid, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace kvq

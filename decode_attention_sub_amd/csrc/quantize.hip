@@ -20,11 +20,11 @@
 
 #include "kvq_device.h"
 #include "kvq_launch.h"
+#include "quant_row.h"
 
 namespace kvq {
 namespace {
 
-constexpr int kRowLanes = 32;  // lanes per row: 128 channels, 4 per lane
 
 struct QArgs {
   Layout L;
@@ -40,282 +40,6 @@ struct QArgs {
   int lloyd;
   int fit;           // kFitDefault, or a variant fit of the storage format
 };
-
-// compile-time loop: f(std::integral_constant<int, I>) for I = 0 .. N-1
-template <int N, int I = 0, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (I < N) {
-    f(std::integral_constant<int, I>{});
-    static_for<N, I + 1>(f);
-  }
-}
-
-// ---------------------------------------------------------------- group reductions
-template <int L>
-__device__ __forceinline__ float group_sum_tree(float a0, float a1, float a2, float a3) {
-  float t = (a0 + a2) + (a1 + a3);   // tree steps w = 2L, w = L
-  if constexpr (L >= 32) t = t + xor_f32<16>(t);
-  if constexpr (L >= 16) t = t + xor_f32<8>(t);
-  if constexpr (L >= 8) t = t + xor_f32<4>(t);
-  if constexpr (L >= 4) t = t + xor_f32<2>(t);
-  if constexpr (L >= 2) t = t + xor_f32<1>(t);
-  return t;
-}
-template <int L>
-__device__ __forceinline__ int group_isum(int v) {
-  if constexpr (L >= 32) v += xor_i32<16>(v);
-  if constexpr (L >= 16) v += xor_i32<8>(v);
-  if constexpr (L >= 8) v += xor_i32<4>(v);
-  if constexpr (L >= 4) v += xor_i32<2>(v);
-  if constexpr (L >= 2) v += xor_i32<1>(v);
-  return v;
-}
-template <int L>
-__device__ __forceinline__ int group_ior(int v) {
-  if constexpr (L >= 32) v |= xor_i32<16>(v);
-  if constexpr (L >= 16) v |= xor_i32<8>(v);
-  if constexpr (L >= 8) v |= xor_i32<4>(v);
-  if constexpr (L >= 4) v |= xor_i32<2>(v);
-  if constexpr (L >= 2) v |= xor_i32<1>(v);
-  return v;
-}
-template <int L>
-__device__ __forceinline__ float group_min(float v) {
-  if constexpr (L >= 32) v = fminf(v, xor_f32<16>(v));
-  if constexpr (L >= 16) v = fminf(v, xor_f32<8>(v));
-  if constexpr (L >= 8) v = fminf(v, xor_f32<4>(v));
-  if constexpr (L >= 4) v = fminf(v, xor_f32<2>(v));
-  if constexpr (L >= 2) v = fminf(v, xor_f32<1>(v));
-  return v;
-}
-template <int L>
-__device__ __forceinline__ float group_max(float v) {
-  if constexpr (L >= 32) v = fmaxf(v, xor_f32<16>(v));
-  if constexpr (L >= 16) v = fmaxf(v, xor_f32<8>(v));
-  if constexpr (L >= 8) v = fmaxf(v, xor_f32<4>(v));
-  if constexpr (L >= 4) v = fmaxf(v, xor_f32<2>(v));
-  if constexpr (L >= 2) v = fmaxf(v, xor_f32<1>(v));
-  return v;
-}
-
-// ---------------------------------------------------------------- per-row state
-struct RowOut {
-  uint32_t code[4];   // per element
-  uint32_t flag[4];   // outlier flags
-  uint32_t meta[2];   // group metadata held by the group's lane 0 (up to 8 bytes)
-};
-
-// nearest of 4 centroids by |x - c| (fl32), first index on ties
-__device__ __forceinline__ uint32_t nearest4(float x, const float c[4]) {
-  float best = __builtin_fabsf(x - c[0]);
-  uint32_t k = 0;
-#pragma unroll
-  for (int j = 1; j < 4; ++j) {
-    const float d = __builtin_fabsf(x - c[j]);
-    if (d < best) { best = d; k = (uint32_t)j; }
-  }
-  return k;
-}
-
-// Outlier predicate: e * (g-1) > fl32(tau^2) * Q2 with e = (x - mean)^2, Q2 = sum of e.
-template <int G>
-__device__ __forceinline__ void outlier_flags(const float x[4], float tau2, bool keep[4]) {
-  constexpr int L = G / 4;
-  const float mean = group_sum_tree<L>(x[0], x[1], x[2], x[3]) * (1.0f / (float)G);
-  float e[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) { const float d = x[i] - mean; e[i] = d * d; }
-  const float q2 = group_sum_tree<L>(e[0], e[1], e[2], e[3]);
-  const float rhs = tau2 * q2;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) keep[i] = !(e[i] * (float)(G - 1) > rhs);
-}
-
-// Asymmetric integer fit ("The Sub-10ms Barrier ...", section "2. FP4/INT4 KV-Cache
-// Quantization"): S = (max - min) / (2^b - 1) over the non-outliers, fp16 S and zero =
-// fp16(min), code = rint(clamp((x - z) / S)).  LEVELS = 2^b - 1: 15 for INT4, 7 for the
-// asymmetric 3-bit codes of "Sub-5ms MoE Inference ...", section "Sub-Byte KV-Cache
-// Quantization".
-template <int G, int LEVELS = 15>
-__device__ void fit_int4(const float x[4], const bool keep[4], RowOut& o) {
-  constexpr int L = G / 4;
-  float mn = INFINITY, mx = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    if (keep[i]) { mn = fminf(mn, x[i]); mx = fmaxf(mx, x[i]); }
-  mn = group_min<L>(mn) + 0.0f;  // a zero minimum is taken as +0
-  mx = group_max<L>(mx) + 0.0f;
-  const float s = (mx - mn) / (float)LEVELS;
-  const uint32_t sh = f32_to_half_bits(s), zh = f32_to_half_bits(mn);
-  const float S = half_bits_to_f32(sh), Z = half_bits_to_f32(zh);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float xx = keep[i] ? x[i] : 0.0f;
-    uint32_t q = 0;
-    if (S > 0.0f) {
-      const float y = (xx - Z) / S;
-      q = (uint32_t)__builtin_rintf(fminf(fmaxf(y, 0.0f), (float)LEVELS));
-    }
-    o.code[i] = q;
-  }
-  o.meta[0] = sh | (zh << 16);
-  o.meta[1] = 0;
-}
-
-template <int G>
-__device__ void fit_fp4(const float x[4], const bool keep[4], RowOut& o) {
-  constexpr int L = G / 4;
-  float a = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    if (keep[i]) a = fmaxf(a, __builtin_fabsf(x[i]));
-  a = group_max<L>(a);
-  const uint32_t s8 = f32_to_e4m3(a / 6.0f);
-  const float sv = e4m3_to_f32(s8);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float xx = keep[i] ? x[i] : 0.0f;
-    o.code[i] = sv > 0.0f ? f32_to_e2m1(xx / sv) : 0u;
-  }
-  o.meta[0] = s8;
-  o.meta[1] = 0;
-}
-
-// Symmetric INT4 ("The Sub-10ms Barrier ...", section "2. FP4/INT4 KV-Cache Quantization", the
-// quantize_kv_cache_fp4 listing): scale absmax/7 over the non-outliers, at least 1e-5, stored as
-// fp16 S; code = clamp(round(x / S), -8, 7) + 8, stored as INT4 with zero -8 S.
-template <int G>
-__device__ void fit_int4sym(const float x[4], const bool keep[4], RowOut& o) {
-  constexpr int L = G / 4;
-  float a = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    if (keep[i]) a = fmaxf(a, __builtin_fabsf(x[i]));
-  a = group_max<L>(a);
-  const uint32_t sh = f32_to_half_bits(fmaxf(a / 7.0f, 1e-5f));
-  const float S = half_bits_to_f32(sh);
-  const uint32_t zh = f32_to_half_bits(-8.0f * S);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float xx = keep[i] ? x[i] : 0.0f;
-    o.code[i] = (uint32_t)((int)fminf(fmaxf(__builtin_rintf(xx / S), -8.0f), 7.0f) + 8);
-  }
-  o.meta[0] = sh | (zh << 16);
-  o.meta[1] = 0;
-}
-
-// Uniform 2-bit codebook ("Hierarchical Token Routing and Sub-2-Bit Non-Linear KV Compression
-// ...", the compress_kv_head listing): the group's values with the outlier slots set to 0, 4
-// centroids linspace(min, max) formed as torch.linspace does (step fl32((max - min) / 3); min,
-// min + step, max - step, max), fp16 centroids, nearest centroid (first index on ties).
-template <int G>
-__device__ void fit_u2(const float x[4], const bool keep[4], RowOut& o) {
-  constexpr int L = G / 4;
-  float xx[4], mn = INFINITY, mx = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    xx[i] = keep[i] ? x[i] : 0.0f;
-    mn = fminf(mn, xx[i]);
-    mx = fmaxf(mx, xx[i]);
-  }
-  mn = group_min<L>(mn) + 0.0f;  // a zero end is taken as +0
-  mx = group_max<L>(mx) + 0.0f;
-  const float step = (mx - mn) / 3.0f;
-  const float c[4] = {mn, mn + step, mx - step, mx};
-  uint32_t hb[4];
-  float ch[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) { hb[j] = f32_to_half_bits(c[j]); ch[j] = half_bits_to_f32(hb[j]); }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) o.code[i] = nearest4(xx[i], ch);
-  o.meta[0] = hb[0] | (hb[1] << 16);
-  o.meta[1] = hb[2] | (hb[3] << 16);
-}
-
-// 2-bit centroids: seeds at ranks floor((2j+1) n / 8) of the sorted non-outliers, then
-// `iters` Lloyd iterations (empty clusters keep their centroid), fp16 centroids.
-template <int G>
-__device__ void fit_c2(const float x[4], const bool keep[4], int jg, int iters, RowOut& o) {
-  constexpr int L = G / 4;
-  int nloc = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) nloc += keep[i] ? 1 : 0;
-  const int n = group_isum<L>(nloc);
-  // stable rank of each kept element among the kept elements of the group: element (src, e)
-  // of the group (index src + L e, broadcast from lane src of the 16-lane row that holds the
-  // group) precedes my element i (index jg + L i) when it is smaller, or equal with a lower
-  // index.  Outliers compare as +inf, which precedes no kept element.
-  static_assert(G == 64, "one group per 16-lane DPP row");
-  float xs[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) xs[i] = keep[i] ? x[i] : INFINITY;
-  int rank[4] = {0, 0, 0, 0};
-  const uint32_t xb[4] = {as_u32(x[0]), as_u32(x[1]), as_u32(x[2]), as_u32(x[3])};
-  static_for<L>([&](auto src_c) {
-    constexpr int src = decltype(src_c)::value;
-    const bool before_me = src < jg;   // same e: the source's index is lower when src < jg
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float v = as_f32((uint32_t)row_bcast_i32<src>((int)as_u32(xs[e])));
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool less = e < i ? v <= xs[i] : e > i ? v < xs[i] : (before_me ? v <= xs[i] : v < xs[i]);
-        rank[i] += less ? 1 : 0;
-      }
-    }
-  });
-  float c[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int r = ((2 * j + 1) * n) >> 3;
-    uint32_t bits = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) bits |= (keep[i] && rank[i] == r) ? xb[i] : 0u;
-    c[j] = as_f32((uint32_t)group_ior<L>((int)bits));
-  }
-  for (int it = 0; it < iters; ++it) {
-    uint32_t a[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = nearest4(x[i], c);
-    float nc[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float s[4];
-      int cl = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool m = keep[i] && a[i] == (uint32_t)j;
-        s[i] = m ? x[i] : 0.0f;
-        cl += m ? 1 : 0;
-      }
-      const float sum = group_sum_tree<L>(s[0], s[1], s[2], s[3]);
-      const int cnt = group_isum<L>(cl);
-      nc[j] = cnt > 0 ? sum / (float)cnt : c[j];
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) c[j] = nc[j];
-  }
-  uint32_t hb[4];
-  float ch[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) { hb[j] = f32_to_half_bits(c[j]); ch[j] = half_bits_to_f32(hb[j]); }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) o.code[i] = nearest4(keep[i] ? x[i] : 0.0f, ch);
-  o.meta[0] = hb[0] | (hb[1] << 16);
-  o.meta[1] = hb[2] | (hb[3] << 16);
-}
-
-// FP8 tier row: scale = absmax/448 over the 128 channels (1 if zero), codes E4M3(x/scale)
-__device__ void fit_fp8row(const float x[4], RowOut& o) {
-  float a = fmaxf(fmaxf(__builtin_fabsf(x[0]), __builtin_fabsf(x[1])),
-                  fmaxf(__builtin_fabsf(x[2]), __builtin_fabsf(x[3])));
-  a = group_max<32>(a);
-  const float s = a > 0.0f ? a / 448.0f : 1.0f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) { o.code[i] = f32_to_e4m3(x[i] / s); o.flag[i] = 0; }
-  o.meta[0] = as_u32(s);
-  o.meta[1] = 0;
-}
 
 // ---------------------------------------------------------------- kernel
 template <int FMT, int G, int NW>
@@ -471,30 +195,7 @@ __global__ void __launch_bounds__(64 * NW) quantize_append_kernel(QArgs a) {
         }
       }
       const int bits = tr ? 8 : code_bits(FMT);
-      const int per_word = 32 / bits;
-      if (bits == 3) {
-        // one LSB-first bit stream: channel c in stream bits 3c..3c+2; word `lane` holds stream
-        // bits 32 lane .. 32 lane + 31, the channels that start in it and the head of one that
-        // starts in the word before
-        if (lane < cb / 4) {
-          uint32_t w = 0;
-          const int c0 = (32 * lane) / 3, c1 = (32 * lane + 31) / 3;
-          for (int c = c0; c <= c1; ++c) {
-            const int sh = 3 * c - 32 * lane;
-            const uint32_t v = s_code[slot][c];
-            w |= sh >= 0 ? v << sh : v >> -sh;
-          }
-          ((uint32_t*)codes_dst)[lane] = w;
-        }
-      } else if (lane < cb / 4) {
-        // 2-bit: channel 4s + j of the word's 16 goes to byte j, bit pair s; otherwise LSB first
-        uint32_t w = 0;
-        for (int k = 0; k < per_word; ++k) {
-          const int sh = bits == 2 ? 8 * (k & 3) + 2 * (k >> 2) : bits * k;
-          w |= (uint32_t)s_code[slot][lane * per_word + k] << sh;
-        }
-        ((uint32_t*)codes_dst)[lane] = w;
-      }
+      if (lane < cb / 4) ((uint32_t*)codes_dst)[lane] = pack_word(s_code[slot], lane, bits);
       if (lane < mb / 4) ((uint32_t*)meta_dst)[lane] = s_meta[slot][lane];
       else if (mb < 4 && lane == 0) {
         for (int k = 0; k < mb; ++k) meta_dst[k] = ((uint8_t*)s_meta[slot])[k];

@@ -199,19 +199,28 @@ int32_t kvq_quantize_append(const kvq_params* p, const kvq_cache* cache, const f
                             const float* v_new, int32_t max_new, const int32_t* positions,
                             const int32_t* counts, const int32_t* block_table, void* stream);
 
-/* Workspace for kvq_decode_attention: split-K partials B * Hq * ceil(max_seq_len/chunk) *
- * (D + 2) floats (0 when a single chunk covers max_seq_len).  split_chunk 0 selects the
- * default: 4096 for paged caches; for contiguous caches enough chunks for 256 (2-bit, FP4 g32)
- * or 1024 (INT4, FP4 g64) (sequence, KV head, chunk) units, chunks of at least 512 / 64 tokens,
- * rounded up to a multiple of 64. */
+/* Workspace for kvq_decode_attention.
+ * 2-bit caches, and contiguous FP4 caches with groups of 32 (the MFMA decoder; paged pools
+ * whose rows need byte offsets of 2^32 or more take the generic decoder): N workgroups share the
+ * 32-token steps of all (sequence, KV head) lists evenly, each a contiguous range of steps in
+ * (sequence, head, token) order; a list cut between workgroups is merged afterwards by
+ * log-sum-exp from two (max, sum, output) slots per workgroup: N * 2 * (Hq / H) * (D + 2)
+ * floats.  split_chunk 0: N = min(256, ceil(B * H * ceil(max_seq_len / 32) / 12)) (one
+ * workgroup per CU of an MI355X, at least 12 steps each); split_chunk > 0: N = min(B * H *
+ * ceil(max_seq_len / 32), 16384, ceil(B * H * max_seq_len / split_chunk)).
+ * Other formats (the generic decoder): split-K chunks of each list, B * Hq *
+ * ceil(max_seq_len / chunk) * (D + 2) floats (0 when one chunk covers max_seq_len); chunk =
+ * split_chunk, or by default 4096 for paged caches and, for contiguous caches, enough chunks for
+ * 1024 (sequence, KV head, chunk) units, chunks of at least 64 tokens, rounded up to a multiple
+ * of 64.  split_chunk must be a multiple of 64. */
 int32_t kvq_workspace_bytes(const kvq_params* p, int32_t split_chunk, uint64_t* out_bytes);
 
 /* Fused dequantize + flash-decoding attention ("Fused Dequantization & FlashAttention
  * Kernel" of the figure in "The Bottleneck"; "Attention Phase / Flash-Decoding Engine" of
  * the figure in "The Twin Bottlenecks").  For each b and query head hq (KV head
  * hq * H / Hq): out[b][hq] = softmax_t(sm_scale * q . k_t) . v_t over tokens t < seq_lens[b],
- * with k_t, v_t dequantized on the fly; chunks of split_chunk tokens (a multiple of 64) are
- * merged by log-sum-exp.  sm_scale: any finite value, or NaN for the default 1/sqrt(head_dim);
+ * with k_t, v_t dequantized on the fly; the parts of a list that different workgroups take
+ * (see kvq_workspace_bytes) are merged by log-sum-exp.  sm_scale: any finite value, or NaN for the default 1/sqrt(head_dim);
  * an infinite scale is rejected.  q_bf16: device bfloat16 [B][Hq][D] (values must be finite
  * and within fp16 range); seq_lens: device int32 [B], 1 <= seq_lens[b] <= max_seq_len and no
  * more than the tokens appended; a sequence whose length is out of that range sets *status to
@@ -284,6 +293,32 @@ int32_t kvq_retier(const kvq_params* p, const kvq_cache* cache, int32_t* block_t
                    const int32_t* seq_lens, const float* page_mass, float keep_frac,
                    const int32_t* free_slots, int32_t n_free, int32_t* freed_slots,
                    int32_t* n_moved, void* workspace, uint64_t ws_bytes, void* stream);
+
+/* Attention prologue of one decode step in a single kernel ("Sub-5ms MoE Inference ...",
+ * section "Engineering Real-Time Autonomous Workflows", item 1: RMSNorm, the self-attention
+ * projection and the KV-cache write fused into one kernel).  For every sequence b:
+ *   x = h_b / sqrt(mean_i h_b[i]^2 + eps) * gain            (RMSNorm, d = d_model channels)
+ *   y = W x,  W [(Hq + 2H) * D][d]: rows of Q heads 0..Hq-1, then K heads 0..H-1, then V heads
+ *   q[b][hq] = y[hq D .. hq D + D - 1] rounded to bfloat16 (nearest even) -> q_bf16_out
+ *   the K and V rows of KV head h (y[(Hq + h) D ..], y[(Hq + H + h) D ..]) are appended to the
+ *   cache at token positions[b], exactly as kvq_quantize_append of those float32 rows with
+ *   count 1 (positions[b] < 0: no write for that sequence; >= max_seq_len: *status is set to
+ *   KVQ_ERR_INVALID_ARG and nothing is written).  No bias and no rotary embedding.
+ * Arithmetic: bf16(h * gain) x W on bf16 MFMA with fp32 accumulation, scaled per row by
+ * 1 / sqrt(sum(h^2) / d + eps) after the product; deterministic (independent of scheduling).
+ * hidden_bf16 [B][d], gain_bf16 [d], weight_bf16 as above: device bfloat16, 16-byte aligned;
+ * d_model a multiple of 128; eps >= 0 and finite; positions: device int32 [B]; block_table as
+ * for appends (paged) or NULL; q_bf16_out: device bfloat16 [B][Hq][D]; proj_out: NULL or device
+ * float32 [B][(Hq + 2H) D] receiving y (the rows the cache write quantizes); workspace: device,
+ * ws_bytes >= kvq_prologue_workspace_bytes, zero-filled before its first use with this
+ * library (every call leaves its arrival counters at zero again; calls sharing a workspace must
+ * not overlap). */
+int32_t kvq_prologue_workspace_bytes(const kvq_params* p, int32_t d_model, uint64_t* out_bytes);
+int32_t kvq_attention_prologue(const kvq_params* p, const kvq_cache* cache, const void* hidden_bf16,
+                               const void* gain_bf16, const void* weight_bf16, int32_t d_model,
+                               float eps, const int32_t* positions, const int32_t* block_table,
+                               void* q_bf16_out, float* proj_out, void* workspace,
+                               uint64_t ws_bytes, void* stream);
 
 /* Streaming read of `bytes` (multiple of 16) from device buffer src, XOR-reduced into sink
  * (device, >= 4 * 1024 * 256 bytes): measures the practical HBM read ceiling. */

@@ -1,5 +1,5 @@
 """GPU parity at the workloads' full sizes, in the launch configuration bench.py times (the
-workload's own split-K chunk, default softmax scale): the whole cache is built on the device,
+workload's own split, default softmax scale) and split into one workgroup per 2048 tokens: the whole cache is built on the device,
 then sampled (sequence, KV head) pairs are checked against the oracle - the packed rows and
 outlier records of the first and last tokens of each sampled list bit for bit, and the decode
 output of every query head of the pair within the 2e-3 max-abs bar."""
@@ -59,6 +59,9 @@ def test_full_size_sampled(name):
     log(f"[gpu] full-size {name}: decode with split {w.split_chunk or 'default'}")
     got = run_decode(dc, split_chunk=w.split_chunk)
     assert np.all(np.isfinite(got))
+    # the same decode split into one workgroup per 2048 tokens of all lists (many more cut lists)
+    log(f"[gpu] full-size {name}: decode with split 2048")
+    got2 = run_decode(dc, split_chunk=2048)
     rng = np.random.default_rng(1234)
     lens = dc.seq_lens_host
     pairs = {(int(np.argmax(lens)), int(rng.integers(w.H))), (int(rng.integers(w.B)), int(rng.integers(w.H)))}
@@ -76,3 +79,5 @@ def test_full_size_sampled(name):
         for hq, o in ref.items():
             err = np.abs(got[b, hq] - o).max()
             assert err <= ATOL, f"{name} b={b} hq={hq}: max-abs {err}"
+            err2 = np.abs(got2[b, hq] - o).max()
+            assert err2 <= ATOL, f"{name} b={b} hq={hq} split 2048: max-abs {err2}"

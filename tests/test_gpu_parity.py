@@ -206,7 +206,9 @@ def test_out_of_range_position_reports_status():
 @pytest.mark.parametrize("name", ["c2_g8_small", "int4_g64_small", "tiered_small"])
 def test_invalid_seq_len_reports_status(name):
     """A sequence length of 0 or past the capacity is reported through the status word; that
-    sequence is skipped and every other sequence's output is the one of a valid call."""
+    sequence is skipped and every other sequence's output is the one of a valid call, up to the
+    order of float32 sums (the MFMA decoder shares the steps of all valid lists among its
+    workgroups, so the points where lists are cut depend on every length)."""
     import dataclasses
     import decode_attention_sub_amd as K
     w = SMALL[name]
@@ -223,7 +225,7 @@ def test_invalid_seq_len_reports_status(name):
             got = run_decode(dcb, split_chunk=split)
             assert dc.cache.status() == K.KVQ_ERR_INVALID_ARG
             dc.cache.tensors["status"].zero_()
-            assert np.array_equal(got[1:], good[1:])
+            assert np.allclose(got[1:], good[1:], rtol=1e-4, atol=1e-5)
 
 
 def test_zero_count_append_leaves_sequence_untouched():

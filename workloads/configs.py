@@ -53,7 +53,7 @@ CONFIGS = {
                                  fp8_page_frac=0.10),
     # long-context flash-decoding: B=4, 64/8 heads, S=131072, FP4 g32 + E4M3 scale
     "fp4_b4_s128k": Workload("fp4_b4_s128k", 4, 64, 8, 128, 131072, "fp4", 32, "fp16", 3.0, 4,
-                             "normal", split_chunk=2048),
+                             "normal"),
 }
 
 HEADLINE = "c2_b64_s32k"
