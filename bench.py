@@ -306,7 +306,10 @@ def main():
     if args.prologue:
         d_model = G.model_width(w)
         log(f"prologue: generating the {(w.Hq + 2 * w.H) * w.D} x {d_model} projection")
-        W_dev = torch.from_numpy(G.projection(w, d_model).view(np.int16)).cuda()
+        W_row = torch.from_numpy(G.projection(w, d_model).view(np.int16)).cuda()
+        W_dev = torch.empty_like(W_row)
+        K.kvq_prologue_pack_weights(p, W_row, W_dev)   # once, as at model load
+        del W_row
         gain_dev = torch.from_numpy(G.norm_gain(w, d_model).view(np.int16)).cuda()
         n_hid = min(n_total, 8)
         hid = [torch.from_numpy(G.hidden_states(w, s, d_model).view(np.int16)).cuda() for s in range(n_hid)]

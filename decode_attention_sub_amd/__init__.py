@@ -27,7 +27,7 @@ OUTL = {"none": 0, "fp16": 1, "e4m3": 2}
 EXPORTED = ("kvq_kv_bytes", "kvq_cache_sizes", "kvq_quantize_append", "kvq_workspace_bytes",
             "kvq_decode_attention", "kvq_decode_attention_noalloc", "kvq_mass_workspace_bytes",
             "kvq_decode_attention_mass", "kvq_retier_workspace_bytes", "kvq_retier",
-            "kvq_prologue_workspace_bytes", "kvq_attention_prologue",
+            "kvq_prologue_workspace_bytes", "kvq_prologue_pack_weights", "kvq_attention_prologue",
             "kvq_probe_read", "kvq_probe_copy", "kvq_status_string")
 NOALLOC_SCRATCH_BYTES = 32 << 20   # KVQ_NOALLOC_SCRATCH_BYTES
 
@@ -81,6 +81,7 @@ def _load():
         "kvq_retier": (C.c_int32, [P, Pc, vp, vp, vp, C.c_float, vp, C.c_int32, vp, vp, vp,
                                    C.c_uint64, vp]),
         "kvq_prologue_workspace_bytes": (C.c_int32, [P, C.c_int32, C.POINTER(C.c_uint64)]),
+        "kvq_prologue_pack_weights": (C.c_int32, [P, C.c_int32, vp, vp, vp]),
         "kvq_attention_prologue": (C.c_int32, [P, Pc, vp, vp, vp, C.c_int32, C.c_float, vp, vp, vp,
                                                vp, vp, C.c_uint64, vp]),
         "kvq_probe_read": (C.c_int32, [vp, C.c_uint64, vp, vp]),
@@ -280,16 +281,26 @@ def kvq_prologue_workspace_bytes(p: kvq_params, d_model: int) -> int:
     return n.value
 
 
-def kvq_attention_prologue(p: kvq_params, cache: KVCache, hidden_bf16, gain_bf16, weight_bf16,
+def kvq_prologue_pack_weights(p: kvq_params, weight_bf16, packed, stream=None):
+    """weight_bf16: row-major [(Hq + 2H) * D, d] 16-bit tensor; packed: a distinct tensor of the
+    same size receiving the block order kvq_attention_prologue reads (both device)."""
+    d_model = weight_bf16.shape[-1]
+    assert packed.numel() * packed.element_size() == weight_bf16.numel() * weight_bf16.element_size()
+    _check(_lib.kvq_prologue_pack_weights(C.byref(p), d_model, _ptr(weight_bf16), _ptr(packed),
+                                          _stream(stream)), "kvq_prologue_pack_weights")
+
+
+def kvq_attention_prologue(p: kvq_params, cache: KVCache, hidden_bf16, gain_bf16, weight_packed,
                            eps: float, positions, q_out, workspace, block_table=None,
                            proj_out=None, stream=None):
-    """hidden_bf16: bfloat16 [B, d]; gain_bf16: [d]; weight_bf16: [(Hq + 2H) * D, d]; positions:
-    int32 [B]; q_out: bfloat16 [B, Hq, D]; proj_out: optional float32 [B, (Hq + 2H) * D];
-    workspace: zero-filled before its first use (all device)."""
+    """hidden_bf16: bfloat16 [B, d]; gain_bf16: [d]; weight_packed: the projection packed by
+    kvq_prologue_pack_weights; positions: int32 [B]; q_out: bfloat16 [B, Hq, D]; proj_out:
+    optional float32 [B, (Hq + 2H) * D]; workspace: zero-filled before its first use (all
+    device)."""
     d_model = hidden_bf16.shape[-1]
     ws_bytes = workspace.numel() * workspace.element_size()
     _check(_lib.kvq_attention_prologue(C.byref(p), C.byref(cache.struct), _ptr(hidden_bf16),
-                                       _ptr(gain_bf16), _ptr(weight_bf16), d_model, float(eps),
+                                       _ptr(gain_bf16), _ptr(weight_packed), d_model, float(eps),
                                        _ptr(positions), _ptr(block_table), _ptr(q_out),
                                        _ptr(proj_out), _ptr(workspace), ws_bytes, _stream(stream)),
            "kvq_attention_prologue")

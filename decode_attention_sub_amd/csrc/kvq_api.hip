@@ -489,6 +489,19 @@ int32_t kvq_prologue_workspace_bytes(const kvq_params* pin, int32_t d_model, uin
   return KVQ_OK;
 }
 
+int32_t kvq_prologue_pack_weights(const kvq_params* pin, int32_t d_model, const void* weight_bf16,
+                                  void* packed_bf16, void* stream) {
+  uint64_t need = 0;
+  int32_t st = kvq_prologue_workspace_bytes(pin, d_model, &need);
+  if (st) return st;
+  if (!weight_bf16 || !packed_bf16 || weight_bf16 == packed_bf16) return KVQ_ERR_INVALID_ARG;
+  if (((uintptr_t)weight_bf16 | (uintptr_t)packed_bf16) & 15) return KVQ_ERR_INVALID_ARG;
+  const int64_t rows = (int64_t)(pin->num_q_heads + 2 * pin->num_kv_heads) * kHeadDim;
+  if (launch_pack_weights(weight_bf16, packed_bf16, d_model, rows, (hipStream_t)stream) != hipSuccess)
+    return KVQ_ERR_HIP;
+  return KVQ_OK;
+}
+
 int32_t kvq_attention_prologue(const kvq_params* pin, const kvq_cache* cache, const void* hidden_bf16,
                                const void* gain_bf16, const void* weight_bf16, int32_t d_model,
                                float eps, const int32_t* positions, const int32_t* block_table,

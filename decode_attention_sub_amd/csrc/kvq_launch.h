@@ -98,7 +98,8 @@ struct PrologueLaunch {
   kvq_cache cache;
   const uint16_t* hidden;     // bf16 [B][d]
   const uint16_t* gain;       // bf16 [d]
-  const uint16_t* weight;     // bf16 [(Hq + 2H) * 128][d]: Q heads, K heads, V heads
+  const uint16_t* weight;     // bf16 [(Hq + 2H) * 128][d] (rows: Q heads, K heads, V heads) in
+                              // the packed block order of launch_pack_weights
   const int32_t* positions;   // [B]: token of the new K / V rows, < 0: no write
   const int32_t* block_table;
   uint16_t* q_out;            // bf16 [B][Hq][128]
@@ -121,6 +122,7 @@ struct PrologueLaunch {
 };
 
 hipError_t launch_prologue(const PrologueLaunch& a, hipStream_t st);
+hipError_t launch_pack_weights(const void* w, void* out, int d, int64_t rows, hipStream_t st);
 hipError_t launch_mass_normalize(const MassLaunch& m, hipStream_t st);
 hipError_t launch_retier_select(const RetierLaunch& r, hipStream_t st);
 hipError_t launch_retier_demote(const RetierLaunch& r, hipStream_t st);

@@ -35,7 +35,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kPThreads = 256;            // 4 waves, 32 output columns each
+constexpr int kPThreads = 512;            // 8 waves, 16 output columns each
 constexpr int kPRows = kPrologueRows;     // batch rows of a row block
 constexpr int kPKc = 128;                 // d_model columns per LDS stage
 constexpr int kPStride = kPKc + 8;        // bf16 per staged row: 272 bytes, conflict-free reads
@@ -52,6 +52,7 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float x) {
 // memory instructions, which agent-scope atomic loads and stores carry: they reach the device's
 // coherence point, past the XCD's own L2.
 constexpr int kSc1 = 16;
+constexpr int kNT = 2;    // cache policy of data read once (non-temporal)
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
@@ -60,6 +61,15 @@ __device__ __forceinline__ void store_coherent(__amdgpu_buffer_rsrc_t r, uint32_
 }
 __device__ __forceinline__ floatx4 load_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kSc1));
+}
+
+// A workgroup barrier that orders LDS accesses only: global loads in flight stay in flight
+// across it (a full __syncthreads also waits for every outstanding global load, which would
+// drain the weight stream at every stage).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // LDS staging of the rows quantized in one round of a K / V epilogue
@@ -144,7 +154,7 @@ __device__ void append_row(const PrologueLaunch& a, bool valid, int b, int h, in
     else if constexpr (MB == 4) { st.meta[slot][gi] = o.meta[0]; }
     else { ((uint8_t*)st.meta[slot])[gi] = (uint8_t)o.meta[0]; }
   }
-  __syncthreads();
+  lds_barrier();
 
   if (row_ok) {
     uint8_t* codes_dst;
@@ -211,11 +221,11 @@ __device__ void append_row(const PrologueLaunch& a, bool valid, int b, int h, in
     }
     if (lane == 0) a.cache.outl_count[lid] = (int32_t)min(running + total, Lo.outl_cap);
   }
-  __syncthreads();   // the staging is reused by the next round
+  lds_barrier();   // the staging is reused by the next round
 }
 
 template <int FMT, int G>
-__global__ void __launch_bounds__(kPThreads) prologue_kernel(PrologueLaunch a) {
+__global__ void __launch_bounds__(kPThreads, 4) prologue_kernel(PrologueLaunch a) {
   // the staged activations of two 128-column stages; the last workgroup of a tile reuses them
   // for the tile's summed rows
   __shared__ __attribute__((aligned(16))) uint16_t s_a[2][kPRows * kPStride];
@@ -257,102 +267,116 @@ __global__ void __launch_bounds__(kPThreads) prologue_kernel(PrologueLaunch a) {
   const int per = (nch + splits - 1) / splits;
   const int c0 = min(nch, split * per), c1 = min(nch, c0 + per);
 
-  // staging map: thread -> 8 columns (kseg) of rows srow + 16 i
+  // staging map: thread -> 8 columns (kseg) of rows srow + 32 i
+  constexpr int kSR = kPThreads / 16;   // rows staged per pass
+  constexpr int kSI = kPRows / kSR;     // passes
   const int kseg = tid & 15, srow = tid >> 4;
-  // MFMA map: lane (r16, kg); wave -> columns 32 wave .. 32 wave + 31
+  // MFMA map: lane (r16, kg); wave -> columns 16 wave .. 16 wave + 15
   const int r16 = lane & 15, kg = lane >> 4;
-  const uint16_t* wrow0 = a.weight + (size_t)(col0 + 32 * wave + r16) * d + 8 * kg;
-  const uint16_t* wrow1 = wrow0 + (size_t)16 * d;
+  const uint16_t* wrow = a.weight + (size_t)(col0 + 16 * wave + r16) * d + 8 * kg;
 
-  float ss[4] = {0.f, 0.f, 0.f, 0.f};
-  floatx4 acc[4][2];
+  float ss[kSI];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) acc[mt][0] = acc[mt][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < kSI; ++i) ss[i] = 0.0f;
+  floatx4 acc[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) acc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  uint4 hv[4], gv;
-  auto load_h = [&](int c) {
-    const int k0 = c * kPKc + 8 * kseg;
-    gv = *(const uint4*)(a.gain + k0);
+  // Activations one stage and weights two stages ahead of their use; weights are read once:
+  // non-temporal loads.  Every stage issues the same loads without conditions (past the slice,
+  // or past the row block, an offset beyond the buffer range reads zeros without touching
+  // memory), so the wait counters stay exact and the loads in flight are never drained.
+  constexpr uint32_t kOOB = 0xFFFFFFF0u;
+  // the wave's 16 output rows: d / 32 consecutive 1 KB blocks of the packed weights
+  const __amdgpu_buffer_rsrc_t rw =
+      make_rsrc(a.weight + (size_t)(col0 / 16 + wave) * (d / 32) * 512, (uint32_t)(d / 32) * 1024u);
+  const __amdgpu_buffer_rsrc_t rh = make_rsrc(a.hidden + (size_t)row0 * d, (uint32_t)(nrows * d * 2));
+  const __amdgpu_buffer_rsrc_t rg = make_rsrc(a.gain, (uint32_t)(d * 2));
+  const uint32_t wlane = (uint32_t)lane * 16u;   // lane (r16, kg) of a block: row r16, columns 8 kg ..
+  struct HSlot { u32x4 h[kSI]; u32x4 g; };
+  HSlot h0, h1;
+  u32x4 w0[4], w1[4], w2[4];
+  auto load_h = [&](HSlot& hs, int c) {
+    const bool in = c < c1;
+    const uint32_t k0 = (uint32_t)(c * kPKc + 8 * kseg) * 2u;
+    hs.g = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rg, (int)(in ? k0 : kOOB), 0, 0));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = srow + 16 * i;
-      hv[i] = r < nrows ? *(const uint4*)(a.hidden + (size_t)(row0 + r) * d + k0) : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < kSI; ++i) {
+      const int r = srow + kSR * i;
+      const uint32_t off = in && r < nrows ? (uint32_t)(r * d) * 2u + k0 : kOOB;
+      hs.h[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rh, (int)off, 0, 0));
     }
   };
-  // weights are read once: non-temporal loads, two stages ahead of their use
-  u32x4 w0[2][4], w1[2][4], w2[2][4];
-  auto load_w = [&](u32x4 (&w)[2][4], int c) {
+  auto load_w = [&](u32x4 (&w)[4], int c) {
+    const uint32_t base = c < c1 ? wlane + (uint32_t)c * 4096u : kOOB;   // 4 blocks per stage
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      w[0][ks] = __builtin_nontemporal_load((const u32x4*)(wrow0 + c * kPKc + 32 * ks));
-      w[1][ks] = __builtin_nontemporal_load((const u32x4*)(wrow1 + c * kPKc + 32 * ks));
-    }
+    for (int ks = 0; ks < 4; ++ks)
+      w[ks] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            rw, (int)(base == kOOB ? kOOB : base + 1024u * ks), 0, kNT));
   };
   // bf16(h * g) of the staged columns into LDS, h^2 into the row sums
-  auto stage = [&](int buf) {
-    const uint32_t g[4] = {gv.x, gv.y, gv.z, gv.w};
+  auto stage = [&](const HSlot& hs, int buf) {
+    const uint32_t g[4] = {hs.g[0], hs.g[1], hs.g[2], hs.g[3]};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t hw[4] = {hv[i].x, hv[i].y, hv[i].z, hv[i].w};
+    for (int i = 0; i < kSI; ++i) {
+      const uint32_t hw[4] = {hs.h[i][0], hs.h[i][1], hs.h[i][2], hs.h[i][3]};
       uint32_t o[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float h0 = bf16_to_f32(hw[j] & 0xFFFFu), h1 = bf16_to_f32(hw[j] >> 16);
+        const float f0 = bf16_to_f32(hw[j] & 0xFFFFu), f1 = bf16_to_f32(hw[j] >> 16);
         const float g0 = bf16_to_f32(g[j] & 0xFFFFu), g1 = bf16_to_f32(g[j] >> 16);
-        ss[i] += h0 * h0;
-        ss[i] += h1 * h1;
-        o[j] = f32_to_bf16(h0 * g0) | (f32_to_bf16(h1 * g1) << 16);
+        ss[i] += f0 * f0;
+        ss[i] += f1 * f1;
+        o[j] = f32_to_bf16(f0 * g0) | (f32_to_bf16(f1 * g1) << 16);
       }
-      *(uint4*)&s_a[buf][(srow + 16 * i) * kPStride + 8 * kseg] = make_uint4(o[0], o[1], o[2], o[3]);
+      *(uint4*)&s_a[buf][(srow + kSR * i) * kPStride + 8 * kseg] = make_uint4(o[0], o[1], o[2], o[3]);
     }
   };
-  auto mfma = [&](int buf, const u32x4 (&w)[2][4]) {
+  auto mfma = [&](int buf, const u32x4 (&w)[4]) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const bf16x8 b0 = __builtin_bit_cast(bf16x8, w[0][ks]);
-      const bf16x8 b1 = __builtin_bit_cast(bf16x8, w[1][ks]);
+      const bf16x8 bw = __builtin_bit_cast(bf16x8, w[ks]);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         const bf16x8 av = __builtin_bit_cast(
             bf16x8, *(const uint4*)&s_a[buf][(16 * mt + r16) * kPStride + 32 * ks + 8 * kg]);
-        acc[mt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b0, acc[mt][0], 0, 0, 0);
-        acc[mt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b1, acc[mt][1], 0, 0, 0);
+        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bw, acc[mt], 0, 0, 0);
       }
     }
   };
 
-  // ---- the K-slice: stage c (activations one stage ahead), multiply c (weights two ahead)
+  // ---- the K-slice: stage c, issue the loads of c + 1 (activations) and c + 2 (weights),
+  // multiply c.  Six stages per turn: the activation slots alternate, the weight slots rotate.
   if (c0 < c1) {
-    load_h(c0);
+    load_h(h0, c0);
     load_w(w0, c0);
-    if (c0 + 1 < c1) load_w(w1, c0 + 1);
+    load_w(w1, c0 + 1);
     int buf = 0;
-    for (int c = c0; c < c1; c += 3) {
-      stage(buf);
-      if (c + 1 < c1) load_h(c + 1);
-      if (c + 2 < c1) load_w(w2, c + 2);
-      __syncthreads();
-      mfma(buf, w0);
+    auto one = [&](int c, HSlot& hs, HSlot& hn, const u32x4 (&w)[4], u32x4 (&wn)[4]) {
+      stage(hs, buf);
+      load_h(hn, c + 1);
+      load_w(wn, c + 2);
+      lds_barrier();
+      mfma(buf, w);
       buf ^= 1;
+    };
+    for (int c = c0; c < c1; c += 6) {
+      one(c, h0, h1, w0, w2);
       if (c + 1 >= c1) break;
-      stage(buf);
-      if (c + 2 < c1) load_h(c + 2);
-      if (c + 3 < c1) load_w(w0, c + 3);
-      __syncthreads();
-      mfma(buf, w1);
-      buf ^= 1;
+      one(c + 1, h1, h0, w1, w0);
       if (c + 2 >= c1) break;
-      stage(buf);
-      if (c + 3 < c1) load_h(c + 3);
-      if (c + 4 < c1) load_w(w1, c + 4);
-      __syncthreads();
-      mfma(buf, w2);
-      buf ^= 1;
+      one(c + 2, h0, h1, w2, w1);
+      if (c + 3 >= c1) break;
+      one(c + 3, h1, h0, w0, w2);
+      if (c + 4 >= c1) break;
+      one(c + 4, h0, h1, w1, w0);
+      if (c + 5 >= c1) break;
+      one(c + 5, h1, h0, w2, w1);
     }
   }
   // row sums of h^2 over the slice: the 16 threads of a row are one 16-lane DPP row
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < kSI; ++i) {
     ss[i] += xor_f32<8>(ss[i]);
     ss[i] += xor_f32<4>(ss[i]);
     ss[i] += xor_f32<2>(ss[i]);
@@ -365,12 +389,10 @@ __global__ void __launch_bounds__(kPThreads) prologue_kernel(PrologueLaunch a) {
   const __amdgpu_buffer_rsrc_t rpart = make_rsrc(a.partials + ((size_t)rb * nx + wg) * kPart, kPart * 4);
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-      store_coherent(rpart, ((32 * wave + 16 * nt + r16) * kPRows + 16 * mt + 4 * kg) * 4, acc[mt][nt]);
+    store_coherent(rpart, ((16 * wave + r16) * kPRows + 16 * mt + 4 * kg) * 4, acc[mt]);
   if (kseg == 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s_r[srow + 16 * i] = ss[i];
+    for (int i = 0; i < kSI; ++i) s_r[srow + kSR * i] = ss[i];
   }
   __syncthreads();
   if (tid < kPRows / 4)
@@ -517,7 +539,29 @@ hipError_t launch_fmt(const PrologueLaunch& a, dim3 grid, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Packed projection weights: for each group of 16 output rows (cg) and each step of 32 inputs
+// (ks), one 1 KB block at (cg * d / 32 + ks) * 1 KB whose 16-byte lane l = 16 q + j holds
+// W[16 cg + j][32 ks + 8 q .. 32 ks + 8 q + 7]: the B operand of one MFMA for one wave.  A
+// wave's stream through d is then contiguous.
+__global__ void __launch_bounds__(256) pack_weights_kernel(const uint4* __restrict__ w, uint4* __restrict__ out,
+                                                            int d, int64_t n16) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;   // 16-byte unit of the output
+  if (i >= n16) return;
+  const int64_t blk = i >> 6;
+  const int l = (int)(i & 63), j = l & 15, q = l >> 4;
+  const int nks = d / 32;
+  const int64_t cg = blk / nks, ks = blk % nks;
+  const int64_t row = 16 * cg + j, col = 32 * ks + 8 * q;
+  out[i] = w[(row * d + col) / 8];
+}
+
 }  // namespace
+
+hipError_t launch_pack_weights(const void* w, void* out, int d, int64_t rows, hipStream_t st) {
+  const int64_t n16 = rows * d / 8;
+  pack_weights_kernel<<<(unsigned)((n16 + 255) / 256), 256, 0, st>>>((const uint4*)w, (uint4*)out, d, n16);
+  return hipGetLastError();
+}
 
 hipError_t launch_prologue(const PrologueLaunch& a, hipStream_t st) {
   const dim3 grid((2 * a.L.H * a.splits_kv + a.Hq * a.splits_q) * a.row_blocks);

@@ -306,7 +306,8 @@ int32_t kvq_retier(const kvq_params* p, const kvq_cache* cache, int32_t* block_t
  *   KVQ_ERR_INVALID_ARG and nothing is written).  No bias and no rotary embedding.
  * Arithmetic: bf16(h * gain) x W on bf16 MFMA with fp32 accumulation, scaled per row by
  * 1 / sqrt(sum(h^2) / d + eps) after the product; deterministic (independent of scheduling).
- * hidden_bf16 [B][d], gain_bf16 [d], weight_bf16 as above: device bfloat16, 16-byte aligned;
+ * hidden_bf16 [B][d], gain_bf16 [d]: device bfloat16, 16-byte aligned; weight_bf16: W packed
+ * by kvq_prologue_pack_weights (device, 16-byte aligned);
  * d_model a multiple of 128; eps >= 0 and finite; positions: device int32 [B]; block_table as
  * for appends (paged) or NULL; q_bf16_out: device bfloat16 [B][Hq][D]; proj_out: NULL or device
  * float32 [B][(Hq + 2H) D] receiving y (the rows the cache write quantizes); workspace: device,
@@ -314,6 +315,14 @@ int32_t kvq_retier(const kvq_params* p, const kvq_cache* cache, int32_t* block_t
  * library (every call leaves its arrival counters at zero again; calls sharing a workspace must
  * not overlap). */
 int32_t kvq_prologue_workspace_bytes(const kvq_params* p, int32_t d_model, uint64_t* out_bytes);
+/* Repacks W ([(Hq + 2H) D][d_model] bfloat16, row-major, as above) once into the block order
+ * kvq_attention_prologue reads: for each group of 16 output rows cg and each step of 32 inputs
+ * ks, one 1 KB block at byte (cg * d_model / 32 + ks) * 1024 whose 16-byte unit u = 16 q + j
+ * (q < 4, j < 16) holds W[16 cg + j][32 ks + 8 q .. 32 ks + 8 q + 7], so that each wave streams
+ * its rows through d_model contiguously.  weight_bf16 and packed_bf16: distinct device buffers
+ * of (Hq + 2H) D d_model bfloat16, 16-byte aligned; enqueued on `stream`. */
+int32_t kvq_prologue_pack_weights(const kvq_params* p, int32_t d_model, const void* weight_bf16,
+                                  void* packed_bf16, void* stream);
 int32_t kvq_attention_prologue(const kvq_params* p, const kvq_cache* cache, const void* hidden_bf16,
                                const void* gain_bf16, const void* weight_bf16, int32_t d_model,
                                float eps, const int32_t* positions, const int32_t* block_table,

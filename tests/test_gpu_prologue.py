@@ -63,7 +63,9 @@ def _run(dc, d, h, g, W, positions, ws=None):
     dev = "cuda"
     ht = torch.from_numpy(h.view(np.int16)).to(dev)
     gt = torch.from_numpy(g.view(np.int16)).to(dev)
-    Wt = torch.from_numpy(W.view(np.int16)).to(dev)
+    Wr = torch.from_numpy(W.view(np.int16)).to(dev)
+    Wt = torch.empty_like(Wr)
+    K.kvq_prologue_pack_weights(p, Wr, Wt)
     pos = torch.tensor(positions, dtype=torch.int32, device=dev)
     q = torch.zeros((w.B, w.Hq, w.D), dtype=torch.int16, device=dev)
     proj = torch.full((w.B, (w.Hq + 2 * w.H) * w.D), float("nan"), dtype=torch.float32, device=dev)
@@ -153,6 +155,31 @@ def test_prologue_matches_oracle(name):
         for hq, o in oracle_attention(dc, b, range(w.Hq), sm).items():
             err = np.abs(got[b, hq] - o).max()
             assert err <= ATOL, f"{name} decode after the prologue b={b} hq={hq}: {err}"
+
+
+def _pack_reference(W):
+    """The block order of the packed weights, by index arithmetic on the host: block (cg, ks) of
+    16 output rows x 32 inputs, its 16-byte unit 16 q + j = W[16 cg + j][32 ks + 8 q: +8]."""
+    n, d = W.shape
+    blocks = W.reshape(n // 16, 16, d // 32, 4, 8)        # [cg][j][ks][q][8]
+    return np.ascontiguousarray(blocks.transpose(0, 2, 3, 1, 4)).reshape(-1)   # [cg][ks][q][j][8]
+
+
+def test_packed_weights_layout():
+    w = WD.variant(CONFIGS["c2_b16_s8k"], B=1, H=2, Hq=8, S=64)
+    p = WD.make_params(w, 64)
+    d = 384
+    W = G.projection(w, d)
+    Wr = torch.from_numpy(W.view(np.int16)).cuda()
+    Wp = torch.empty_like(Wr)
+    K.kvq_prologue_pack_weights(p, Wr, Wp)
+    torch.cuda.synchronize()
+    got = Wp.cpu().numpy().view(np.uint16).reshape(-1)
+    assert np.array_equal(got, _pack_reference(W))
+    # one hand-checked unit: block (cg 1, ks 2), unit 16 * 3 + 5 = W[16 + 5][64 + 24 .. 64 + 31]
+    nks = d // 32
+    u = ((1 * nks + 2) * 64 + 16 * 3 + 5) * 8
+    assert np.array_equal(got[u:u + 8], W[21, 88:96])
 
 
 def test_prologue_rejects_bad_arguments():
