@@ -67,6 +67,11 @@ constexpr int kWaves = 12;
 constexpr int kPF = 1;                     // steps of codes / records in flight per wave
 // Paged caches: a workgroup lists the pages of its piece by tier, this many pages at a time.
 constexpr int kSegPages = 1024;
+// Work split: each list counts as kPieceSteps steps more than it holds, the fixed cost of a piece
+// (its setup, page listing and epilogue) in units of one step of a workgroup, half before its
+// steps and half after them (a list cut in two costs a piece in each workgroup), so that
+// workgroups whose ranges cover many short lists take fewer steps.
+template <bool PAGED> constexpr int kPieceSteps = PAGED ? 48 : 16;
 constexpr uint32_t kDead = 0xFFFFFFFFu;    // no page: its rows read as zeros
 
 template <int FMT> struct Buf;
@@ -292,6 +297,20 @@ constexpr int kRowRor8 = 0x128;   // lane i <- lane (i + 8) mod 16 of its row
 // MASS (paged caches): every step also writes, per query head and page, log2 of the sum of the
 // page's exp2-domain probabilities (the page's log-sum-exp), and the epilogue writes each query
 // head's total; a later pass turns them into page attention masses.
+// a / b for the merge descriptor's 64-bit counts, in 32 bits when both fit (64-bit division is
+// a long instruction sequence)
+__device__ __forceinline__ uint64_t udivq(uint64_t a, uint64_t b) {
+  return ((a | b) >> 32) == 0 ? (uint64_t)((uint32_t)a / (uint32_t)b) : a / b;
+}
+
+// The merge descriptors follow the partials: two int4 per workgroup, {b, h, i0, slot of i0}
+// of the cut list that ends in the workgroup's range ({-1, ...} when there is none), then the
+// total step count U in its first two words.
+__device__ __forceinline__ int4* cut_of(const DecodeLaunch& d, int wg) {
+  const size_t nf = (size_t)d.nwg * 2 * (size_t)(d.Hq / d.L.H) * (kHeadDim + 2);
+  return (int4*)(d.partials + nf) + 2 * (size_t)wg;
+}
+
 template <int FMT, int OUTL, bool CMP, bool PAGED, bool MASS>
 __global__ void __launch_bounds__(kWaves * 64) decode_mfma_kernel(DecodeLaunch d) {
   __shared__ __attribute__((aligned(16))) _Float16 s_lds[kWaves * kTile];
@@ -301,7 +320,8 @@ __global__ void __launch_bounds__(kWaves * 64) decode_mfma_kernel(DecodeLaunch d
   __shared__ __attribute__((aligned(16))) uint32_t s_pl[PAGED ? 2 : 1][PAGED ? kSegPages : 1][2];
   __shared__ int s_wn[PAGED ? kSegPages / 64 : 1][2];   // pages per tier of each listing wave
   __shared__ uint64_t s_sc[kWaves];   // per-wave sums of the work split
-  __shared__ int s_loc[3];            // the list and step where the workgroup's range starts
+  __shared__ int s_loc[3];            // the list and unit where the workgroup's range starts
+  __shared__ uint64_t s_loc64[5];     // its sequence's first unit, units per list; U, the range
 
   const Layout& L = d.L;
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
@@ -342,18 +362,22 @@ __global__ void __launch_bounds__(kWaves * 64) decode_mfma_kernel(DecodeLaunch d
 
 
   // ---- this workgroup's share of the work.  Every list (sequence b, KV head h) of a valid
-  // sequence is cut into n_b = ceil(S_b / 32) steps; the lists are laid end to end in (sequence,
-  // head) order, U steps in all, and workgroup i of N takes steps [floor(i U / N),
-  // floor((i + 1) U / N)).  A piece is the part of one list inside that range: only the first
-  // and the last piece of a workgroup can be parts of a list, every other piece is a whole list.
-  // Steps per head of every sequence, summed, then scanned to find the sequence that holds the
-  // range's first step: all threads of the workgroup, 768 sequences at a time.
+  // sequence is cut into n_b = ceil(S_b / 32) steps and weighs m_b = K0 + n_b units: K0a units
+  // of fixed cost, one per step, K0b units of fixed cost (K0a + K0b = K0 = kPieceSteps).  The
+  // lists are laid end to end
+  // in (sequence, head) order, U units in all, and workgroup i of N takes units [floor(i U /
+  // N), floor((i + 1) U / N)): the steps of those units.  A piece is the part of one list
+  // inside that range: only the first and the last piece of a workgroup can be parts of a list,
+  // every other piece is a whole list.  Units per head of every sequence, summed, then scanned
+  // to find the sequence that holds the range's first unit: all threads of the workgroup, 768
+  // sequences at a time.
+  constexpr int K0 = kPieceSteps<PAGED>, K0a = K0 / 2, K0b = K0 - K0a;
   constexpr int kT = kWaves * 64;
   const int tid = threadIdx.x;
   auto seq_steps = [&](int bb) -> uint64_t {
     if (bb >= L.B) return 0u;
     const int Sb = d.seq_lens[bb];
-    return Sb >= 1 && Sb <= L.S_cap ? (uint64_t)((Sb + kStep - 1) / kStep) : 0u;
+    return Sb >= 1 && Sb <= L.S_cap ? (uint64_t)((Sb + kStep - 1) / kStep + K0) : 0u;
   };
   auto wave_sum = [&](uint64_t v) {
 #pragma unroll
@@ -370,7 +394,7 @@ __global__ void __launch_bounds__(kWaves * 64) decode_mfma_kernel(DecodeLaunch d
   };
   const uint64_t nwg = gridDim.x;
   uint64_t U = 0, ub = 0, ue = 0;
-  int b = 0, h = 0, s0 = 0;   // the list and step of the first piece
+  int b = 0, h = 0, off = 0;   // the list of the first piece and the range's unit offset in it
   if (L.B <= kT) {
     // one sequence per thread: one scan gives the total and every sequence's first step
     uint64_t n = 0;
@@ -378,7 +402,7 @@ __global__ void __launch_bounds__(kWaves * 64) decode_mfma_kernel(DecodeLaunch d
       const int Sb = d.seq_lens[tid];
       const bool ok = Sb >= 1 && Sb <= L.S_cap;
       if (!ok && blockIdx.x == 0) report(d.cache.status, KVQ_ERR_INVALID_ARG);
-      n = ok ? (uint64_t)((Sb + kStep - 1) / kStep) : 0u;
+      n = ok ? (uint64_t)((Sb + kStep - 1) / kStep + K0) : 0u;
     }
     const uint64_t incl = wave_scan(n);
     if (lane == 63) s_sc[wave] = incl;
@@ -392,12 +416,20 @@ __global__ void __launch_bounds__(kWaves * 64) decode_mfma_kernel(DecodeLaunch d
     U *= (uint64_t)L.H;
     ub = (uint64_t)blockIdx.x * U / nwg;
     ue = ((uint64_t)blockIdx.x + 1) * U / nwg;
-    if (ub >= ue) return;
+    if (ub >= ue) {
+      if (tid == 0) cut_of(d, blockIdx.x)[0] = make_int4(-1, 0, 0, 0);
+      return;
+    }
     const uint64_t lo = (woff + incl - n) * (uint64_t)L.H;   // the sequence's first step
     if (n > 0 && lo <= ub && ub < lo + n * (uint64_t)L.H) {
       s_loc[0] = tid;
       s_loc[1] = (int)((ub - lo) / n);
       s_loc[2] = (int)((ub - lo) % n);
+      s_loc64[0] = lo;
+      s_loc64[1] = n;
+      s_loc64[2] = U;
+      s_loc64[3] = ub;
+      s_loc64[4] = ue;
     }
     __syncthreads();
   } else {
@@ -407,7 +439,7 @@ __global__ void __launch_bounds__(kWaves * 64) decode_mfma_kernel(DecodeLaunch d
       const int Sb = d.seq_lens[bb];
       const bool ok = Sb >= 1 && Sb <= L.S_cap;
       if (!ok && blockIdx.x == 0) report(d.cache.status, KVQ_ERR_INVALID_ARG);
-      mine += ok ? (uint64_t)((Sb + kStep - 1) / kStep) : 0u;
+      mine += ok ? (uint64_t)((Sb + kStep - 1) / kStep + K0) : 0u;
     }
     mine = wave_sum(mine);
     if (lane == 0) s_sc[wave] = mine;
@@ -418,7 +450,10 @@ __global__ void __launch_bounds__(kWaves * 64) decode_mfma_kernel(DecodeLaunch d
     __syncthreads();
     ub = (uint64_t)blockIdx.x * U / nwg;
     ue = ((uint64_t)blockIdx.x + 1) * U / nwg;
-    if (ub >= ue) return;
+    if (ub >= ue) {
+      if (tid == 0) cut_of(d, blockIdx.x)[0] = make_int4(-1, 0, 0, 0);
+      return;
+    }
     uint64_t carry = 0;   // steps per head of the sequences before this block of sequences
     for (int c0 = 0;; c0 += kT) {
       const int bb = c0 + tid;
@@ -437,6 +472,11 @@ __global__ void __launch_bounds__(kWaves * 64) decode_mfma_kernel(DecodeLaunch d
         s_loc[0] = bb;
         s_loc[1] = (int)((ub - lo) / n);
         s_loc[2] = (int)((ub - lo) % n);
+        s_loc64[0] = lo;
+        s_loc64[1] = n;
+        s_loc64[2] = U;
+        s_loc64[3] = ub;
+        s_loc64[4] = ue;
       }
       __syncthreads();
       if ((carry + tot) * (uint64_t)L.H > ub) break;   // found in this block
@@ -445,15 +485,17 @@ __global__ void __launch_bounds__(kWaves * 64) decode_mfma_kernel(DecodeLaunch d
   }
   b = s_loc[0];
   h = s_loc[1];
-  s0 = s_loc[2];
+  off = s_loc[2];
 
-  uint32_t left = (uint32_t)(ue - ub);   // steps of the range not yet taken
-  for (bool first = true;; first = false) {
+  uint64_t left = ue - ub;   // units of the range not yet taken
+  for (bool first = true;;) {
   const int S = d.seq_lens[b];
   const int nb = (S + kStep - 1) / kStep;
-  const int s1 = (int)min((uint32_t)nb, (uint32_t)s0 + left);
+  const int take = (int)min(left, (uint64_t)(nb + K0 - off));   // units of this list in the range
+  const int s0 = max(off - K0a, 0), s1 = min(max(off + take - K0a, 0), nb);   // its steps [s0, s1)
   const int t0 = kStep * s0, t1 = min(kStep * s1, S);   // the piece's tokens
   const bool whole = s0 == 0 && s1 == nb;
+  if (s1 > s0) {   // (only the first and the last list of a range can have no steps in it)
 
   // query operand (B of S^T = K^ Q^T): lane (row r, k-group kg), positions 32*ks + 8*kg + e
   half8 qop[4];
@@ -1124,99 +1166,94 @@ __global__ void __launch_bounds__(kWaves * 64) decode_mfma_kernel(DecodeLaunch d
     }
   }
   if (lane == 0) *prog_mine = 0;
-  left -= (uint32_t)(s1 - s0);
+  }
+  left -= (uint64_t)take;
   if (left == 0) break;
-  __syncthreads();   // the tiles and the wave states are reused by the next piece
-  s0 = 0;
+  if (s1 > s0) {
+    first = false;
+    __syncthreads();   // the tiles and the wave states are reused by the next piece
+  }
+  off = 0;
   if (++h == L.H) {   // the next list with steps (a sequence of invalid length has none)
     h = 0;
     do { ++b; } while (!(d.seq_lens[b] >= 1 && d.seq_lens[b] <= L.S_cap));
   }
   }
+  // The merge descriptor of this workgroup, written by one thread of the last wave once its work
+  // is done (no other wave waits for it): a list whose first step lies in an earlier
+  // workgroup's range and whose last lies in this one is merged after the decode by the merge's
+  // block of this workgroup; every workgroup writes its entry.  From the setup: the range's
+  // first list (sequence s_loc[0], head s_loc[1]), its sequence's first unit and units per list,
+  // U and the range.
+  if (tid == kT - 64) {
+    const uint64_t lo = s_loc64[0], m = s_loc64[1], UU = s_loc64[2], ub0 = s_loc64[3], ue0 = s_loc64[4];
+    const uint64_t hh = udivq(ub0 - lo, m), off0 = (ub0 - lo) - hh * m, n = m - K0;
+    const uint64_t pl = lo + hh * m;                       // the list's first unit
+    int4 c = make_int4(-1, 0, 0, 0);
+    if (off0 > (uint64_t)K0a && off0 < K0a + n && ue0 >= pl + K0a + n) {
+      const uint64_t u0 = pl + K0a;                        // the unit of its first step
+      const uint64_t i0 = udivq((u0 + 1) * nwg - 1, UU);   // the workgroup that holds it
+      // its first piece is this list (slot 0) unless its range holds steps of an earlier list
+      c = make_int4(s_loc[0], (int)hh, (int)i0, udivq(i0 * UU, nwg) + K0b >= pl ? 0 : 1);
+    }
+    int4* const e = cut_of(d, blockIdx.x);
+    e[0] = c;
+    e[1] = make_int4((int)(uint32_t)UU, (int)(uint32_t)(UU >> 32), 0, 0);
+  }
 }
 
-// Lists cut between workgroups: the block of (sequence b, query head hq) merges the partials of
-// the workgroups that worked on its list (b, hq's KV head), in workgroup order, into out[b][hq]
-// (and the total log2-sum-exp of a decode with page masses), out = sum_i 2^(m_i - M) o_i /
-// sum_i 2^(m_i - M) l_i with M = max_i m_i.  The owner of step u (the workgroup whose range
-// holds it) is floor(((u + 1) N - 1) / U), the inverse of the ranges [floor(i U / N),
-// floor((i + 1) U / N)).  A list that one workgroup finished whole was written by the decode;
-// workgroups with empty ranges (more workgroups than steps) hold nothing.  Thread (group g,
-// channel) folds every kMergeGroups-th partial from the g-th, in workgroup order (its loads do not
-// wait on its arithmetic, so an unrolled batch of them is in flight at once); the groups' states
-// are combined in group order: deterministic.
-constexpr int kMergeGroups = 4;
-constexpr int kMergeThreads = kMergeGroups * kHeadDim;
+// Lists cut between workgroups.  The list ending in workgroup i1's range that started in an
+// earlier one (the decode's descriptor of i1) is merged by block i1 from the partials of
+// workgroups i0 .. i1: out = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i with M = max_i m_i
+// (and with page masses the total log2-sum-exp M + log2 sum_i 2^(m_i - M) l_i).  Workgroup i0
+// holds the list's start in its first piece (slot 0) if its range starts there, else in its
+// last (slot 1); every later one holds a part in its first piece.  Workgroups with empty ranges
+// (more workgroups than steps) hold nothing and are skipped.  Each thread folds the parts of one
+// (query row, channel) in workgroup order, loading a batch of 16 parts (always at valid addresses)
+// before folding them: deterministic, and one memory round trip per batch.
+constexpr int kMergeThreads = 1024;
+constexpr int kMergeBatch = 16;
 __global__ void __launch_bounds__(kMergeThreads) streamk_merge_kernel(DecodeLaunch d) {
-  __shared__ uint64_t s_red[kMergeThreads / 64][2];
-  __shared__ float s_st[kMergeGroups][3][kHeadDim];
-  const Layout& L = d.L;
-  const int hq = blockIdx.x, b = blockIdx.y;
-  const int tid = threadIdx.x, ch = tid % kHeadDim, g = tid / kHeadDim;
-  const int S = d.seq_lens[b];
-  if (S < 1 || S > L.S_cap) return;   // reported by the decode; out[b] is not written
-  // steps per head of the sequences before b and of all sequences (each thread sums a strided
-  // share of the sequences; the waves' sums are added in order)
-  uint64_t before = 0, total = 0;
-  for (int bb = tid; bb < L.B; bb += kMergeThreads) {
-    const int Sb = d.seq_lens[bb];
-    const uint64_t n = Sb >= 1 && Sb <= L.S_cap ? (uint64_t)((Sb + kStep - 1) / kStep) : 0u;
-    before += bb < b ? n : 0u;
-    total += n;
-  }
+  const int i1 = blockIdx.x;
+  const int4* const e = cut_of(d, i1);
+  const int4 c = e[0];
+  if (c.x < 0) return;
+  const int4 cu = e[1];
+  const uint64_t U = (uint64_t)(uint32_t)cu.x | ((uint64_t)(uint32_t)cu.y << 32);
+  const uint64_t N = (uint64_t)d.nwg;
+  const bool may_be_empty = U < N;
+  const int b = c.x, h = c.y, i0 = c.z, slot0 = c.w;
+  const int G = d.Hq / d.L.H;
+  for (int p = threadIdx.x; p < G * kHeadDim; p += kMergeThreads) {
+    const int row = p / kHeadDim, ch = p % kHeadDim;
+    float M = -INFINITY, den = 0.0f, num = 0.0f;
+    for (int ib = i0; ib <= i1; ib += kMergeBatch) {
+      float m[kMergeBatch], l[kMergeBatch], o[kMergeBatch];
+      bool use[kMergeBatch];
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    before += __shfl_xor(before, o, 64);
-    total += __shfl_xor(total, o, 64);
-  }
-  if ((tid & 63) == 0) { s_red[tid >> 6][0] = before; s_red[tid >> 6][1] = total; }
-  __syncthreads();
-  before = 0;
-  total = 0;
+      for (int k = 0; k < kMergeBatch; ++k) {
+        const int i = ib + k;
+        use[k] = i <= i1 && !(may_be_empty && i > i0 && (uint64_t)i * U / N == (uint64_t)(i + 1) * U / N);
+        const size_t slot = use[k] ? (size_t)i * 2 + (i == i0 ? slot0 : 0) : (size_t)i0 * 2 + slot0;
+        const float* q = d.partials + (slot * G + row) * (kHeadDim + 2);
+        m[k] = q[0];
+        l[k] = q[1];
+        o[k] = q[2 + ch];
+      }
 #pragma unroll
-  for (int w = 0; w < kMergeThreads / 64; ++w) { before += s_red[w][0]; total += s_red[w][1]; }
-  const int G = d.Hq / L.H, h = hq / G, row = hq % G;
-  const uint64_t nb = (uint64_t)((S + kStep - 1) / kStep);
-  const uint64_t U = total * (uint64_t)L.H, N = (uint64_t)d.nwg;
-  const uint64_t u0 = before * (uint64_t)L.H + (uint64_t)h * nb, u1 = u0 + nb - 1;
-  const int i0 = (int)(((u0 + 1) * N - 1) / U), i1 = (int)(((u1 + 1) * N - 1) / U);
-  if (i0 == i1) return;
-  // workgroup i0 holds the list's start in its first piece (slot 0) if its range starts there,
-  // else in its last piece (slot 1); every later workgroup holds a part in its first piece
-  const int slot0 = (uint64_t)i0 * U / N == u0 ? 0 : 1;
-  const int np = i1 - i0 + 1;
-  float M = -INFINITY, den = 0.0f, num = 0.0f;
-#pragma unroll 4
-  for (int k = g; k < np; k += kMergeGroups) {
-    const uint64_t i = (uint64_t)(i0 + k);
-    if (k > 0 && i * U / N == (i + 1) * U / N) continue;   // a workgroup without steps
-    const size_t slot = (size_t)i * 2 + (k == 0 ? slot0 : 0);
-    const float* q = d.partials + (slot * G + row) * (kHeadDim + 2);
-    const float m = q[0], l = q[1], o = q[2 + ch];      // a part holding tokens: m finite
-    const float Mn = fmaxf(M, m);
-    const float al = exp2f(M - Mn), w = exp2f(m - Mn);   // al = 0 while M is -inf
-    den = fmaf(w, l, den * al);
-    num = fmaf(w, o, num * al);
-    M = Mn;
+      for (int k = 0; k < kMergeBatch; ++k) {
+        if (!use[k]) continue;
+        const float Mn = fmaxf(M, m[k]);                     // a part holding tokens: m finite
+        const float al = exp2f(M - Mn), w = exp2f(m[k] - Mn);   // al = 0 while M is -inf
+        den = fmaf(w, l[k], den * al);
+        num = fmaf(w, o[k], num * al);
+        M = Mn;
+      }
+    }
+    const int hq = h * G + row;
+    d.out[((size_t)b * d.Hq + hq) * kHeadDim + ch] = num / den;
+    if (d.total_lse && ch == 0) d.total_lse[(size_t)b * d.Hq + hq] = M + __builtin_log2f(den);
   }
-  s_st[g][0][ch] = M;
-  s_st[g][1][ch] = den;
-  s_st[g][2][ch] = num;
-  __syncthreads();
-  if (g != 0) return;
-  float Mt = -INFINITY;
-#pragma unroll
-  for (int k = 0; k < kMergeGroups; ++k) Mt = fmaxf(Mt, s_st[k][0][ch]);
-  float Dn = 0.0f, Nm = 0.0f;
-#pragma unroll
-  for (int k = 0; k < kMergeGroups; ++k) {
-    const float Mk = s_st[k][0][ch];
-    const float f = Mk == -INFINITY ? 0.0f : exp2f(Mk - Mt);   // a group with no part
-    Dn = fmaf(f, s_st[k][1][ch], Dn);
-    Nm = fmaf(f, s_st[k][2][ch], Nm);
-  }
-  d.out[((size_t)b * d.Hq + hq) * kHeadDim + ch] = Nm / Dn;
-  if (d.total_lse && ch == 0) d.total_lse[(size_t)b * d.Hq + hq] = Mt + __builtin_log2f(Dn);
 }
 
 template <int FMT, bool CMP, bool PAGED, bool MASS>
@@ -1248,7 +1285,7 @@ hipError_t launch_decode_mfma(const DecodeLaunch& d, hipStream_t st, bool* handl
   *handled = true;
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  streamk_merge_kernel<<<dim3(d.Hq, d.L.B), kMergeThreads, 0, st>>>(d);
+  streamk_merge_kernel<<<dim3(d.nwg), kMergeThreads, 0, st>>>(d);
   return hipGetLastError();
 }
 

@@ -135,11 +135,12 @@ int64_t decode_wgs(const kvq_params* p, int32_t split_chunk) {
                               : std::min(kDecodeWGs, (steps + 11) / 12);
   return std::max<int64_t>(1, std::min({n, steps, kMaxDecodeWGs}));
 }
-// partials of the MFMA decoder: two (max, sum, output) slots of Hq / H query heads per workgroup
+// partials of the MFMA decoder: two (max, sum, output) slots of Hq / H query heads per
+// workgroup, then 32 bytes per workgroup describing the cut list that ends in its range
 uint64_t mfma_partial_bytes(const kvq_params* p, int32_t split_chunk) {
   if (!mfma_format(p)) return 0;
-  return (uint64_t)decode_wgs(p, split_chunk) * 2ull * (uint64_t)(p->num_q_heads / p->num_kv_heads) *
-         (kHeadDim + 2) * 4ull;
+  const uint64_t n = (uint64_t)decode_wgs(p, split_chunk);
+  return n * 2ull * (uint64_t)(p->num_q_heads / p->num_kv_heads) * (kHeadDim + 2) * 4ull + n * 32ull;
 }
 
 uint64_t align256(uint64_t x) { return (x + 255) & ~255ull; }

@@ -202,12 +202,15 @@ int32_t kvq_quantize_append(const kvq_params* p, const kvq_cache* cache, const f
 /* Workspace for kvq_decode_attention.
  * 2-bit caches, and contiguous FP4 caches with groups of 32 (the MFMA decoder; paged pools
  * whose rows need byte offsets of 2^32 or more take the generic decoder): N workgroups share the
- * 32-token steps of all (sequence, KV head) lists evenly, each a contiguous range of steps in
- * (sequence, head, token) order; a list cut between workgroups is merged afterwards by
- * log-sum-exp from two (max, sum, output) slots per workgroup: N * 2 * (Hq / H) * (D + 2)
- * floats.  split_chunk 0: N = min(256, ceil(B * H * ceil(max_seq_len / 32) / 12)) (one
- * workgroup per CU of an MI355X, at least 12 steps each); split_chunk > 0: N = min(B * H *
- * ceil(max_seq_len / 32), 16384, ceil(B * H * max_seq_len / split_chunk)).
+ * 32-token steps of all (sequence, KV head) lists, each a contiguous range in (sequence, head,
+ * token) order, the ranges even in a weight of one per step plus a fixed cost per list (so that
+ * ranges over many short lists take fewer steps).  A list cut between workgroups is merged
+ * afterwards by log-sum-exp from two (max, sum, output) slots per workgroup, N * 2 * (Hq / H) *
+ * (D + 2) floats, followed by 32 bytes per workgroup naming the cut list that ends in its range:
+ * N * (8 * (Hq / H) * (D + 2) + 32) bytes.  split_chunk 0: N = min(256, ceil(B * H *
+ * ceil(max_seq_len / 32) / 12)) (one workgroup per CU of an MI355X, at least 12 steps each);
+ * split_chunk > 0: N = min(B * H * ceil(max_seq_len / 32), 16384, ceil(B * H * max_seq_len /
+ * split_chunk)).
  * Other formats (the generic decoder): split-K chunks of each list, B * Hq *
  * ceil(max_seq_len / chunk) * (D + 2) floats (0 when one chunk covers max_seq_len); chunk =
  * split_chunk, or by default 4096 for paged caches and, for contiguous caches, enough chunks for

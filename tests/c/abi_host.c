@@ -41,10 +41,10 @@ int main(void) {
         s.meta_bytes_per_row == 16, "cache_sizes INT3 rows");
 
   uint64_t ws = 1;
-  CHECK(kvq_workspace_bytes(&p, 0, &ws) == KVQ_OK && ws == 256ull * 2 * 8 * (128 + 2) * 4,
+  CHECK(kvq_workspace_bytes(&p, 0, &ws) == KVQ_OK && ws == 256ull * (2 * 8 * (128 + 2) * 4 + 32),
         "workspace of 256 workgroups");
   CHECK(kvq_workspace_bytes(&p, 4096, &ws) == KVQ_OK &&
-        ws == 4096ull * 2 * 8 * (128 + 2) * 4, "workspace of one workgroup per 4096 tokens");
+        ws == 4096ull * (2 * 8 * (128 + 2) * 4 + 32), "workspace of one workgroup per 4096 tokens");
 
   kvq_params bad = p;
   bad.head_dim = 96;

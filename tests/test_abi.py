@@ -42,17 +42,17 @@ def test_cache_sizes_and_workspace():
     assert s.codes == 64 * 8 * 32768 * 32 and s.meta == 64 * 8 * 32768 * 16
     assert s.outl_idx == 64 * 8 * 100 * 4 and s.outl_val == 64 * 8 * 100
     assert s.outl_block_start == 64 * 8 * 2 * 2048 * 4
-    # MFMA decoder: two partial slots of Hq / H = 8 query heads per workgroup; 256 workgroups by
-    # default, one per 2048 tokens of all lists with a split
-    assert K.kvq_workspace_bytes(p) == 256 * 2 * 8 * 130 * 4
-    assert K.kvq_workspace_bytes(p, 2048) == (64 * 8 * 32768 // 2048) * 2 * 8 * 130 * 4
+    # MFMA decoder: two partial slots of Hq / H = 8 query heads and a 32-byte merge descriptor
+    # per workgroup; 256 workgroups by default, one per 2048 tokens of all lists with a split
+    assert K.kvq_workspace_bytes(p) == 256 * (2 * 8 * 130 * 4 + 32)
+    assert K.kvq_workspace_bytes(p, 2048) == (64 * 8 * 32768 // 2048) * (2 * 8 * 130 * 4 + 32)
     # default split of formats on the generic decoder: 64-token chunks for a short context
     pi = K.make_params(1, 8, 2, 1024, "int4", 32, "fp16")
     assert K.kvq_workspace_bytes(pi) == 1 * 8 * 16 * 130 * 4
     # FP4 g32 (MFMA decoder): 256 workgroups
-    assert K.kvq_workspace_bytes(K.make_params(4, 64, 8, 131072, "fp4", 32, "fp16")) == 256 * 2 * 8 * 130 * 4
+    assert K.kvq_workspace_bytes(K.make_params(4, 64, 8, 131072, "fp4", 32, "fp16")) == 256 * (2 * 8 * 130 * 4 + 32)
     # few steps: at least 12 per workgroup (1 x 2 lists of 32 steps -> 6 workgroups)
-    assert K.kvq_workspace_bytes(K.make_params(1, 8, 2, 1024, "c2", 64, "e4m3")) == 6 * 2 * 4 * 130 * 4
+    assert K.kvq_workspace_bytes(K.make_params(1, 8, 2, 1024, "c2", 64, "e4m3")) == 6 * (2 * 4 * 130 * 4 + 32)
     p4 = K.make_params(4, 64, 8, 131072, "fp4", 32, "fp16")
     s4 = K.kvq_cache_sizes(p4, 10)
     assert (s4.code_bytes_per_row, s4.meta_bytes_per_row) == (64, 4)
@@ -99,7 +99,7 @@ def test_paged_params_validation():
 
 def test_split_chunk_must_be_multiple_of_64():
     p = K.make_params(2, 8, 2, 1000, "c2", 64, "e4m3")
-    assert K.kvq_workspace_bytes(p, 128) == (2 * 2 * 1000 + 127) // 128 * 2 * 4 * 130 * 4
+    assert K.kvq_workspace_bytes(p, 128) == (2 * 2 * 1000 + 127) // 128 * (2 * 4 * 130 * 4 + 32)
     with pytest.raises(K.KvqError):
         K.kvq_workspace_bytes(p, 100)
 
