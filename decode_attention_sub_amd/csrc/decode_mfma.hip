@@ -303,12 +303,97 @@ __device__ __forceinline__ uint64_t udivq(uint64_t a, uint64_t b) {
   return ((a | b) >> 32) == 0 ? (uint64_t)((uint32_t)a / (uint32_t)b) : a / b;
 }
 
-// The merge descriptors follow the partials: two int4 per workgroup, {b, h, i0, slot of i0}
-// of the cut list that ends in the workgroup's range ({-1, ...} when there is none), then the
-// total step count U in its first two words.
-__device__ __forceinline__ int4* cut_of(const DecodeLaunch& d, int wg) {
+// After the partials, 32 bytes per workgroup; the first 8 of workgroup i count the parts of the
+// cut list whose last step i holds: (call nonce << 32) | parts finished (a word tagged with
+// another call's nonce counts as zero, so the workspace needs no clearing).
+__device__ __forceinline__ uint64_t* arrivals_of(const DecodeLaunch& d, int wg) {
   const size_t nf = (size_t)d.nwg * 2 * (size_t)(d.Hq / d.L.H) * (kHeadDim + 2);
-  return (int4*)(d.partials + nf) + 2 * (size_t)wg;
+  return (uint64_t*)((int4*)(d.partials + nf) + 2 * (size_t)wg);
+}
+
+// Partials of cut lists cross workgroups on different XCDs, whose L2 caches are not coherent
+// with each other: they are stored and loaded with the cache policy bit sc1 of gfx940-family
+// memory instructions, which reaches the device's coherence point.
+constexpr int kSc1 = 16;
+constexpr int kMergeBatch = 16;   // parts of a cut list whose loads are in flight at once
+__device__ __forceinline__ void store_sc1(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(as_u32(v), r, (int)off, 0, kSc1);
+}
+__device__ __forceinline__ float load_sc1(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return as_f32(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, kSc1));
+}
+
+// A cut list: the last workgroup to finish a part of it merges the parts of workgroups i0 .. i1
+// (the owners of its first and last steps): out = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i,
+// M = max_i m_i (with page masses also the total log2-sum-exp).  Workgroup i0 holds the list's
+// start in its first piece (slot 0) unless its range holds steps of an earlier list (slot 1);
+// every later one holds a part in its first piece; workgroups with empty ranges hold nothing.
+// Nobody waits: the last to arrive does the work.  Called by every thread of the workgroup after
+// its parts are stored, for the list of sequence b, head h (nb steps, first unit pl); s_loc64[1]
+// = U.
+template <bool MASS>
+__device__ __forceinline__ void merge_cut_list(const DecodeLaunch& d, int b, int h, int nb, uint64_t pl,
+                                               int K0a, int K0b, const uint64_t* s_loc64, int* s_mg) {
+  const int tid = threadIdx.x;
+  const int G = d.Hq / d.L.H;
+  const uint64_t nwg = gridDim.x;
+  const __amdgpu_buffer_rsrc_t rpart = make_rsrc(d.partials, (uint32_t)(nwg * 2u * (uint64_t)G * (kHeadDim + 2) * 4u));
+  if (tid == 0) {
+    const uint64_t UU = s_loc64[1];
+    const uint64_t u0 = pl + (uint64_t)K0a, ul = u0 + (uint64_t)(nb - 1);   // units of its first and last steps
+    const uint64_t i0 = udivq((u0 + 1) * nwg - 1, UU), i1 = udivq((ul + 1) * nwg - 1, UU);
+    uint32_t np = (uint32_t)(i1 - i0 + 1);
+    if (UU < nwg) {
+      np = 0;
+      for (uint64_t i = i0; i <= i1; ++i) np += udivq(i * UU, nwg) < udivq((i + 1) * UU, nwg) ? 1u : 0u;
+    }
+    uint64_t* const w = arrivals_of(d, (int)i1);
+    uint64_t old = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), nw;
+    do {
+      nw = (uint32_t)(old >> 32) == d.nonce ? old + 1u : ((uint64_t)d.nonce << 32) | 1u;
+    } while (!__hip_atomic_compare_exchange_strong(w, &old, nw, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT));
+    s_mg[0] = (uint32_t)nw == np;
+    s_mg[1] = (int)i0;
+    s_mg[2] = (int)i1;
+    s_mg[3] = udivq(i0 * UU, nwg) + (uint64_t)K0b >= pl ? 0 : 1;
+  }
+  __syncthreads();
+  if (!s_mg[0]) return;
+  const int i0 = s_mg[1], i1 = s_mg[2], slot0 = s_mg[3];
+  const uint64_t UU = s_loc64[1];
+  const bool may_be_empty = UU < nwg;
+  for (int p = tid; p < G * kHeadDim; p += blockDim.x) {
+    const int row = p / kHeadDim, ch = p % kHeadDim;
+    float M = -INFINITY, den = 0.0f, num = 0.0f;
+    for (int ib = i0; ib <= i1; ib += kMergeBatch) {
+      float mm[kMergeBatch], ll[kMergeBatch], oo[kMergeBatch];
+      bool use[kMergeBatch];
+#pragma unroll
+      for (int k = 0; k < kMergeBatch; ++k) {   // a batch of parts' loads in flight, at valid slots
+        const int i = ib + k;
+        use[k] = i <= i1 && !(may_be_empty && i > i0 &&
+                              udivq((uint64_t)i * UU, nwg) == udivq((uint64_t)(i + 1) * UU, nwg));
+        const uint32_t slot = use[k] ? (uint32_t)i * 2u + (i == i0 ? (uint32_t)slot0 : 0u) : (uint32_t)i0 * 2u + (uint32_t)slot0;
+        const uint32_t o = ((slot * (uint32_t)G + (uint32_t)row) * (kHeadDim + 2)) * 4u;
+        mm[k] = load_sc1(rpart, o);
+        ll[k] = load_sc1(rpart, o + 4u);
+        oo[k] = load_sc1(rpart, o + (2u + (uint32_t)ch) * 4u);
+      }
+#pragma unroll
+      for (int k = 0; k < kMergeBatch; ++k) {
+        if (!use[k]) continue;
+        const float Mn = fmaxf(M, mm[k]);                      // a part holding tokens: m finite
+        const float al = exp2f(M - Mn), wk = exp2f(mm[k] - Mn);   // al = 0 while M is -inf
+        den = fmaf(wk, ll[k], den * al);
+        num = fmaf(wk, oo[k], num * al);
+        M = Mn;
+      }
+    }
+    const size_t hq = (size_t)h * G + row;
+    d.out[((size_t)b * d.Hq + hq) * kHeadDim + ch] = num / den;
+    if (MASS && ch == 0) d.total_lse[(size_t)b * d.Hq + hq] = M + __builtin_log2f(den);
+  }
 }
 
 template <int FMT, int OUTL, bool CMP, bool PAGED, bool MASS>
@@ -321,7 +406,10 @@ __global__ void __launch_bounds__(kWaves * 64) decode_mfma_kernel(DecodeLaunch d
   __shared__ int s_wn[PAGED ? kSegPages / 64 : 1][2];   // pages per tier of each listing wave
   __shared__ uint64_t s_sc[kWaves];   // per-wave sums of the work split
   __shared__ int s_loc[3];            // the list and unit where the workgroup's range starts
-  __shared__ uint64_t s_loc64[5];     // its sequence's first unit, units per list; U, the range
+  __shared__ uint64_t s_loc64[2];     // the current list's first unit; U
+  __shared__ int s_mg[4];             // a cut list's merge: last part?, i0, i1, slot of i0
+  __shared__ int s_cut[2][3];         // the lists of the parts in slots 0 and 1: b (-1: none), h, steps
+  __shared__ uint64_t s_cut64[2];     // and their first units
 
   const Layout& L = d.L;
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
@@ -393,6 +481,7 @@ __global__ void __launch_bounds__(kWaves * 64) decode_mfma_kernel(DecodeLaunch d
     return v;
   };
   const uint64_t nwg = gridDim.x;
+  if (tid == 0) { s_cut[0][0] = -1; s_cut[1][0] = -1; }
   uint64_t U = 0, ub = 0, ue = 0;
   int b = 0, h = 0, off = 0;   // the list of the first piece and the range's unit offset in it
   if (L.B <= kT) {
@@ -416,20 +505,14 @@ __global__ void __launch_bounds__(kWaves * 64) decode_mfma_kernel(DecodeLaunch d
     U *= (uint64_t)L.H;
     ub = (uint64_t)blockIdx.x * U / nwg;
     ue = ((uint64_t)blockIdx.x + 1) * U / nwg;
-    if (ub >= ue) {
-      if (tid == 0) cut_of(d, blockIdx.x)[0] = make_int4(-1, 0, 0, 0);
-      return;
-    }
+    if (ub >= ue) return;
     const uint64_t lo = (woff + incl - n) * (uint64_t)L.H;   // the sequence's first step
     if (n > 0 && lo <= ub && ub < lo + n * (uint64_t)L.H) {
       s_loc[0] = tid;
       s_loc[1] = (int)((ub - lo) / n);
       s_loc[2] = (int)((ub - lo) % n);
-      s_loc64[0] = lo;
-      s_loc64[1] = n;
-      s_loc64[2] = U;
-      s_loc64[3] = ub;
-      s_loc64[4] = ue;
+      s_loc64[0] = lo + (ub - lo) / n * n;
+      s_loc64[1] = U;
     }
     __syncthreads();
   } else {
@@ -450,10 +533,7 @@ __global__ void __launch_bounds__(kWaves * 64) decode_mfma_kernel(DecodeLaunch d
     __syncthreads();
     ub = (uint64_t)blockIdx.x * U / nwg;
     ue = ((uint64_t)blockIdx.x + 1) * U / nwg;
-    if (ub >= ue) {
-      if (tid == 0) cut_of(d, blockIdx.x)[0] = make_int4(-1, 0, 0, 0);
-      return;
-    }
+    if (ub >= ue) return;
     uint64_t carry = 0;   // steps per head of the sequences before this block of sequences
     for (int c0 = 0;; c0 += kT) {
       const int bb = c0 + tid;
@@ -472,11 +552,8 @@ __global__ void __launch_bounds__(kWaves * 64) decode_mfma_kernel(DecodeLaunch d
         s_loc[0] = bb;
         s_loc[1] = (int)((ub - lo) / n);
         s_loc[2] = (int)((ub - lo) % n);
-        s_loc64[0] = lo;
-        s_loc64[1] = n;
-        s_loc64[2] = U;
-        s_loc64[3] = ub;
-        s_loc64[4] = ue;
+        s_loc64[0] = lo + (ub - lo) / n * n;
+        s_loc64[1] = U;
       }
       __syncthreads();
       if ((carry + tot) * (uint64_t)L.H > ub) break;   // found in this block
@@ -1136,6 +1213,7 @@ __global__ void __launch_bounds__(kWaves * 64) decode_mfma_kernel(DecodeLaunch d
   l_row += __shfl_xor(l_row, 16, 64);
   l_row += __shfl_xor(l_row, 32, 64);
   float* s_o = (float*)(s_lds + wave * kTile);   // [16 rows][128 channels] of this wave
+  const __amdgpu_buffer_rsrc_t rpart = make_rsrc(d.partials, (uint32_t)(nwg * 2u * (uint64_t)G * (kHeadDim + 2) * 4u));
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
@@ -1160,10 +1238,18 @@ __global__ void __launch_bounds__(kWaves * 64) decode_mfma_kernel(DecodeLaunch d
     } else {
       // a part of a list leaves a (max, sum, output) partial per query head in slot 0 (the
       // workgroup's first piece) or 1 (its last)
-      float* pp = d.partials + (((size_t)blockIdx.x * 2 + (first ? 0 : 1)) * G + row) * (kHeadDim + 2);
-      if (ch == 0) { pp[0] = M; pp[1] = den; }
-      pp[2 + ch] = num;
+      const uint32_t o = (uint32_t)(((blockIdx.x * 2u + (first ? 0u : 1u)) * (uint32_t)G + (uint32_t)row) *
+                                    (kHeadDim + 2)) * 4u;
+      if (ch == 0) { store_sc1(rpart, o, M); store_sc1(rpart, o + 4u, den); }
+      store_sc1(rpart, o + (2u + (uint32_t)ch) * 4u, num);
     }
+  }
+  if (!whole && tid == 0) {   // the list of a part, merged once the workgroup's work is done
+    const int sl = first ? 0 : 1;
+    s_cut[sl][0] = b;
+    s_cut[sl][1] = h;
+    s_cut[sl][2] = nb;
+    s_cut64[sl] = s_loc64[0];
   }
   if (lane == 0) *prog_mine = 0;
   }
@@ -1171,88 +1257,25 @@ __global__ void __launch_bounds__(kWaves * 64) decode_mfma_kernel(DecodeLaunch d
   if (left == 0) break;
   if (s1 > s0) {
     first = false;
-    __syncthreads();   // the tiles and the wave states are reused by the next piece
+    __syncthreads();   // the tiles, the wave states and the list's first unit are reused next
   }
+  if (tid == 0) s_loc64[0] += (uint64_t)(nb + K0);
   off = 0;
   if (++h == L.H) {   // the next list with steps (a sequence of invalid length has none)
     h = 0;
     do { ++b; } while (!(d.seq_lens[b] >= 1 && d.seq_lens[b] <= L.S_cap));
   }
   }
-  // The merge descriptor of this workgroup, written by one thread of the last wave once its work
-  // is done (no other wave waits for it): a list whose first step lies in an earlier
-  // workgroup's range and whose last lies in this one is merged after the decode by the merge's
-  // block of this workgroup; every workgroup writes its entry.  From the setup: the range's
-  // first list (sequence s_loc[0], head s_loc[1]), its sequence's first unit and units per list,
-  // U and the range.
-  if (tid == kT - 64) {
-    const uint64_t lo = s_loc64[0], m = s_loc64[1], UU = s_loc64[2], ub0 = s_loc64[3], ue0 = s_loc64[4];
-    const uint64_t hh = udivq(ub0 - lo, m), off0 = (ub0 - lo) - hh * m, n = m - K0;
-    const uint64_t pl = lo + hh * m;                       // the list's first unit
-    int4 c = make_int4(-1, 0, 0, 0);
-    if (off0 > (uint64_t)K0a && off0 < K0a + n && ue0 >= pl + K0a + n) {
-      const uint64_t u0 = pl + K0a;                        // the unit of its first step
-      const uint64_t i0 = udivq((u0 + 1) * nwg - 1, UU);   // the workgroup that holds it
-      // its first piece is this list (slot 0) unless its range holds steps of an earlier list
-      c = make_int4(s_loc[0], (int)hh, (int)i0, udivq(i0 * UU, nwg) + K0b >= pl ? 0 : 1);
-    }
-    int4* const e = cut_of(d, blockIdx.x);
-    e[0] = c;
-    e[1] = make_int4((int)(uint32_t)UU, (int)(uint32_t)(UU >> 32), 0, 0);
-  }
-}
-
-// Lists cut between workgroups.  The list ending in workgroup i1's range that started in an
-// earlier one (the decode's descriptor of i1) is merged by block i1 from the partials of
-// workgroups i0 .. i1: out = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i with M = max_i m_i
-// (and with page masses the total log2-sum-exp M + log2 sum_i 2^(m_i - M) l_i).  Workgroup i0
-// holds the list's start in its first piece (slot 0) if its range starts there, else in its
-// last (slot 1); every later one holds a part in its first piece.  Workgroups with empty ranges
-// (more workgroups than steps) hold nothing and are skipped.  Each thread folds the parts of one
-// (query row, channel) in workgroup order, loading a batch of 16 parts (always at valid addresses)
-// before folding them: deterministic, and one memory round trip per batch.
-constexpr int kMergeThreads = 1024;
-constexpr int kMergeBatch = 16;
-__global__ void __launch_bounds__(kMergeThreads) streamk_merge_kernel(DecodeLaunch d) {
-  const int i1 = blockIdx.x;
-  const int4* const e = cut_of(d, i1);
-  const int4 c = e[0];
-  if (c.x < 0) return;
-  const int4 cu = e[1];
-  const uint64_t U = (uint64_t)(uint32_t)cu.x | ((uint64_t)(uint32_t)cu.y << 32);
-  const uint64_t N = (uint64_t)d.nwg;
-  const bool may_be_empty = U < N;
-  const int b = c.x, h = c.y, i0 = c.z, slot0 = c.w;
-  const int G = d.Hq / d.L.H;
-  for (int p = threadIdx.x; p < G * kHeadDim; p += kMergeThreads) {
-    const int row = p / kHeadDim, ch = p % kHeadDim;
-    float M = -INFINITY, den = 0.0f, num = 0.0f;
-    for (int ib = i0; ib <= i1; ib += kMergeBatch) {
-      float m[kMergeBatch], l[kMergeBatch], o[kMergeBatch];
-      bool use[kMergeBatch];
+  // ---- the parts of cut lists: stored (coherently) by the pieces above; the last workgroup to
+  // finish a part of a list merges it
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_waitcnt(0);   // this workgroup's partial stores have completed
+  __syncthreads();
 #pragma unroll
-      for (int k = 0; k < kMergeBatch; ++k) {
-        const int i = ib + k;
-        use[k] = i <= i1 && !(may_be_empty && i > i0 && (uint64_t)i * U / N == (uint64_t)(i + 1) * U / N);
-        const size_t slot = use[k] ? (size_t)i * 2 + (i == i0 ? slot0 : 0) : (size_t)i0 * 2 + slot0;
-        const float* q = d.partials + (slot * G + row) * (kHeadDim + 2);
-        m[k] = q[0];
-        l[k] = q[1];
-        o[k] = q[2 + ch];
-      }
-#pragma unroll
-      for (int k = 0; k < kMergeBatch; ++k) {
-        if (!use[k]) continue;
-        const float Mn = fmaxf(M, m[k]);                     // a part holding tokens: m finite
-        const float al = exp2f(M - Mn), w = exp2f(m[k] - Mn);   // al = 0 while M is -inf
-        den = fmaf(w, l[k], den * al);
-        num = fmaf(w, o[k], num * al);
-        M = Mn;
-      }
-    }
-    const int hq = h * G + row;
-    d.out[((size_t)b * d.Hq + hq) * kHeadDim + ch] = num / den;
-    if (d.total_lse && ch == 0) d.total_lse[(size_t)b * d.Hq + hq] = M + __builtin_log2f(den);
+  for (int sl = 0; sl < 2; ++sl) {
+    if (s_cut[sl][0] >= 0)
+      merge_cut_list<MASS>(d, s_cut[sl][0], s_cut[sl][1], s_cut[sl][2], s_cut64[sl], K0a, K0b, s_loc64, s_mg);
+    __syncthreads();   // s_mg is written again
   }
 }
 
@@ -1283,9 +1306,6 @@ hipError_t launch_decode_mfma(const DecodeLaunch& d, hipStream_t st, bool* handl
   else if (d.fmt == FMT_C2) launch_fmt<FMT_C2, false>(d, grid, st);
   else launch_fmt<FMT_FP4, false>(d, grid, st);
   *handled = true;
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  streamk_merge_kernel<<<dim3(d.nwg), kMergeThreads, 0, st>>>(d);
   return hipGetLastError();
 }
 

@@ -4,6 +4,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <mutex>
 
 #include "kvq_device.h"
@@ -199,6 +200,16 @@ int32_t scratch_ptr(void** out) {
   return KVQ_OK;
 }
 
+// A nonzero number that differs from call to call (it wraps after 2^32 - 1 calls): it tags the
+// arrival counts that the MFMA decoder leaves in the workspace, so that counts of earlier calls
+// (or any other content) read as zero and the workspace needs no clearing.
+uint32_t next_nonce() {
+  static std::atomic<uint32_t> counter{0};
+  uint32_t n;
+  do { n = counter.fetch_add(1, std::memory_order_relaxed) + 1; } while (n == 0);
+  return n;
+}
+
 // Validation and launches of a decode.  workspace == nullptr with use_scratch: the split-K
 // partials go to this device's scratch array (kvq_decode_attention_noalloc).
 int32_t decode_impl(const kvq_params* pin, const kvq_cache* cache, const void* q_bf16,
@@ -246,6 +257,7 @@ int32_t decode_impl(const kvq_params* pin, const kvq_cache* cache, const void* q
   d.n_chunks = (p->max_seq_len + chunk - 1) / chunk;
   d.partials = need ? (float*)workspace : nullptr;
   d.nwg = (int)decode_wgs(p, split_chunk);
+  d.nonce = next_nonce();
   d.page_lse = nullptr;
   d.total_lse = nullptr;
   if (page_mass) {

@@ -43,6 +43,8 @@ struct DecodeLaunch {
   int n_chunks;               // ceil(S_cap / chunk)
   float scale_log2;           // sm_scale * log2(e)
   int nwg;                    // MFMA decoder: workgroups sharing the steps of all lists
+  uint32_t nonce;             // MFMA decoder: nonzero, different for every call (tags the arrival
+                              // counts of cut lists in the workspace)
 };
 
 // The MFMA decoder takes 2-bit caches and FP4 caches with groups of 32 (contiguous), and paged

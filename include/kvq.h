@@ -204,9 +204,11 @@ int32_t kvq_quantize_append(const kvq_params* p, const kvq_cache* cache, const f
  * whose rows need byte offsets of 2^32 or more take the generic decoder): N workgroups share the
  * 32-token steps of all (sequence, KV head) lists, each a contiguous range in (sequence, head,
  * token) order, the ranges even in a weight of one per step plus a fixed cost per list (so that
- * ranges over many short lists take fewer steps).  A list cut between workgroups is merged
- * afterwards by log-sum-exp from two (max, sum, output) slots per workgroup, N * 2 * (Hq / H) *
- * (D + 2) floats, followed by 32 bytes per workgroup naming the cut list that ends in its range:
+ * ranges over many short lists take fewer steps).  A list cut between workgroups is merged by
+ * log-sum-exp by the last workgroup to finish a part of it, from two (max, sum, output) slots per
+ * workgroup, N * 2 * (Hq / H) * (D + 2) floats, followed by 32 bytes per workgroup whose first 8
+ * count the finished parts of the cut list ending in its range, tagged with the call (so the
+ * workspace needs no clearing; calls that share a workspace must not overlap):
  * N * (8 * (Hq / H) * (D + 2) + 32) bytes.  split_chunk 0: N = min(256, ceil(B * H *
  * ceil(max_seq_len / 32) / 12)) (one workgroup per CU of an MI355X, at least 12 steps each);
  * split_chunk > 0: N = min(B * H * ceil(max_seq_len / 32), 16384, ceil(B * H * max_seq_len /
