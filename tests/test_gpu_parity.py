@@ -120,6 +120,37 @@ def test_decode_deterministic(small):
     assert np.array_equal(a, b)
 
 
+@pytest.mark.parametrize("name", ["c2_small", "fp4_small", "tiered_small"])
+def test_decode_workspace_contents_do_not_matter(name):
+    """Lists cut between workgroups are merged by the last workgroup to finish a part, counted on
+    arrival words in the workspace that carry a per-call tag: whatever the workspace holds
+    (random bytes, or the words of earlier calls with another split), the result is the same,
+    bit for bit."""
+    import decode_attention_sub_amd as K
+    w = SMALL[name]
+    dc = WD.build(w)
+    p = dc.params
+    ref = run_decode(dc, split_chunk=256)
+    nbytes = max(K.kvq_workspace_bytes(p, s) for s in (0, 128, 256))
+    work = torch.empty(nbytes // 4 + 1, dtype=torch.int32, device="cuda")
+    gen = torch.Generator(device="cuda").manual_seed(7)
+
+    def decode(split):
+        out = torch.full((w.B, w.Hq, w.D), float("nan"), dtype=torch.float32, device="cuda")
+        K.kvq_decode_attention(p, dc.cache, dc.q, dc.seq_lens, out, work, dc.block_table,
+                               split_chunk=split)
+        torch.cuda.synchronize()
+        return out.cpu().numpy()
+
+    work.random_(generator=gen)                      # random bytes
+    assert np.array_equal(decode(256), ref)
+    assert np.array_equal(decode(256), ref)          # the words of the call before
+    decode(128)                                      # other splits leave other words
+    decode(0)
+    assert np.array_equal(decode(256), ref)
+    assert dc.cache.status() == 0
+
+
 def test_bulk_equals_incremental():
     """Appending S tokens in one call equals S one-token appends, bit for bit."""
     import decode_attention_sub_amd as K
