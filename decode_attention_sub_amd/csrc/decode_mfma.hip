@@ -847,13 +847,6 @@ __global__ void __launch_bounds__(kWaves * 64) decode_mfma_kernel(DecodeLaunch d
     // start at power-of-two-aligned offsets, and walking them in lockstep would send every
     // workgroup to the same HBM channels at the same time.
     const int rot = nfull > 0 ? (int)(((uint64_t)blockIdx.x * (uint64_t)nfull) / nwg) : 0;
-    // token start of full step number c (c >= nfull: past the piece, every load reads zeros)
-    auto step_ts = [&](int c) {
-      if (c >= nfull) return t1 + 2 * kStep;
-      int a = c + rot;
-      if (a >= nfull) a -= nfull;
-      return t0 + kStep * a;
-    };
     // RAGGED: the step may hold tokens >= t1 (only the list's last step); the buffer ranges end
     // at row t1, so those rows read as zeros
     auto issue_codes = [&](Buf<FMT>& bf, int tsi) {
@@ -908,24 +901,37 @@ __global__ void __launch_bounds__(kWaves * 64) decode_mfma_kernel(DecodeLaunch d
         rc.v = rc.k;
       }
     };
-    // ---- software pipeline: codes and records of the next kPF steps in flight, the record
-    // bounds of the step after them too.  Wave wi takes its full steps wi, wi + wpc,
-    // ...; whole groups of NB steps run without conditions, so every ring slot keeps its
-    // registers and the wait counters stay exact.  Loads for steps past the piece return zeros
-    // without touching memory.
+    // ---- software pipeline: codes and records of the next step in flight, the record bounds of
+    // the step after it too.  Wave wi takes its full steps wi, wi + wpc, ... of the rotated
+    // order; whole groups of NB steps run without conditions, so every ring slot keeps its
+    // registers and the wait counters stay exact.  The token starts of the three steps in
+    // flight are kept in scalar registers and advanced by one step each time (position a of the
+    // next step in the rotated order, modulo nfull); steps past the wave's share start past the
+    // piece (every load reads zeros without touching memory).
+    static_assert(kPF == 1 && NB == 2, "the walk keeps three steps in flight");
     Buf<FMT> buf[NB];
     Recs rec[NB];
     uint32_t bnd[NB];
     const int nmine = wi < nfull ? (nfull - wi + wpc - 1) / wpc : 0;
-    auto wts = [&](int j) { return step_ts(j < nmine ? wi + wpc * j : nfull); };
+    const int tpast = t1 + 2 * kStep;
+    int jn = 0;                                  // the wave's next step to start
+    int an = wi + rot;                           // its position in the piece's full steps
+    if (an >= nfull) an -= nfull;
+    auto next_ts = [&]() {   // (selects, no branches; an is used only while jn < nmine, and
+      // wpc >= nfull only when the wave has a single step)
+      const int ts = jn < nmine ? t0 + kStep * an : tpast;
+      an += wpc;
+      an = an >= nfull ? an - nfull : an;
+      ++jn;
+      return ts;
+    };
+    int tsA = next_ts();   // the step consumed next
+    int tsB = next_ts();   // the step whose codes and records are in flight
     int partner_seen = 0;
-#pragma unroll
-    for (int k = 0; k < NB; ++k) bnd[k] = issue_bounds(wts(k));
-#pragma unroll
-    for (int k = 0; k < kPF; ++k) {
-      issue_recs(rec[k], bnd[k], wts(k));
-      issue_codes(buf[k], wts(k));
-    }
+    bnd[0] = issue_bounds(tsA);
+    bnd[1] = issue_bounds(tsB);
+    issue_recs(rec[0], bnd[0], tsA);
+    issue_codes(buf[0], tsA);
     const int ngroups = nmine / NB;
     for (int g = 0; g < ngroups; ++g) {
       if (g > partner_seen) __builtin_amdgcn_s_setprio(0);
@@ -933,26 +939,21 @@ __global__ void __launch_bounds__(kWaves * 64) decode_mfma_kernel(DecodeLaunch d
       if (lane == 0) *prog_mine = g;
 #pragma unroll
       for (int u = 0; u < NB; ++u) {
-        const int jj = g * NB + u;
-        bnd[u] = issue_bounds(wts(jj + NB));
-        issue_recs(rec[(u + kPF) % NB], bnd[(u + kPF) % NB], wts(jj + kPF));
-        issue_codes(buf[(u + kPF) % NB], wts(jj + kPF));
-        const uint32_t base = (uint32_t)wts(jj) * 128u;
+        const int tsC = next_ts();
+        bnd[u] = issue_bounds(tsC);
+        issue_recs(rec[1 - u], bnd[1 - u], tsB);
+        issue_codes(buf[1 - u], tsB);
+        const uint32_t base = (uint32_t)tsA * 128u;
         consume(buf[u], no8, rec[u], base, base, kStep, 0, 0, std::true_type{}, std::false_type{});
+        tsA = tsB;
+        tsB = tsC;
       }
       partner_seen = min(__builtin_amdgcn_readfirstlane(*prog_p1), __builtin_amdgcn_readfirstlane(*prog_p2));
     }
     __builtin_amdgcn_s_setprio(0);
-#pragma unroll
-    for (int u = 0; u < NB; ++u) {
-      const int jj = ngroups * NB + u;
-      if (jj < nmine) {
-        bnd[u] = issue_bounds(wts(jj + NB));
-        issue_recs(rec[(u + kPF) % NB], bnd[(u + kPF) % NB], wts(jj + kPF));
-        issue_codes(buf[(u + kPF) % NB], wts(jj + kPF));
-        const uint32_t base = (uint32_t)wts(jj) * 128u;
-        consume(buf[u], no8, rec[u], base, base, kStep, 0, 0, std::true_type{}, std::false_type{});
-      }
+    if (nmine % NB != 0) {   // the wave's odd last step (ring slot 0; nothing follows it)
+      const uint32_t base = (uint32_t)tsA * 128u;
+      consume(buf[0], no8, rec[0], base, base, kStep, 0, 0, std::true_type{}, std::false_type{});
     }
     if (ragged && wi == 0) {
       const int ts = t0 + kStep * (nsteps - 1);
