@@ -901,17 +901,17 @@ __global__ void __launch_bounds__(kWaves * 64) decode_mfma_kernel(DecodeLaunch d
         rc.v = rc.k;
       }
     };
-    // ---- software pipeline: codes and records of the next step in flight, the record bounds of
-    // the step after it too.  Wave wi takes its full steps wi, wi + wpc, ... of the rotated
-    // order; whole groups of NB steps run without conditions, so every ring slot keeps its
-    // registers and the wait counters stay exact.  The token starts of the three steps in
-    // flight are kept in scalar registers and advanced by one step each time (position a of the
-    // next step in the rotated order, modulo nfull); steps past the wave's share start past the
-    // piece (every load reads zeros without touching memory).
-    static_assert(kPF == 1 && NB == 2, "the walk keeps three steps in flight");
+    // ---- software pipeline: codes and records of the next kPF steps in flight, the record
+    // bounds of the step after them too.  Wave wi takes its full steps wi, wi + wpc, ... of the
+    // rotated order; whole groups of NB steps run without conditions, so every ring slot keeps
+    // its registers and the wait counters stay exact.  Ring slot u holds the step that is
+    // consumed at its turn; its token start is then replaced by the one of the step NB later
+    // (position an of the wave's next step in the rotated order, advanced modulo nfull).  Steps
+    // past the wave's share start past the piece: every load reads zeros without touching memory.
     Buf<FMT> buf[NB];
     Recs rec[NB];
     uint32_t bnd[NB];
+    int tsr[NB];
     const int nmine = wi < nfull ? (nfull - wi + wpc - 1) / wpc : 0;
     const int tpast = t1 + 2 * kStep;
     int jn = 0;                                  // the wave's next step to start
@@ -925,36 +925,39 @@ __global__ void __launch_bounds__(kWaves * 64) decode_mfma_kernel(DecodeLaunch d
       ++jn;
       return ts;
     };
-    int tsA = next_ts();   // the step consumed next
-    int tsB = next_ts();   // the step whose codes and records are in flight
     int partner_seen = 0;
-    bnd[0] = issue_bounds(tsA);
-    bnd[1] = issue_bounds(tsB);
-    issue_recs(rec[0], bnd[0], tsA);
-    issue_codes(buf[0], tsA);
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      tsr[k] = next_ts();
+      bnd[k] = issue_bounds(tsr[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < kPF; ++k) {
+      issue_recs(rec[k], bnd[k], tsr[k]);
+      issue_codes(buf[k], tsr[k]);
+    }
+    auto walk_step = [&](int u) {
+      const uint32_t base = (uint32_t)tsr[u] * 128u;
+      tsr[u] = next_ts();
+      bnd[u] = issue_bounds(tsr[u]);
+      const int up = (u + kPF) % NB;
+      issue_recs(rec[up], bnd[up], tsr[up]);
+      issue_codes(buf[up], tsr[up]);
+      consume(buf[u], no8, rec[u], base, base, kStep, 0, 0, std::true_type{}, std::false_type{});
+    };
     const int ngroups = nmine / NB;
     for (int g = 0; g < ngroups; ++g) {
       if (g > partner_seen) __builtin_amdgcn_s_setprio(0);
       else __builtin_amdgcn_s_setprio(1);
       if (lane == 0) *prog_mine = g;
 #pragma unroll
-      for (int u = 0; u < NB; ++u) {
-        const int tsC = next_ts();
-        bnd[u] = issue_bounds(tsC);
-        issue_recs(rec[1 - u], bnd[1 - u], tsB);
-        issue_codes(buf[1 - u], tsB);
-        const uint32_t base = (uint32_t)tsA * 128u;
-        consume(buf[u], no8, rec[u], base, base, kStep, 0, 0, std::true_type{}, std::false_type{});
-        tsA = tsB;
-        tsB = tsC;
-      }
+      for (int u = 0; u < NB; ++u) walk_step(u);
       partner_seen = min(__builtin_amdgcn_readfirstlane(*prog_p1), __builtin_amdgcn_readfirstlane(*prog_p2));
     }
     __builtin_amdgcn_s_setprio(0);
-    if (nmine % NB != 0) {   // the wave's odd last step (ring slot 0; nothing follows it)
-      const uint32_t base = (uint32_t)tsA * 128u;
-      consume(buf[0], no8, rec[0], base, base, kStep, 0, 0, std::true_type{}, std::false_type{});
-    }
+#pragma unroll
+    for (int u = 0; u < NB - 1; ++u)   // the wave's last nmine % NB steps
+      if (ngroups * NB + u < nmine) walk_step(u);
     if (ragged && wi == 0) {
       const int ts = t0 + kStep * (nsteps - 1);
       const uint32_t b0 = issue_bounds(ts);
