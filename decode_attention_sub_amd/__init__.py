@@ -25,7 +25,8 @@ FMT = {"fp16": 0, "fp8row": 1, "int4": 2, "fp4": 3, "c2": 4, "bf16": 5, "u2": 6,
 OUTL = {"none": 0, "fp16": 1, "e4m3": 2}
 
 EXPORTED = ("kvq_kv_bytes", "kvq_cache_sizes", "kvq_quantize_append", "kvq_workspace_bytes",
-            "kvq_decode_attention", "kvq_decode_attention_noalloc", "kvq_mass_workspace_bytes",
+            "kvq_decode_attention", "kvq_decode_attention_noalloc", "kvq_append_decode",
+            "kvq_mass_workspace_bytes",
             "kvq_decode_attention_mass", "kvq_retier_workspace_bytes", "kvq_retier",
             "kvq_prologue_workspace_bytes", "kvq_prologue_pack_weights", "kvq_attention_prologue",
             "kvq_probe_read", "kvq_probe_copy", "kvq_status_string")
@@ -74,6 +75,8 @@ def _load():
                                              C.c_uint64, vp]),
         "kvq_decode_attention_noalloc": (C.c_int32, [P, Pc, vp, vp, vp, C.c_float, C.c_int32,
                                                      vp, vp]),
+        "kvq_append_decode": (C.c_int32, [P, Pc, vp, vp, vp, vp, C.c_float, C.c_int32, vp, vp,
+                                          C.c_uint64, vp]),
         "kvq_mass_workspace_bytes": (C.c_int32, [P, C.c_int32, C.POINTER(C.c_uint64)]),
         "kvq_decode_attention_mass": (C.c_int32, [P, Pc, vp, vp, vp, C.c_float, C.c_int32, vp, vp,
                                                   vp, C.c_uint64, vp]),
@@ -217,6 +220,20 @@ def kvq_decode_attention(p: kvq_params, cache: KVCache, q_bf16, seq_lens, out, w
                                      _ptr(seq_lens), _ptr(block_table), sm_scale, split_chunk,
                                      _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)),
            "kvq_decode_attention")
+
+
+def kvq_append_decode(p: kvq_params, cache: KVCache, k_new, v_new, q_bf16, seq_lens, out,
+                      workspace=None, sm_scale: Optional[float] = None, split_chunk: int = 0,
+                      stream=None):
+    """One decode step with the append fused: k_new, v_new float32 [B, H, D] (device) are
+    appended at token seq_lens[b] - 1, then attention over seq_lens as kvq_decode_attention."""
+    if sm_scale is None:
+        sm_scale = math.nan
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.kvq_append_decode(C.byref(p), C.byref(cache.struct), _ptr(k_new), _ptr(v_new),
+                                  _ptr(q_bf16), _ptr(seq_lens), sm_scale, split_chunk, _ptr(out),
+                                  _ptr(workspace), ws_bytes, _stream(stream)),
+           "kvq_append_decode")
 
 
 def kvq_decode_attention_noalloc(p: kvq_params, cache: KVCache, q_bf16, seq_lens, out,

@@ -211,11 +211,13 @@ uint32_t next_nonce() {
 }
 
 // Validation and launches of a decode.  workspace == nullptr with use_scratch: the split-K
-// partials go to this device's scratch array (kvq_decode_attention_noalloc).
+// partials go to this device's scratch array (kvq_decode_attention_noalloc).  k_new / v_new
+// (kvq_append_decode): the decode also appends each sequence's last token.
 int32_t decode_impl(const kvq_params* pin, const kvq_cache* cache, const void* q_bf16,
                     const int32_t* seq_lens, const int32_t* block_table, float sm_scale,
                     int32_t split_chunk, float* out, void* workspace, uint64_t ws_bytes,
-                    bool use_scratch, void* stream, float* page_mass = nullptr) {
+                    bool use_scratch, void* stream, float* page_mass = nullptr,
+                    const float* k_new = nullptr, const float* v_new = nullptr) {
   int32_t st = check_params(pin);
   if (st) return st;
   const Params n(pin);
@@ -225,6 +227,8 @@ int32_t decode_impl(const kvq_params* pin, const kvq_cache* cache, const void* q
   if (isnan(sm_scale)) sm_scale = 1.0f / sqrtf((float)p->head_dim);   // the default scale
   if (!q_bf16 || !seq_lens || !out || !isfinite(sm_scale)) return KVQ_ERR_INVALID_ARG;
   if (p->page_size && !block_table) return KVQ_ERR_INVALID_ARG;
+  if ((k_new != nullptr) != (v_new != nullptr)) return KVQ_ERR_INVALID_ARG;
+  if (k_new && (p->page_size || !mfma_format(p))) return KVQ_ERR_UNSUPPORTED;
   const int chunk = resolve_chunk(p, split_chunk);
   if (chunk < 0) return KVQ_ERR_INVALID_ARG;
   uint64_t need = 0;
@@ -265,6 +269,11 @@ int32_t decode_impl(const kvq_params* pin, const kvq_cache* cache, const void* q
     d.total_lse = d.page_lse + (size_t)p->batch * p->num_q_heads * p->max_pages_per_seq;
   }
   d.scale_log2 = sm_scale * 1.4426950408889634f;
+  d.k_new = k_new;
+  d.v_new = v_new;
+  d.tau2 = p->outlier_sigma * p->outlier_sigma;
+  d.fit = n.fit;
+  d.lloyd = p->lloyd_iters;
   hipStream_t s = (hipStream_t)stream;
   bool handled = false;
   if (launch_decode_mfma(d, s, &handled) != hipSuccess) return KVQ_ERR_HIP;
@@ -404,6 +413,15 @@ int32_t kvq_decode_attention_noalloc(const kvq_params* pin, const kvq_cache* cac
                                      int32_t split_chunk, float* out, void* stream) {
   return decode_impl(pin, cache, q_bf16, seq_lens, block_table, sm_scale, split_chunk, out,
                      nullptr, 0, true, stream);
+}
+
+int32_t kvq_append_decode(const kvq_params* pin, const kvq_cache* cache, const float* k_new,
+                          const float* v_new, const void* q_bf16, const int32_t* seq_lens,
+                          float sm_scale, int32_t split_chunk, float* out, void* workspace,
+                          uint64_t ws_bytes, void* stream) {
+  if (!k_new || !v_new) return KVQ_ERR_INVALID_ARG;
+  return decode_impl(pin, cache, q_bf16, seq_lens, nullptr, sm_scale, split_chunk, out, workspace,
+                     ws_bytes, false, stream, nullptr, k_new, v_new);
 }
 
 int32_t kvq_mass_workspace_bytes(const kvq_params* pin, int32_t split_chunk, uint64_t* out_bytes) {

@@ -45,6 +45,13 @@ struct DecodeLaunch {
   int nwg;                    // MFMA decoder: workgroups sharing the steps of all lists
   uint32_t nonce;             // MFMA decoder: nonzero, different for every call (tags the arrival
                               // counts of cut lists in the workspace)
+  // fused append (contiguous MFMA caches; k_new null otherwise): the row of token seq_lens[b] - 1
+  // of every list, float32 [B][H][D] each, is quantized into the cache by the decode
+  const float* k_new;
+  const float* v_new;
+  float tau2;                 // fl32(tau * tau)
+  int fit;                    // kFitDefault or the variant fit of the storage format
+  int lloyd;
 };
 
 // The MFMA decoder takes 2-bit caches and FP4 caches with groups of 32 (contiguous), and paged

@@ -369,5 +369,166 @@ __device__ __forceinline__ uint32_t pack_word(const uint8_t* code, int w, int bi
   return out;
 }
 
+// ---------------------------------------------------------------- appending a row to a list
+// The helpers below take any launch descriptor `a` with the fields L (Layout), cache
+// (kvq_cache), block_table, outl, tau2, fit and lloyd.
+
+// LDS staging of the rows quantized together (NS row slots of 32 lanes)
+template <int NS>
+struct RowStage {
+  uint8_t code[NS][kHeadDim];
+  uint8_t flag[NS][kHeadDim];
+  float x[NS][kHeadDim];
+  uint32_t meta[NS][8];
+};
+
+// The records of list (b, h, kv) of tokens < t: those before t's 16-token block plus those of
+// the block's rows before t (a block holds at most 16 rows of D records, and the list is sorted,
+// so each of the n lanes stops at its first record of a token >= t); the lanes' counts are
+// summed over the n-lane group (n a power of two, aligned in the wave).
+template <int N, class A>
+__device__ int64_t records_before(const A& a, int b, int h, int kv, int t, int lane) {
+  const Layout& Lo = a.L;
+  int64_t start = 0;
+  int cnt = 0;
+  if (t > 0) {
+    const size_t lid = list_id(Lo, b, h, kv);
+    const uint32_t* oidx = a.cache.outl_idx[kv] + ((size_t)b * Lo.H + h) * (size_t)Lo.outl_cap;
+    start = max((int64_t)0, min((int64_t)a.cache.outl_block_start[lid * (size_t)Lo.nblk + ((t - 1) >> 4)],
+                                Lo.outl_cap));
+    const int64_t old = max((int64_t)0, min((int64_t)a.cache.outl_count[lid], Lo.outl_cap));
+    const int64_t lim = min(old, start + (int64_t)kBlock * kHeadDim);
+    for (int64_t r = start + lane; r < lim; r += N) {
+      if (oidx[r] >= (uint32_t)t * kHeadDim) break;
+      ++cnt;
+    }
+  }
+#pragma unroll
+  for (int o = N / 2; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o, N);
+  return start + cnt;
+}
+
+// Appends one token's row (32 lanes of one slot; lane = gi * (G / 4) + jg holds channels
+// gi * G + jg + (G / 4) e) to list (b, h, kv) at token t, after the `running` records of tokens
+// < t (the list is cut back to them): the row is quantized (FP8 tier or outlier isolation + fit),
+// its codes and metadata are written to its row slot and its outlier records appended in channel
+// order.  sync() orders the staging's LDS accesses between the lanes that call this together
+// (a workgroup barrier when the slots span waves; a wave fence when they share one wave): every
+// lane of those calls it once per round, and the staging is free again on return.  `valid` false:
+// the slot has no row this round.  Returns the list's record count after the row.
+template <int FMT, int G, class A, int NS, class Sync>
+__device__ int64_t append_row(const A& a, bool valid, int b, int h, int kv, int t, int64_t running,
+                              const float x[4], int lane, int slot, RowStage<NS>& st, Sync sync) {
+  constexpr int L = G / 4;
+  constexpr int CB = kHeadDim * code_bits(FMT) / 8;
+  const Layout& Lo = a.L;
+  const int gi = lane / L, jg = lane % L;
+  if (valid && t >= Lo.S_cap) {
+    if (lane == 0) report(a.cache.status, KVQ_ERR_INVALID_ARG);
+    valid = false;
+  }
+  const size_t lid = list_id(Lo, b, h, kv);
+  int32_t* bstart = a.cache.outl_block_start + lid * (size_t)Lo.nblk;
+  uint32_t* oidx = a.cache.outl_idx[kv] + ((size_t)b * Lo.H + h) * (size_t)Lo.outl_cap;
+  uint8_t* oval = (uint8_t*)a.cache.outl_val[kv] +
+                  ((size_t)b * Lo.H + h) * (size_t)Lo.outl_cap * (a.outl == KVQ_OUTL_FP16 ? 2 : 1);
+
+  int tier1 = 0;
+  size_t pslot = 0;
+  bool row_ok = valid;
+  if (Lo.paged && valid) {
+    row_ok = page_slot(Lo, a.block_table, b, t, &tier1, &pslot);
+    if (!row_ok && lane == 0) report(a.cache.status, KVQ_ERR_INVALID_ARG);
+  }
+  RowOut o;
+  quantize_row<FMT, G>(x, tier1, a.cache.chan_mask, a.outl, a.tau2, a.fit, a.lloyd, kv, h, Lo.H, gi,
+                       jg, o);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int c = gi * G + jg + L * e;
+    st.code[slot][c] = (uint8_t)o.code[e];
+    st.flag[slot][c] = valid ? (uint8_t)o.flag[e] : 0;
+    st.x[slot][c] = x[e];
+  }
+  if (tier1) {
+    if (lane == 0) st.meta[slot][0] = o.meta[0];
+  } else if (jg == 0) {
+    constexpr int MB = meta_bytes_per_group(FMT);
+    if constexpr (MB == 8) { st.meta[slot][2 * gi] = o.meta[0]; st.meta[slot][2 * gi + 1] = o.meta[1]; }
+    else if constexpr (MB == 4) { st.meta[slot][gi] = o.meta[0]; }
+    else { ((uint8_t*)st.meta[slot])[gi] = (uint8_t)o.meta[0]; }
+  }
+  sync();
+
+  if (row_ok) {
+    uint8_t* codes_dst;
+    uint8_t* meta_dst;
+    int cb, mb;
+    if (!Lo.paged) {
+      const size_t row = ((size_t)b * Lo.H + h) * (size_t)Lo.S_cap + (size_t)t;
+      codes_dst = (uint8_t*)a.cache.codes[kv] + row * CB;
+      meta_dst = (uint8_t*)a.cache.meta[kv] + row * Lo.meta_bytes;
+      cb = CB; mb = Lo.meta_bytes;
+    } else {
+      const size_t prow = (pslot * Lo.H + h) * kBlock + (t & 15);
+      if (tier1) {
+        codes_dst = (uint8_t*)a.cache.codes8[kv] + prow * kHeadDim;
+        meta_dst = (uint8_t*)(a.cache.scale8[kv] + prow);
+        cb = kHeadDim; mb = 4;
+      } else {
+        codes_dst = (uint8_t*)a.cache.codes[kv] + prow * CB;
+        meta_dst = (uint8_t*)a.cache.meta[kv] + prow * Lo.meta_bytes;
+        cb = CB; mb = Lo.meta_bytes;
+      }
+    }
+    const int bits = tier1 ? 8 : code_bits(FMT);
+    if (lane < cb / 4) ((uint32_t*)codes_dst)[lane] = pack_word(st.code[slot], lane, bits);
+    if (lane < mb / 4) ((uint32_t*)meta_dst)[lane] = st.meta[slot][lane];
+    else if (mb < 4 && lane == 0) {
+      for (int k = 0; k < mb; ++k) meta_dst[k] = ((uint8_t*)st.meta[slot])[k];
+    }
+  }
+
+  // the row's outlier records in channel order: channels 4 lane .. 4 lane + 3
+  uint32_t fl = 0;
+  int cnt = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t f = st.flag[slot][4 * lane + k];
+    fl |= f << k;
+    cnt += (int)f;
+  }
+  int incl = cnt;
+#pragma unroll
+  for (int dd = 1; dd < kRowLanes; dd <<= 1) {
+    const int y = __shfl_up(incl, dd, kRowLanes);
+    if (lane >= dd) incl += y;
+  }
+  const int total = __shfl(incl, kRowLanes - 1, kRowLanes);
+  const int64_t count = min(running + total, Lo.outl_cap);
+  if (valid) {
+    if ((t & 15) == 0 && lane == 0) bstart[t >> 4] = (int32_t)min(running, (int64_t)INT32_MAX);
+    int64_t k = running + (incl - cnt);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if ((fl >> q) & 1u) {
+        const int c = 4 * lane + q;
+        if (k < Lo.outl_cap) {
+          oidx[k] = (uint32_t)t * kHeadDim + (uint32_t)c;
+          const float xv = st.x[slot][c];
+          if (a.outl == KVQ_OUTL_FP16) ((uint16_t*)oval)[k] = (uint16_t)f32_to_half_bits(xv);
+          else oval[k] = (uint8_t)f32_to_e4m3(xv);
+        } else {
+          report(a.cache.status, KVQ_ERR_CAPACITY);
+        }
+        ++k;
+      }
+    }
+    if (lane == 0) a.cache.outl_count[lid] = (int32_t)count;
+  }
+  sync();   // the staging is reused by the next round
+  return count;
+}
+
 }  // namespace
 }  // namespace kvq

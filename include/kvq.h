@@ -239,6 +239,24 @@ int32_t kvq_decode_attention(const kvq_params* p, const kvq_cache* cache, const 
                              float sm_scale, int32_t split_chunk, float* out, void* workspace,
                              uint64_t ws_bytes, void* stream);
 
+/* One decode step with the quantize-on-append fused into the decode ("Sub-5ms MoE Inference
+ * ...", section "Engineering Real-Time Autonomous Workflows", item 1: the KV-cache write fused
+ * with the attention step): the same result as kvq_quantize_append of one token per sequence at
+ * position seq_lens[b] - 1 (positions = seq_lens - 1, counts = 1, max_new = 1) followed by
+ * kvq_decode_attention over seq_lens, in one launch.  The cache bytes it writes (codes,
+ * metadata, outlier records, block starts, counts) are those of that append; the attention
+ * output is that decode's within its floating-point rounding (the new token's contribution is
+ * computed from the row it stores).  k_new, v_new: device float32 [B][H][D], the new token of
+ * every (sequence, KV head); q_bf16, seq_lens, sm_scale, split_chunk, out, workspace, ws_bytes
+ * as for kvq_decode_attention (same workspace size).  A sequence whose length is out of range
+ * sets *status to KVQ_ERR_INVALID_ARG; nothing is appended to it and its out[b] is left
+ * unwritten.  Contiguous caches of the MFMA decoder's formats (2-bit, FP4 with groups of 32)
+ * only: any other cache returns KVQ_ERR_UNSUPPORTED and launches nothing (use the two calls). */
+int32_t kvq_append_decode(const kvq_params* p, const kvq_cache* cache, const float* k_new,
+                          const float* v_new, const void* q_bf16, const int32_t* seq_lens,
+                          float sm_scale, int32_t split_chunk, float* out, void* workspace,
+                          uint64_t ws_bytes, void* stream);
+
 /* kvq_decode_attention for callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the same computation and the
  * same kernels, with the split-K partials in a scratch array the library holds in each GPU's
