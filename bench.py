@@ -1,13 +1,15 @@
 """Benchmark of the quantized-KV decode step on one MI355X.
 
 One step = quantize-append of one new token per sequence (re-appending the last position, so the
-context stays at S) followed by fused dequantize + decode attention over S tokens.  Inputs are
-seeded synthetic data resident in HBM before timing starts.
+context stays at S) and fused dequantize + decode attention over S tokens: an append launch and
+a decode launch, or with ``--fused`` one launch that does both (kvq_append_decode; contiguous
+2-bit and FP4 caches).  Inputs are seeded synthetic data resident in HBM before timing starts.
 
 Prints one JSON line.  ``value`` is algorithmic KV bytes moved per second by the whole step;
-``roofline`` reports the decode kernel alone (its bytes / its average launch time measured with
-HIP events on the stream it runs on) against the 8 TB/s HBM peak; ``cpu_baseline`` is the oracle
-timed on a bounded sample of the same step on the host cores.
+``roofline`` reports the decode launch alone (its bytes, with the appended rows' bytes when the
+launch also appends, / its average launch time measured with HIP events on the stream it runs
+on) against the 8 TB/s HBM peak; ``cpu_baseline`` is the oracle timed on a bounded sample of
+the same step on the host cores.
 
     python bench.py [--gpus 1] [--steps 100] [--warmup 40] [--workload c2_b64_s32k] [--flush auto]
 
@@ -248,6 +250,10 @@ def main():
                     help="each step runs the fused attention prologue (RMSNorm, Q/K/V projection of "
                          "width Hq*D with seeded bf16 weights, KV-cache write of the new token) in "
                          "place of the append, and decodes with the queries it produced")
+    ap.add_argument("--fused", action="store_true",
+                    help="one launch per step that appends and decodes (kvq_append_decode; "
+                         "contiguous 2-bit and FP4 g32 caches, without --prologue or "
+                         "--retier-every) instead of an append launch and a decode launch")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 1 GiB device copy (reference for byte counters)")
     args = ap.parse_args()
@@ -317,6 +323,11 @@ def main():
                           device="cuda")
         q_dec = torch.empty((w.B, w.Hq, w.D), dtype=torch.int16, device="cuda")
     stream = torch.cuda.current_stream()
+    fused = args.fused
+    if fused and (args.prologue or args.retier_every or w.paged
+                  or not (w.fmt in ("c2", "u2") or (w.fmt == "fp4" and w.group == 32))):
+        sys.exit("--fused needs a contiguous 2-bit or FP4 g32 cache, without --prologue or "
+                 "--retier-every")
     n_est = int(cache.tensors["count"].sum().item())
     flush = args.flush == "on" or (args.flush == "auto" and
                                     algorithmic_bytes(dc, n_est, dc.seq_lens_host) < (768 << 20))
@@ -376,6 +387,14 @@ def main():
             K.kvq_probe_read(fbuf, fsink)
         if ev is not None:
             ev[2].record(stream)
+        if fused:   # one launch: the append of every sequence's token S - 1 and the decode
+            if ev is not None:
+                ev[0].record(stream)
+            K.kvq_append_decode(p, cache, new_k[s], new_v[s], q_dec, lens, out, work,
+                                split_chunk=split)
+            if ev is not None:
+                ev[1].record(stream)
+            return
         if args.prologue:
             K.kvq_attention_prologue(p, cache, hid[s % n_hid], gain_dev, W_dev, 1e-5, pos, q_dec, pws,
                                      block_table=dc.block_table)
@@ -461,7 +480,9 @@ def main():
         app_bytes = pro_bytes
     step_bytes = dec_bytes + app_bytes
     value = step_bytes / (ms_step * 1e-3) / 1e9
-    achieved = dec_bytes / (dec_ms * 1e-3) / 1e9
+    # the timed kernel: the decode, or in a fused step the launch that also appends
+    kern_bytes = dec_bytes + (app_bytes if fused else 0)
+    achieved = kern_bytes / (dec_ms * 1e-3) / 1e9
     elems = 2 * w.H * int(lens_h.sum()) * w.D
     res = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
@@ -472,7 +493,8 @@ def main():
                    "S": int(lens_h.max()), "format": w.fmt, "group": w.group,
                    "outliers": w.outlier, "tau": w.sigma, "split_chunk": split if split else "default",
                    "layers": 1, "cache_flush_per_step": flush, "channel_mask": w.chan_mask,
-                   "clock_ramp_steps": n_ramp},
+                   "clock_ramp_steps": n_ramp,
+                   "step": "fused append+decode launch" if fused else "append launch + decode launch"},
         "us_per_step_decode": round(dec_ms * 1e3, 2),
         "us_decode_p10_p50_p90": [round(float(np.percentile(dec_all, q)) * 1e3, 2) for q in (10, 50, 90)],
         "us_per_step": round(ms_step * 1e3, 2),
@@ -482,6 +504,7 @@ def main():
         "tokens_heads_per_s": round(int(lens_h.sum()) * w.H / (dec_ms * 1e-3), 1),
         "outliers": n_out, "outlier_fraction": round(n_out / elems, 6),
         "decode_bytes": dec_bytes,
+        "kernel_bytes": kern_bytes,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      **measured_counters(w.name)},

@@ -75,9 +75,10 @@ constexpr int kSegPages = 1024;
 // workgroups whose ranges cover many short lists take fewer steps.
 template <bool PAGED> constexpr int kPieceSteps = PAGED ? 48 : 16;
 constexpr uint32_t kDead = 0xFFFFFFFFu;    // no page: its rows read as zeros
-// Fused append: the wave that quantizes a list's new token hands this many of its full steps of
-// the piece to the other waves (one each), about the VALU work of the row fits (eight Lloyd
-// iterations for 2-bit rows, one pass for FP4 rows) in units of one step.
+// Fused append: the work of appending a list's new token in units of one step (about the VALU
+// work of the row fits: eight Lloyd iterations for 2-bit rows, one pass for FP4 rows), counted
+// with the list's fixed cost after its steps, so that the workgroup holding the list's last step
+// takes that many fewer steps.
 template <int FMT> constexpr int kAppSteps = FMT == FMT_C2 ? 11 : 3;
 
 template <int FMT> struct Buf;
@@ -402,12 +403,12 @@ __device__ __forceinline__ void merge_cut_list(const DecodeLaunch& d, int b, int
   }
 }
 
-// APP (contiguous caches): fused append.  The walk covers tokens < seq_lens[b] - 1; the row of
-// token seq_lens[b] - 1 (k_new, v_new) is quantized into the cache (as an append at that
-// position) by one wave of the workgroup that holds the list's last step (or, for a list with no
-// earlier token, its last unit of work), which also adds that token to its softmax state from
-// the dequantized row.  The walk never reads the new row or its records (rows past the walk read
-// as zeros, records of tokens past a step are skipped), so no other wave waits for the append.
+// APP (contiguous caches): fused append.  In the workgroup that holds a list's last step, one
+// wave first quantizes the row of token seq_lens[b] - 1 (k_new, v_new) into the cache, as an
+// append at that position does, then decodes the list's last step from the cache (after its
+// stores have completed and this CU's L1 is invalidated), then its share of the other steps.
+// No other wave reads the last step's rows or records (the records of later tokens that a step's
+// loads may see are skipped), so nobody waits for the append.
 template <int FMT, int OUTL, bool CMP, bool PAGED, bool MASS, bool APP>
 __global__ void __launch_bounds__(kWaves * 64) decode_mfma_kernel(DecodeLaunch d) {
   __shared__ __attribute__((aligned(16))) _Float16 s_lds[kWaves * kTile];
@@ -471,14 +472,16 @@ __global__ void __launch_bounds__(kWaves * 64) decode_mfma_kernel(DecodeLaunch d
   // every other piece is a whole list.  Units per head of every sequence, summed, then scanned
   // to find the sequence that holds the range's first unit: all threads of the workgroup, 768
   // sequences at a time.
-  constexpr int K0 = kPieceSteps<PAGED>, K0a = K0 / 2, K0b = K0 - K0a;
-  constexpr int kApp = APP ? 1 : 0;   // tokens of a sequence that the walk leaves to the append
+  // (fused append: the list's post units also count the append, so that the workgroup holding
+  // its last step takes fewer steps)
+  constexpr int K0 = kPieceSteps<PAGED> + (APP ? kAppSteps<FMT> : 0);
+  constexpr int K0a = kPieceSteps<PAGED> / 2, K0b = K0 - K0a;
   constexpr int kT = kWaves * 64;
   const int tid = threadIdx.x;
   auto seq_steps = [&](int bb) -> uint64_t {
     if (bb >= L.B) return 0u;
     const int Sb = d.seq_lens[bb];
-    return Sb >= 1 && Sb <= L.S_cap ? (uint64_t)((Sb - kApp + kStep - 1) / kStep + K0) : 0u;
+    return Sb >= 1 && Sb <= L.S_cap ? (uint64_t)((Sb + kStep - 1) / kStep + K0) : 0u;
   };
   auto wave_sum = [&](uint64_t v) {
 #pragma unroll
@@ -504,7 +507,7 @@ __global__ void __launch_bounds__(kWaves * 64) decode_mfma_kernel(DecodeLaunch d
       const int Sb = d.seq_lens[tid];
       const bool ok = Sb >= 1 && Sb <= L.S_cap;
       if (!ok && blockIdx.x == 0) report(d.cache.status, KVQ_ERR_INVALID_ARG);
-      n = ok ? (uint64_t)((Sb - kApp + kStep - 1) / kStep + K0) : 0u;
+      n = ok ? (uint64_t)((Sb + kStep - 1) / kStep + K0) : 0u;
     }
     const uint64_t incl = wave_scan(n);
     if (lane == 63) s_sc[wave] = incl;
@@ -535,7 +538,7 @@ __global__ void __launch_bounds__(kWaves * 64) decode_mfma_kernel(DecodeLaunch d
       const int Sb = d.seq_lens[bb];
       const bool ok = Sb >= 1 && Sb <= L.S_cap;
       if (!ok && blockIdx.x == 0) report(d.cache.status, KVQ_ERR_INVALID_ARG);
-      mine += ok ? (uint64_t)((Sb - kApp + kStep - 1) / kStep + K0) : 0u;
+      mine += ok ? (uint64_t)((Sb + kStep - 1) / kStep + K0) : 0u;
     }
     mine = wave_sum(mine);
     if (lane == 0) s_sc[wave] = mine;
@@ -579,15 +582,14 @@ __global__ void __launch_bounds__(kWaves * 64) decode_mfma_kernel(DecodeLaunch d
 
   uint64_t left = ue - ub;   // units of the range not yet taken
   for (bool first = true;;) {
-  const int S = d.seq_lens[b] - kApp;   // tokens of the walk
+  const int S = d.seq_lens[b];
   const int nb = (S + kStep - 1) / kStep;
   const int take = (int)min(left, (uint64_t)(nb + K0 - off));   // units of this list in the range
   const int s0 = min(max(off - K0a, 0), nb), s1 = min(max(off + take - K0a, 0), nb);   // its steps [s0, s1)
   const int t0 = kStep * s0, t1 = min(kStep * s1, S);   // the piece's tokens
   const bool whole = s0 == 0 && s1 == nb;
-  // fused append: this piece appends the list's new token (held by the owner of the last step,
-  // or of the last unit when the walk is empty)
-  const bool app = APP && (nb > 0 ? s1 == nb && s1 > s0 : off + take == nb + K0);
+  // fused append: the piece that holds the list's last step appends its new token (token S - 1)
+  const bool app = APP && s1 == nb && s1 > s0;
   if (s1 > s0 || app) {   // (only the first and the last list of a range can have no steps in it)
 
   // query operand (B of S^T = K^ Q^T): lane (row r, k-group kg), positions 32*ks + 8*kg + e
@@ -850,17 +852,14 @@ __global__ void __launch_bounds__(kWaves * 64) decode_mfma_kernel(DecodeLaunch d
     }
   };
 
-  // Fused append, by one wave: the list's new token (token S, after the walk's S tokens) is
-  // quantized into the cache as an append at that position would do it (lanes 0-31 the K row,
-  // lanes 32-63 the V row, staged in the wave's tile, which is free until its walk), then added
-  // to the wave's softmax state from the row as a decode would read it back: its scores with
-  // the query rows (from the wave's query operand), the running maximum and the (hi) output
-  // columns updated exactly, the probability counted once per query row.
-  auto append_new_token = [&]() {
+  // Fused append, by one wave: the row of the list's token S - 1 is quantized into the cache as
+  // an append at that position does it (lanes 0-31 the K row, lanes 32-63 the V row, staged in
+  // the wave's tile, which is free until its walk); the list's new record counts (K, V) are
+  // returned for the last step's record bounds.
+  auto append_token = [&]() -> int2 {
     constexpr int GQ = FMT == FMT_C2 ? 64 : 32;   // quantization group
     constexpr int QL = GQ / 4;
     RowStage<2>& st = *(RowStage<2>*)ktile;
-    float* const rowv = (float*)(ktile + sizeof(RowStage<2>) / sizeof(_Float16));   // [2][128]
     const int kv = lane >> 5, rl = lane & 31, gi = rl / QL, jg = rl % QL;
     const float* src = (kv ? d.v_new : d.k_new) + ((size_t)b * L.H + h) * kHeadDim;
     float x[4];
@@ -871,54 +870,9 @@ __global__ void __launch_bounds__(kWaves * 64) decode_mfma_kernel(DecodeLaunch d
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
     };
-    const int64_t run = records_before<kRowLanes>(d, b, h, kv, S, rl);
-    append_row<FMT, GQ>(d, true, b, h, kv, S, run, x, rl, kv, st, wsync);
-    // the row's values as stored: outliers at their stored precision, the rest from codes
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int c = 4 * rl + k;
-      const uint32_t code = st.code[kv][c];
-      float v;
-      if (HAS_OUTL && st.flag[kv][c]) {
-        v = OUTL == KVQ_OUTL_FP16 ? half_bits_to_f32(f32_to_half_bits(st.x[kv][c]))
-                                  : e4m3_to_f32(f32_to_e4m3(st.x[kv][c]));
-      } else if constexpr (FMT == FMT_C2) {
-        const uint32_t m = st.meta[kv][2 * (c / 64) + (code >> 1)];
-        v = half_bits_to_f32((code & 1u) ? m >> 16 : m & 0xFFFFu);
-      } else {
-        v = e2m1_to_f32(code) * e4m3_to_f32(((const uint8_t*)st.meta[kv])[c / 32]);
-      }
-      rowv[kv * kHeadDim + c] = v;
-    }
-    wsync();
-    // scores: lane (r, kg) sums its query operand's channels 32 ks + 8 kg + e, then the k-groups
-    float part = 0.0f;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) part += (float)qop[ks][e] * rowv[32 * ks + 8 * kg + e];
-    part += __shfl_xor(part, 16, 64);
-    part += __shfl_xor(part, 32, 64);
-    if constexpr (CMP) part = dpp_f32<kRowShr8, 0xC>(part, part);   // lanes r >= 8: query r - 8
-    const float xs = part * sl2;
-    const float m_new = fmaxf(m_run, xs);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 while m_run is -inf
-    l_run *= alpha;
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt) oacc[mt] *= alpha;
-    m_run = m_new;
-    m_thr = sl2 > 0.0f ? (m_run + 8.0f) / sl2 : (m_run == -INFINITY ? -INFINITY : INFINITY);
-    const float pn = __builtin_amdgcn_exp2f(xs - m_run);
-    const bool hi_col = !CMP || r < 8;   // with CMP, columns r >= 8 carry lo parts
-    if (hi_col && kg == 0) l_run += pn;
-    if (hi_col) {
-      const float* vrowv = rowv + kHeadDim;
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) oacc[mt][v] += pn * vrowv[16 * mt + 4 * kg + v];
-    }
-    wsync();   // the tile is the wave's again
+    const int64_t run = records_before<kRowLanes>(d, b, h, kv, S - 1, rl);
+    const int cnt = (int)append_row<FMT, GQ>(d, true, b, h, kv, S - 1, run, x, rl, kv, st, wsync);
+    return int2{__builtin_amdgcn_readlane(cnt, 0), __builtin_amdgcn_readlane(cnt, 32)};
   };
 
   const Buf8 no8{};
@@ -926,21 +880,18 @@ __global__ void __launch_bounds__(kWaves * 64) decode_mfma_kernel(DecodeLaunch d
 
   if constexpr (!PAGED) {
     // The piece's full 32-token steps are spread over the waves; the list's ragged last step (if
-    // it is in the piece) is left to the first wave after the others.
+    // it is in the piece) is left to the first wave after the others, and in a piece that
+    // appends, the list's last step to the appending wave.
     const int nsteps = (t1 - t0 + kStep - 1) / kStep;
     const bool ragged = (t1 - t0) % kStep != 0;
-    const int nfull = nsteps - (ragged ? 1 : 0);
+    const int nfull = nsteps - (ragged || app ? 1 : 0);
     // Workgroups walk their full steps in rotated order, starting at evenly spread points: lists
     // start at power-of-two-aligned offsets, and walking them in lockstep would send every
     // workgroup to the same HBM channels at the same time.
     const int rot = nfull > 0 ? (int)(((uint64_t)blockIdx.x * (uint64_t)nfull) / nwg) : 0;
-    // fused append: wave aw appends the list's new token first and hands its last R full steps
-    // to the other waves (one each), so that its SIMD is not left with the append on top of an
-    // equal share (the assignment stays fixed, and with it the result)
+    // fused append: wave aw appends the list's new token, then takes the list's last step (which
+    // is left out of the other waves' steps)
     const int aw = APP ? (int)(((size_t)b * L.H + h) % kWaves) : 0;
-    const int naw = aw < nfull ? (nfull - aw + wpc - 1) / wpc : 0;
-    const int R = app ? min(naw, kAppSteps<FMT>) : 0;
-    if (app && wi == aw) append_new_token();
     // RAGGED: the step may hold tokens >= t1 (only the list's last step); the buffer ranges end
     // at row t1, so those rows read as zeros
     auto issue_codes = [&](Buf<FMT>& bf, int tsi) {
@@ -1006,7 +957,25 @@ __global__ void __launch_bounds__(kWaves * 64) decode_mfma_kernel(DecodeLaunch d
     Recs rec[NB];
     uint32_t bnd[NB];
     int tsr[NB];
-    const int nmine = (wi < nfull ? (nfull - wi + wpc - 1) / wpc : 0) - (wi == aw ? R : 0);
+    // the list's last step, alone (tokens < t1 of it)
+    auto last_step = [&]() {
+      const int ts = t0 + kStep * (nsteps - 1);
+      const uint32_t b0 = issue_bounds(ts);
+      issue_recs(rec[0], b0, ts);
+      issue_codes(buf[0], ts);
+      consume(buf[0], no8, rec[0], (uint32_t)ts * 128u, (uint32_t)ts * 128u, t1 - ts, 0, 0,
+              std::false_type{}, std::false_type{});
+    };
+    if (app && wi == aw) {
+      const int2 nc = append_token();
+      cntK = nc.x;   // the last step's record bounds
+      cntV = nc.y;
+      // the stores are complete, and this CU's L1 holds no line that other waves read before
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      last_step();
+    }
+    const int nmine = wi < nfull ? (nfull - wi + wpc - 1) / wpc : 0;
     const int tpast = t1 + 2 * kStep;
     int jn = 0;                                  // the wave's next step to start
     int an = wi + rot;                           // its position in the piece's full steps
@@ -1052,27 +1021,7 @@ __global__ void __launch_bounds__(kWaves * 64) decode_mfma_kernel(DecodeLaunch d
 #pragma unroll
     for (int u = 0; u < NB - 1; ++u)   // the wave's last nmine % NB steps
       if (ngroups * NB + u < nmine) walk_step(u);
-    if (R > 0 && wi != aw) {   // a step handed over by the appending wave
-      const int k = wi < aw ? wi : wi - 1;
-      if (k < R) {
-        int a = aw + wpc * (naw - R + k) + rot;
-        if (a >= nfull) a -= nfull;
-        const int ts = t0 + kStep * a;
-        const uint32_t b0 = issue_bounds(ts);
-        issue_recs(rec[0], b0, ts);
-        issue_codes(buf[0], ts);
-        consume(buf[0], no8, rec[0], (uint32_t)ts * 128u, (uint32_t)ts * 128u, kStep, 0, 0,
-                std::true_type{}, std::false_type{});
-      }
-    }
-    if (ragged && wi == 0) {
-      const int ts = t0 + kStep * (nsteps - 1);
-      const uint32_t b0 = issue_bounds(ts);
-      issue_recs(rec[0], b0, ts);
-      issue_codes(buf[0], ts);
-      consume(buf[0], no8, rec[0], (uint32_t)ts * 128u, (uint32_t)ts * 128u, t1 - ts, 0, 0,
-              std::false_type{}, std::false_type{});
-    }
+    if (ragged && !app && wi == 0) last_step();
   } else {
     // ---------------------------------------------------------------- paged caches
     const int pend = (t1 + kBlock - 1) / kBlock;   // pages [t0 / 16, pend) of the piece
