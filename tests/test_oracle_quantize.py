@@ -284,6 +284,60 @@ def test_c2_lloyd_matches_independent_fp64():
     assert close.mean() > 0.98
 
 
+def _lloyd_fp64_margin(x, iters):
+    """The float64 Lloyd above, also returning the smallest gap between an element's nearest
+    and second-nearest centroid over every assignment it makes (the seeds' and each iteration's)
+    and the final assignment's."""
+    v = sorted(x)
+    n = len(v)
+    c = [v[((2 * j + 1) * n) // 8] for j in range(4)]
+    gap = float("inf")
+    for it in range(iters + 1):
+        sums, cnts = [0.0] * 4, [0] * 4
+        for xi in x:
+            d = sorted((abs(xi - cj), j) for j, cj in enumerate(c))
+            gap = min(gap, d[1][0] - d[0][0])
+            a = min(range(4), key=lambda j: (abs(xi - c[j]), j))
+            sums[a] += xi
+            cnts[a] += 1
+        if it == iters:
+            break
+        c = [sums[j] / cnts[j] if cnts[j] else c[j] for j in range(4)]
+    return np.array(c), gap
+
+
+@pytest.mark.parametrize("iters", [1, 2, 8])
+def test_c2_lloyd_equals_fp64_where_no_assignment_is_close(iters):
+    """Where no element lies within a small margin of two centroids at any iteration, float32
+    and float64 Lloyd make the same assignments, so their centroids differ only by the
+    rounding of the float32 sums: the stored fp16 centroids must equal the float64 centroids
+    rounded to fp16, except for a value within that rounding of an fp16 rounding boundary."""
+    rng = np.random.default_rng(140 + iters)
+    x = (rng.standard_normal((400, 64)) * rng.lognormal(0, 1, (400, 1))).astype(F32)
+    spec = Q.QuantSpec("c2", 64, "none", lloyd_iters=iters)
+    q = Q.quantize_rows(x, spec)
+    cent = F.fp16_from_bits(q.meta.view(np.uint16).reshape(400, 4)).astype(np.float64)
+    checked = 0
+    for r in range(400):
+        row = [float(t) for t in x[r]]
+        ref, gap = _lloyd_fp64_margin(row, iters)
+        scale = max(abs(t) for t in row)
+        if gap <= 1e-4 * scale:
+            continue
+        want = F.fp16_round(ref.astype(F32)).astype(np.float64)
+        for j in range(4):
+            if cent[r, j] == want[j]:
+                continue
+            # a float64 centroid this close to an fp16 rounding boundary may round either way
+            ulp = np.spacing(np.float16(want[j])).astype(np.float64)
+            lo, hi = sorted((cent[r, j], want[j]))
+            mid = (lo + hi) / 2
+            assert hi - lo <= ulp * 1.0001 and abs(ref[j] - mid) <= 1e-5 * abs(ref[j]), \
+                (r, j, cent[r, j], want[j], ref[j])
+        checked += 1
+    assert checked >= 300, checked
+
+
 def test_c2_sse_vs_bruteforce_optimum_and_monotone():
     rng = np.random.default_rng(15)
     spec_it = [Q.QuantSpec("c2", 64, "none", lloyd_iters=i) for i in range(9)]
