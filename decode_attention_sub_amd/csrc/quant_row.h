@@ -85,6 +85,12 @@ __device__ __forceinline__ float group_max(float v) {
   return v;
 }
 
+// lane Q of the lane's quad (DPP quad_perm [Q, Q, Q, Q])
+template <int Q>
+__device__ __forceinline__ float quad_bcast_f32(float v) {
+  return as_f32((uint32_t)__builtin_amdgcn_mov_dpp((int)as_u32(v), Q * 0x55, 0xF, 0xF, false));
+}
+
 // ---------------------------------------------------------------- per-row state
 struct RowOut {
   uint32_t code[4];   // per element
@@ -260,27 +266,35 @@ __device__ __forceinline__ void fit_c2(const float x[4], const bool keep[4], int
     for (int i = 0; i < 4; ++i) bits |= (keep[i] && rank[i] == r) ? xb[i] : 0u;
     c[j] = as_f32((uint32_t)group_ior<L>((int)bits));
   }
+  // Each Lloyd iteration: the members' sums by the fixed tree, the four member counts in one
+  // reduction (a byte each: a group has at most 64 members), and the four divisions spread
+  // over the lanes of each quad (lane jg computes centroid jg % 4; a quad broadcast gives every
+  // lane all four), the same correctly rounded quotients in fewer instructions.
+  const int jq = jg & 3;
   for (int it = 0; it < iters; ++it) {
     uint32_t a[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) a[i] = nearest4(x[i], c);
-    float nc[4];
+    uint32_t pk = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pk += keep[i] ? 1u << (8u * a[i]) : 0u;
+    const uint32_t cnts = (uint32_t)group_isum<L>((int)pk);
+    float sum[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       float s[4];
-      int cl = 0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool m = keep[i] && a[i] == (uint32_t)j;
-        s[i] = m ? x[i] : 0.0f;
-        cl += m ? 1 : 0;
-      }
-      const float sum = group_sum_tree<L>(s[0], s[1], s[2], s[3]);
-      const int cnt = group_isum<L>(cl);
-      nc[j] = cnt > 0 ? sum / (float)cnt : c[j];
+      for (int i = 0; i < 4; ++i) s[i] = keep[i] && a[i] == (uint32_t)j ? x[i] : 0.0f;
+      sum[j] = group_sum_tree<L>(s[0], s[1], s[2], s[3]);
     }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) c[j] = nc[j];
+    const float my_sum = jq == 0 ? sum[0] : jq == 1 ? sum[1] : jq == 2 ? sum[2] : sum[3];
+    const float my_c = jq == 0 ? c[0] : jq == 1 ? c[1] : jq == 2 ? c[2] : c[3];
+    const int my_cnt = (int)((cnts >> (8 * jq)) & 0xFFu);
+    const float my_nc = my_cnt > 0 ? my_sum / (float)my_cnt : my_c;
+    c[0] = quad_bcast_f32<0>(my_nc);
+    c[1] = quad_bcast_f32<1>(my_nc);
+    c[2] = quad_bcast_f32<2>(my_nc);
+    c[3] = quad_bcast_f32<3>(my_nc);
   }
   uint32_t hb[4];
   float ch[4];

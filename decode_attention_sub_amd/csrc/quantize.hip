@@ -68,6 +68,15 @@ __global__ void __launch_bounds__(64 * NW) quantize_append_kernel(QArgs a) {
 
   const int p = a.positions[b];
   const int n = a.counts[b];
+  // the first rows' values are loaded with the position and count (row min(slot, max_new - 1)
+  // is inside k_new / v_new whatever the count; rows past it are zeroed below)
+  const float* src = (kv == 0 ? a.k_new : a.v_new) + ((size_t)b * Lo.H + h) * (size_t)a.max_new * kHeadDim;
+  float x0[4];
+  {
+    const int srow = min(slot, a.max_new - 1);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x0[e] = src[(size_t)srow * kHeadDim + gi * G + jg + L * e];
+  }
   if (n <= 0) return;
   if (p < 0 || n > a.max_new || (int64_t)p + n > Lo.S_cap) {
     if (tid == 0) report(a.cache.status, KVQ_ERR_INVALID_ARG);
@@ -79,32 +88,21 @@ __global__ void __launch_bounds__(64 * NW) quantize_append_kernel(QArgs a) {
   uint8_t* oval = (uint8_t*)a.cache.outl_val[kv] +
                   ((size_t)b * Lo.H + h) * (size_t)Lo.outl_cap * (a.outl == KVQ_OUTL_FP16 ? 2 : 1);
 
-  // the first rows' values are loaded before the list truncation, which waits on memory too
-  const float* src = (kv == 0 ? a.k_new : a.v_new) + ((size_t)b * Lo.H + h) * (size_t)a.max_new * kHeadDim;
-  float x0[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e)
-    x0[e] = slot < n ? src[(size_t)slot * kHeadDim + gi * G + jg + L * e] : 0.0f;
-
-  // truncate the list to the records of tokens < p: the records before the start of p's
+  // The list is truncated to the records of tokens < p: the records before the start of p's
   // 16-token block, plus those of the block's rows before p.  A block holds at most 16 rows of D
   // records, and the list is sorted, so each thread stops at its first record of a token >= p.
+  // The scan's bounds and first loads are issued here; it is finished after the first rows'
+  // fits (which do not need it), before their records are written.
   if (tid == 0) s_trunc = 0;
-  __syncthreads();
-  int64_t running = 0;
+  int64_t start = 0, lim = 0;
+  uint32_t first_idx = 0xFFFFFFFFu;
   if (p > 0) {
-    const int64_t start = max((int64_t)0, min((int64_t)bstart[(p - 1) >> 4], Lo.outl_cap));
+    start = max((int64_t)0, min((int64_t)bstart[(p - 1) >> 4], Lo.outl_cap));
     const int64_t old = max((int64_t)0, min((int64_t)a.cache.outl_count[lid], Lo.outl_cap));
-    const int64_t lim = min(old, start + (int64_t)kBlock * kHeadDim);
-    int cnt = 0;
-    for (int64_t r = start + tid; r < lim; r += blockDim.x) {
-      if (oidx[r] >= (uint32_t)p * kHeadDim) break;
-      ++cnt;
-    }
-    if (cnt) atomicAdd(&s_trunc, cnt);
-    __syncthreads();
-    running = start + s_trunc;
+    lim = min(old, start + (int64_t)kBlock * kHeadDim);
+    if (start + tid < lim) first_idx = oidx[start + tid];
   }
+  int64_t running = 0;
 
   for (int i0 = 0; i0 < n; i0 += RPI) {
     const int r = i0 + slot;
@@ -113,7 +111,7 @@ __global__ void __launch_bounds__(64 * NW) quantize_append_kernel(QArgs a) {
     float x[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      x[e] = i0 == 0 ? x0[e] : valid ? src[(size_t)r * kHeadDim + gi * G + jg + L * e] : 0.0f;
+      x[e] = !valid ? 0.0f : i0 == 0 ? x0[e] : src[(size_t)r * kHeadDim + gi * G + jg + L * e];
     int tier1 = 0;
     size_t pslot = 0;
     bool row_ok = valid;
@@ -170,6 +168,19 @@ __global__ void __launch_bounds__(64 * NW) quantize_append_kernel(QArgs a) {
     }
     if (lane == 0) s_tier[slot] = tier1;
     __syncthreads();
+    if (i0 == 0 && p > 0) {   // the truncation scan, finished (every thread of the workgroup)
+      int cnt = 0;
+      if (first_idx < (uint32_t)p * kHeadDim) {
+        cnt = 1;
+        for (int64_t rr = start + tid + blockDim.x; rr < lim; rr += blockDim.x) {
+          if (oidx[rr] >= (uint32_t)p * kHeadDim) break;
+          ++cnt;
+        }
+      }
+      if (cnt) atomicAdd(&s_trunc, cnt);
+      __syncthreads();
+      running = start + s_trunc;
+    }
 
     // pack codes and write the row
     if (row_ok) {
