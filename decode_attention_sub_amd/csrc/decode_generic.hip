@@ -12,7 +12,9 @@
 // Each 64-token step dequantizes K and V rows into LDS as fp32 (outlier positions overwritten
 // from the side lists), computes scores in fp32, updates the online softmax and accumulates
 // P.V in fp32.  Exact fp32 dequantization makes this the path for formats whose values are
-// not fp16-representable (INT4 scale * code + zero).
+// not fp16-representable (INT4 scale * code + zero).  Short contexts make it latency-bound, so
+// the dependent loads are few: the queries go out with the sequence length, each step's
+// outlier bounds and first records with its codes.
 #include "kvq_device.h"
 #include "kvq_launch.h"
 
@@ -111,6 +113,17 @@ __global__ void __launch_bounds__(256) decode_generic_kernel(DecodeLaunch d) {
 
   const Layout& L = d.L;
   const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int G = d.Hq / L.H;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  // the group's query rows (contiguous in q) are loaded with the sequence length
+  float qv[kMaxRows * kHeadDim / 256];
+  const uint16_t* qg = d.q + ((size_t)b * d.Hq + (size_t)h * G) * kHeadDim;
+#pragma unroll
+  for (int k = 0; k < kMaxRows * kHeadDim / 256; ++k) {
+    const int i = tid + 256 * k;
+    qv[k] = i < G * kHeadDim ? bf16_to_f32(qg[i]) : 0.0f;
+  }
   const int S = d.seq_lens[b];
   if (S < 1 || S > L.S_cap) {
     if (threadIdx.x == 0 && chunk == 0 && h == 0) report(d.cache.status, KVQ_ERR_INVALID_ARG);
@@ -119,13 +132,11 @@ __global__ void __launch_bounds__(256) decode_generic_kernel(DecodeLaunch d) {
   const int t0 = chunk * d.chunk;
   if (t0 >= S) return;
   const int t1 = min(t0 + d.chunk, S);
-  const int G = d.Hq / L.H;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
 
-  for (int i = tid; i < G * kHeadDim; i += 256) {
-    const int r = i / kHeadDim, ch = i % kHeadDim;
-    s_q[r][ch] = bf16_to_f32(d.q[((size_t)b * d.Hq + (size_t)h * G + r) * kHeadDim + ch]);
+#pragma unroll
+  for (int k = 0; k < kMaxRows * kHeadDim / 256; ++k) {
+    const int i = tid + 256 * k;
+    if (i < G * kHeadDim) s_q[i / kHeadDim][i % kHeadDim] = qv[k];
   }
   if (tid < kMaxRows) { s_m[tid] = -INFINITY; s_l[tid] = 0.0f; }
   float o[kMaxRows / 2];
@@ -139,8 +150,29 @@ __global__ void __launch_bounds__(256) decode_generic_kernel(DecodeLaunch d) {
   const size_t vbytes = d.outl == KVQ_OUTL_FP16 ? 2 : 1;
   __syncthreads();
 
+  const bool has_outl = d.outl != KVQ_OUTL_NONE;
+  const int64_t cntK = has_outl ? d.cache.outl_count[lidK] : 0;
+  const int64_t cntV = has_outl ? d.cache.outl_count[lidV] : 0;
+  const uint32_t* idxK = d.cache.outl_idx[0] + lbase;
+  const uint32_t* idxV = d.cache.outl_idx[1] + lbase;
+  const void* valsK = (const uint8_t*)d.cache.outl_val[0] + lbase * vbytes;
+  const void* valsV = (const uint8_t*)d.cache.outl_val[1] + lbase * vbytes;
+  constexpr uint32_t kNoRec = 0xFFFFFFFFu;
+
   for (int ts = t0; ts < t1; ts += kT) {
     const int te = min(ts + kT, t1);
+    // the step's outlier records [r0, r1) of K and V, and each thread's first record of each
+    int64_t rk0 = 0, rk1 = 0, rv0 = 0, rv1 = 0;
+    uint32_t fk = kNoRec, fv = kNoRec;
+    float vk = 0.0f, vv = 0.0f;
+    if (has_outl) {
+      rk0 = max((int64_t)0, min((int64_t)bsK[ts >> 4], L.outl_cap));
+      rk1 = max(rk0, min((te < S) ? (int64_t)bsK[te >> 4] : cntK, L.outl_cap));
+      rv0 = max((int64_t)0, min((int64_t)bsV[ts >> 4], L.outl_cap));
+      rv1 = max(rv0, min((te < S) ? (int64_t)bsV[te >> 4] : cntV, L.outl_cap));
+      if (rk0 + tid < rk1) { fk = idxK[rk0 + tid]; vk = outlier_value(valsK, rk0 + tid, d.outl); }
+      if (rv0 + tid < rv1) { fv = idxV[rv0 + tid]; vv = outlier_value(valsV, rv0 + tid, d.outl); }
+    }
     {  // dequantize 64 rows of K and V: thread -> (token tid/4, 32 channels)
       const int tt = tid >> 2, part = tid & 3;
       float buf[32];
@@ -161,16 +193,18 @@ __global__ void __launch_bounds__(256) decode_generic_kernel(DecodeLaunch d) {
       for (int k = 0; k < 32; ++k) s_v[tt][32 * part + k] = buf[k];
     }
     __syncthreads();
-    if (d.outl != KVQ_OUTL_NONE) {  // overwrite outlier positions of this step
+    if (has_outl) {  // overwrite outlier positions of this step
       for (int kv = 0; kv < 2; ++kv) {
-        const int32_t* bs = kv ? bsV : bsK;
-        const int64_t cnt = d.cache.outl_count[kv ? lidV : lidK];
-        const int64_t r0 = max((int64_t)0, min((int64_t)bs[ts >> 4], L.outl_cap));
-        const int64_t r1 = max(r0, min((te < S) ? (int64_t)bs[te >> 4] : cnt, L.outl_cap));
-        const uint32_t* idx = d.cache.outl_idx[kv] + lbase;
-        const void* vals = (const uint8_t*)d.cache.outl_val[kv] + lbase * vbytes;
+        const uint32_t f = kv ? fv : fk;
+        const int64_t r0 = kv ? rv0 : rk0, r1 = kv ? rv1 : rk1;
+        const uint32_t* idx = kv ? idxV : idxK;
+        const void* vals = kv ? valsV : valsK;
         float (*tile)[kStride] = kv ? s_v : s_k;
-        for (int64_t r = r0 + tid; r < r1; r += 256) {
+        if (f != kNoRec) {
+          const int t = (int)(f / kHeadDim), ch = (int)(f % kHeadDim);
+          if (t >= ts && t < te) tile[t - ts][ch] = kv ? vv : vk;
+        }
+        for (int64_t r = r0 + tid + 256; r < r1; r += 256) {
           const uint32_t ix = idx[r];
           const int t = (int)(ix / kHeadDim), ch = (int)(ix % kHeadDim);
           if (t >= ts && t < te) tile[t - ts][ch] = outlier_value(vals, r, d.outl);

@@ -237,7 +237,7 @@ int32_t decode_impl(const kvq_params* pin, const kvq_cache* cache, const void* q
   if (page_mass) {   // per-page and per-head log-sum-exps after the partials
     if (!p->page_size) return KVQ_ERR_UNSUPPORTED;
     need_mass = mass_ws_bytes(p, need);
-    if (!workspace || ws_bytes < need_mass) return KVQ_ERR_WORKSPACE;
+    if (!workspace || ws_bytes < need_mass || ((uintptr_t)workspace & 15)) return KVQ_ERR_WORKSPACE;
   }
   if (use_scratch && need) {
     if (need > KVQ_NOALLOC_SCRATCH_BYTES) return KVQ_ERR_WORKSPACE;
@@ -245,7 +245,7 @@ int32_t decode_impl(const kvq_params* pin, const kvq_cache* cache, const void* q
     if (st) return st;
     ws_bytes = KVQ_NOALLOC_SCRATCH_BYTES;
   }
-  if (need && (!workspace || ws_bytes < need)) return KVQ_ERR_WORKSPACE;
+  if (need && (!workspace || ws_bytes < need || ((uintptr_t)workspace & 15))) return KVQ_ERR_WORKSPACE;
   DecodeLaunch d;
   d.L = make_layout(p, cache->outl_capacity);
   d.cache = *cache;

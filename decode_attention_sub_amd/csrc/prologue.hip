@@ -121,7 +121,6 @@ __global__ void __launch_bounds__(kPThreads, 4) prologue_kernel(PrologueLaunch a
   const int kseg = tid & 15, srow = tid >> 4;
   // MFMA map: lane (r16, kg); wave -> columns 16 wave .. 16 wave + 15
   const int r16 = lane & 15, kg = lane >> 4;
-  const uint16_t* wrow = a.weight + (size_t)(col0 + 16 * wave + r16) * d + 8 * kg;
 
   float ss[kSI];
 #pragma unroll

@@ -81,7 +81,8 @@ typedef enum {
   KVQ_OK = 0,
   KVQ_ERR_INVALID_ARG = -1,  /* shape, pointer or range check failed on the host or device */
   KVQ_ERR_UNSUPPORTED = -2,  /* format / group / head-dim combination not implemented */
-  KVQ_ERR_WORKSPACE = -3,    /* workspace pointer NULL or smaller than kvq_workspace_bytes */
+  KVQ_ERR_WORKSPACE = -3,    /* workspace pointer NULL, not 16-byte aligned, or smaller than
+                                kvq_workspace_bytes */
   KVQ_ERR_HIP = -4,          /* a HIP launch returned an error */
   KVQ_ERR_CAPACITY = -5      /* device status only: an outlier list overflowed its capacity */
 } kvq_status;
@@ -213,11 +214,12 @@ int32_t kvq_quantize_append(const kvq_params* p, const kvq_cache* cache, const f
  * ceil(max_seq_len / 32) / 12)) (one workgroup per CU of an MI355X, at least 12 steps each);
  * split_chunk > 0: N = min(B * H * ceil(max_seq_len / 32), 16384, ceil(B * H * max_seq_len /
  * split_chunk)).
- * Other formats (the generic decoder): split-K chunks of each list, B * Hq *
- * ceil(max_seq_len / chunk) * (D + 2) floats (0 when one chunk covers max_seq_len); chunk =
- * split_chunk, or by default 4096 for paged caches and, for contiguous caches, enough chunks for
- * 1024 (sequence, KV head, chunk) units, chunks of at least 64 tokens, rounded up to a multiple
- * of 64.  split_chunk must be a multiple of 64. */
+ * Other formats (the generic decoder): split-K chunks of each list, whose (max, sum, output)
+ * partials a second kernel merges by log-sum-exp: B * Hq * ceil(max_seq_len / chunk) * (D + 2)
+ * floats (0 when one chunk covers max_seq_len); chunk = split_chunk, or by default 4096 for
+ * paged caches and, for contiguous caches, enough chunks for 1024 (sequence, KV head, chunk)
+ * units, chunks of at least 64 tokens, rounded up to a multiple of 64.  split_chunk must be a
+ * multiple of 64.  The workspace must be 16-byte aligned. */
 int32_t kvq_workspace_bytes(const kvq_params* p, int32_t split_chunk, uint64_t* out_bytes);
 
 /* Fused dequantize + flash-decoding attention ("Fused Dequantization & FlashAttention

@@ -101,6 +101,25 @@ int main(void) {
     hostile_ok &= kvq_quantize_append(&p, &c, dummy, dummy, 1, idummy, idummy, NULL, NULL) < 0;
     hostile_ok &= kvq_decode_attention(&p, &c, dummy, idummy, NULL, 0.1f, 0, dummy, NULL, 0,
                                        NULL) < 0;
+    {
+      /* a workspace that is not 16-byte aligned is rejected before anything is launched (the
+         buffers are host stand-ins that the rejected call never touches) */
+      static uint64_t wsbuf[64];
+      kvq_cache cf;
+      memset(&cf, 0, sizeof cf);
+      for (int kv = 0; kv < 2; ++kv) {
+        cf.codes[kv] = dummy; cf.meta[kv] = dummy; cf.outl_idx[kv] = (uint32_t*)idummy;
+        cf.outl_val[kv] = dummy;
+      }
+      cf.outl_count = idummy; cf.outl_block_start = idummy; cf.outl_capacity = 1;
+      kvq_params pi = p;
+      pi.batch = 1; pi.num_q_heads = 8; pi.num_kv_heads = 2; pi.max_seq_len = 1024;
+      pi.format = KVQ_FMT_INT4_ASYM; pi.group_size = 32; pi.outlier_dtype = KVQ_OUTL_FP16;
+      hostile_ok &= kvq_decode_attention(&pi, &cf, dummy, idummy, NULL, 0.1f, 0, dummy,
+                                         (char*)wsbuf + 4, sizeof wsbuf - 4, NULL) == KVQ_ERR_WORKSPACE;
+      hostile_ok &= kvq_decode_attention(&p, &cf, dummy, idummy, NULL, 0.1f, 0, dummy,
+                                         (char*)wsbuf + 8, 1ull << 40, NULL) == KVQ_ERR_WORKSPACE;
+    }
     hostile_ok &= kvq_probe_read(NULL, 16, dummy, NULL) < 0 && kvq_probe_read(dummy, 15, dummy, NULL) < 0;
     hostile_ok &= kvq_probe_copy(dummy, NULL, 16, NULL) < 0 && kvq_probe_copy(dummy, dummy, 0, NULL) < 0;
     hostile_ok &= strcmp(kvq_status_string(-12345), "unknown status") == 0;

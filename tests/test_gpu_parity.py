@@ -120,12 +120,13 @@ def test_decode_deterministic(small):
     assert np.array_equal(a, b)
 
 
-@pytest.mark.parametrize("name", ["c2_small", "fp4_small", "tiered_small"])
+@pytest.mark.parametrize("name", ["c2_small", "fp4_small", "tiered_small", "int4_small", "int3_small"])
 def test_decode_workspace_contents_do_not_matter(name):
-    """Lists cut between workgroups are merged by the last workgroup to finish a part, counted on
-    arrival words in the workspace that carry a per-call tag: whatever the workspace holds
-    (random bytes, or the words of earlier calls with another split), the result is the same,
-    bit for bit."""
+    """Lists cut between workgroups are merged by the last workgroup to finish a part (MFMA
+    decoder), counted on arrival words in the workspace that carry a per-call tag; split-K chunks
+    of the generic decoder are merged by a second kernel: whatever the workspace holds (random
+    bytes, or the words of earlier calls with another split), the result is the same, bit for
+    bit."""
     import decode_attention_sub_amd as K
     w = SMALL[name]
     dc = WD.build(w)
@@ -256,6 +257,7 @@ def test_invalid_seq_len_reports_status(name):
             got = run_decode(dcb, split_chunk=split)
             assert dc.cache.status() == K.KVQ_ERR_INVALID_ARG
             dc.cache.tensors["status"].zero_()
+            assert np.isnan(got[0]).all(), "the rejected sequence's output was written"
             assert np.allclose(got[1:], good[1:], rtol=1e-4, atol=1e-5)
 
 
