@@ -75,11 +75,13 @@ constexpr int kSegPages = 1024;
 // workgroups whose ranges cover many short lists take fewer steps.
 template <bool PAGED> constexpr int kPieceSteps = PAGED ? 48 : 16;
 constexpr uint32_t kDead = 0xFFFFFFFFu;    // no page: its rows read as zeros
-// Fused append: the work of appending a list's new token in units of one step (about the VALU
-// work of the row fits: eight Lloyd iterations for 2-bit rows, one pass for FP4 rows), counted
-// with the list's fixed cost after its steps, so that the workgroup holding the list's last step
-// takes that many fewer steps.
-template <int FMT> constexpr int kAppSteps = FMT == FMT_C2 ? 11 : 3;
+// Fused append: the cost of appending a list's new token in units of one step, counted with the
+// list's fixed cost after its steps, so that the workgroup holding the list's last step takes
+// that many fewer steps.  The appending wave's fits (eight Lloyd iterations for 2-bit rows, one
+// pass for FP4 rows) and their dependent loads hold the workgroup back by far more than their
+// VALU work: the weights are measured (2-bit: 64 against 11, 32, 96 and 128, on 128 lists of
+// 8192 tokens; FP4: 48 against 3 and 96, on 32 lists of 131072 tokens).
+template <int FMT> constexpr int kAppSteps = FMT == FMT_C2 ? 64 : 48;
 
 template <int FMT> struct Buf;
 template <> struct Buf<FMT_C2> { uint4 kc, vc; uint2 km, vm; };
