@@ -161,3 +161,50 @@ def test_fused_rejects_unsupported_caches():
     with pytest.raises(K.KvqError) as e:
         K.kvq_append_decode(dc.params, dc.cache, k, k, dc.q, dc.seq_lens, out)
     assert e.value.status == K.KVQ_ERR_UNSUPPORTED
+
+
+FULL = ["c2_b16_s8k", "c2_b64_s32k", "fp4_b4_s128k"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_fused_full_size_sampled(name):
+    """The fused call at the workload's full size (the launch bench.py --fused times): the new
+    rows and the tail of sampled lists bit for bit, and the sampled (sequence, KV head) pairs'
+    attention within the bar of the oracle over the cache's bytes."""
+    w = CONFIGS[name]
+    log(f"[gpu] fused full-size {name}: building the cache")
+    dc = WD.build(w)
+    assert dc.cache.status() == 0
+    kh, vh = new_rows(w, 99)
+    lens_t = dc.seq_lens
+    log(f"[gpu] fused full-size {name}: append + decode")
+    got = run_fused(dc, dc.cache, torch.from_numpy(kh).cuda(), torch.from_numpy(vh).cuda(), lens_t,
+                    w.split_chunk)
+    assert dc.cache.status() == 0
+    assert np.all(np.isfinite(got))
+    lens = dc.seq_lens_host
+    rng = np.random.default_rng(4321)
+    pairs = {(w.B - 1, w.H - 1), (int(rng.integers(w.B)), int(rng.integers(w.H)))}
+    sm = 1.0 / math.sqrt(w.D)
+    G_ = w.Hq // w.H
+    for b, h in sorted(pairs):
+        S = int(lens[b])
+        ta = max(0, (S - 160) // 16 * 16)
+        for kv in (0, 1):
+            x = G.kv_rows(w, b, h, kv, ta, S)
+            x[-1] = (kh if kv == 0 else vh)[b, h]
+            spec, _ = specs(w, h, kv)
+            ref = OC.build_list(x, spec)
+            dev = read_list(dc, b, h, kv)
+            what = f"{name} b={b} h={h} kv={kv} rows {ta}..{S}"
+            assert np.array_equal(dev["packed"][ta:S], ref.packed), what + ": codes"
+            assert np.array_equal(dev["meta"][ta:S], ref.meta), what + ": metadata"
+            tok = dev["idx"].astype(np.int64) >> 7
+            sel = (tok >= ta) & (tok < S)
+            assert np.array_equal(dev["idx"][sel].astype(np.int64) - ta * w.D, ref.idx.astype(np.int64)), \
+                what + ": outlier indices"
+            assert np.array_equal(dev["vals"][sel], ref.vals), what + ": outlier values"
+        log(f"[gpu] fused full-size {name}: oracle attention b={b} h={h} S={S}")
+        for hq, o in oracle_attention(dc, b, range(h * G_, (h + 1) * G_), sm).items():
+            err = np.abs(got[b, hq] - o).max()
+            assert err <= ATOL, f"{name} b={b} hq={hq}: max-abs {err}"
